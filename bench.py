@@ -1,0 +1,382 @@
+"""Benchmark of the fused gated group-RMSNorm on one MI355X.
+
+A step is one launch of the fused kernel over the 8192 x 7680 bf16 prefill
+batch (group size 960, intermediate cast on): every stage of the op (widen,
+silu gate, group sum of squares, normaliser, optional intermediate cast,
+weight multiply, narrow and store) runs inside it.  Inputs are resident in
+HBM before timing; several copies of them are rotated so no step finds its
+inputs in the 256 MB last-level cache.
+
+Printed (one JSON line): whole-job HBM throughput in GB/s over the timed
+steps, the kernel's roofline figures (event-timed average launch), the
+decode latency (1 x 7680, 21 layers back to back, eager and graph-replayed,
+next to an empty kernel of the same grid), and the CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|copy]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (fraction of peak) at 8192x7680 bf16; µs/launch at 1x7680 decode"
+PEAK_HBM_GBS = 8000.0
+PREFILL = "mamba2_prefill_8192x7680_bf16_g960"
+DECODE = "mamba2_decode_1x7680_bf16_g960"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_8192x7680_bf16.json")
+KERNEL_SOURCES = ["gated_group_rmsnorm_amd/csrc/kernels.cuh", "gated_group_rmsnorm_amd/csrc/table_bf16.hip"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads"], default=None)
+    ap.add_argument("--decode-bursts", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shape", default=None, help="force a kernel shape 'lanes,vectors'")
+    return ap.parse_args()
+
+
+class Setup:
+    """Device copies of a workload's inputs (several rotating sets) and outputs."""
+
+    def __init__(self, torch, S, w, sets: int, layer: int = 0):
+        import numpy as np
+
+        self.w = w
+        tdt = {S.F32: torch.float32, S.F16: torch.float16, S.BF16: torch.bfloat16}[w.dtype]
+        ybuf, gbuf, wt, lay = S.make_inputs(w, layer)
+        self.lay = lay
+
+        def dev(a):
+            t = torch.from_numpy(a.view(np.int16) if w.dtype != S.F32 else a)
+            return (t.view(tdt) if w.dtype != S.F32 else t).cuda()
+
+        self.weight = torch.from_numpy(wt).cuda()
+        base_y = dev(ybuf)
+        base_g = base_y if w.fused_width else dev(gbuf)
+        self.sets = []
+        for i in range(sets):
+            yb = base_y if i == 0 else base_y.clone()
+            gb = yb if w.fused_width else (base_g if i == 0 else base_g.clone())
+            out = torch.empty(w.rows * w.width, dtype=tdt, device="cuda")
+            self.sets.append((yb[lay["y_offset"]:], gb[lay["gate_offset"]:], out))
+        torch.cuda.synchronize()
+
+    def launch(self, g, i, stream, shape=None):
+        w, lay = self.w, self.lay
+        y, gt, out = self.sets[i % len(self.sets)]
+        args = (y.data_ptr(), gt.data_ptr(), self.weight.data_ptr(), out.data_ptr(), w.rows,
+                w.width, w.group_size, lay["y_row_stride"], lay["gate_row_stride"], w.width,
+                w.eps, w.dtype, w.round_intermediate)
+        if shape:
+            st = g.ggrms_forward_with_shape(*args, shape[0], shape[1], stream)
+        else:
+            st = g.ggrms_forward(*args, stream)
+        if st != 0:
+            raise RuntimeError(f"ggrms_forward: {g.ggrms_status_string(st)}")
+
+
+def time_kernel(torch, g, setup, steps, warmup, shape=None):
+    """Whole-job wall time over `steps` launches plus per-launch HIP events on
+    the launch stream.  Returns (wall_s, [kernel_ms])."""
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for i in range(warmup):
+        setup.launch(g, i, sp, shape)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        setup.launch(g, i, sp, shape)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def bench_prefill(torch, g, S, args, shape):
+    w = S.WORKLOADS[PREFILL]
+    nbytes = w.algorithmic_bytes()
+    sets = max(2, math.ceil(3 * 256e6 / nbytes))  # > 3x the 256 MB Infinity Cache per rotation
+    log(f"prefill: generating {w.name}, {sets} rotating input sets")
+    setup = Setup(torch, S, w, sets)
+    wall, kms = time_kernel(torch, g, setup, args.steps, args.warmup, shape)
+    st, plan = g.ggrms_plan(setup.sets[0][0].data_ptr(), setup.sets[0][1].data_ptr(),
+                            setup.weight.data_ptr(), setup.sets[0][2].data_ptr(), w.rows, w.width,
+                            w.group_size, w.width, w.width, w.width, w.eps, w.dtype,
+                            w.round_intermediate)
+    avg_ms = statistics.fmean(kms)
+    res = {
+        "workload": w,
+        "bytes": nbytes,
+        "wall_s": wall,
+        "kernel_ms_avg": avg_ms,
+        "kernel_ms_median": statistics.median(kms),
+        "kernel_ms_min": min(kms),
+        "plan": plan,
+        "sets": sets,
+    }
+    log(f"prefill: wall {wall * 1e3 / args.steps:.2f} ms/step, kernel avg {avg_ms * 1e3:.2f} us "
+        f"(median {res['kernel_ms_median'] * 1e3:.2f}, min {min(kms) * 1e3:.2f}), "
+        f"{nbytes / (avg_ms * 1e-3) / 1e9:.0f} GB/s")
+    return res
+
+
+def bench_decode(torch, g, S, bursts):
+    """21 back-to-back launches (distinct layer inputs) per burst, timed with
+    events around each burst; eager and as one replayed HIP graph; next to an
+    empty kernel launched with the same grid the same ways."""
+    w = S.WORKLOADS[DECODE]
+    L = S.DECODE_LAYERS
+    layers = [Setup(torch, S, w, 1, layer) for layer in range(L)]
+    aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
+    aux.ggrms_bench_empty.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    s0 = layers[0].sets[0]
+    st, plan = g.ggrms_plan(s0[0].data_ptr(), s0[1].data_ptr(), layers[0].weight.data_ptr(),
+                            s0[2].data_ptr(), w.rows, w.width, w.group_size, w.width, w.width,
+                            w.width, w.eps, w.dtype, w.round_intermediate)
+    blocks, threads = plan["workgroups"], plan["block_threads"]
+
+    def fused_burst(stream):
+        for ly in layers:
+            ly.launch(g, 0, stream)
+
+    def empty_burst(stream):
+        for _ in range(L):
+            if aux.ggrms_bench_empty(blocks, threads, stream) != 0:
+                raise RuntimeError("empty kernel launch failed")
+
+    def timed(burst_fn):
+        stream = torch.cuda.current_stream()
+        sp = stream.cuda_stream
+        for _ in range(10):
+            burst_fn(sp)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(bursts)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            burst_fn(sp)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3 / L
+
+    def graphed(burst_fn):
+        cs = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cs):
+            burst_fn(cs.cuda_stream)
+        stream = torch.cuda.current_stream()
+        for _ in range(10):
+            graph.replay()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(bursts)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3 / L
+
+    res = {
+        "workload": w.name,
+        "layers": L,
+        "bursts": bursts,
+        "us_per_launch_eager": timed(fused_burst),
+        "floor_us_per_launch_eager": timed(empty_burst),
+        "us_per_launch_graph": graphed(fused_burst),
+        "floor_us_per_launch_graph": graphed(empty_burst),
+        "grid": [blocks, threads],
+    }
+    log(f"decode: {json.dumps(res)}")
+    return res
+
+
+def bench_copy(torch, steps):
+    """The plain 16-byte copy used to calibrate the traffic counters."""
+    aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
+    aux.ggrms_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p]
+    nbytes = 256 << 20
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    sp = torch.cuda.current_stream().cuda_stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        if aux.ggrms_bench_copy(src.data_ptr(), dst.data_ptr(), nbytes, sp) != 0:
+            raise RuntimeError("copy launch failed")
+        b.record()
+    torch.cuda.synchronize()
+    ms = statistics.fmean(a.elapsed_time(b) for a, b in ev)
+    log(f"copy: {nbytes} B read + {nbytes} B written per launch, {ms * 1e3:.1f} us, "
+        f"{2 * nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "kernel_ms_avg": ms}
+
+
+def bench_workloads(torch, g, S, steps):
+    """Kernel time of the other configured workloads (reported beside the headline)."""
+    out = {}
+    for name in ("strided_256x4800_f16_g100", "gdn_head_16384x8192_f16_g128"):
+        w = S.WORKLOADS[name]
+        sets = max(2, math.ceil(3 * 256e6 / w.algorithmic_bytes()))
+        setup = Setup(torch, S, w, min(sets, 64))
+        _, kms = time_kernel(torch, g, setup, steps, 5)
+        avg = statistics.fmean(kms)
+        out[name] = {"kernel_us_avg": avg * 1e3,
+                     "gbs": w.algorithmic_bytes() / (avg * 1e-3) / 1e9,
+                     "frac_of_peak": w.algorithmic_bytes() / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "rows_per_s": w.rows / (avg * 1e-3)}
+        del setup
+        torch.cuda.empty_cache()
+    log(f"workloads: {json.dumps(out)}")
+    return out
+
+
+def cpu_baseline(S, seconds):
+    """The oracle, single-threaded, on leading rows of the prefill workload,
+    repeated for about `seconds` of CPU time."""
+    import numpy as np
+
+    import oracle
+
+    w = S.WORKLOADS[PREFILL]
+    rows = 256
+    y, gt = S.make_rows(w, np.arange(rows))
+    wt = S.make_weight(w)
+    y, gt = y.reshape(-1), gt.reshape(-1)
+    sample_bytes = 3 * rows * w.width * w.esize + 4 * w.width
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(y, gt, wt, rows=rows, width=w.width, group_size=w.group_size,
+                       y_row_stride=w.width, gate_row_stride=w.width, out_row_stride=w.width,
+                       eps=w.eps, dtype=w.dtype, round_intermediate=w.round_intermediate)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = reps * sample_bytes / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of the 8192 rows of {w.name}, {reps} passes in {el:.1f} s "
+                      f"(single-threaded C, one host core)",
+            "rows_per_s": round(reps * rows / el, 1)}
+
+
+def traffic_figure(launch_bytes):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    (scaled by the copy-kernel calibration); None if the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the fused "
+              "norm has no cross-GPU step (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    import gated_group_rmsnorm_amd as g
+    import synthetic as S
+
+    S.build(force=False)
+    shape = tuple(int(v) for v in args.shape.split(",")) if args.shape else None
+
+    if args.only == "copy":
+        bench_copy(torch, args.steps)
+        return
+    if args.only == "decode":
+        bench_decode(torch, g, S, args.decode_bursts)
+        return
+    if args.only == "workloads":
+        bench_workloads(torch, g, S, args.steps)
+        return
+
+    pre = bench_prefill(torch, g, S, args, shape)
+    if args.only == "prefill":
+        return
+    decode = bench_decode(torch, g, S, args.decode_bursts)
+    others = bench_workloads(torch, g, S, max(20, args.steps // 4))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(S, args.cpu_seconds)
+
+    w = pre["workload"]
+    nbytes = pre["bytes"]
+    value = args.steps * nbytes / pre["wall_s"] / 1e9
+    achieved = nbytes / (pre["kernel_ms_avg"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["wall_s"] * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded counter-based N(0, sigma=2) y and gate, U(0.5,1.5) f32 weight",
+        "config": {"workload": w.name, "rows": w.rows, "width": w.width,
+                   "group_size": w.group_size, "eps": w.eps,
+                   "round_intermediate": w.round_intermediate,
+                   "rotating_input_sets": pre["sets"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_figure(nbytes),
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "kernel_us_avg": round(pre["kernel_ms_avg"] * 1e3, 2),
+                     "kernel_us_median": round(pre["kernel_ms_median"] * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "decode": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in decode.items()},
+        "other_workloads": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in others.items()},
+        "kernel": pre["plan"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+"""Fused gated group-RMSNorm for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libggrms.so`` (C ABI in ``include/ggrms.h``).
+Every step of the computation runs in the library's HIP kernels; this
+module only marshals arguments.  PyTorch supplies device memory and the
+current stream.  There is no fallback: if the library is missing, importing
+the binding raises.
+
+The operation, per row n and group g of ``group_size`` contiguous columns
+(page "gated_group_rmsnorm", math block)::
+
+    gated = f32(y) * silu(f32(gate))
+    nf    = rsqrt(sum(gated^2) / group_size + eps)
+    out   = cast(f32(w) * f32(cast(gated * nf, dtype)), dtype)   # round_intermediate
+    out   = cast(f32(w) * (gated * nf), dtype)                   # otherwise
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "F32", "F16", "BF16", "SUCCESS", "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED",
+    "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError", "ggrms_forward", "ggrms_forward_with_shape",
+    "ggrms_plan",
+    "ggrms_status_string", "ggrms_abi_version", "forward", "plan", "expand_head_scale",
+    "library_path",
+]
+
+F32, F16, BF16 = 0, 1, 2
+SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
+KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libggrms.so")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+class GgrmsError(RuntimeError):
+    def __init__(self, status: int, what: str = "ggrms_forward"):
+        self.status = status
+        super().__init__(f"{what}: {ggrms_status_string(status)} (status {status})")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("vector_bytes", ctypes.c_int32),
+                ("lanes_per_group", ctypes.c_int32), ("vectors_per_lane", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("workgroups", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m gated_group_rmsnorm_amd._build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    fwd = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32]
+    L.ggrms_forward.argtypes = fwd + [vp]
+    L.ggrms_forward.restype = i32
+    L.ggrms_forward_with_shape.argtypes = fwd + [i32, i32, vp]
+    L.ggrms_forward_with_shape.restype = i32
+    L.ggrms_plan.argtypes = fwd + [ctypes.POINTER(_Plan)]
+    L.ggrms_plan.restype = i32
+    L.ggrms_status_string.argtypes = [i32]
+    L.ggrms_status_string.restype = ctypes.c_char_p
+    L.ggrms_abi_version.argtypes = []
+    L.ggrms_abi_version.restype = i32
+    return L
+
+
+_lib = _load()
+
+
+# ----------------------------------------------------------- raw C calls
+
+def ggrms_forward(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
+                  group_size: int, y_row_stride: int, gate_row_stride: int,
+                  out_row_stride: int, eps: float, dtype: int, round_intermediate: int,
+                  stream: int) -> int:
+    """The C entry point with device pointers as integers; returns the status."""
+    return _lib.ggrms_forward(y, gate, norm_weight, out, rows, width, group_size,
+                              y_row_stride, gate_row_stride, out_row_stride, eps, dtype,
+                              round_intermediate, stream)
+
+
+def ggrms_forward_with_shape(y: int, gate: int, norm_weight: int, out: int, rows: int,
+                             width: int, group_size: int, y_row_stride: int,
+                             gate_row_stride: int, out_row_stride: int, eps: float, dtype: int,
+                             round_intermediate: int, lanes_per_group: int,
+                             vectors_per_lane: int, stream: int) -> int:
+    """ggrms_forward with a caller-chosen kernel shape; returns the status."""
+    return _lib.ggrms_forward_with_shape(y, gate, norm_weight, out, rows, width, group_size,
+                                         y_row_stride, gate_row_stride, out_row_stride, eps,
+                                         dtype, round_intermediate, lanes_per_group,
+                                         vectors_per_lane, stream)
+
+
+def ggrms_plan(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
+               group_size: int, y_row_stride: int, gate_row_stride: int, out_row_stride: int,
+               eps: float, dtype: int, round_intermediate: int):
+    """(status, plan dict or None) -- the kernel ggrms_forward would launch; no device call."""
+    p = _Plan()
+    st = _lib.ggrms_plan(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                         gate_row_stride, out_row_stride, eps, dtype, round_intermediate,
+                         ctypes.byref(p))
+    if st != SUCCESS:
+        return st, None
+    d = {f: getattr(p, f) for f, _ in _Plan._fields_}
+    d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
+    return st, d
+
+
+def ggrms_status_string(status: int) -> str:
+    return _lib.ggrms_status_string(status).decode()
+
+
+def ggrms_abi_version() -> int:
+    return _lib.ggrms_abi_version()
+
+
+# ----------------------------------------------------------- torch level
+
+def _torch_dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def _as_rows(t, name: str):
+    """View t (..., width) as rows with one row stride; returns (rows, row_stride)."""
+    if t.dim() < 1:
+        raise ValueError(f"{name} needs at least one dimension")
+    if t.stride(-1) != 1 and t.size(-1) > 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+    width = t.size(-1)
+    rows = t.numel() // width if width else 0
+    if t.dim() == 1:
+        return rows, width
+    # leading axes must fold into a single row stride
+    lead = [(s, st) for s, st in zip(t.shape[:-1], t.stride()[:-1]) if s != 1]
+    if not lead:
+        return rows, max(width, t.stride(-2))
+    row_stride = lead[-1][1]
+    expect = row_stride
+    for s, st in reversed(lead):
+        if st != expect:
+            raise ValueError(f"{name}'s leading axes do not fold into one row stride")
+        expect = st * s
+    return rows, row_stride
+
+
+def expand_head_scale(scale, heads: int):
+    """A per-head scale of C elements shared by every head (any float dtype,
+    shaped (C), (1, C) or (C, 1)) as the f32 per-column weight of heads*C
+    columns.  The widening is exact; call once per weight, not per step."""
+    s = scale.reshape(-1).float()
+    return s.repeat(heads).contiguous()
+
+
+def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
+            round_intermediate: bool = True, out=None, stream=None):
+    """out = fused gated group-RMSNorm of (y, gate) with the f32 per-column
+    ``weight`` over groups of ``group_size`` columns of the last axis.
+
+    y and gate: same shape (..., width), same dtype (f32/f16/bf16), on the
+    GPU, unit stride in the last axis (they may be strided column slices of
+    one fused buffer).  out (optional) must match y's shape and dtype; it is
+    allocated like y when omitted.  Enqueued on ``stream`` (default: torch's
+    current stream); no synchronisation.
+    """
+    import torch
+
+    if y.shape != gate.shape:
+        raise ValueError(f"y {tuple(y.shape)} and gate {tuple(gate.shape)} differ in shape")
+    if y.dtype != gate.dtype:
+        raise TypeError("y and gate must share a dtype")
+    code = _torch_dtype_code(y)
+    width = y.size(-1)
+    if weight.dtype != torch.float32 or weight.numel() != width or weight.dim() != 1:
+        raise TypeError("weight must be a 1-D float32 tensor with width elements "
+                        "(expand_head_scale builds one from a per-head scale)")
+    if not weight.is_contiguous():
+        raise ValueError("weight must be contiguous")
+    if out is None:
+        out = torch.empty(y.shape, dtype=y.dtype, device=y.device)
+    elif out.shape != y.shape or out.dtype != y.dtype:
+        raise ValueError("out must have y's shape and dtype")
+    if not (y.is_cuda and gate.is_cuda and weight.is_cuda and out.is_cuda):
+        raise ValueError("all tensors must be on the GPU")
+    rows, sy = _as_rows(y, "y")
+    _, sg = _as_rows(gate, "gate")
+    _, so = _as_rows(out, "out")
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    with torch.cuda.device(y.device):
+        st = ggrms_forward(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), out.data_ptr(),
+                           rows, width, group_size, sy, sg, so, float(eps), code,
+                           int(bool(round_intermediate)), stream)
+    if st != SUCCESS:
+        raise GgrmsError(st)
+    return out
+
+
+def plan(y, gate, weight, group_size: int, eps: float = 1e-5, round_intermediate: bool = True,
+         out=None) -> dict:
+    """The kernel forward() would launch for these tensors (no device call)."""
+    code = _torch_dtype_code(y)
+    width = y.size(-1)
+    rows, sy = _as_rows(y, "y")
+    _, sg = _as_rows(gate, "gate")
+    o = out if out is not None else y.new_empty(y.shape)
+    _, so = _as_rows(o, "out")
+    st, p = ggrms_plan(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), o.data_ptr(), rows,
+                       width, group_size, sy, sg, so, float(eps), code,
+                       int(bool(round_intermediate)))
+    if st != SUCCESS:
+        raise GgrmsError(st, "ggrms_plan")
+    return p

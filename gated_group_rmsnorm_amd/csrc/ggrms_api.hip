@@ -1,0 +1,119 @@
+// ggrms_api.hip -- ggrms_forward: checks, device check, kernel launches.
+//
+// The host side is deliberately thin: make_plan (plan.cpp) validates and
+// picks the kernel shape without touching the device; this file confirms the
+// current device is gfx950 (cached per device), fills the kernel arguments
+// and enqueues one launch per row chunk on the caller's stream.  No
+// allocation, no synchronisation, nothing that would break stream capture
+// after the first call on a device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "ggrms.h"
+#include "ggrms_internal.h"
+
+namespace ggrms {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool device_is_gfx950() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    int st = dev < kMaxDevices ? g_device_state[dev].load(std::memory_order_acquire) : 0;
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return false;
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (dev < kMaxDevices) g_device_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1;
+}
+
+const void* pick(int dtype, int kernel, int vb, int lanes, int vpt) {
+    switch (dtype) {
+    case GGRMS_F32: return pick_f32(kernel, vb, lanes, vpt);
+    case GGRMS_F16: return pick_f16(kernel, vb, lanes, vpt);
+    case GGRMS_BF16: return pick_bf16(kernel, vb, lanes, vpt);
+    default: return nullptr;
+    }
+}
+
+ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_weight, void* out,
+                            int64_t rows, int64_t width, int64_t group_size, int64_t y_row_stride,
+                            int64_t gate_row_stride, int64_t out_row_stride, float eps,
+                            ggrms_dtype_t dtype, int round_intermediate, int force_lanes,
+                            int force_vpt, void* stream) {
+    LaunchPlan lp;
+    ggrms_status_t st = make_plan(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                                  gate_row_stride, out_row_stride, eps, (int)dtype,
+                                  round_intermediate, force_lanes, force_vpt, &lp);
+    if (st != GGRMS_SUCCESS || lp.pub.kernel == GGRMS_KERNEL_NONE) return st;
+    if (!device_is_gfx950()) return GGRMS_ERROR_NOT_SUPPORTED;
+
+    const ggrms_plan_t& p = lp.pub;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const void* fn = pick((int)dtype, p.kernel, p.vector_bytes, p.lanes_per_group,
+                          p.vectors_per_lane);
+    if (!fn) return GGRMS_ERROR_NOT_SUPPORTED;
+
+    if (rows == 1) y_row_stride = gate_row_stride = out_row_stride = width;
+    KArgs a;
+    a.w = norm_weight;
+    a.sy = y_row_stride;
+    a.sg = gate_row_stride;
+    a.so = out_row_stride;
+    a.groups = (uint32_t)lp.groups;
+    div_magic(a.groups, &a.div_m, &a.div_s);
+    a.G = (uint32_t)group_size;
+    a.nvec = (uint32_t)lp.nvec;
+    a.Gf = (float)group_size;
+    a.eps = eps;
+    a.ri = dtype == GGRMS_F32 ? 0 : round_intermediate;
+    const int es = lp.esize;
+    const int64_t thread_per_unit = p.kernel == GGRMS_KERNEL_WIDE ? kWideBlock : p.lanes_per_group;
+
+    for (int64_t r0 = 0; r0 < rows; r0 += lp.rows_per_launch) {
+        const int64_t r = rows - r0 < lp.rows_per_launch ? rows - r0 : lp.rows_per_launch;
+        a.y = static_cast<const char*>(y) + r0 * y_row_stride * es;
+        a.gate = static_cast<const char*>(gate) + r0 * gate_row_stride * es;
+        a.out = static_cast<char*>(out) + r0 * out_row_stride * es;
+        a.units = (uint32_t)(r * lp.groups);
+        const int64_t blocks = ((int64_t)a.units * thread_per_unit + p.block_threads - 1) /
+                               p.block_threads;
+        void* args[] = {&a};
+        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3((uint32_t)p.block_threads), args, 0,
+                            s) != hipSuccess)
+            return GGRMS_ERROR_LAUNCH;
+    }
+    return GGRMS_SUCCESS;
+}
+
+}  // namespace
+}  // namespace ggrms
+
+extern "C" ggrms_status_t ggrms_forward(const void* y, const void* gate,
+                                        const float* norm_weight, void* out, int64_t rows,
+                                        int64_t width, int64_t group_size, int64_t y_row_stride,
+                                        int64_t gate_row_stride, int64_t out_row_stride,
+                                        float eps, ggrms_dtype_t dtype, int round_intermediate,
+                                        void* stream) {
+    return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                               gate_row_stride, out_row_stride, eps, dtype, round_intermediate, 0,
+                               0, stream);
+}
+
+extern "C" ggrms_status_t ggrms_forward_with_shape(
+    const void* y, const void* gate, const float* norm_weight, void* out, int64_t rows,
+    int64_t width, int64_t group_size, int64_t y_row_stride, int64_t gate_row_stride,
+    int64_t out_row_stride, float eps, ggrms_dtype_t dtype, int round_intermediate,
+    int lanes_per_group, int vectors_per_lane, void* stream) {
+    if (lanes_per_group == 0 && vectors_per_lane == 0) return GGRMS_ERROR_INVALID_VALUE;
+    return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                               gate_row_stride, out_row_stride, eps, dtype, round_intermediate,
+                               lanes_per_group, vectors_per_lane, stream);
+}

@@ -1,0 +1,82 @@
+// ggrms_internal.h -- declarations shared by the host planner, the kernel
+// tables and the launcher of libggrms.  Not installed; not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "ggrms.h"
+
+namespace ggrms {
+
+// Kernel arguments, passed by value.  Pointers already include the row
+// offset of the launch chunk.  Strides are in elements.
+struct KArgs {
+    const void* y;
+    const void* gate;
+    const float* w;
+    void* out;
+    int64_t sy, sg, so;
+    uint32_t units;   // (row, group) units in this launch
+    uint32_t groups;  // groups per row
+    uint32_t div_m;   // magic multiplier for unit / groups
+    uint32_t div_s;   // shift for unit / groups
+    uint32_t G;       // group size in elements
+    uint32_t nvec;    // vectors per group
+    float Gf;         // (float)G
+    float eps;
+    int32_t ri;       // round the intermediate (16-bit types only)
+};
+
+// Supported shapes.  WAVE: lanes in {1..64} (powers of two); vectors per lane
+// 1 for lanes < 64, 1..4 for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
+// vectors per lane in {1,2,4}.  WIDE: 1024 lanes, vectors per lane 0 (it
+// loops over the group).
+constexpr int kWaveBlock = 256;
+constexpr int kWideBlock = 1024;
+constexpr int kMaxBlockLanes = 1024;
+constexpr int kMaxWaveVpt = 4;
+
+inline bool shape_supported(int kernel, int lanes, int vpt) {
+    switch (kernel) {
+    case GGRMS_KERNEL_WAVE:
+        if (lanes == 64) return vpt >= 1 && vpt <= 4;
+        return (lanes == 1 || lanes == 2 || lanes == 4 || lanes == 8 || lanes == 16 ||
+                lanes == 32) &&
+               vpt == 1;
+    case GGRMS_KERNEL_BLOCK:
+        return (lanes == 128 || lanes == 256 || lanes == 512 || lanes == 1024) &&
+               (vpt == 1 || vpt == 2 || vpt == 4);
+    case GGRMS_KERNEL_WIDE:
+        return lanes == kWideBlock;
+    default:
+        return false;
+    }
+}
+
+// Full launch plan: the public plan plus what the launcher needs.
+struct LaunchPlan {
+    ggrms_plan_t pub;
+    int esize;
+    int64_t groups;
+    int64_t nvec;
+    int64_t rows_per_launch;  // rows handled by each launch (the last one may have fewer)
+};
+
+// Validation and kernel choice; no HIP calls.  Implemented in plan.cpp.
+// force_lanes / force_vpt = 0 / 0 picks the shape; otherwise that shape is
+// used if it is built and covers the group (GGRMS_ERROR_NOT_SUPPORTED if not).
+ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const void* out,
+                         int64_t rows, int64_t width, int64_t group_size, int64_t sy,
+                         int64_t sg, int64_t so, float eps, int dtype, int ri,
+                         int force_lanes, int force_vpt, LaunchPlan* plan);
+
+// Magic numbers for n / d with n < 2^31 and 1 <= d < 2^31:
+// q = (umulhi(n, m) + n) >> s.
+void div_magic(uint32_t d, uint32_t* m, uint32_t* s);
+
+// Kernel lookup per dtype (kernel tables); nullptr if the shape is not built.
+const void* pick_f32(int kernel, int vb, int lanes, int vpt);
+const void* pick_f16(int kernel, int vb, int lanes, int vpt);
+const void* pick_bf16(int kernel, int vb, int lanes, int vpt);
+
+}  // namespace ggrms

@@ -1,0 +1,454 @@
+// kernels.cuh -- gfx950 (CDNA4) device code of the fused gated group-RMSNorm.
+//
+// Per (row n, group g) unit of G contiguous columns, col = g*G + j (the page
+// "gated_group_rmsnorm", math block):
+//   a_j  = f32(y) * silu(f32(gate))                      (widen, gate)
+//   m2   = sum_j a_j^2                                    (group reduction, f32)
+//   nf   = rsqrt(m2 / G + eps)                            (eps after the mean)
+//   out  = cast(w[col] * f32(cast(a_j * nf, dtype)), dtype) with the inner cast
+//          only when round_intermediate is set.
+//
+// The op is HBM-bound (two 16-bit input streams and one output stream; a few
+// VALU ops per element), so the design is about moving bytes:
+//   * every y/gate/out access is a VB-byte vector (16 B when alignment allows),
+//     one vector per lane per step, so a wave instruction covers a contiguous
+//     64*VB-byte run;
+//   * a unit is read once into registers; its reduction happens in registers
+//     and the outputs are written from the same registers (single pass);
+//   * lanes past the end of a group re-load the group's last vector (an L1/L2
+//     hit, no extra HBM traffic) and contribute 0, so no load is predicated
+//     and all loads of a lane are issued before the first use;
+//   * the group sum uses DPP row operations inside 16-lane rows and
+//     v_readlane across rows: no LDS and no barrier unless a group spans
+//     several waves (BLOCK), where one LDS slot per wave and one barrier
+//     combine the partial sums;
+//   * every lane of a group ends with a bit-identical m2 (the same additions
+//     in the same order), so nf is uniform over the group and the result is
+//     deterministic run to run.
+// Nothing here uses MFMA: there is no contraction to feed it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "ggrms_internal.h"
+
+namespace ggrms {
+
+using u16 = unsigned short;
+using u32 = unsigned int;
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Element types.  kSize = bytes per element.
+struct TF32 { static constexpr int kSize = 4; };
+struct TF16 { static constexpr int kSize = 2; };
+struct TBF16 { static constexpr int kSize = 2; };
+
+// Storage word for a VB-byte vector.
+template <int VB> struct VecWord;
+template <> struct VecWord<16> { using type = u32x4; };
+template <> struct VecWord<8> { using type = u32x2; };
+template <> struct VecWord<4> { using type = u32; };
+template <> struct VecWord<2> { using type = u16; };
+
+// ------------------------------------------------------------ conversions
+// 16-bit -> f32 widening is exact.  f32 -> 16-bit narrowing uses the gfx950
+// conversion instructions (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), which round
+// to nearest even under the default mode and keep subnormals.
+
+template <class T> struct Cvt;
+
+template <> struct Cvt<TF32> {
+    static constexpr int kPerWord = 1;
+    __device__ static inline void unpack_word(u32 w, float* f) { f[0] = __uint_as_float(w); }
+    __device__ static inline u32 pack_word(const float* f) { return __float_as_uint(f[0]); }
+    __device__ static inline void round_trip(float*) {}
+};
+
+template <> struct Cvt<TBF16> {
+    static constexpr int kPerWord = 2;
+    __device__ static inline void unpack_word(u32 w, float* f) {
+        f[0] = __uint_as_float(w << 16);
+        f[1] = __uint_as_float(w & 0xFFFF0000u);
+    }
+    __device__ static inline u32 pack_word(const float* f) {
+        f32x2 v = {f[0], f[1]};
+        return __builtin_bit_cast(u32, __builtin_convertvector(v, bf16x2));
+    }
+    __device__ static inline float unpack_half(u16 h) { return __uint_as_float((u32)h << 16); }
+    __device__ static inline u16 pack_half(float f) {
+        return __builtin_bit_cast(u16, (__bf16)f);
+    }
+    __device__ static inline void round_trip(float* f) { unpack_word(pack_word(f), f); }
+};
+
+template <> struct Cvt<TF16> {
+    static constexpr int kPerWord = 2;
+    __device__ static inline void unpack_word(u32 w, float* f) {
+        f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+        f[0] = v.x;
+        f[1] = v.y;
+    }
+    __device__ static inline u32 pack_word(const float* f) {
+        f32x2 v = {f[0], f[1]};
+        return __builtin_bit_cast(u32, __builtin_convertvector(v, f16x2));
+    }
+    __device__ static inline float unpack_half(u16 h) {
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+    __device__ static inline u16 pack_half(float f) {
+        return __builtin_bit_cast(u16, (_Float16)f);
+    }
+    __device__ static inline void round_trip(float* f) { unpack_word(pack_word(f), f); }
+};
+
+// A VB-byte vector of T: N elements.
+template <class T, int VB> struct Packet {
+    static constexpr int N = VB / T::kSize;
+    using W = typename VecWord<VB>::type;
+
+    __device__ static inline void unpack(const W& v, float (&f)[N]) {
+        if constexpr (VB == 2) {
+            f[0] = Cvt<T>::unpack_half(v);
+        } else if constexpr (VB == 4) {
+            Cvt<T>::unpack_word(v, f);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VB / 4; ++i) Cvt<T>::unpack_word(v[i], f + i * Cvt<T>::kPerWord);
+        }
+    }
+
+    __device__ static inline W pack(const float (&f)[N]) {
+        if constexpr (VB == 2) {
+            return Cvt<T>::pack_half(f[0]);
+        } else if constexpr (VB == 4) {
+            return Cvt<T>::pack_word(f);
+        } else {
+            W v;
+#pragma unroll
+            for (int i = 0; i < VB / 4; ++i) v[i] = Cvt<T>::pack_word(f + i * Cvt<T>::kPerWord);
+            return v;
+        }
+    }
+
+    // cast to T and back, element-wise
+    __device__ static inline void round_trip(float (&f)[N]) {
+        if constexpr (VB == 2) {
+            f[0] = Cvt<T>::unpack_half(Cvt<T>::pack_half(f[0]));
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; i += Cvt<T>::kPerWord) Cvt<T>::round_trip(f + i);
+        }
+    }
+};
+
+// N consecutive f32 weights; p is aligned to min(16, 4N) bytes.
+template <int N> __device__ inline void load_weights(const float* p, float (&w)[N]) {
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
+            w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+        }
+    } else if constexpr (N == 2) {
+        f32x2 v = *reinterpret_cast<const f32x2*>(p);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        w[0] = p[0];
+    }
+}
+
+// ------------------------------------------------------------ arithmetic
+
+// silu(x) = x / (1 + e^-x): e^-x by v_exp_f32 (2^t with t = -x*log2 e), the
+// reciprocal by v_rcp_f32, five VALU operations.  The reciprocal is only
+// trusted while its result is a normal number, i.e. while 1 + e^-x < 2^126
+// (x > -87.33); below that it may flush to zero where the quotient is a tiny
+// non-zero number.  silu_exact scales both operands by 2^-64 once the
+// denominator passes 2^64, which keeps the reciprocal normal and changes no
+// bits elsewhere (power-of-two scalings are exact); kernels take it only when
+// some gate of the wave is below kSiluFastMin.
+constexpr float kSiluFastMin = -87.0f;
+
+__device__ inline float silu_fast(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ inline float silu_exact(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+    const float d = 1.0f + e;
+    const float sc = d > 0x1p64f ? 0x1p-64f : 1.0f;
+    return (x * sc) * __builtin_amdgcn_rcpf(d * sc);
+}
+
+// DPP move with all rows and banks enabled.
+template <int CTRL> __device__ inline float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ inline float readlane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned segments of SEG lanes (SEG a power of two, <= 64).  Every
+// lane of a segment gets the same bits.  Steps: swap neighbours, swap pairs
+// (quad_perm), mirror within 8 (row_half_mirror), mirror within 16
+// (row_mirror); then whole 16-lane rows are combined with v_readlane.
+template <int SEG> __device__ inline float segment_sum(float v) {
+    if constexpr (SEG >= 2) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (SEG >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (SEG >= 8) v += dpp<0x141>(v);  // row_half_mirror
+    if constexpr (SEG >= 16) v += dpp<0x140>(v); // row_mirror
+    if constexpr (SEG == 32) {
+        const float r0 = readlane(v, 0), r1 = readlane(v, 16);
+        const float r2 = readlane(v, 32), r3 = readlane(v, 48);
+        v = (threadIdx.x & 32) ? (r2 + r3) : (r0 + r1);
+    }
+    if constexpr (SEG == 64) {
+        const float r0 = readlane(v, 0), r1 = readlane(v, 16);
+        const float r2 = readlane(v, 32), r3 = readlane(v, 48);
+        v = (r0 + r1) + (r2 + r3);
+    }
+    return v;
+}
+
+__device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t s) {
+    return (__umulhi(n, m) + n) >> s;
+}
+
+// ------------------------------------------------------------ one unit
+
+// Lane `sl` of the SEG lanes that own `unit` loads VPT vectors (indices
+// sl, sl+SEG, ...), computes its share, reduces with `reduce`, and stores if
+// `store_ok`.
+template <class T, int VB, int SEG, int VPT, class Reduce>
+__device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t unit, uint32_t sl,
+                                          bool store_ok, Reduce reduce) {
+    using P = Packet<T, VB>;
+    using W = typename P::W;
+    constexpr int N = P::N;
+    using S = typename VecWord<T::kSize>::type;  // element storage
+
+    const uint32_t n = fast_div(unit, a.div_m, a.div_s);
+    const uint32_t g = unit - n * a.groups;
+    const int64_t col0 = (int64_t)g * a.G;
+    const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy + col0);
+    const W* gv =
+        reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + col0);
+    W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + col0);
+    const float* wp = a.w + col0;
+
+    W yr[VPT], gr[VPT];
+    float wr[VPT][N];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const uint32_t idx = sl + k * SEG;
+        const uint32_t ci = idx < a.nvec ? idx : a.nvec - 1;
+        yr[k] = yv[ci];
+        gr[k] = gv[ci];
+        load_weights<N>(wp + (int64_t)ci * N, wr[k]);
+    }
+
+    // a = y * silu(gate) for every loaded element; lanes past the group's end
+    // hold a copy of its last vector and their partial sum is dropped by one
+    // select per vector (no per-element predication).
+    float av[VPT][N];
+    float acc = 0.0f;
+    float gmin = __builtin_inff();
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        float yf[N], gf[N];
+        P::unpack(yr[k], yf);
+        P::unpack(gr[k], gf);
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            gmin = __builtin_fminf(gmin, gf[e]);
+            const float x = yf[e] * silu_fast(gf[e]);
+            av[k][e] = x;
+            part = __builtin_fmaf(x, x, part);
+        }
+        acc += (sl + k * SEG < a.nvec) ? part : 0.0f;
+    }
+    if (__builtin_expect(__any(gmin < kSiluFastMin), 0)) {
+        // Rare: a gate deep in silu's underflow range.  Redo the wave's
+        // elements with the exact form (identical bits for every other gate).
+        acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            float yf[N], gf[N];
+            P::unpack(yr[k], yf);
+            P::unpack(gr[k], gf);
+            float part = 0.0f;
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                const float x = yf[e] * silu_exact(gf[e]);
+                av[k][e] = x;
+                part = __builtin_fmaf(x, x, part);
+            }
+            acc += (sl + k * SEG < a.nvec) ? part : 0.0f;
+        }
+    }
+
+    const float m2 = reduce(acc);
+    const float nf = 1.0f / __builtin_sqrtf(m2 / a.Gf + a.eps);
+
+    auto finish = [&](auto ri_tag) {
+        constexpr bool RI = decltype(ri_tag)::value;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const uint32_t idx = sl + k * SEG;
+            if (store_ok && idx < a.nvec) {
+                float t[N];
+#pragma unroll
+                for (int e = 0; e < N; ++e) t[e] = av[k][e] * nf;
+                if constexpr (RI) P::round_trip(t);
+#pragma unroll
+                for (int e = 0; e < N; ++e) t[e] = wr[k][e] * t[e];
+                ov[idx] = P::pack(t);
+            }
+        }
+    };
+    if (a.ri)
+        finish(std::true_type{});
+    else
+        finish(std::false_type{});
+}
+
+// ------------------------------------------------------------ kernels
+
+// WAVE: SEG (<= 64) lanes per unit, 256-thread workgroups, no LDS, no barrier.
+template <class T, int VB, int SEG, int VPT>
+__global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
+    const uint32_t t = blockIdx.x * (uint32_t)kWaveBlock + threadIdx.x;
+    const uint32_t unit = t / SEG;
+    if (unit >= a.units) return;  // whole segments leave together
+    unit_pass<T, VB, SEG, VPT>(a, unit, threadIdx.x & (SEG - 1), true,
+                               [](float v) { return segment_sum<SEG>(v); });
+}
+
+// BLOCK: a unit spans SEG/64 waves; the per-wave sums meet in LDS after one
+// barrier and every wave adds them in the same order.
+template <class T, int VB, int SEG, int VPT>
+__global__ __launch_bounds__(SEG > 256 ? SEG : 256) void ggrms_block_kernel(KArgs a) {
+    constexpr int BT = SEG > 256 ? SEG : 256;
+    constexpr int WPG = SEG / 64;
+    __shared__ float part[BT / 64];
+    const uint32_t t = blockIdx.x * (uint32_t)BT + threadIdx.x;
+    uint32_t unit = t / SEG;
+    const bool live = unit < a.units;
+    if (!live) unit = a.units - 1;  // stay in bounds and reach the barrier
+    const uint32_t wave = threadIdx.x >> 6;
+    const uint32_t first_wave = (threadIdx.x / SEG) * WPG;
+    unit_pass<T, VB, SEG, VPT>(a, unit, threadIdx.x & (SEG - 1), live, [&](float v) {
+        const float s = segment_sum<64>(v);
+        if ((threadIdx.x & 63) == 0) part[wave] = s;
+        __syncthreads();
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WPG; ++i) m += part[first_wave + i];
+        return m;
+    });
+}
+
+// WIDE: one 1024-thread workgroup per unit, for groups with more vectors than
+// the BLOCK shapes hold in registers.  Pass 1 reads the group and reduces;
+// pass 2 reads it again and writes (the only path that reads inputs twice).
+template <class T, int VB>
+__global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
+    using P = Packet<T, VB>;
+    using W = typename P::W;
+    constexpr int N = P::N;
+    using S = typename VecWord<T::kSize>::type;
+    __shared__ float part[kWideBlock / 64];
+
+    const uint32_t unit = blockIdx.x;
+    const uint32_t n = fast_div(unit, a.div_m, a.div_s);
+    const uint32_t g = unit - n * a.groups;
+    const int64_t col0 = (int64_t)g * a.G;
+    const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy + col0);
+    const W* gv =
+        reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + col0);
+    W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + col0);
+    const float* wp = a.w + col0;
+
+    float acc = 0.0f;
+    for (uint32_t i = threadIdx.x; i < a.nvec; i += kWideBlock) {
+        float yf[N], gf[N];
+        P::unpack(yv[i], yf);
+        P::unpack(gv[i], gf);
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+            const float x = yf[e] * silu_exact(gf[e]);
+            acc = __builtin_fmaf(x, x, acc);
+        }
+    }
+    const float s = segment_sum<64>(acc);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    float m2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWideBlock / 64; ++i) m2 += part[i];
+    const float nf = 1.0f / __builtin_sqrtf(m2 / a.Gf + a.eps);
+
+    for (uint32_t i = threadIdx.x; i < a.nvec; i += kWideBlock) {
+        float yf[N], gf[N], wv[N], t[N];
+        P::unpack(yv[i], yf);
+        P::unpack(gv[i], gf);
+        load_weights<N>(wp + (int64_t)i * N, wv);
+#pragma unroll
+        for (int e = 0; e < N; ++e) t[e] = yf[e] * silu_exact(gf[e]) * nf;
+        if (a.ri) P::round_trip(t);
+#pragma unroll
+        for (int e = 0; e < N; ++e) t[e] = wv[e] * t[e];
+        ov[i] = P::pack(t);
+    }
+}
+
+// ------------------------------------------------------------ table
+
+template <class T, int VB>
+inline const void* pick_vb(int kernel, int lanes, int vpt) {
+#define GG_W(L, V) \
+    if (lanes == L && vpt == V) return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, L, V>)
+#define GG_B(L, V) \
+    if (lanes == L && vpt == V) return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V>)
+    if (kernel == GGRMS_KERNEL_WAVE) {
+        GG_W(1, 1); GG_W(2, 1); GG_W(4, 1); GG_W(8, 1); GG_W(16, 1); GG_W(32, 1);
+        GG_W(64, 1); GG_W(64, 2); GG_W(64, 3); GG_W(64, 4);
+    } else if (kernel == GGRMS_KERNEL_BLOCK) {
+        GG_B(128, 1); GG_B(128, 2); GG_B(128, 4);
+        GG_B(256, 1); GG_B(256, 2); GG_B(256, 4);
+        GG_B(512, 1); GG_B(512, 2); GG_B(512, 4);
+        GG_B(1024, 1); GG_B(1024, 2); GG_B(1024, 4);
+    } else if (kernel == GGRMS_KERNEL_WIDE) {
+        return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB>);
+    }
+#undef GG_W
+#undef GG_B
+    return nullptr;
+}
+
+template <class T>
+inline const void* pick_type(int kernel, int vb, int lanes, int vpt) {
+    switch (vb) {
+    case 16: return pick_vb<T, 16>(kernel, lanes, vpt);
+    case 8: return pick_vb<T, 8>(kernel, lanes, vpt);
+    case 4: return pick_vb<T, 4>(kernel, lanes, vpt);
+    case 2:
+        if constexpr (T::kSize == 2) return pick_vb<T, 2>(kernel, lanes, vpt);
+        return nullptr;
+    default: return nullptr;
+    }
+}
+
+}  // namespace ggrms

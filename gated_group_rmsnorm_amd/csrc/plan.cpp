@@ -1,0 +1,237 @@
+// plan.cpp -- argument checks and kernel choice for ggrms_forward / ggrms_plan.
+// Pure host C++: no HIP call happens here, so every error path can be
+// exercised on a machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "ggrms_internal.h"
+
+namespace ggrms {
+namespace {
+
+bool mul_add_ok(int64_t a, int64_t b, int64_t c, int64_t* r) {
+    int64_t m;
+    if (__builtin_mul_overflow(a, b, &m)) return false;
+    return !__builtin_add_overflow(m, c, r);
+}
+
+// Byte extent of a [rows, width] view: (rows-1)*stride + width elements.
+bool extent_bytes(int64_t rows, int64_t width, int64_t stride, int esize, int64_t* bytes) {
+    int64_t elems;
+    if (!mul_add_ok(rows - 1, rows > 1 ? stride : 0, width, &elems)) return false;
+    if (__builtin_mul_overflow(elems, (int64_t)esize, bytes)) return false;
+    return true;
+}
+
+// Whether two [rows, width] views with byte row strides sa, sb and a row
+// length of len bytes share any element.  Exact for equal strides; for
+// unequal strides any overlap of the address ranges counts.
+bool views_overlap(uintptr_t a, int64_t sa, uintptr_t b, int64_t sb, int64_t rows, int64_t len,
+                   int64_t ext_a, int64_t ext_b) {
+    // address ranges [a, a+ext_a) and [b, b+ext_b)
+    if (a + (uintptr_t)ext_a <= b || b + (uintptr_t)ext_b <= a) return false;
+    if (rows == 1 || sa != sb) return true;
+    // element (i, c) of A meets element (j, d) of B iff (i-j)*s = D + d - c
+    // for |d - c| < len, i.e. some k in [-(rows-1), rows-1] has |k*s - D| < len.
+    const int64_t s = sa;
+    const int64_t D = (int64_t)(b - a);  // wraps correctly for b < a
+    int64_t k0 = D / s;                  // truncates toward zero
+    for (int64_t k = k0 - 1; k <= k0 + 1; ++k) {
+        if (k < -(rows - 1) || k > rows - 1) continue;
+        const int64_t diff = k * s - D;
+        if (diff < len && diff > -len) return true;
+    }
+    return false;
+}
+
+int64_t round_up_pow2(int64_t x) {
+    int64_t p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+int kernel_for_shape(int lanes, int vpt) {
+    if (vpt == 0) return GGRMS_KERNEL_WIDE;
+    return lanes <= 64 ? GGRMS_KERNEL_WAVE : GGRMS_KERNEL_BLOCK;
+}
+
+// Kernel shape for a group of nvec vectors.
+void choose_shape(int64_t nvec, int* kernel, int* lanes, int* vpt) {
+    if (nvec <= 64) {
+        // Narrow groups: the smallest power-of-two lane segment, several
+        // groups per wave, one vector per lane.
+        *kernel = GGRMS_KERNEL_WAVE;
+        *lanes = (int)round_up_pow2(nvec);
+        *vpt = 1;
+        return;
+    }
+    if (nvec <= 64 * kMaxWaveVpt) {
+        // One wave per group, up to four vectors in flight per lane.
+        *kernel = GGRMS_KERNEL_WAVE;
+        *lanes = 64;
+        *vpt = (int)((nvec + 63) / 64);
+        return;
+    }
+    if (nvec <= (int64_t)kMaxBlockLanes * 4) {
+        // Several waves per group: fewest idle slots; among equals prefer two
+        // vectors per lane, then one, then four.
+        static const int pref_vpt[3] = {2, 1, 4};
+        int64_t best_slots = INT64_MAX;
+        for (int vi = 0; vi < 3; ++vi) {
+            const int v = pref_vpt[vi];
+            for (int l = 128; l <= kMaxBlockLanes; l <<= 1) {
+                const int64_t slots = (int64_t)l * v;
+                if (slots >= nvec && slots < best_slots) {
+                    best_slots = slots;
+                    *kernel = GGRMS_KERNEL_BLOCK;
+                    *lanes = l;
+                    *vpt = v;
+                }
+            }
+        }
+        return;
+    }
+    *kernel = GGRMS_KERNEL_WIDE;
+    *lanes = kWideBlock;
+    *vpt = 0;
+}
+
+}  // namespace
+
+void div_magic(uint32_t d, uint32_t* m, uint32_t* s) {
+    // Round-up method of Granlund and Montgomery ("Division by invariant
+    // integers using multiplication", PLDI 1994): l = ceil(log2 d),
+    // m = floor(2^32 (2^l - d) / d) + 1; for n < 2^31, n / d = (mulhi(m, n) + n) >> l.
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t mm = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    *m = (uint32_t)mm;
+    *s = l;
+}
+
+ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const void* out,
+                         int64_t rows, int64_t width, int64_t group_size, int64_t sy,
+                         int64_t sg, int64_t so, float eps, int dtype, int ri,
+                         int force_lanes, int force_vpt, LaunchPlan* plan) {
+    if (!plan) return GGRMS_ERROR_INVALID_VALUE;
+    memset(plan, 0, sizeof *plan);
+    if (rows < 0 || width <= 0 || group_size <= 0 || width % group_size != 0)
+        return GGRMS_ERROR_INVALID_VALUE;
+    if (ri != 0 && ri != 1) return GGRMS_ERROR_INVALID_VALUE;
+    if (!std::isfinite(eps) || eps < 0.0f) return GGRMS_ERROR_INVALID_VALUE;
+    if (dtype != GGRMS_F32 && dtype != GGRMS_F16 && dtype != GGRMS_BF16)
+        return GGRMS_ERROR_NOT_SUPPORTED;
+    const int esize = dtype == GGRMS_F32 ? 4 : 2;
+    plan->esize = esize;
+    plan->groups = width / group_size;
+    if (rows == 0) {
+        plan->pub.kernel = GGRMS_KERNEL_NONE;
+        return GGRMS_SUCCESS;
+    }
+    if (!y || !gate || !w || !out) return GGRMS_ERROR_INVALID_VALUE;
+    if (rows > 1 && (sy < width || sg < width || so < width)) return GGRMS_ERROR_INVALID_VALUE;
+    const uintptr_t py = (uintptr_t)y, pg = (uintptr_t)gate, po = (uintptr_t)out,
+                    pw = (uintptr_t)w;
+    if (py % esize || pg % esize || po % esize || pw % 4) return GGRMS_ERROR_INVALID_VALUE;
+    if (rows == 1) sy = sg = so = width;  // strides of a single row are never used
+    int64_t ey, eg, eo, ew, row_bytes;
+    if (!extent_bytes(rows, width, sy, esize, &ey) || !extent_bytes(rows, width, sg, esize, &eg) ||
+        !extent_bytes(rows, width, so, esize, &eo) || __builtin_mul_overflow(width, (int64_t)4, &ew) ||
+        __builtin_mul_overflow(width, (int64_t)esize, &row_bytes))
+        return GGRMS_ERROR_INVALID_VALUE;
+    if (py + (uintptr_t)ey < py || pg + (uintptr_t)eg < pg || po + (uintptr_t)eo < po ||
+        pw + (uintptr_t)ew < pw)
+        return GGRMS_ERROR_INVALID_VALUE;
+    // out may be y or gate exactly (in place); any other shared element is an error.
+    const int64_t by = sy * esize, bg = sg * esize, bo = so * esize;
+    const bool alias_y = po == py && bo == by;
+    const bool alias_g = po == pg && bo == bg;
+    if (!alias_y && views_overlap(po, bo, py, by, rows, row_bytes, eo, ey))
+        return GGRMS_ERROR_INVALID_VALUE;
+    if (!alias_g && views_overlap(po, bo, pg, bg, rows, row_bytes, eo, eg))
+        return GGRMS_ERROR_INVALID_VALUE;
+
+    // Widest vector every access can use: the three views' base pointers and
+    // row strides, the group's byte length, and the matching weight loads.
+    int vb = esize;
+    for (int cand = 16; cand > esize; cand >>= 1) {
+        const int64_t wal = cand / esize * 4 < 16 ? cand / esize * 4 : 16;
+        if (py % cand == 0 && pg % cand == 0 && po % cand == 0 && (by % cand == 0) &&
+            (bg % cand == 0) && (bo % cand == 0) && (group_size * esize) % cand == 0 &&
+            pw % wal == 0) {
+            vb = cand;
+            break;
+        }
+    }
+    const int64_t nvec = group_size * esize / vb;
+    int kernel = 0, lanes = 0, vpt = 0;
+    if (force_lanes || force_vpt) {
+        kernel = kernel_for_shape(force_lanes, force_vpt);
+        lanes = force_lanes;
+        vpt = force_vpt;
+        if (!shape_supported(kernel, lanes, vpt)) return GGRMS_ERROR_NOT_SUPPORTED;
+        if (kernel != GGRMS_KERNEL_WIDE && (int64_t)lanes * vpt < nvec)
+            return GGRMS_ERROR_NOT_SUPPORTED;
+    } else {
+        choose_shape(nvec, &kernel, &lanes, &vpt);
+    }
+
+    const int64_t groups = plan->groups;
+    int block = kWaveBlock;
+    if (kernel == GGRMS_KERNEL_BLOCK) block = lanes > 256 ? lanes : 256;
+    if (kernel == GGRMS_KERNEL_WIDE) block = kWideBlock;
+    // Units per launch stay below 2^31 and so do threads per launch, so the
+    // kernels index with 32-bit integers; larger jobs are split by rows.
+    const int64_t thread_per_unit = kernel == GGRMS_KERNEL_WIDE ? kWideBlock : lanes;
+    const int64_t max_units = ((int64_t)1 << 31) / thread_per_unit;
+    int64_t rows_per_launch = max_units / groups;
+    if (rows_per_launch < 1) return GGRMS_ERROR_INVALID_VALUE;  // one row alone too large
+    if (rows_per_launch > rows) rows_per_launch = rows;
+    const int64_t launches = (rows + rows_per_launch - 1) / rows_per_launch;
+    int64_t workgroups = 0;
+    for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+        const int64_t r = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+        const int64_t units = r * groups;
+        workgroups += (units * thread_per_unit + block - 1) / block;
+    }
+    plan->nvec = nvec;
+    plan->rows_per_launch = rows_per_launch;
+    plan->pub.kernel = kernel;
+    plan->pub.vector_bytes = vb;
+    plan->pub.lanes_per_group = lanes;
+    plan->pub.vectors_per_lane = vpt;
+    plan->pub.block_threads = block;
+    plan->pub.launches = (int32_t)launches;
+    plan->pub.workgroups = workgroups;
+    return GGRMS_SUCCESS;
+}
+
+}  // namespace ggrms
+
+extern "C" ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_weight,
+                                     void* out, int64_t rows, int64_t width, int64_t group_size,
+                                     int64_t y_row_stride, int64_t gate_row_stride,
+                                     int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                     int round_intermediate, ggrms_plan_t* plan) {
+    if (!plan) return GGRMS_ERROR_INVALID_VALUE;
+    ggrms::LaunchPlan lp;
+    const ggrms_status_t st = ggrms::make_plan(y, gate, norm_weight, out, rows, width, group_size,
+                                               y_row_stride, gate_row_stride, out_row_stride, eps,
+                                               (int)dtype, round_intermediate, 0, 0, &lp);
+    if (st == GGRMS_SUCCESS) *plan = lp.pub;
+    return st;
+}
+
+extern "C" const char* ggrms_status_string(ggrms_status_t status) {
+    switch (status) {
+    case GGRMS_SUCCESS: return "success";
+    case GGRMS_ERROR_INVALID_VALUE: return "invalid argument";
+    case GGRMS_ERROR_NOT_SUPPORTED: return "not supported (dtype or device)";
+    case GGRMS_ERROR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int ggrms_abi_version(void) { return GGRMS_ABI_VERSION; }

@@ -1,0 +1,171 @@
+/*
+ * ggrms.h -- C ABI of the fused gated group-RMSNorm library (libggrms.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  The page "gated_group_rmsnorm" (Mojo module doc on
+ * max.modular.com; the math block after its intro and the paragraph after
+ * it) defines, for a row n of the intermediate axis split into contiguous
+ * groups of group_size = G columns, group g, col = g*G + j:
+ *
+ *     gated = f32(y[n,col]) * silu(f32(gate[n,col]))      f32
+ *     m2    = sum over the G columns of gated^2           f32
+ *     nf    = rsqrt(m2 / G + eps)                        eps added after the mean
+ *     out[n,col] = cast(f32(norm_weight[col]) * f32(cast(gated*nf, y.dtype)), out.dtype)
+ *
+ * This is the norm_before_gate = False branch of the Mamba-2 mixer's gated
+ * RMSNorm; one launch replaces the four-op chain (widen, silu-gate, group
+ * RMSNorm, weight multiply and narrow) the page's intro describes.  With
+ * round_intermediate = 0 the intermediate cast(gated*nf, y.dtype) is skipped
+ * and every intermediate stays f32 until the final store (the mode that the
+ * page "com.microsoft.GatedRMSNorm", Description section, describes for its
+ * operator).  Casts round to nearest, ties to even, keep subnormals and
+ * overflow to infinity.
+ *
+ * Layout.  y, gate and out are row-major [rows, width] views with unit column
+ * stride and their own row strides, so y and gate may be column slices of one
+ * fused in-projection buffer (the page's Parallelization section reads strided
+ * views directly).  Rows are tokens of one or more sequences, flattened
+ * (the page's "standalone varlen op"); leading axes fold into rows.
+ *
+ * Threading and ownership.  The caller owns every buffer.  The library
+ * allocates nothing, frees nothing, keeps no pointer after a call returns,
+ * never synchronises, and is safe to call from several threads at once.
+ * ggrms_forward only enqueues work on `stream` and returns (the page's
+ * "Enqueues" entry point); results are ready when the stream reaches that
+ * point.  Faults inside the kernel surface at the caller's next
+ * synchronisation with that stream.
+ */
+#ifndef GGRMS_H
+#define GGRMS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GGRMS_ABI_VERSION 1
+
+/* Element type shared by y, gate and out.  The weight is always f32. */
+typedef enum {
+    GGRMS_F32 = 0,  /* IEEE binary32 */
+    GGRMS_F16 = 1,  /* IEEE binary16 */
+    GGRMS_BF16 = 2  /* bfloat16: the upper 16 bits of a binary32 */
+} ggrms_dtype_t;
+
+typedef enum {
+    GGRMS_SUCCESS = 0,
+    /* An argument violates the contract below; nothing was enqueued. */
+    GGRMS_ERROR_INVALID_VALUE = 1,
+    /* Unknown dtype, or the current device is not gfx950; nothing was enqueued. */
+    GGRMS_ERROR_NOT_SUPPORTED = 2,
+    /* The HIP runtime refused a kernel launch. */
+    GGRMS_ERROR_LAUNCH = 3
+} ggrms_status_t;
+
+/*
+ * ggrms_forward -- enqueue the fused gated group-RMSNorm on `stream`.
+ *
+ *   y, gate       device pointers to the first element of [rows, width]
+ *                 views of `dtype`; read only.  They may overlap each other.
+ *   norm_weight   device pointer to `width` f32 values, indexed by column;
+ *                 read only; 4-byte aligned.
+ *   out           device pointer to the first element of a [rows, width]
+ *                 view of `dtype`; every element of the view is written,
+ *                 nothing outside it is touched.  out may be exactly y or
+ *                 exactly gate (same pointer and same row stride: in place);
+ *                 any other overlap with y or gate is rejected.
+ *   rows          number of rows (tokens), >= 0.  rows == 0 enqueues nothing.
+ *   width         columns per row, > 0, a multiple of group_size.
+ *   group_size    columns per normalisation group (G), > 0.
+ *   *_row_stride  distance between consecutive rows, in elements; >= width
+ *                 when rows > 1 (ignored when rows == 1).
+ *   eps           added to the mean of squares; finite and >= 0.
+ *   dtype         a ggrms_dtype_t.
+ *   round_intermediate
+ *                 1: cast gated*nf to `dtype` and back before the weight
+ *                 multiply; 0: keep it f32.  For GGRMS_F32 both are identical.
+ *   stream        a hipStream_t, or NULL for the null stream.
+ *
+ * Every element pointer must be aligned to its element size.
+ *
+ * Returns GGRMS_SUCCESS once the work is enqueued.  Argument checks run
+ * before any HIP call: GGRMS_ERROR_INVALID_VALUE for a negative rows, a
+ * non-positive width or group_size, width % group_size != 0, a NULL pointer
+ * when rows > 0, a row stride < width when rows > 1, a misaligned pointer,
+ * round_intermediate other than 0 or 1, a NaN, infinite or negative eps,
+ * extents that overflow 64-bit addressing, or a disallowed overlap of out
+ * with y or gate; GGRMS_ERROR_NOT_SUPPORTED for an unknown dtype.  Then the
+ * current device is checked (GGRMS_ERROR_NOT_SUPPORTED unless gfx950) and
+ * the kernels are launched (GGRMS_ERROR_LAUNCH if the runtime refuses one).
+ */
+ggrms_status_t ggrms_forward(const void* y, const void* gate, const float* norm_weight,
+                             void* out, int64_t rows, int64_t width, int64_t group_size,
+                             int64_t y_row_stride, int64_t gate_row_stride,
+                             int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                             int round_intermediate, void* stream);
+
+/* Which kernel ggrms_forward would launch for a set of arguments. */
+typedef enum {
+    GGRMS_KERNEL_NONE = 0,   /* rows == 0: nothing to launch */
+    GGRMS_KERNEL_WAVE = 1,   /* one span of <= 64 lanes per (row, group); no LDS, no barrier */
+    GGRMS_KERNEL_BLOCK = 2,  /* one (row, group) across 2..16 waves; LDS combine, one barrier */
+    GGRMS_KERNEL_WIDE = 3    /* groups too wide for registers: two passes over the group */
+} ggrms_kernel_t;
+
+typedef struct {
+    int32_t kernel;           /* a ggrms_kernel_t */
+    int32_t vector_bytes;     /* bytes per y/gate/out load and store (16, 8, 4 or 2) */
+    int32_t lanes_per_group;  /* lanes that share one (row, group) */
+    int32_t vectors_per_lane; /* vectors each lane holds per group (0 for WIDE: it loops) */
+    int32_t block_threads;    /* threads per workgroup */
+    int32_t launches;         /* kernel launches (rows are split if a grid would be too large) */
+    int64_t workgroups;       /* workgroups over all launches */
+} ggrms_plan_t;
+
+/*
+ * ggrms_plan -- run ggrms_forward's argument checks and kernel choice
+ * without touching the device; fills *plan on GGRMS_SUCCESS.  Makes no HIP
+ * call, so it works on a host without a GPU.
+ */
+ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_weight,
+                          void* out, int64_t rows, int64_t width, int64_t group_size,
+                          int64_t y_row_stride, int64_t gate_row_stride,
+                          int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                          int round_intermediate, ggrms_plan_t* plan);
+
+/*
+ * ggrms_forward_with_shape -- ggrms_forward with the kernel shape chosen by
+ * the caller instead of by the library, for tuning and for cross-checking
+ * the kernel families against each other.  Same arguments, semantics and
+ * results as ggrms_forward, plus:
+ *
+ *   lanes_per_group   1, 2, 4, ..., 64 (WAVE kernel) or 128, 256, 512, 1024
+ *                     (BLOCK kernel; 1024 with vectors_per_lane = 0 is WIDE)
+ *   vectors_per_lane  1 for lanes < 64; 1..4 for 64 lanes; 1, 2 or 4 for the
+ *                     BLOCK kernel; 0 for WIDE
+ *
+ * The vector width still follows the pointers' alignment.  Returns
+ * GGRMS_ERROR_INVALID_VALUE for 0 / 0 (use ggrms_forward), and
+ * GGRMS_ERROR_NOT_SUPPORTED for a shape that is not built or whose
+ * lanes_per_group * vectors_per_lane vectors do not cover one group.
+ */
+ggrms_status_t ggrms_forward_with_shape(const void* y, const void* gate,
+                                        const float* norm_weight, void* out, int64_t rows,
+                                        int64_t width, int64_t group_size,
+                                        int64_t y_row_stride, int64_t gate_row_stride,
+                                        int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                        int round_intermediate, int lanes_per_group,
+                                        int vectors_per_lane, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* ggrms_status_string(ggrms_status_t status);
+
+/* GGRMS_ABI_VERSION of the loaded library. */
+int ggrms_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GGRMS_H */

@@ -1,0 +1,254 @@
+"""The C ABI on the CPU: the library loads, exports what include/ggrms.h
+declares, rejects bad arguments before any HIP call, and plans kernels as
+documented.  Nothing here launches a kernel or needs a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ggrms.h")
+
+F32, F16, BF16 = 0, 1, 2
+OK, INVALID, NOTSUP = 0, 1, 2
+A = 1 << 20  # a 256-byte aligned fake device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gated_group_rmsnorm_amd as g
+
+    return g
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ggrms_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(g):
+    names = _declared_functions()
+    assert {"ggrms_forward", "ggrms_plan", "ggrms_status_string", "ggrms_abi_version"} <= set(names)
+    lib = ctypes.CDLL(g.library_path())
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ggrms.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", g.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    public = {n for n in exported if n.startswith("ggrms_")}
+    assert public == set(names), f"exported but undeclared: {public - set(names)}"
+
+
+def test_abi_version_and_strings(g):
+    assert g.ggrms_abi_version() == 1
+    for st in range(4):
+        assert g.ggrms_status_string(st)
+    assert g.ggrms_status_string(99) == "unknown status"
+
+
+def _fwd(g, **kw):
+    args = dict(y=A, gate=A + (1 << 24), norm_weight=A + (2 << 24), out=A + (3 << 24), rows=4,
+                width=256, group_size=64, y_row_stride=256, gate_row_stride=256,
+                out_row_stride=256, eps=1e-5, dtype=BF16, round_intermediate=1)
+    args.update(kw)
+    st_plan, plan = g.ggrms_plan(*args.values())
+    # ggrms_forward is only called where its checks reject the arguments (or
+    # there is nothing to launch), so no call here reaches the HIP runtime.
+    st_fwd = g.ggrms_forward(*args.values(), 0) if (st_plan != OK or args["rows"] == 0) else None
+    return st_plan, st_fwd, plan
+
+
+BAD = [
+    dict(rows=-1), dict(width=0), dict(group_size=0), dict(group_size=-64), dict(group_size=48),
+    dict(y=0), dict(gate=0), dict(norm_weight=0), dict(out=0),
+    dict(y_row_stride=255), dict(gate_row_stride=100), dict(out_row_stride=-256),
+    dict(y=A + 1), dict(out=A + (3 << 24) + 1), dict(norm_weight=A + (2 << 24) + 2),
+    dict(dtype=F32, y=A + 2),
+    dict(round_intermediate=2), dict(round_intermediate=-1),
+    dict(eps=float("nan")), dict(eps=float("inf")), dict(eps=-1e-5),
+    # out overlapping an input other than exactly in place
+    dict(out=A + 2), dict(out=A, out_row_stride=512),
+    dict(out=A + (1 << 24) + 64),
+    # extents that overflow 64-bit addressing
+    dict(rows=1 << 40, y_row_stride=1 << 40, gate_row_stride=1 << 40, out_row_stride=1 << 40),
+]
+
+
+@pytest.mark.parametrize("kw", BAD, ids=lambda k: ",".join(f"{a}={v}" for a, v in k.items()))
+def test_invalid_arguments(g, kw):
+    st_plan, st_fwd, _ = _fwd(g, **kw)
+    assert st_plan == INVALID and st_fwd == INVALID
+
+
+def test_unknown_dtype(g):
+    st_plan, st_fwd, _ = _fwd(g, dtype=7)
+    assert st_plan == NOTSUP and st_fwd == NOTSUP
+
+
+def test_zero_rows_is_a_no_op(g):
+    st_plan, st_fwd, plan = _fwd(g, rows=0, y=0, gate=0, out=0, norm_weight=0)
+    assert st_plan == OK and st_fwd == OK and plan["kernel_name"] == "none"
+
+
+def test_single_row_ignores_strides(g):
+    st, plan = g.ggrms_plan(A, A + 4096, A + 8192, A + 12288, 1, 256, 64, 0, 0, 0, 1e-5, BF16, 1)
+    assert st == OK and plan["vector_bytes"] == 16
+
+
+def test_in_place_is_allowed(g):
+    for alias in ("y", "gate"):
+        kw = {"out": A if alias == "y" else A + (1 << 24)}
+        st, _, plan = _fwd(g, **kw)
+        assert st == OK, alias
+
+
+def test_interleaved_views_do_not_overlap(g):
+    """y and gate as column slices of one fused buffer, out in a third
+    column slice of the same buffer: no element is shared, so it is allowed."""
+    st, _, plan = _fwd(g, rows=8, width=100, group_size=100, y=A, gate=A + 200, out=A + 400,
+                       y_row_stride=300, gate_row_stride=300, out_row_stride=300, dtype=F16)
+    assert st == OK
+    st, _, _ = _fwd(g, rows=8, width=100, group_size=100, y=A, gate=A + 200, out=A + 398,
+                    y_row_stride=300, gate_row_stride=300, out_row_stride=300, dtype=F16)
+    assert st == INVALID
+
+
+def _plan(g, rows, width, G, dtype, sy=None, sg=None, so=None, y=A, gate=A + (1 << 30),
+          w=A + (2 << 30), out=A + (3 << 30)):
+    sy = width if sy is None else sy
+    sg = width if sg is None else sg
+    so = width if so is None else so
+    st, p = g.ggrms_plan(y, gate, w, out, rows, width, G, sy, sg, so, 1e-5, dtype, 1)
+    assert st == OK
+    return p
+
+
+def test_plans_for_the_workloads(g):
+    # 8192x7680 bf16, G = 960: 120 16-byte vectors per group -> one wave, two per lane
+    p = _plan(g, 8192, 7680, 960, BF16)
+    assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 16, 64, 2)
+    assert p["workgroups"] == 8192 * 8 * 64 // 256 and p["launches"] == 1
+    # decode 1x7680: 8 groups
+    p = _plan(g, 1, 7680, 960, BF16)
+    assert p["workgroups"] == 2
+    # 16384x8192 fp16, G = 128: 16 vectors -> 16-lane segments, four groups per wave
+    p = _plan(g, 16384, 8192, 128, F16)
+    assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 16, 16, 1)
+    # 256x4800 fp16 slices of a [256, 9856] buffer, G = 100: 200-byte groups -> 8-byte vectors
+    p = _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)
+    assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"]) == ("wave", 8, 32)
+    # tiny f32, G = 64: 16 vectors
+    p = _plan(g, 4, 256, 64, F32)
+    assert (p["vector_bytes"], p["lanes_per_group"]) == (16, 16)
+
+
+def test_vector_width_follows_alignment(g):
+    assert _plan(g, 4, 256, 64, BF16)["vector_bytes"] == 16
+    assert _plan(g, 4, 256, 64, BF16, y=A + 8)["vector_bytes"] == 8
+    assert _plan(g, 4, 256, 64, BF16, out=A + (3 << 30) + 4)["vector_bytes"] == 4
+    assert _plan(g, 4, 256, 64, BF16, y=A + 2)["vector_bytes"] == 2
+    assert _plan(g, 4, 258, 258, BF16, sy=258, sg=258, so=258)["vector_bytes"] == 4
+    assert _plan(g, 4, 256, 64, BF16, sy=260)["vector_bytes"] == 8
+    assert _plan(g, 3, 63 * 5, 63, BF16)["vector_bytes"] == 2
+    # the weight loads must be aligned for the matching width too
+    # (two bf16 per 4-byte vector take an 8-byte weight load, so a 4-byte
+    # aligned weight leaves one element per access)
+    assert _plan(g, 4, 256, 64, BF16, w=A + (2 << 30) + 4)["vector_bytes"] == 2
+    assert _plan(g, 4, 256, 64, F32, w=A + (2 << 30) + 4)["vector_bytes"] == 4
+
+
+def test_kernel_family_by_group_width(g):
+    cases = {
+        8: ("wave", 1, 1),        # one 16-byte vector: a group per lane
+        64: ("wave", 8, 1),
+        512: ("wave", 64, 1),
+        960: ("wave", 64, 2),
+        1032: ("wave", 64, 3),   # 129 vectors
+        2048: ("wave", 64, 4),
+        2056: ("block", 128, 3),  # 257 vectors -> 512 slots beat 384? see below
+        7680: ("block", 512, 2),
+        32768: ("block", 1024, 4),
+        32776: ("wide", 1024, 0),
+    }
+    for G, (kname, lanes, vpt) in cases.items():
+        p = _plan(g, 2, G, G, BF16)
+        if G == 2056:
+            # 257 vectors: the best shapes cover 384 (128x3 is not built) or 512
+            assert p["kernel_name"] == "block" and p["lanes_per_group"] * p["vectors_per_lane"] == 512
+            continue
+        assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"]) == (kname, lanes, vpt), G
+
+
+def test_division_magic_numbers(tmp_path):
+    """unit / groups by multiply-high: exhaustive small divisors and dividends,
+    plus random large ones, against integer division."""
+    drv = tmp_path / "divcheck.cpp"
+    drv.write_text(r'''
+#include <cstdint>
+#include <cstdio>
+#include <random>
+#include "ggrms_internal.h"
+static uint32_t q(uint32_t n, uint32_t m, uint32_t s) {
+    return (uint32_t)((((uint64_t)n * m) >> 32) + n) >> s;
+}
+int main() {
+    std::mt19937_64 rng(1);
+    for (uint32_t d = 1; d < 5000; ++d) {
+        uint32_t m, s; ggrms::div_magic(d, &m, &s);
+        for (uint32_t n = 0; n < 20000; ++n) if (q(n, m, s) != n / d) { printf("%u %u\n", n, d); return 1; }
+        for (int i = 0; i < 2000; ++i) { uint32_t n = rng() & 0x7FFFFFFF; if (q(n, m, s) != n / d) { printf("%u %u\n", n, d); return 1; } }
+    }
+    for (int i = 0; i < 200000; ++i) {
+        uint32_t d = (uint32_t)(rng() % 0x7FFFFFFF) + 1, n = rng() & 0x7FFFFFFF, m, s;
+        ggrms::div_magic(d, &m, &s);
+        if (q(n, m, s) != n / d) { printf("%u %u\n", n, d); return 1; }
+        n = 0x7FFFFFFF; if (q(n, m, s) != n / d) { printf("%u %u\n", n, d); return 1; }
+    }
+    return 0;
+}
+''')
+    exe = tmp_path / "divcheck"
+    csrc = os.path.join(ROOT, "gated_group_rmsnorm_amd", "csrc")
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), "-I", csrc,
+                    str(drv), os.path.join(csrc, "plan.cpp"), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout
+
+
+def test_planner_host_sanitizers(tmp_path):
+    """The planner (pure host C++) under AddressSanitizer and UBSan over a
+    sweep of shapes, strides and pointers."""
+    drv = tmp_path / "plansweep.cpp"
+    drv.write_text(r'''
+#include <cstdint>
+#include <cstdio>
+#include <initializer_list>
+#include "ggrms.h"
+int main() {
+    const int64_t Gs[] = {1, 2, 3, 7, 8, 63, 64, 65, 100, 128, 960, 4096, 7680, 32768, 65536};
+    const uintptr_t base = 1u << 20;
+    long n_ok = 0;
+    for (int64_t G : Gs) for (int64_t rows : {0, 1, 3, 257}) for (int dt = 0; dt < 4; ++dt)
+    for (int off = 0; off < 3; ++off) {
+        ggrms_plan_t p;
+        int64_t width = G * 3;
+        ggrms_status_t st = ggrms_plan((void*)(base + off * 2), (void*)(base + (1u << 28)),
+                                       (const float*)(base + (2u << 28)), (void*)(base + (3u << 28)),
+                                       rows, width, G, width + off, width, width, 1e-5f,
+                                       (ggrms_dtype_t)dt, 1, &p);
+        n_ok += st == GGRMS_SUCCESS;
+    }
+    printf("%ld\n", n_ok);
+    return n_ok > 0 ? 0 : 1;
+}
+''')
+    exe = tmp_path / "plansweep"
+    csrc = os.path.join(ROOT, "gated_group_rmsnorm_amd", "csrc")
+    subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"), "-I", csrc,
+                    str(drv), os.path.join(csrc, "plan.cpp"), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
