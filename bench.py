@@ -104,23 +104,24 @@ class Setup:
 
 
 def time_kernel(torch, g, setup, steps, warmup, shape=None):
-    """Whole-job wall time over `steps` launches plus per-launch HIP events on
-    the launch stream.  Returns (wall_s, [kernel_ms])."""
+    """`steps` back-to-back launches between two HIP events recorded on the
+    launch stream, plus the host wall clock around them.  Returns
+    (wall_s, event_ms_total)."""
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     for i in range(warmup):
         setup.launch(g, i, sp, shape)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        starts[i].record(stream)
         setup.launch(g, i, sp, shape)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, start.elapsed_time(end)
 
 
 def bench_prefill(torch, g, S, args, shape):
@@ -129,25 +130,22 @@ def bench_prefill(torch, g, S, args, shape):
     sets = max(2, math.ceil(3 * 256e6 / nbytes))  # > 3x the 256 MB Infinity Cache per rotation
     log(f"prefill: generating {w.name}, {sets} rotating input sets")
     setup = Setup(torch, S, w, sets)
-    wall, kms = time_kernel(torch, g, setup, args.steps, args.warmup, shape)
+    wall, ev_ms = time_kernel(torch, g, setup, args.steps, args.warmup, shape)
     st, plan = g.ggrms_plan(setup.sets[0][0].data_ptr(), setup.sets[0][1].data_ptr(),
                             setup.weight.data_ptr(), setup.sets[0][2].data_ptr(), w.rows, w.width,
                             w.group_size, w.width, w.width, w.width, w.eps, w.dtype,
                             w.round_intermediate)
-    avg_ms = statistics.fmean(kms)
+    avg_ms = ev_ms / args.steps
     res = {
         "workload": w,
         "bytes": nbytes,
         "wall_s": wall,
         "kernel_ms_avg": avg_ms,
-        "kernel_ms_median": statistics.median(kms),
-        "kernel_ms_min": min(kms),
         "plan": plan,
         "sets": sets,
     }
-    log(f"prefill: wall {wall * 1e3 / args.steps:.2f} ms/step, kernel avg {avg_ms * 1e3:.2f} us "
-        f"(median {res['kernel_ms_median'] * 1e3:.2f}, min {min(kms) * 1e3:.2f}), "
-        f"{nbytes / (avg_ms * 1e-3) / 1e9:.0f} GB/s")
+    log(f"prefill: wall {wall * 1e3 / args.steps:.4f} ms/step, event avg {avg_ms * 1e3:.2f} us "
+        f"per launch, {nbytes / (avg_ms * 1e-3) / 1e9:.0f} GB/s")
     return res
 
 
@@ -253,8 +251,8 @@ def bench_workloads(torch, g, S, steps):
         w = S.WORKLOADS[name]
         sets = max(2, math.ceil(3 * 256e6 / w.algorithmic_bytes()))
         setup = Setup(torch, S, w, min(sets, 64))
-        _, kms = time_kernel(torch, g, setup, steps, 5)
-        avg = statistics.fmean(kms)
+        _, ev_ms = time_kernel(torch, g, setup, steps, 5)
+        avg = ev_ms / steps
         out[name] = {"kernel_us_avg": avg * 1e3,
                      "gbs": w.algorithmic_bytes() / (avg * 1e-3) / 1e9,
                      "frac_of_peak": w.algorithmic_bytes() / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -368,8 +366,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic_figure(nbytes),
                      "algorithmic_bytes_per_launch": nbytes,
-                     "kernel_us_avg": round(pre["kernel_ms_avg"] * 1e3, 2),
-                     "kernel_us_median": round(pre["kernel_ms_median"] * 1e3, 2)},
+                     "kernel_us_avg": round(pre["kernel_ms_avg"] * 1e3, 2)},
         "cpu_baseline": cpu,
         "decode": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in decode.items()},
         "other_workloads": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in others.items()},
