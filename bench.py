@@ -34,8 +34,9 @@ METRIC = "achieved HBM GB/s (fraction of peak) at 8192x7680 bf16; µs/launch at 
 PEAK_HBM_GBS = 8000.0
 PREFILL = "mamba2_prefill_8192x7680_bf16_g960"
 DECODE = "mamba2_decode_1x7680_bf16_g960"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_8192x7680_bf16.json")
-KERNEL_SOURCES = ["gated_group_rmsnorm_amd/csrc/kernels.cuh", "gated_group_rmsnorm_amd/csrc/table_bf16.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_8192x7680_bf16.md")
+KERNEL_SOURCES = ["gated_group_rmsnorm_amd/csrc/kernels.cuh", "gated_group_rmsnorm_amd/csrc/table_bf16.hip",
+                  "gated_group_rmsnorm_amd/csrc/plan.cpp"]
 
 
 def log(msg):
@@ -53,13 +54,16 @@ def kernel_source_hash() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed launches for this long after the warmup steps")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads"], default=None)
     ap.add_argument("--decode-bursts", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--shape", default=None, help="force a kernel shape 'lanes,vectors'")
+    ap.add_argument("--shape", default=None,
+                    help="force a kernel shape 'lanes,vectors[,rows_per_workgroup]'")
     return ap.parse_args()
 
 
@@ -96,21 +100,39 @@ class Setup:
                 w.width, w.group_size, lay["y_row_stride"], lay["gate_row_stride"], w.width,
                 w.eps, w.dtype, w.round_intermediate)
         if shape:
-            st = g.ggrms_forward_with_shape(*args, shape[0], shape[1], stream)
+            st = g.ggrms_forward_with_shape(*args, shape[0], shape[1], stream,
+                                            shape[2] if len(shape) > 2 else 0)
         else:
             st = g.ggrms_forward(*args, stream)
         if st != 0:
             raise RuntimeError(f"ggrms_forward: {g.ggrms_status_string(st)}")
 
 
-def time_kernel(torch, g, setup, steps, warmup, shape=None):
-    """`steps` back-to-back launches between two HIP events recorded on the
-    launch stream, plus the host wall clock around them.  Returns
-    (wall_s, event_ms_total)."""
+def settle(torch, launch, seconds):
+    """Untimed launches until `seconds` of wall time have passed: from idle the
+    GPU needs ~30 ms (~500 launches of the prefill kernel) to reach its
+    steady clocks, and a measurement taken inside that ramp reads ~5-10% low."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(32):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
+
+
+def time_kernel(torch, g, setup, steps, warmup, shape=None, settle_s=0.2):
+    """`warmup` untimed launches, then untimed launches for `settle_s`
+    seconds, then `steps` back-to-back launches between two HIP events
+    recorded on the launch stream, with the host wall clock around them.
+    Returns (wall_s, event_ms_total)."""
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     for i in range(warmup):
         setup.launch(g, i, sp, shape)
+    settle(torch, lambda i: setup.launch(g, i, sp, shape), settle_s)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -130,7 +152,8 @@ def bench_prefill(torch, g, S, args, shape):
     sets = max(2, math.ceil(3 * 256e6 / nbytes))  # > 3x the 256 MB Infinity Cache per rotation
     log(f"prefill: generating {w.name}, {sets} rotating input sets")
     setup = Setup(torch, S, w, sets)
-    wall, ev_ms = time_kernel(torch, g, setup, args.steps, args.warmup, shape)
+    wall, ev_ms = time_kernel(torch, g, setup, args.steps, args.warmup, shape,
+                              args.settle_ms / 1e3)
     st, plan = g.ggrms_plan(setup.sets[0][0].data_ptr(), setup.sets[0][1].data_ptr(),
                             setup.weight.data_ptr(), setup.sets[0][2].data_ptr(), w.rows, w.width,
                             w.group_size, w.width, w.width, w.width, w.eps, w.dtype,
@@ -176,8 +199,7 @@ def bench_decode(torch, g, S, bursts):
     def timed(burst_fn):
         stream = torch.cuda.current_stream()
         sp = stream.cuda_stream
-        for _ in range(10):
-            burst_fn(sp)
+        settle(torch, lambda i: burst_fn(sp), 0.1)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(bursts)]
         torch.cuda.synchronize()
@@ -195,8 +217,7 @@ def bench_decode(torch, g, S, bursts):
         with torch.cuda.graph(graph, stream=cs):
             burst_fn(cs.cuda_stream)
         stream = torch.cuda.current_stream()
-        for _ in range(10):
-            graph.replay()
+        settle(torch, lambda i: graph.replay(), 0.1)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(bursts)]
         torch.cuda.synchronize()
@@ -251,7 +272,7 @@ def bench_workloads(torch, g, S, steps):
         w = S.WORKLOADS[name]
         sets = max(2, math.ceil(3 * 256e6 / w.algorithmic_bytes()))
         setup = Setup(torch, S, w, min(sets, 64))
-        _, ev_ms = time_kernel(torch, g, setup, steps, 5)
+        _, ev_ms = time_kernel(torch, g, setup, steps, 5, settle_s=0.1)
         avg = ev_ms / steps
         out[name] = {"kernel_us_avg": avg * 1e3,
                      "gbs": w.algorithmic_bytes() / (avg * 1e-3) / 1e9,
@@ -293,24 +314,31 @@ def cpu_baseline(S, seconds):
             "rows_per_s": round(reps * rows / el, 1)}
 
 
-def traffic_figure(launch_bytes):
-    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE/WRITE_SIZE runs
-    (scaled by the copy-kernel calibration); None if the kernel changed since."""
+def traffic_figure():
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (scaled by the copy-kernel calibration) recorded in the profile summary;
+    None if the kernel sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            text = f.read()
+    except OSError:
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    fields = dict(line.split(":", 1) for line in text.splitlines()
+                  if line.startswith(("hbm_bytes_per_launch:", "kernel_source_hash:")))
+    if fields.get("kernel_source_hash", "").strip() != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return int(fields["hbm_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the fused "
-              "norm has no cross-GPU step (see the sharding notes in DESIGN.md).", file=sys.stderr)
+              "norm has no cross-GPU step -- every (row, group) unit is independent, so rows or "
+              "whole groups shard across GPUs with no communication.", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -361,10 +389,11 @@ def main():
         "config": {"workload": w.name, "rows": w.rows, "width": w.width,
                    "group_size": w.group_size, "eps": w.eps,
                    "round_intermediate": w.round_intermediate,
-                   "rotating_input_sets": pre["sets"], "parallelism": "single GPU"},
+                   "rotating_input_sets": pre["sets"], "settle_ms": args.settle_ms,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_figure(nbytes),
+                     "traffic": traffic_figure(),
                      "algorithmic_bytes_per_launch": nbytes,
                      "kernel_us_avg": round(pre["kernel_ms_avg"] * 1e3, 2)},
         "cpu_baseline": cpu,

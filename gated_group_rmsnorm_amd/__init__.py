@@ -49,6 +49,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("vector_bytes", ctypes.c_int32),
                 ("lanes_per_group", ctypes.c_int32), ("vectors_per_lane", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("rows_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64)]
 
 
@@ -62,7 +63,7 @@ def _load() -> ctypes.CDLL:
     fwd = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32]
     L.ggrms_forward.argtypes = fwd + [vp]
     L.ggrms_forward.restype = i32
-    L.ggrms_forward_with_shape.argtypes = fwd + [i32, i32, vp]
+    L.ggrms_forward_with_shape.argtypes = fwd + [i32, i32, i32, vp]
     L.ggrms_forward_with_shape.restype = i32
     L.ggrms_plan.argtypes = fwd + [ctypes.POINTER(_Plan)]
     L.ggrms_plan.restype = i32
@@ -92,12 +93,13 @@ def ggrms_forward_with_shape(y: int, gate: int, norm_weight: int, out: int, rows
                              width: int, group_size: int, y_row_stride: int,
                              gate_row_stride: int, out_row_stride: int, eps: float, dtype: int,
                              round_intermediate: int, lanes_per_group: int,
-                             vectors_per_lane: int, stream: int) -> int:
+                             vectors_per_lane: int, stream: int,
+                             rows_per_workgroup: int = 0) -> int:
     """ggrms_forward with a caller-chosen kernel shape; returns the status."""
     return _lib.ggrms_forward_with_shape(y, gate, norm_weight, out, rows, width, group_size,
                                          y_row_stride, gate_row_stride, out_row_stride, eps,
                                          dtype, round_intermediate, lanes_per_group,
-                                         vectors_per_lane, stream)
+                                         vectors_per_lane, rows_per_workgroup, stream)
 
 
 def ggrms_plan(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,

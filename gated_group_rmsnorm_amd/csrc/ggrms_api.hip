@@ -34,11 +34,11 @@ bool device_is_gfx950() {
     return st == 1;
 }
 
-const void* pick(int dtype, int kernel, int vb, int lanes, int vpt) {
+const void* pick(int dtype, int kernel, int vb, int lanes, int vpt, int upb) {
     switch (dtype) {
-    case GGRMS_F32: return pick_f32(kernel, vb, lanes, vpt);
-    case GGRMS_F16: return pick_f16(kernel, vb, lanes, vpt);
-    case GGRMS_BF16: return pick_bf16(kernel, vb, lanes, vpt);
+    case GGRMS_F32: return pick_f32(kernel, vb, lanes, vpt, upb);
+    case GGRMS_F16: return pick_f16(kernel, vb, lanes, vpt, upb);
+    case GGRMS_BF16: return pick_bf16(kernel, vb, lanes, vpt, upb);
     default: return nullptr;
     }
 }
@@ -47,18 +47,18 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
                             int64_t rows, int64_t width, int64_t group_size, int64_t y_row_stride,
                             int64_t gate_row_stride, int64_t out_row_stride, float eps,
                             ggrms_dtype_t dtype, int round_intermediate, int force_lanes,
-                            int force_vpt, void* stream) {
+                            int force_vpt, int force_upb, void* stream) {
     LaunchPlan lp;
     ggrms_status_t st = make_plan(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
                                   gate_row_stride, out_row_stride, eps, (int)dtype,
-                                  round_intermediate, force_lanes, force_vpt, &lp);
+                                  round_intermediate, force_lanes, force_vpt, force_upb, &lp);
     if (st != GGRMS_SUCCESS || lp.pub.kernel == GGRMS_KERNEL_NONE) return st;
     if (!device_is_gfx950()) return GGRMS_ERROR_NOT_SUPPORTED;
 
     const ggrms_plan_t& p = lp.pub;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const void* fn = pick((int)dtype, p.kernel, p.vector_bytes, p.lanes_per_group,
-                          p.vectors_per_lane);
+                          p.vectors_per_lane, p.rows_per_workgroup);
     if (!fn) return GGRMS_ERROR_NOT_SUPPORTED;
 
     if (rows == 1) y_row_stride = gate_row_stride = out_row_stride = width;
@@ -76,6 +76,7 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     a.ri = dtype == GGRMS_F32 ? 0 : round_intermediate;
     const int es = lp.esize;
     const int64_t thread_per_unit = p.kernel == GGRMS_KERNEL_WIDE ? kWideBlock : p.lanes_per_group;
+    const int upb = p.rows_per_workgroup;
 
     for (int64_t r0 = 0; r0 < rows; r0 += lp.rows_per_launch) {
         const int64_t r = rows - r0 < lp.rows_per_launch ? rows - r0 : lp.rows_per_launch;
@@ -83,11 +84,15 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
         a.gate = static_cast<const char*>(gate) + r0 * gate_row_stride * es;
         a.out = static_cast<char*>(out) + r0 * out_row_stride * es;
         a.units = (uint32_t)(r * lp.groups);
-        const int64_t blocks = ((int64_t)a.units * thread_per_unit + p.block_threads - 1) /
-                               p.block_threads;
+        a.rows = (uint32_t)r;
+        int64_t blocks;
+        if (p.kernel == GGRMS_KERNEL_BLOCK)
+            blocks = (r + upb - 1) / upb * lp.groups;  // row tiles x groups
+        else
+            blocks = ((int64_t)a.units * thread_per_unit + p.block_threads - 1) / p.block_threads;
         void* args[] = {&a};
-        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3((uint32_t)p.block_threads), args, 0,
-                            s) != hipSuccess)
+        if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3((uint32_t)p.block_threads), args,
+                            (size_t)p.lds_bytes, s) != hipSuccess)
             return GGRMS_ERROR_LAUNCH;
     }
     return GGRMS_SUCCESS;
@@ -104,16 +109,17 @@ extern "C" ggrms_status_t ggrms_forward(const void* y, const void* gate,
                                         void* stream) {
     return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
                                gate_row_stride, out_row_stride, eps, dtype, round_intermediate, 0,
-                               0, stream);
+                               0, 0, stream);
 }
 
 extern "C" ggrms_status_t ggrms_forward_with_shape(
     const void* y, const void* gate, const float* norm_weight, void* out, int64_t rows,
     int64_t width, int64_t group_size, int64_t y_row_stride, int64_t gate_row_stride,
     int64_t out_row_stride, float eps, ggrms_dtype_t dtype, int round_intermediate,
-    int lanes_per_group, int vectors_per_lane, void* stream) {
+    int lanes_per_group, int vectors_per_lane, int rows_per_workgroup, void* stream) {
     if (lanes_per_group == 0 && vectors_per_lane == 0) return GGRMS_ERROR_INVALID_VALUE;
+    if (rows_per_workgroup < 0) return GGRMS_ERROR_INVALID_VALUE;
     return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
                                gate_row_stride, out_row_stride, eps, dtype, round_intermediate,
-                               lanes_per_group, vectors_per_lane, stream);
+                               lanes_per_group, vectors_per_lane, rows_per_workgroup, stream);
 }

@@ -17,9 +17,10 @@ struct KArgs {
     void* out;
     int64_t sy, sg, so;
     uint32_t units;   // (row, group) units in this launch
+    uint32_t rows;    // rows in this launch
     uint32_t groups;  // groups per row
-    uint32_t div_m;   // magic multiplier for unit / groups
-    uint32_t div_s;   // shift for unit / groups
+    uint32_t div_m;   // magic multiplier for x / groups
+    uint32_t div_s;   // shift for x / groups
     uint32_t G;       // group size in elements
     uint32_t nvec;    // vectors per group
     float Gf;         // (float)G
@@ -29,12 +30,19 @@ struct KArgs {
 
 // Supported shapes.  WAVE: lanes in {1..64} (powers of two); vectors per lane
 // 1 for lanes < 64, 1..4 for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
-// vectors per lane in {1,2,4}.  WIDE: 1024 lanes, vectors per lane 0 (it
-// loops over the group).
+// vectors per lane 1..4.  WIDE: 1024 lanes, vectors per lane 0 (it loops over
+// the group).
 constexpr int kWaveBlock = 256;
 constexpr int kWideBlock = 1024;
-constexpr int kMaxBlockLanes = 1024;
-constexpr int kMaxWaveVpt = 4;
+
+// Rows of one group per BLOCK workgroup (the workgroup stays <= 512 threads).
+inline bool rows_per_workgroup_supported(int kernel, int lanes, int upb) {
+    if (upb == 1) return true;
+    if (kernel != GGRMS_KERNEL_BLOCK) return false;
+    if (lanes == 128) return upb == 2 || upb == 4;
+    if (lanes == 256) return upb == 2;
+    return false;
+}
 
 inline bool shape_supported(int kernel, int lanes, int vpt) {
     switch (kernel) {
@@ -44,8 +52,8 @@ inline bool shape_supported(int kernel, int lanes, int vpt) {
                 lanes == 32) &&
                vpt == 1;
     case GGRMS_KERNEL_BLOCK:
-        return (lanes == 128 || lanes == 256 || lanes == 512 || lanes == 1024) &&
-               (vpt == 1 || vpt == 2 || vpt == 4);
+        return (lanes == 128 || lanes == 256 || lanes == 512 || lanes == 1024) && vpt >= 1 &&
+               vpt <= 4;
     case GGRMS_KERNEL_WIDE:
         return lanes == kWideBlock;
     default:
@@ -65,18 +73,20 @@ struct LaunchPlan {
 // Validation and kernel choice; no HIP calls.  Implemented in plan.cpp.
 // force_lanes / force_vpt = 0 / 0 picks the shape; otherwise that shape is
 // used if it is built and covers the group (GGRMS_ERROR_NOT_SUPPORTED if not).
+// force_upb = 0 picks the rows per BLOCK workgroup; otherwise it must be built
+// for the shape and the weights must allow staging.
 ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const void* out,
                          int64_t rows, int64_t width, int64_t group_size, int64_t sy,
                          int64_t sg, int64_t so, float eps, int dtype, int ri,
-                         int force_lanes, int force_vpt, LaunchPlan* plan);
+                         int force_lanes, int force_vpt, int force_upb, LaunchPlan* plan);
 
 // Magic numbers for n / d with n < 2^31 and 1 <= d < 2^31:
 // q = (umulhi(n, m) + n) >> s.
 void div_magic(uint32_t d, uint32_t* m, uint32_t* s);
 
 // Kernel lookup per dtype (kernel tables); nullptr if the shape is not built.
-const void* pick_f32(int kernel, int vb, int lanes, int vpt);
-const void* pick_f16(int kernel, int vb, int lanes, int vpt);
-const void* pick_bf16(int kernel, int vb, int lanes, int vpt);
+const void* pick_f32(int kernel, int vb, int lanes, int vpt, int upb);
+const void* pick_f16(int kernel, int vb, int lanes, int vpt, int upb);
+const void* pick_bf16(int kernel, int vb, int lanes, int vpt, int upb);
 
 }  // namespace ggrms

@@ -242,19 +242,22 @@ __device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t s) {
 
 // ------------------------------------------------------------ one unit
 
-// Lane `sl` of the SEG lanes that own `unit` loads VPT vectors (indices
-// sl, sl+SEG, ...), computes its share, reduces with `reduce`, and stores if
-// `store_ok`.
-template <class T, int VB, int SEG, int VPT, class Reduce>
-__device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t unit, uint32_t sl,
-                                          bool store_ok, Reduce reduce) {
+// Where the output multiply takes its weights from: each lane loads its own
+// from global memory, or the workgroup staged the group's weights in LDS.
+enum class WSource { Global, Lds };
+
+// Lane `sl` of the SEG lanes that own the unit (row n, group g) loads VPT
+// vectors (indices sl, sl+SEG, ...), computes its share, reduces with
+// `reduce`, and stores if `store_ok`.  With WSource::Lds, `wl` points at the
+// group's weights in LDS, valid once `reduce` has passed its barrier.
+template <class T, int VB, int SEG, int VPT, WSource WS, class Reduce>
+__device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g, uint32_t sl,
+                                          bool store_ok, const float* wl, Reduce reduce) {
     using P = Packet<T, VB>;
     using W = typename P::W;
     constexpr int N = P::N;
     using S = typename VecWord<T::kSize>::type;  // element storage
 
-    const uint32_t n = fast_div(unit, a.div_m, a.div_s);
-    const uint32_t g = unit - n * a.groups;
     const int64_t col0 = (int64_t)g * a.G;
     const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy + col0);
     const W* gv =
@@ -264,13 +267,14 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t unit, uint32_
 
     W yr[VPT], gr[VPT];
     float wr[VPT][N];
+    uint32_t ci[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const uint32_t idx = sl + k * SEG;
-        const uint32_t ci = idx < a.nvec ? idx : a.nvec - 1;
-        yr[k] = load_stream(yv + ci);
-        gr[k] = load_stream(gv + ci);
-        load_weights<N>(wp + (int64_t)ci * N, wr[k]);
+        ci[k] = idx < a.nvec ? idx : a.nvec - 1;
+        yr[k] = load_stream(yv + ci[k]);
+        gr[k] = load_stream(gv + ci[k]);
+        if constexpr (WS == WSource::Global) load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
     }
 
     // a = y * silu(gate) for every loaded element; lanes past the group's end
@@ -316,6 +320,10 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t unit, uint32_
 
     const float m2 = reduce(acc);
     const float nf = 1.0f / __builtin_sqrtf(m2 / a.Gf + a.eps);
+    if constexpr (WS == WSource::Lds) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) load_weights<N>(wl + ci[k] * N, wr[k]);
+    }
 
     // Wait for every load (the weights included) before the first store:
     // vmcnt retires in issue order on gfx9, so a weight load still counted
@@ -356,30 +364,63 @@ __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
     const uint32_t t = blockIdx.x * (uint32_t)kWaveBlock + threadIdx.x;
     const uint32_t unit = t / SEG;
     if (unit >= a.units) return;  // whole segments leave together
-    unit_pass<T, VB, SEG, VPT>(a, unit, threadIdx.x & (SEG - 1), true,
-                               [](float v) { return segment_sum<SEG>(v); });
+    const uint32_t n = fast_div(unit, a.div_m, a.div_s);
+    unit_pass<T, VB, SEG, VPT, WSource::Global>(a, n, unit - n * a.groups, threadIdx.x & (SEG - 1),
+                                                true, nullptr,
+                                                [](float v) { return segment_sum<SEG>(v); });
 }
 
 // BLOCK: a unit spans SEG/64 waves; the per-wave sums meet in LDS after one
-// barrier and every wave adds them in the same order.
-template <class T, int VB, int SEG, int VPT>
-__global__ __launch_bounds__(SEG > 256 ? SEG : 256) void ggrms_block_kernel(KArgs a) {
-    constexpr int BT = SEG > 256 ? SEG : 256;
+// barrier and every wave adds them in the same order.  A workgroup holds UPB
+// units: UPB consecutive rows of one group (workgroup b = row tile b / groups,
+// group b % groups).  With UPB > 1 the group's f32 weights are fetched once
+// per workgroup -- contiguous 16-byte loads spread over all its threads --
+// and parked in LDS before the reduction barrier, instead of every unit
+// fetching its own copy: weight traffic from L2 falls by UPB and the L1
+// miss slots it held go back to the HBM streams.
+template <class T, int VB, int SEG, int VPT, int UPB>
+__global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
+    constexpr int BT = SEG * UPB;
     constexpr int WPG = SEG / 64;
+    constexpr int N = Packet<T, VB>::N;
     __shared__ float part[BT / 64];
-    const uint32_t t = blockIdx.x * (uint32_t)BT + threadIdx.x;
-    uint32_t unit = t / SEG;
-    const bool live = unit < a.units;
-    if (!live) unit = a.units - 1;  // stay in bounds and reach the barrier
+    extern __shared__ __attribute__((aligned(16))) float wl[];  // a.G floats when UPB > 1
+    const uint32_t tile = fast_div(blockIdx.x, a.div_m, a.div_s);
+    const uint32_t g = blockIdx.x - tile * a.groups;
+    const uint32_t u = threadIdx.x / SEG;
+    uint32_t n = tile * UPB + u;
+    const bool live = n < a.rows;
+    if (!live) n = a.rows - 1;  // stay in bounds and reach the barrier
     const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t first_wave = (threadIdx.x / SEG) * WPG;
-    unit_pass<T, VB, SEG, VPT>(a, unit, threadIdx.x & (SEG - 1), live, [&](float v) {
+
+    // Staged weights: G/4 float4 of the group, thread j takes j, j+BT, ...
+    constexpr int SV = UPB > 1 ? (VPT * N + 4 * UPB - 1) / (4 * UPB) : 1;
+    f32x4 wst[SV];
+    if constexpr (UPB > 1) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.w + (int64_t)g * a.G);
+        const uint32_t nw4 = a.G / 4;
+#pragma unroll
+        for (int i = 0; i < SV; ++i) {
+            const uint32_t j = threadIdx.x + i * BT;
+            if (j < nw4) wst[i] = src[j];
+        }
+    }
+    constexpr WSource WS = UPB > 1 ? WSource::Lds : WSource::Global;
+    unit_pass<T, VB, SEG, VPT, WS>(a, n, g, threadIdx.x & (SEG - 1), live, wl, [&](float v) {
         const float s = segment_sum<64>(v);
         if ((threadIdx.x & 63) == 0) part[wave] = s;
+        if constexpr (UPB > 1) {
+            const uint32_t nw4 = a.G / 4;
+#pragma unroll
+            for (int i = 0; i < SV; ++i) {
+                const uint32_t j = threadIdx.x + i * BT;
+                if (j < nw4) reinterpret_cast<f32x4*>(wl)[j] = wst[i];
+            }
+        }
         __syncthreads();
         float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < WPG; ++i) m += part[first_wave + i];
+        for (int i = 0; i < WPG; ++i) m += part[u * WPG + i];
         return m;
     });
 }
@@ -441,35 +482,40 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
 // ------------------------------------------------------------ table
 
 template <class T, int VB>
-inline const void* pick_vb(int kernel, int lanes, int vpt) {
+inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
 #define GG_W(L, V) \
     if (lanes == L && vpt == V) return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, L, V>)
-#define GG_B(L, V) \
-    if (lanes == L && vpt == V) return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V>)
+#define GG_B(L, V, U)                     \
+    if (lanes == L && vpt == V && upb == U) \
+    return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V, U>)
+#define GG_B4(L, U) GG_B(L, 1, U); GG_B(L, 2, U); GG_B(L, 3, U); GG_B(L, 4, U)
     if (kernel == GGRMS_KERNEL_WAVE) {
+        if (upb != 1) return nullptr;
         GG_W(1, 1); GG_W(2, 1); GG_W(4, 1); GG_W(8, 1); GG_W(16, 1); GG_W(32, 1);
         GG_W(64, 1); GG_W(64, 2); GG_W(64, 3); GG_W(64, 4);
     } else if (kernel == GGRMS_KERNEL_BLOCK) {
-        GG_B(128, 1); GG_B(128, 2); GG_B(128, 4);
-        GG_B(256, 1); GG_B(256, 2); GG_B(256, 4);
-        GG_B(512, 1); GG_B(512, 2); GG_B(512, 4);
-        GG_B(1024, 1); GG_B(1024, 2); GG_B(1024, 4);
+        GG_B4(128, 1); GG_B4(128, 2); GG_B4(128, 4);
+        GG_B4(256, 1); GG_B4(256, 2);
+        GG_B4(512, 1);
+        GG_B4(1024, 1);
     } else if (kernel == GGRMS_KERNEL_WIDE) {
+        if (upb != 1) return nullptr;
         return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB>);
     }
 #undef GG_W
 #undef GG_B
+#undef GG_B4
     return nullptr;
 }
 
 template <class T>
-inline const void* pick_type(int kernel, int vb, int lanes, int vpt) {
+inline const void* pick_type(int kernel, int vb, int lanes, int vpt, int upb) {
     switch (vb) {
-    case 16: return pick_vb<T, 16>(kernel, lanes, vpt);
-    case 8: return pick_vb<T, 8>(kernel, lanes, vpt);
-    case 4: return pick_vb<T, 4>(kernel, lanes, vpt);
+    case 16: return pick_vb<T, 16>(kernel, lanes, vpt, upb);
+    case 8: return pick_vb<T, 8>(kernel, lanes, vpt, upb);
+    case 4: return pick_vb<T, 4>(kernel, lanes, vpt, upb);
     case 2:
-        if constexpr (T::kSize == 2) return pick_vb<T, 2>(kernel, lanes, vpt);
+        if constexpr (T::kSize == 2) return pick_vb<T, 2>(kernel, lanes, vpt, upb);
         return nullptr;
     default: return nullptr;
     }

@@ -57,45 +57,57 @@ int kernel_for_shape(int lanes, int vpt) {
     return lanes <= 64 ? GGRMS_KERNEL_WAVE : GGRMS_KERNEL_BLOCK;
 }
 
-// Kernel shape for a group of nvec vectors.
-void choose_shape(int64_t nvec, int* kernel, int* lanes, int* vpt) {
+// Kernel shape for a group of nvec vectors, and the rows of one group a
+// BLOCK workgroup takes (1 means no weight staging).  The table comes from a
+// sweep of every built shape on gfx950 at ~377 MB per launch (8192-row bf16
+// jobs over group widths 8..32768, plus fp16 and f32 spot checks), timed
+// after the clocks settle:
+//   * up to 64 vectors: one vector per lane, the smallest power-of-two lane
+//     segment, several groups per wave (WAVE kernel, 77-80% of HBM peak);
+//   * 65-96: one wave, two vectors per lane (74%; 128 lanes idle too many);
+//   * 97-512: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
+//     workgroup sharing staged weights (79-81%); 4 rows only with one vector
+//     per lane, since the staging registers cost occupancy at 2+;
+//   * 513-4096: 256-1024 lanes x 4 vectors, one row per workgroup (staging
+//     at 4 vectors per lane measured 57% against 76% without);
+//   * wider groups loop over the row twice (WIDE).
+struct ShapeRule {
+    int64_t max_nvec;
+    int kernel, lanes, vpt, upb;
+};
+const ShapeRule kRules[] = {
+    {96, GGRMS_KERNEL_WAVE, 64, 2, 1},
+    {128, GGRMS_KERNEL_BLOCK, 128, 1, 4},
+    {192, GGRMS_KERNEL_BLOCK, 128, 2, 2},
+    {256, GGRMS_KERNEL_BLOCK, 256, 1, 2},
+    {384, GGRMS_KERNEL_BLOCK, 128, 3, 2},
+    {512, GGRMS_KERNEL_BLOCK, 256, 2, 2},
+    {1024, GGRMS_KERNEL_BLOCK, 256, 4, 1},
+    {2048, GGRMS_KERNEL_BLOCK, 512, 4, 1},
+    {4096, GGRMS_KERNEL_BLOCK, 1024, 4, 1},
+};
+
+void choose_shape(int64_t nvec, int* kernel, int* lanes, int* vpt, int* upb) {
     if (nvec <= 64) {
-        // Narrow groups: the smallest power-of-two lane segment, several
-        // groups per wave, one vector per lane.
         *kernel = GGRMS_KERNEL_WAVE;
         *lanes = (int)round_up_pow2(nvec);
         *vpt = 1;
+        *upb = 1;
         return;
     }
-    if (nvec <= 64 * kMaxWaveVpt) {
-        // One wave per group, up to four vectors in flight per lane.
-        *kernel = GGRMS_KERNEL_WAVE;
-        *lanes = 64;
-        *vpt = (int)((nvec + 63) / 64);
-        return;
-    }
-    if (nvec <= (int64_t)kMaxBlockLanes * 4) {
-        // Several waves per group: fewest idle slots; among equals prefer two
-        // vectors per lane, then one, then four.
-        static const int pref_vpt[3] = {2, 1, 4};
-        int64_t best_slots = INT64_MAX;
-        for (int vi = 0; vi < 3; ++vi) {
-            const int v = pref_vpt[vi];
-            for (int l = 128; l <= kMaxBlockLanes; l <<= 1) {
-                const int64_t slots = (int64_t)l * v;
-                if (slots >= nvec && slots < best_slots) {
-                    best_slots = slots;
-                    *kernel = GGRMS_KERNEL_BLOCK;
-                    *lanes = l;
-                    *vpt = v;
-                }
-            }
+    for (const ShapeRule& r : kRules) {
+        if (nvec <= r.max_nvec) {
+            *kernel = r.kernel;
+            *lanes = r.lanes;
+            *vpt = r.vpt;
+            *upb = r.upb;
+            return;
         }
-        return;
     }
     *kernel = GGRMS_KERNEL_WIDE;
     *lanes = kWideBlock;
     *vpt = 0;
+    *upb = 1;
 }
 
 }  // namespace
@@ -114,7 +126,7 @@ void div_magic(uint32_t d, uint32_t* m, uint32_t* s) {
 ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const void* out,
                          int64_t rows, int64_t width, int64_t group_size, int64_t sy,
                          int64_t sg, int64_t so, float eps, int dtype, int ri,
-                         int force_lanes, int force_vpt, LaunchPlan* plan) {
+                         int force_lanes, int force_vpt, int force_upb, LaunchPlan* plan) {
     if (!plan) return GGRMS_ERROR_INVALID_VALUE;
     memset(plan, 0, sizeof *plan);
     if (rows < 0 || width <= 0 || group_size <= 0 || width % group_size != 0)
@@ -166,7 +178,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         }
     }
     const int64_t nvec = group_size * esize / vb;
-    int kernel = 0, lanes = 0, vpt = 0;
+    int kernel = 0, lanes = 0, vpt = 0, rule_upb = 1;
     if (force_lanes || force_vpt) {
         kernel = kernel_for_shape(force_lanes, force_vpt);
         lanes = force_lanes;
@@ -174,13 +186,32 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         if (!shape_supported(kernel, lanes, vpt)) return GGRMS_ERROR_NOT_SUPPORTED;
         if (kernel != GGRMS_KERNEL_WIDE && (int64_t)lanes * vpt < nvec)
             return GGRMS_ERROR_NOT_SUPPORTED;
+        rule_upb = rows_per_workgroup_supported(kernel, lanes, 4) ? 4
+                   : rows_per_workgroup_supported(kernel, lanes, 2) ? 2 : 1;
+        if (vpt > 1 && rule_upb > 2) rule_upb = 2;
+        if (vpt > 2) rule_upb = 1;
     } else {
-        choose_shape(nvec, &kernel, &lanes, &vpt);
+        choose_shape(nvec, &kernel, &lanes, &vpt, &rule_upb);
     }
 
     const int64_t groups = plan->groups;
+    // Rows of one group per BLOCK workgroup: the group's weights are staged
+    // once in LDS with 16-byte loads, so the weight must be 16-byte aligned
+    // and the group a multiple of 4 floats; no more rows than the job has.
+    const bool can_stage = pw % 16 == 0 && group_size % 4 == 0;
+    int upb = 1;
+    if (force_upb) {
+        if (!rows_per_workgroup_supported(kernel, lanes, force_upb) ||
+            (force_upb > 1 && !can_stage))
+            return GGRMS_ERROR_NOT_SUPPORTED;
+        upb = force_upb;
+    } else if (can_stage) {
+        upb = rule_upb;
+        while (upb > 1 && (rows < upb || !rows_per_workgroup_supported(kernel, lanes, upb)))
+            upb >>= 1;
+    }
     int block = kWaveBlock;
-    if (kernel == GGRMS_KERNEL_BLOCK) block = lanes > 256 ? lanes : 256;
+    if (kernel == GGRMS_KERNEL_BLOCK) block = lanes * upb;
     if (kernel == GGRMS_KERNEL_WIDE) block = kWideBlock;
     // Units per launch stay below 2^31 and so do threads per launch, so the
     // kernels index with 32-bit integers; larger jobs are split by rows.
@@ -193,8 +224,10 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     int64_t workgroups = 0;
     for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
         const int64_t r = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
-        const int64_t units = r * groups;
-        workgroups += (units * thread_per_unit + block - 1) / block;
+        if (kernel == GGRMS_KERNEL_BLOCK)
+            workgroups += (r + upb - 1) / upb * groups;
+        else
+            workgroups += (r * groups * thread_per_unit + block - 1) / block;
     }
     plan->nvec = nvec;
     plan->rows_per_launch = rows_per_launch;
@@ -204,6 +237,8 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->pub.vectors_per_lane = vpt;
     plan->pub.block_threads = block;
     plan->pub.launches = (int32_t)launches;
+    plan->pub.rows_per_workgroup = upb;
+    plan->pub.lds_bytes = upb > 1 ? (int32_t)(group_size * 4) : 0;
     plan->pub.workgroups = workgroups;
     return GGRMS_SUCCESS;
 }
@@ -219,7 +254,7 @@ extern "C" ggrms_status_t ggrms_plan(const void* y, const void* gate, const floa
     ggrms::LaunchPlan lp;
     const ggrms_status_t st = ggrms::make_plan(y, gate, norm_weight, out, rows, width, group_size,
                                                y_row_stride, gate_row_stride, out_row_stride, eps,
-                                               (int)dtype, round_intermediate, 0, 0, &lp);
+                                               (int)dtype, round_intermediate, 0, 0, 0, &lp);
     if (st == GGRMS_SUCCESS) *plan = lp.pub;
     return st;
 }

@@ -4,8 +4,8 @@
 
 namespace ggrms {
 
-const void* pick_f32(int kernel, int vb, int lanes, int vpt) {
-    return pick_type<TF32>(kernel, vb, lanes, vpt);
+const void* pick_f32(int kernel, int vb, int lanes, int vpt, int upb) {
+    return pick_type<TF32>(kernel, vb, lanes, vpt, upb);
 }
 
 }  // namespace ggrms

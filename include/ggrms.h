@@ -120,6 +120,8 @@ typedef struct {
     int32_t vectors_per_lane; /* vectors each lane holds per group (0 for WIDE: it loops) */
     int32_t block_threads;    /* threads per workgroup */
     int32_t launches;         /* kernel launches (rows are split if a grid would be too large) */
+    int32_t rows_per_workgroup; /* BLOCK: rows of one group per workgroup (weights shared in LDS) */
+    int32_t lds_bytes;        /* dynamic LDS per workgroup (the staged weights) */
     int64_t workgroups;       /* workgroups over all launches */
 } ggrms_plan_t;
 
@@ -142,13 +144,19 @@ ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_wei
  *
  *   lanes_per_group   1, 2, 4, ..., 64 (WAVE kernel) or 128, 256, 512, 1024
  *                     (BLOCK kernel; 1024 with vectors_per_lane = 0 is WIDE)
- *   vectors_per_lane  1 for lanes < 64; 1..4 for 64 lanes; 1, 2 or 4 for the
- *                     BLOCK kernel; 0 for WIDE
+ *   vectors_per_lane  1 for lanes < 64; 1..4 for 64 lanes or the BLOCK
+ *                     kernel; 0 for WIDE
+ *   rows_per_workgroup  0 to let the library choose; 1; or, for the BLOCK
+ *                     kernel, 2 or 4 with 128 lanes and 2 with 256 lanes (the
+ *                     workgroup's rows share one group, whose weights are
+ *                     staged once in LDS; needs a 16-byte aligned weight and
+ *                     group_size % 4 == 0)
  *
  * The vector width still follows the pointers' alignment.  Returns
- * GGRMS_ERROR_INVALID_VALUE for 0 / 0 (use ggrms_forward), and
- * GGRMS_ERROR_NOT_SUPPORTED for a shape that is not built or whose
- * lanes_per_group * vectors_per_lane vectors do not cover one group.
+ * GGRMS_ERROR_INVALID_VALUE for lanes and vectors both 0 (use
+ * ggrms_forward), and GGRMS_ERROR_NOT_SUPPORTED for a shape that is not
+ * built, whose lanes_per_group * vectors_per_lane vectors do not cover one
+ * group, or whose rows_per_workgroup cannot be used.
  */
 ggrms_status_t ggrms_forward_with_shape(const void* y, const void* gate,
                                         const float* norm_weight, void* out, int64_t rows,
@@ -156,7 +164,8 @@ ggrms_status_t ggrms_forward_with_shape(const void* y, const void* gate,
                                         int64_t y_row_stride, int64_t gate_row_stride,
                                         int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
                                         int round_intermediate, int lanes_per_group,
-                                        int vectors_per_lane, void* stream);
+                                        int vectors_per_lane, int rows_per_workgroup,
+                                        void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* ggrms_status_string(ggrms_status_t status);

@@ -127,13 +127,22 @@ def _plan(g, rows, width, G, dtype, sy=None, sg=None, so=None, y=A, gate=A + (1 
 
 
 def test_plans_for_the_workloads(g):
-    # 8192x7680 bf16, G = 960: 120 16-byte vectors per group -> one wave, two per lane
+    # 8192x7680 bf16, G = 960: 120 16-byte vectors per group -> two waves, one vector per lane
+    # and four rows of one group per workgroup, sharing the group's weights in LDS
     p = _plan(g, 8192, 7680, 960, BF16)
-    assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 16, 64, 2)
-    assert p["workgroups"] == 8192 * 8 * 64 // 256 and p["launches"] == 1
-    # decode 1x7680: 8 groups
+    assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("block", 16, 128, 1)
+    assert (p["rows_per_workgroup"], p["block_threads"], p["lds_bytes"]) == (4, 512, 960 * 4)
+    assert p["workgroups"] == 8192 // 4 * 8 and p["launches"] == 1
+    # decode 1x7680: 8 groups of two waves, one row per workgroup, no staging
     p = _plan(g, 1, 7680, 960, BF16)
-    assert p["workgroups"] == 2
+    assert (p["workgroups"], p["rows_per_workgroup"], p["lds_bytes"]) == (8, 1, 0)
+    # three rows: two per workgroup
+    assert _plan(g, 3, 7680, 960, BF16)["rows_per_workgroup"] == 2
+    # weights not 16-byte aligned: no staging
+    p = _plan(g, 64, 7680, 960, BF16, w=A + (2 << 30) + 16)
+    assert p["rows_per_workgroup"] == 4
+    p = _plan(g, 64, 7680, 960, F32, w=A + (2 << 30) + 8)
+    assert p["rows_per_workgroup"] == 1
     # 16384x8192 fp16, G = 128: 16 vectors -> 16-lane segments, four groups per wave
     p = _plan(g, 16384, 8192, 128, F16)
     assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 16, 16, 1)
@@ -161,25 +170,31 @@ def test_vector_width_follows_alignment(g):
 
 
 def test_kernel_family_by_group_width(g):
+    """The measured shape table: (kernel, lanes, vectors per lane, rows per
+    workgroup) by 16-byte vectors per group."""
     cases = {
-        8: ("wave", 1, 1),        # one 16-byte vector: a group per lane
-        64: ("wave", 8, 1),
-        512: ("wave", 64, 1),
-        960: ("wave", 64, 2),
-        1032: ("wave", 64, 3),   # 129 vectors
-        2048: ("wave", 64, 4),
-        2056: ("block", 128, 3),  # 257 vectors -> 512 slots beat 384? see below
-        7680: ("block", 512, 2),
-        32768: ("block", 1024, 4),
-        32776: ("wide", 1024, 0),
+        8: ("wave", 1, 1, 1),         # 1 vector: a group per lane
+        64: ("wave", 8, 1, 1),
+        512: ("wave", 64, 1, 1),      # 64
+        640: ("wave", 64, 2, 1),      # 80
+        960: ("block", 128, 1, 4),    # 120
+        1032: ("block", 128, 2, 4 // 2),  # 129
+        1536: ("block", 128, 2, 2),   # 192
+        2048: ("block", 256, 1, 2),   # 256
+        2056: ("block", 128, 3, 2),   # 257
+        4096: ("block", 256, 2, 2),   # 512
+        7680: ("block", 256, 4, 1),   # 960
+        16384: ("block", 512, 4, 1),  # 2048
+        32768: ("block", 1024, 4, 1),
+        32776: ("wide", 1024, 0, 1),
     }
-    for G, (kname, lanes, vpt) in cases.items():
-        p = _plan(g, 2, G, G, BF16)
-        if G == 2056:
-            # 257 vectors: the best shapes cover 384 (128x3 is not built) or 512
-            assert p["kernel_name"] == "block" and p["lanes_per_group"] * p["vectors_per_lane"] == 512
-            continue
-        assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"]) == (kname, lanes, vpt), G
+    for G, want in cases.items():
+        p = _plan(g, 8, G, G, BF16)
+        got = (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["rows_per_workgroup"])
+        assert got == want, (G, got)
+    # rows per workgroup never exceeds the rows there are
+    assert _plan(g, 1, 960, 960, BF16)["rows_per_workgroup"] == 1
+    assert _plan(g, 3, 960, 960, BF16)["rows_per_workgroup"] == 2
 
 
 def test_division_magic_numbers(tmp_path):

@@ -107,9 +107,10 @@ def run_gpu(g, y, gate, w, out, rows, width, G, sy, sg, so, eps, dtype, ri, shap
     if shape is None:
         return g.ggrms_forward(y.data_ptr(), gate.data_ptr(), w.data_ptr(), out.data_ptr(), rows,
                                width, G, sy, sg, so, eps, dtype, ri, s)
+    upb = shape[2] if len(shape) > 2 else 0
     return g.ggrms_forward_with_shape(y.data_ptr(), gate.data_ptr(), w.data_ptr(), out.data_ptr(),
                                       rows, width, G, sy, sg, so, eps, dtype, ri, shape[0],
-                                      shape[1], s)
+                                      shape[1], s, upb)
 
 
 def random_case(rows, width, dtype, seed, dist=("normal", 1.0), gate_dist=None):
@@ -199,45 +200,46 @@ def test_group_size_sweep(g, orc, G, dtype):
 
 
 # every built (lanes, vectors) shape, forced, on groups it covers
-SHAPES = [(1, 1), (2, 1), (4, 1), (8, 1), (16, 1), (32, 1), (64, 1), (64, 2), (64, 3), (64, 4),
-          (128, 1), (128, 2), (128, 4), (256, 1), (256, 2), (256, 4), (512, 1), (512, 2),
-          (512, 4), (1024, 1), (1024, 2), (1024, 4), (1024, 0)]
+SHAPES = [(1, 1), (2, 1), (4, 1), (8, 1), (16, 1), (32, 1), (64, 1), (64, 2), (64, 3), (64, 4)] + \
+         [(l, v, 1) for l in (128, 256, 512, 1024) for v in (1, 2, 3, 4)] + \
+         [(128, v, u) for v in (1, 2, 3, 4) for u in (2, 4)] + [(256, v, 2) for v in (1, 2, 3, 4)] + \
+         [(1024, 0)]
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_forced_shapes_agree(g, orc, shape):
     """Each kernel shape, forced, on a bf16 group it covers (and one it covers
     with idle lanes) matches the oracle; WAVE and BLOCK kernels agree bit for
     bit with the planner's choice where both cover the group."""
-    lanes, vpt = shape
+    lanes, vpt = shape[:2]
     cap = lanes * (vpt or 8)
     for nvec in sorted({max(1, cap), max(1, cap - 3), max(1, (cap + 1) // 2)}):
         G = nvec * 8  # 16-byte vectors of bf16
         if G > 65536:
             continue
-        rows, groups = 3, 2
+        rows, groups = 7, 2  # 7 rows: the last row tile of 2 or 4 is partly empty
         stats = check_contiguous(g, orc, rows, G * groups, G, BF16, 1, seed=nvec + lanes,
                                  shape=shape, tag=f"forced {lanes}x{vpt} G={G}")
         assert stats["max_ulp"] <= 2
 
 
 def test_forced_shape_matches_auto_bitwise(g):
-    """The same data through the WAVE kernel (64 lanes x 2), the BLOCK kernel
-    (128 x 1, 256 x 1) and the two-pass kernel gives identical bits: the
-    group sums differ only in association order, which these shapes share
-    up to the final per-wave combine -- so compare against tolerance, and
-    require WAVE 64x2 == auto."""
+    """The same data through the planner's choice (two waves x one vector for
+    960-wide bf16 groups) and through other shapes covering the group: the
+    forced 128x1 equals the automatic launch bit for bit; the others differ
+    only in the association order of the group sum, within 2 ulp."""
     rows, G, groups = 64, 960, 8
     y, gt, w = random_case(rows, G * groups, BF16, seed=5)
     yd, gd, wd = dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(w).cuda()
     outs = {}
-    for shape in (None, (64, 2), (128, 1), (256, 1), (1024, 0)):
+    for shape in (None, (128, 1, 4), (128, 1, 1), (128, 1, 2), (64, 2), (256, 1), (1024, 0)):
         od = torch.empty_like(yd)
         assert run_gpu(g, yd, gd, wd, od, rows, G * groups, G, G * groups, G * groups,
                        G * groups, 1e-5, BF16, 1, shape) == g.SUCCESS
         torch.cuda.synchronize()
         outs[shape] = host_bits(od, BF16)
-    assert np.array_equal(outs[None], outs[(64, 2)])
+    for shape in ((128, 1, 4), (128, 1, 1), (128, 1, 2)):
+        assert np.array_equal(outs[None], outs[shape]), shape
     for shape, o in outs.items():
         d = np.abs(ulp_key(o) - ulp_key(outs[None]))
         assert d.max() <= 2, shape
@@ -247,9 +249,12 @@ def test_shape_rejections(g):
     yd = torch.zeros(4 * 960, dtype=torch.bfloat16, device="cuda")
     wd = torch.ones(960, dtype=torch.float32, device="cuda")
     od = torch.empty_like(yd)
-    # 64 lanes x 1 vector cannot cover 120 vectors; 48 lanes is not built
+    # 64 lanes x 1 vector cannot cover 120 vectors; 48 lanes is not built;
+    # rows per workgroup only for 128- and 256-lane groups
     for shape, want in (((64, 1), g.ERROR_NOT_SUPPORTED), ((48, 1), g.ERROR_NOT_SUPPORTED),
-                        ((64, 5), g.ERROR_NOT_SUPPORTED), ((0, 0), g.ERROR_INVALID_VALUE)):
+                        ((64, 5), g.ERROR_NOT_SUPPORTED), ((0, 0), g.ERROR_INVALID_VALUE),
+                        ((64, 2, 2), g.ERROR_NOT_SUPPORTED), ((512, 1, 2), g.ERROR_NOT_SUPPORTED),
+                        ((128, 1, 3), g.ERROR_NOT_SUPPORTED), ((128, 1, 8), g.ERROR_NOT_SUPPORTED)):
         assert run_gpu(g, yd, yd, wd, od, 4, 960, 960, 960, 960, 960, 1e-5, BF16, 1,
                        shape) == want
 
@@ -324,6 +329,28 @@ def test_in_place(g, orc, target):
                    1) == g.SUCCESS
     torch.cuda.synchronize()
     assert_parity(host_bits(od, BF16), ref, BF16, f"in place into {target}")
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=DT_IDS.get)
+def test_unaligned_weight(g, orc, dtype):
+    """A weight pointer 4 bytes past a 16-byte boundary: no LDS staging and
+    narrower accesses; the result still matches the oracle."""
+    rows, width, G = 65, 7680, 960
+    y, gt, w = random_case(rows, width, dtype, seed=88)
+    yd, gd = dev_buf(y, dtype), dev_buf(gt, dtype)
+    wbuf = torch.zeros(width + 4, dtype=torch.float32, device="cuda")
+    wbuf[1:width + 1] = torch.from_numpy(w).cuda()
+    od = torch.empty_like(yd)
+    st, p = g.ggrms_plan(yd.data_ptr(), gd.data_ptr(), wbuf[1:].data_ptr(), od.data_ptr(), rows,
+                         width, G, width, width, width, 1e-5, dtype, 1)
+    assert st == g.SUCCESS and p["rows_per_workgroup"] == 1
+    assert run_gpu(g, yd, gd, wbuf[1:], od, rows, width, G, width, width, width, 1e-5, dtype,
+                   1) == g.SUCCESS
+    torch.cuda.synchronize()
+    ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                      gate_row_stride=width, out_row_stride=width, eps=1e-5, dtype=dtype,
+                      round_intermediate=1)
+    assert_parity(host_bits(od, dtype), ref, dtype, "unaligned weight")
 
 
 def test_strided_equals_contiguous(g):
