@@ -10,8 +10,9 @@ inputs in the 256 MB last-level cache.
 Printed (one JSON line): whole-job HBM throughput in GB/s over the timed
 steps, the kernel's roofline figures (event-timed average launch), the
 decode latency (1 x 7680, 21 layers back to back, eager and graph-replayed,
-next to an empty kernel of the same grid), and the CPU oracle timed on a
-bounded sample of the same workload.
+next to an empty kernel of the same grid), the unfused four-op chain in
+PyTorch eager timed the same ways, and the CPU oracle timed on a bounded
+sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|copy]
 """
@@ -58,7 +59,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for this long after the warmup steps")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads", "unfused"],
+                    default=None)
     ap.add_argument("--decode-bursts", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -284,6 +286,80 @@ def bench_workloads(torch, g, S, steps):
     return out
 
 
+def unfused_chain(torch, y, gate, w, group_size, eps, ri):
+    """The four-op chain the fused kernel replaces, in PyTorch eager: widen,
+    silu(gate) * y, group RMSNorm (torch's rms_norm over groups), weight
+    multiply and narrow (with the intermediate cast when ri is set)."""
+    rows, width = y.shape
+    a = torch.nn.functional.silu(gate.float()) * y.float()
+    t = torch.nn.functional.rms_norm(a.view(rows, width // group_size, group_size),
+                                     (group_size,), eps=eps).view(rows, width)
+    if ri:
+        t = t.to(y.dtype).float()
+    return (w * t).to(y.dtype)
+
+
+def bench_unfused(torch, S, steps):
+    """Per-launch time of the unfused chain beside the fused kernel: the
+    prefill batch (eager, back to back) and the 21-layer decode burst (eager
+    and as one replayed graph)."""
+    import numpy as np
+
+    res = {}
+    w = S.WORKLOADS[PREFILL]
+    yb, gb, wt, _ = S.make_inputs(w)
+    y = torch.from_numpy(yb.view(np.int16)).view(torch.bfloat16).reshape(w.rows, w.width).cuda()
+    gt = torch.from_numpy(gb.view(np.int16)).view(torch.bfloat16).reshape(w.rows, w.width).cuda()
+    wd = torch.from_numpy(wt).cuda()
+    run = lambda i: unfused_chain(torch, y, gt, wd, w.group_size, w.eps, w.round_intermediate)
+    settle(torch, run, 0.2)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        run(i)
+    b.record()
+    torch.cuda.synchronize()
+    res["prefill_us"] = a.elapsed_time(b) * 1e3 / steps
+    del y, gt
+    torch.cuda.empty_cache()
+
+    d = S.WORKLOADS[DECODE]
+    layers = []
+    for layer in range(S.DECODE_LAYERS):
+        yb, gb, wt, _ = S.make_inputs(d, layer)
+        layers.append((torch.from_numpy(yb.view(np.int16)).view(torch.bfloat16).reshape(1, d.width).cuda(),
+                       torch.from_numpy(gb.view(np.int16)).view(torch.bfloat16).reshape(1, d.width).cuda(),
+                       torch.from_numpy(wt).cuda()))
+
+    def burst(i=0):
+        for ly, lg, lw in layers:
+            unfused_chain(torch, ly, lg, lw, d.group_size, d.eps, d.round_intermediate)
+
+    settle(torch, burst, 0.1)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(100)]
+    for x, z in evs:
+        x.record()
+        burst()
+        z.record()
+    torch.cuda.synchronize()
+    res["decode_us_per_layer_eager"] = statistics.median(x.elapsed_time(z) for x, z in evs) * 1e3 / len(layers)
+    cs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        burst()
+    settle(torch, lambda i: graph.replay(), 0.1)
+    for x, z in evs:
+        x.record()
+        graph.replay()
+        z.record()
+    torch.cuda.synchronize()
+    res["decode_us_per_layer_graph"] = statistics.median(x.elapsed_time(z) for x, z in evs) * 1e3 / len(layers)
+    log(f"unfused chain: {json.dumps(res)}")
+    return res
+
+
 def cpu_baseline(S, seconds):
     """The oracle, single-threaded, on leading rows of the prefill workload,
     repeated for about `seconds` of CPU time."""
@@ -361,12 +437,16 @@ def main():
     if args.only == "workloads":
         bench_workloads(torch, g, S, args.steps)
         return
+    if args.only == "unfused":
+        bench_unfused(torch, S, 100)
+        return
 
     pre = bench_prefill(torch, g, S, args, shape)
     if args.only == "prefill":
         return
     decode = bench_decode(torch, g, S, args.decode_bursts)
     others = bench_workloads(torch, g, S, max(20, args.steps // 4))
+    unfused = bench_unfused(torch, S, 100)
     cpu = None if args.no_cpu_baseline else cpu_baseline(S, args.cpu_seconds)
 
     w = pre["workload"]
@@ -399,6 +479,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in decode.items()},
         "other_workloads": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in others.items()},
+        "unfused_chain_torch_eager": {k: round(v, 3) for k, v in unfused.items()},
         "kernel": pre["plan"],
     }
     print(json.dumps(line), flush=True)

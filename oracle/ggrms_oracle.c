@@ -21,6 +21,12 @@
  * and narrows only at the store, as the page "com.microsoft.GatedRMSNorm"
  * (Description section) puts it for its own operator.
  *
+ * That page's operator itself normalises before gating,
+ *     Y = X * rsqrt(mean(X^2) + eps) * scale * SiLU(gate),
+ * with `scale` holding one value per column of a group, shared by every group
+ * (Inputs table).  It is available with GGRMS_ORACLE_NORM_BEFORE_GATE and
+ * GGRMS_ORACLE_WEIGHT_PER_GROUP (which also applies to the gate-first form).
+ *
  * Readings where the pages say nothing (each is listed in the design notes):
  *   - silu(x) = x / (1 + exp(-x)), evaluated in f32 with the C library expf.
  *   - m2 is accumulated in f32 in ascending j, one rounding per product and
@@ -181,23 +187,69 @@ float ggrms_oracle_silu(float x) {
     return x / (1.0f + expf(-x));
 }
 
-/* One (row, group) unit.  `a` is caller scratch of G floats. */
+/*
+ * One (row, group) unit.  `a` is caller scratch of G floats; `w` points at
+ * the weight of the unit's first column.
+ *
+ * Gate first (the "gated_group_rmsnorm" page's math block):
+ *     a = y * silu(gate); nf = rsqrt(sum a^2 / G + eps);
+ *     out = cast(w * [cast](a * nf)).
+ * Norm first (the "com.microsoft.GatedRMSNorm" page, Description section,
+ * its product read left to right in f32, every intermediate f32):
+ *     nf = rsqrt(sum y^2 / G + eps); out = cast(((y * nf) * w) * silu(gate)).
+ */
 static void one_unit(const void* y, const void* gate, const float* w, void* out,
-                     int64_t yoff, int64_t goff, int64_t ooff, int64_t col0,
-                     int64_t G, float eps, int dtype, int ri, float* a) {
+                     int64_t yoff, int64_t goff, int64_t ooff, int64_t G, float eps,
+                     int dtype, int ri, int norm_first, float* a) {
     for (int64_t j = 0; j < G; ++j) {
         float yf = load_elem(y, yoff + j, dtype);
-        float gf = load_elem(gate, goff + j, dtype);
-        a[j] = yf * ggrms_oracle_silu(gf);
+        a[j] = norm_first ? yf : yf * ggrms_oracle_silu(load_elem(gate, goff + j, dtype));
     }
     float m2 = 0.0f;
     for (int64_t j = 0; j < G; ++j) m2 = m2 + a[j] * a[j];
     float nf = 1.0f / sqrtf(m2 / (float)G + eps);
     for (int64_t j = 0; j < G; ++j) {
         float t = a[j] * nf;
-        if (ri) t = round_trip(t, dtype);
-        store_elem(out, ooff + j, dtype, w[col0 + j] * t);
+        if (norm_first) {
+            t = t * w[j];
+            t = t * ggrms_oracle_silu(load_elem(gate, goff + j, dtype));
+            store_elem(out, ooff + j, dtype, t);
+        } else {
+            if (ri) t = round_trip(t, dtype);
+            store_elem(out, ooff + j, dtype, w[j] * t);
+        }
     }
+}
+
+int ggrms_oracle_forward_ex(const void* y, const void* gate, const float* norm_weight,
+                            void* out, int64_t rows, int64_t width, int64_t group_size,
+                            int64_t y_row_stride, int64_t gate_row_stride,
+                            int64_t out_row_stride, float eps, int dtype, int flags,
+                            float* scratch) {
+    if (rows < 0 || width <= 0 || group_size <= 0 || width % group_size != 0) return 1;
+    if (dtype != GGRMS_ORACLE_F32 && dtype != GGRMS_ORACLE_F16 &&
+        dtype != GGRMS_ORACLE_BF16)
+        return 1;
+    if (flags & ~(GGRMS_ORACLE_ROUND_INTERMEDIATE | GGRMS_ORACLE_NORM_BEFORE_GATE |
+                  GGRMS_ORACLE_WEIGHT_PER_GROUP))
+        return 1;
+    int ri = (flags & GGRMS_ORACLE_ROUND_INTERMEDIATE) != 0;
+    int norm_first = (flags & GGRMS_ORACLE_NORM_BEFORE_GATE) != 0;
+    int per_group = (flags & GGRMS_ORACLE_WEIGHT_PER_GROUP) != 0;
+    if (ri && norm_first) return 1; /* the norm-first operator narrows only at the store */
+    if (rows == 0) return 0;
+    if (!y || !gate || !norm_weight || !out || !scratch) return 1;
+    int64_t groups = width / group_size;
+    for (int64_t n = 0; n < rows; ++n) {
+        for (int64_t g = 0; g < groups; ++g) {
+            int64_t col0 = g * group_size;
+            one_unit(y, gate, norm_weight + (per_group ? 0 : col0), out,
+                     n * y_row_stride + col0, n * gate_row_stride + col0,
+                     n * out_row_stride + col0, group_size, eps, dtype, ri, norm_first,
+                     scratch);
+        }
+    }
+    return 0;
 }
 
 int ggrms_oracle_forward(const void* y, const void* gate, const float* norm_weight,
@@ -205,23 +257,11 @@ int ggrms_oracle_forward(const void* y, const void* gate, const float* norm_weig
                          int64_t y_row_stride, int64_t gate_row_stride,
                          int64_t out_row_stride, float eps, int dtype,
                          int round_intermediate, float* scratch) {
-    if (rows < 0 || width <= 0 || group_size <= 0 || width % group_size != 0) return 1;
-    if (dtype != GGRMS_ORACLE_F32 && dtype != GGRMS_ORACLE_F16 &&
-        dtype != GGRMS_ORACLE_BF16)
-        return 1;
     if (round_intermediate != 0 && round_intermediate != 1) return 1;
-    if (rows == 0) return 0;
-    if (!y || !gate || !norm_weight || !out || !scratch) return 1;
-    int64_t groups = width / group_size;
-    for (int64_t n = 0; n < rows; ++n) {
-        for (int64_t g = 0; g < groups; ++g) {
-            int64_t col0 = g * group_size;
-            one_unit(y, gate, norm_weight, out, n * y_row_stride + col0,
-                     n * gate_row_stride + col0, n * out_row_stride + col0, col0,
-                     group_size, eps, dtype, round_intermediate, scratch);
-        }
-    }
-    return 0;
+    return ggrms_oracle_forward_ex(y, gate, norm_weight, out, rows, width, group_size,
+                                   y_row_stride, gate_row_stride, out_row_stride, eps, dtype,
+                                   round_intermediate ? GGRMS_ORACLE_ROUND_INTERMEDIATE : 0,
+                                   scratch);
 }
 
 /* ----------------------------------------------- element-wise casts */

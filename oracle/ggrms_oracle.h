@@ -19,6 +19,13 @@ extern "C" {
 
 enum { GGRMS_ORACLE_F32 = 0, GGRMS_ORACLE_F16 = 1, GGRMS_ORACLE_BF16 = 2 };
 
+/* Flags of ggrms_oracle_forward_ex. */
+enum {
+    GGRMS_ORACLE_ROUND_INTERMEDIATE = 1, /* gate-first: cast gated*nf before the weight */
+    GGRMS_ORACLE_NORM_BEFORE_GATE = 2,   /* Y = X*rsqrt(mean(X^2)+eps)*w*silu(gate) */
+    GGRMS_ORACLE_WEIGHT_PER_GROUP = 4    /* weight has group_size values shared by all groups */
+};
+
 /*
  * out[n, g*G + j] for every row n < rows and column < width, following the
  * math block of the "gated_group_rmsnorm" page (see ggrms_oracle.c).
@@ -30,6 +37,14 @@ int ggrms_oracle_forward(const void* y, const void* gate, const float* norm_weig
                          int64_t y_row_stride, int64_t gate_row_stride,
                          int64_t out_row_stride, float eps, int dtype,
                          int round_intermediate, float* scratch);
+
+/* The same with flags; ROUND_INTERMEDIATE together with NORM_BEFORE_GATE is
+ * rejected (that operator narrows only at the store).  Returns 0 or 1. */
+int ggrms_oracle_forward_ex(const void* y, const void* gate, const float* norm_weight,
+                            void* out, int64_t rows, int64_t width, int64_t group_size,
+                            int64_t y_row_stride, int64_t gate_row_stride,
+                            int64_t out_row_stride, float eps, int dtype, int flags,
+                            float* scratch);
 
 /* silu(x) = x / (1 + expf(-x)) in f32. */
 float ggrms_oracle_silu(float x);

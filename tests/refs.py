@@ -99,6 +99,18 @@ def chain_fp64(yd: np.ndarray, gd: np.ndarray, group_size: int, eps: float) -> n
     return t.reshape(rows, width).numpy()
 
 
+def chain_nbg_fp64(yd: np.ndarray, gd: np.ndarray, w: np.ndarray, group_size: int,
+                   eps: float) -> np.ndarray:
+    """Norm before gate, float64, library routines: rms_norm(y) * w * silu(gate).
+
+    w: float64 [width] (per column; tile a per-group weight first)."""
+    rows, width = yd.shape
+    t = torch.nn.functional.rms_norm(torch.from_numpy(yd).reshape(rows, width // group_size,
+                                                                  group_size),
+                                     (group_size,), eps=eps).reshape(rows, width)
+    return (t * torch.from_numpy(w)[None, :] * torch.nn.functional.silu(torch.from_numpy(gd))).numpy()
+
+
 def oracle_delta(group_size: int) -> float:
     """Relative error bound of the oracle's f32 value of gated*nf (and w*that)
     against the exact one: the f32 sum of G squares (<= (G+2)u), halved by the

@@ -12,6 +12,7 @@ import subprocess
 import pytest
 
 import test_oracle_casts as casts
+import test_oracle_nbg as nbg
 import test_oracle_pins as pins
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -27,10 +28,17 @@ MUTANTS = {
     "no_intermediate_cast": ("if (ri) t = round_trip(t, dtype);", "(void)ri;"),
     "always_intermediate_cast": ("if (ri) t = round_trip(t, dtype);", "t = round_trip(t, dtype == GGRMS_ORACLE_F32 ? GGRMS_ORACLE_BF16 : dtype);"),
     "intermediate_cast_wrong_type": ("if (ri) t = round_trip(t, dtype);", "if (ri) t = round_trip(t, GGRMS_ORACLE_BF16);"),
-    "weight_index": ("w[col0 + j]", "w[j]"),
+    "weight_index": ("norm_weight + (per_group ? 0 : col0)", "norm_weight"),
     "sum_not_squared": ("m2 = m2 + a[j] * a[j]", "m2 = m2 + fabsf(a[j])"),
     "gate_uses_y_stride": ("n * gate_row_stride + col0", "n * y_row_stride + col0"),
-    "y_and_gate_swapped": ("a[j] = yf * ggrms_oracle_silu(gf);", "a[j] = gf * ggrms_oracle_silu(yf);"),
+    "y_and_gate_swapped": ("yf * ggrms_oracle_silu(load_elem(gate, goff + j, dtype));",
+                           "load_elem(gate, goff + j, dtype) * ggrms_oracle_silu(yf);"),
+    "nbg_reduces_gated": ("norm_first ? yf :",
+                          "norm_first ? yf * ggrms_oracle_silu(load_elem(gate, goff + j, dtype)) :"),
+    "nbg_drops_gate": ("            t = t * ggrms_oracle_silu(load_elem(gate, goff + j, dtype));\n", ""),
+    "nbg_weight_index": ("t = t * w[j];", "t = t * w[0];"),
+    "nbg_silu_of_y": ("            t = t * ggrms_oracle_silu(load_elem(gate, goff + j, dtype));",
+                      "            t = t * ggrms_oracle_silu(load_elem(y, yoff + j, dtype));"),
     "ties_away_from_zero": ("(frac == 0.5f && fmodf(k, 2.0f) != 0.0f)", "frac == 0.5f"),
     "truncating_cast": ("if (frac > 0.5f || (frac == 0.5f && fmodf(k, 2.0f) != 0.0f)) k += 1.0f;", ""),
     "flush_subnormals": ("if (lead < emin) lead = emin;", "if (lead < emin) return copysignf(0.0f, x);"),
@@ -57,6 +65,9 @@ PIN_CALLS = [
     lambda m: casts.test_widen_exhaustive(m, casts.BF16),
     lambda m: casts.test_round_special_values(m, casts.BF16),
     lambda m: casts.test_round_special_values(m, casts.F16),
+    lambda m: nbg.test_nbg_matches_fp64_chain(m, 3, 64, 3, nbg.F32, False),
+    lambda m: nbg.test_nbg_matches_fp64_chain(m, 2, 128, 4, nbg.F16, True),
+    lambda m: nbg.test_per_group_weight_gate_first(m, nbg.BF16, 1),
 ]
 
 
