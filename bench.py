@@ -72,12 +72,18 @@ def parse():
 class Setup:
     """Device copies of a workload's inputs (several rotating sets) and outputs."""
 
-    def __init__(self, torch, S, w, sets: int, layer: int = 0):
+    def __init__(self, torch, S, w, sets: int, layer: int = 0, flags=None):
         import numpy as np
 
         self.w = w
+        # operator flags of ggrms_forward_ex: the workload's own gate-first
+        # rounding unless given; a shared group weight takes the first
+        # group_size values of the workload's weight
+        self.flags = (1 if w.round_intermediate else 0) if flags is None else flags
         tdt = {S.F32: torch.float32, S.F16: torch.float16, S.BF16: torch.bfloat16}[w.dtype]
         ybuf, gbuf, wt, lay = S.make_inputs(w, layer)
+        if self.flags & 4:
+            wt = np.ascontiguousarray(wt[:w.group_size])
         self.lay = lay
 
         def dev(a):
@@ -95,19 +101,23 @@ class Setup:
             self.sets.append((yb[lay["y_offset"]:], gb[lay["gate_offset"]:], out))
         torch.cuda.synchronize()
 
-    def launch(self, g, i, stream, shape=None):
+    def args(self, i=0):
         w, lay = self.w, self.lay
         y, gt, out = self.sets[i % len(self.sets)]
-        args = (y.data_ptr(), gt.data_ptr(), self.weight.data_ptr(), out.data_ptr(), w.rows,
+        return (y.data_ptr(), gt.data_ptr(), self.weight.data_ptr(), out.data_ptr(), w.rows,
                 w.width, w.group_size, lay["y_row_stride"], lay["gate_row_stride"], w.width,
-                w.eps, w.dtype, w.round_intermediate)
-        if shape:
-            st = g.ggrms_forward_with_shape(*args, shape[0], shape[1], stream,
-                                            shape[2] if len(shape) > 2 else 0)
-        else:
-            st = g.ggrms_forward(*args, stream)
+                w.eps, w.dtype, self.flags)
+
+    def launch(self, g, i, stream, shape=None):
+        st = g.ggrms_forward_ex(*self.args(i), stream, shape)
         if st != 0:
-            raise RuntimeError(f"ggrms_forward: {g.ggrms_status_string(st)}")
+            raise RuntimeError(f"ggrms_forward_ex: {g.ggrms_status_string(st)}")
+
+    def plan(self, g, shape=None):
+        st, p = g.ggrms_plan_ex(*self.args(), shape)
+        if st != 0:
+            raise RuntimeError(f"ggrms_plan_ex: {g.ggrms_status_string(st)}")
+        return p
 
 
 def settle(torch, launch, seconds):
@@ -156,10 +166,7 @@ def bench_prefill(torch, g, S, args, shape):
     setup = Setup(torch, S, w, sets)
     wall, ev_ms = time_kernel(torch, g, setup, args.steps, args.warmup, shape,
                               args.settle_ms / 1e3)
-    st, plan = g.ggrms_plan(setup.sets[0][0].data_ptr(), setup.sets[0][1].data_ptr(),
-                            setup.weight.data_ptr(), setup.sets[0][2].data_ptr(), w.rows, w.width,
-                            w.group_size, w.width, w.width, w.width, w.eps, w.dtype,
-                            w.round_intermediate)
+    plan = setup.plan(g, shape)
     avg_ms = ev_ms / args.steps
     res = {
         "workload": w,
@@ -183,10 +190,7 @@ def bench_decode(torch, g, S, bursts):
     layers = [Setup(torch, S, w, 1, layer) for layer in range(L)]
     aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
     aux.ggrms_bench_empty.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
-    s0 = layers[0].sets[0]
-    st, plan = g.ggrms_plan(s0[0].data_ptr(), s0[1].data_ptr(), layers[0].weight.data_ptr(),
-                            s0[2].data_ptr(), w.rows, w.width, w.group_size, w.width, w.width,
-                            w.width, w.eps, w.dtype, w.round_intermediate)
+    plan = layers[0].plan(g)
     blocks, threads = plan["workgroups"], plan["block_threads"]
 
     def fused_burst(stream):
@@ -267,19 +271,31 @@ def bench_copy(torch, steps):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "kernel_ms_avg": ms}
 
 
+# (label, workload, ggrms_forward_ex flags or None for the workload's own)
+OTHER_WORKLOADS = [
+    ("strided_256x4800_f16_g100", "strided_256x4800_f16_g100", None),
+    ("gdn_head_16384x8192_f16_g128", "gdn_head_16384x8192_f16_g128", None),
+    # norm first with the 128-value head scale shared by every head
+    ("gdn_head_16384x8192_f16_g128_norm_first", "gdn_head_16384x8192_f16_g128", 2 | 4),
+    ("prefill_8192x7680_bf16_g960_norm_first", PREFILL, 2),
+]
+
+
 def bench_workloads(torch, g, S, steps):
-    """Kernel time of the other configured workloads (reported beside the headline)."""
+    """Kernel time of the other configured workloads and of the norm-first
+    operator (reported beside the headline)."""
     out = {}
-    for name in ("strided_256x4800_f16_g100", "gdn_head_16384x8192_f16_g128"):
+    for label, name, flags in OTHER_WORKLOADS:
         w = S.WORKLOADS[name]
         sets = max(2, math.ceil(3 * 256e6 / w.algorithmic_bytes()))
-        setup = Setup(torch, S, w, min(sets, 64))
+        setup = Setup(torch, S, w, min(sets, 64), flags=flags)
         _, ev_ms = time_kernel(torch, g, setup, steps, 5, settle_s=0.1)
         avg = ev_ms / steps
-        out[name] = {"kernel_us_avg": avg * 1e3,
-                     "gbs": w.algorithmic_bytes() / (avg * 1e-3) / 1e9,
-                     "frac_of_peak": w.algorithmic_bytes() / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "rows_per_s": w.rows / (avg * 1e-3)}
+        nbytes = w.algorithmic_bytes(per_group_weight=bool(setup.flags & 4))
+        out[label] = {"kernel_us_avg": avg * 1e3,
+                      "gbs": nbytes / (avg * 1e-3) / 1e9,
+                      "frac_of_peak": nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "rows_per_s": w.rows / (avg * 1e-3)}
         del setup
         torch.cuda.empty_cache()
     log(f"workloads: {json.dumps(out)}")
@@ -299,9 +315,20 @@ def unfused_chain(torch, y, gate, w, group_size, eps, ri):
     return (w * t).to(y.dtype)
 
 
+def unfused_chain_norm_first(torch, y, gate, w, group_size, eps):
+    """The norm-first operator as PyTorch eager ops: rms_norm over groups of
+    the widened y, times the shared group weight, times silu(gate), narrow."""
+    rows, width = y.shape
+    t = torch.nn.functional.rms_norm(y.float().view(rows, width // group_size, group_size),
+                                     (group_size,), eps=eps)
+    t = (t * w).view(rows, width) * torch.nn.functional.silu(gate.float())
+    return t.to(y.dtype)
+
+
 def bench_unfused(torch, S, steps):
     """Per-launch time of the unfused chain beside the fused kernel: the
-    prefill batch (eager, back to back) and the 21-layer decode burst (eager
+    prefill batch (eager, back to back), the norm-first chain on the
+    16384x8192 fp16 GDN-shaped batch, and the 21-layer decode burst (eager
     and as one replayed graph)."""
     import numpy as np
 
@@ -321,6 +348,22 @@ def bench_unfused(torch, S, steps):
     b.record()
     torch.cuda.synchronize()
     res["prefill_us"] = a.elapsed_time(b) * 1e3 / steps
+    del y, gt
+    torch.cuda.empty_cache()
+
+    n = S.WORKLOADS["gdn_head_16384x8192_f16_g128"]
+    yb, gb, wt, _ = S.make_inputs(n)
+    y = torch.from_numpy(yb.view(np.int16)).view(torch.float16).reshape(n.rows, n.width).cuda()
+    gt = torch.from_numpy(gb.view(np.int16)).view(torch.float16).reshape(n.rows, n.width).cuda()
+    wd = torch.from_numpy(np.ascontiguousarray(wt[:n.group_size])).cuda()
+    run = lambda i: unfused_chain_norm_first(torch, y, gt, wd, n.group_size, n.eps)
+    settle(torch, run, 0.2)
+    a.record()
+    for i in range(steps):
+        run(i)
+    b.record()
+    torch.cuda.synchronize()
+    res["gdn_norm_first_us"] = a.elapsed_time(b) * 1e3 / steps
     del y, gt
     torch.cuda.empty_cache()
 

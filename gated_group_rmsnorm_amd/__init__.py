@@ -13,6 +13,14 @@ The operation, per row n and group g of ``group_size`` contiguous columns
     nf    = rsqrt(sum(gated^2) / group_size + eps)
     out   = cast(f32(w) * f32(cast(gated * nf, dtype)), dtype)   # round_intermediate
     out   = cast(f32(w) * (gated * nf), dtype)                   # otherwise
+
+and, with FLAG_NORM_BEFORE_GATE, the operator of the page
+"com.microsoft.GatedRMSNorm" (Description section), nf taken from y alone::
+
+    out   = cast(((f32(y) * nf) * f32(w)) * silu(f32(gate)), dtype)
+
+The weight has one value per column, or (FLAG_WEIGHT_PER_GROUP) group_size
+values shared by every group.
 """
 from __future__ import annotations
 
@@ -20,16 +28,19 @@ import ctypes
 import os
 
 __all__ = [
-    "F32", "F16", "BF16", "SUCCESS", "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED",
-    "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError", "ggrms_forward", "ggrms_forward_with_shape",
-    "ggrms_plan",
+    "F32", "F16", "BF16", "FLAG_ROUND_INTERMEDIATE", "FLAG_NORM_BEFORE_GATE",
+    "FLAG_WEIGHT_PER_GROUP", "SUCCESS", "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED",
+    "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError", "ggrms_forward", "ggrms_forward_ex",
+    "ggrms_forward_with_shape", "ggrms_plan", "ggrms_plan_ex",
     "ggrms_status_string", "ggrms_abi_version", "forward", "plan", "expand_head_scale",
     "library_path",
 ]
 
 F32, F16, BF16 = 0, 1, 2
+FLAG_ROUND_INTERMEDIATE, FLAG_NORM_BEFORE_GATE, FLAG_WEIGHT_PER_GROUP = 1, 2, 4
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
 KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide"}
+ABI_VERSION = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libggrms.so")
@@ -43,6 +54,11 @@ class GgrmsError(RuntimeError):
     def __init__(self, status: int, what: str = "ggrms_forward"):
         self.status = status
         super().__init__(f"{what}: {ggrms_status_string(status)} (status {status})")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("lanes_per_group", ctypes.c_int32), ("vectors_per_lane", ctypes.c_int32),
+                ("rows_per_workgroup", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
@@ -67,10 +83,18 @@ def _load() -> ctypes.CDLL:
     L.ggrms_forward_with_shape.restype = i32
     L.ggrms_plan.argtypes = fwd + [ctypes.POINTER(_Plan)]
     L.ggrms_plan.restype = i32
+    fwd_ex = fwd[:-1] + [ctypes.c_uint32, ctypes.POINTER(_Shape)]
+    L.ggrms_forward_ex.argtypes = fwd_ex + [vp]
+    L.ggrms_forward_ex.restype = i32
+    L.ggrms_plan_ex.argtypes = fwd_ex + [ctypes.POINTER(_Plan)]
+    L.ggrms_plan_ex.restype = i32
     L.ggrms_status_string.argtypes = [i32]
     L.ggrms_status_string.restype = ctypes.c_char_p
     L.ggrms_abi_version.argtypes = []
     L.ggrms_abi_version.restype = i32
+    if L.ggrms_abi_version() != ABI_VERSION:
+        raise ImportError(f"{_LIB_PATH} has ABI version {L.ggrms_abi_version()}, this binding "
+                          f"expects {ABI_VERSION}: rebuild the library")
     return L
 
 
@@ -100,6 +124,40 @@ def ggrms_forward_with_shape(y: int, gate: int, norm_weight: int, out: int, rows
                                          y_row_stride, gate_row_stride, out_row_stride, eps,
                                          dtype, round_intermediate, lanes_per_group,
                                          vectors_per_lane, rows_per_workgroup, stream)
+
+
+def _shape_arg(shape):
+    if shape is None:
+        return None
+    lanes, vpt = shape[0], shape[1]
+    upb = shape[2] if len(shape) > 2 else 0
+    return ctypes.byref(_Shape(lanes, vpt, upb))
+
+
+def ggrms_forward_ex(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
+                     group_size: int, y_row_stride: int, gate_row_stride: int,
+                     out_row_stride: int, eps: float, dtype: int, flags: int, stream: int,
+                     shape=None) -> int:
+    """The C entry point with operator flags and an optional (lanes, vectors[, rows
+    per workgroup]) shape; returns the status."""
+    return _lib.ggrms_forward_ex(y, gate, norm_weight, out, rows, width, group_size,
+                                 y_row_stride, gate_row_stride, out_row_stride, eps, dtype, flags,
+                                 _shape_arg(shape), stream)
+
+
+def ggrms_plan_ex(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
+                  group_size: int, y_row_stride: int, gate_row_stride: int, out_row_stride: int,
+                  eps: float, dtype: int, flags: int, shape=None):
+    """(status, plan dict or None) for ggrms_forward_ex's arguments; no device call."""
+    p = _Plan()
+    st = _lib.ggrms_plan_ex(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                            gate_row_stride, out_row_stride, eps, dtype, flags,
+                            _shape_arg(shape), ctypes.byref(p))
+    if st != SUCCESS:
+        return st, None
+    d = {f: getattr(p, f) for f, _ in _Plan._fields_}
+    d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
+    return st, d
 
 
 def ggrms_plan(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
@@ -167,16 +225,32 @@ def expand_head_scale(scale, heads: int):
     return s.repeat(heads).contiguous()
 
 
+def _flags(weight, width, group_size, round_intermediate, norm_before_gate) -> int:
+    if round_intermediate is None:
+        round_intermediate = not norm_before_gate
+    per_group = weight.numel() == group_size and group_size != width
+    return ((FLAG_ROUND_INTERMEDIATE if round_intermediate else 0) |
+            (FLAG_NORM_BEFORE_GATE if norm_before_gate else 0) |
+            (FLAG_WEIGHT_PER_GROUP if per_group else 0))
+
+
 def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
-            round_intermediate: bool = True, out=None, stream=None):
-    """out = fused gated group-RMSNorm of (y, gate) with the f32 per-column
-    ``weight`` over groups of ``group_size`` columns of the last axis.
+            round_intermediate=None, out=None, stream=None,
+            norm_before_gate: bool = False):
+    """out = fused gated group-RMSNorm of (y, gate) with the f32 ``weight``
+    over groups of ``group_size`` columns of the last axis.
 
     y and gate: same shape (..., width), same dtype (f32/f16/bf16), on the
     GPU, unit stride in the last axis (they may be strided column slices of
-    one fused buffer).  out (optional) must match y's shape and dtype; it is
-    allocated like y when omitted.  Enqueued on ``stream`` (default: torch's
-    current stream); no synchronisation.
+    one fused buffer).  weight: f32 with width values (one per column) or
+    group_size values (shared by every group).  out (optional) must match
+    y's shape and dtype; it is allocated like y when omitted.
+    round_intermediate (default: on for gate first) casts gated*nf to the
+    dtype before the weight multiply.  norm_before_gate selects
+    out = ((y * nf) * w) * silu(gate) with nf from y alone, every
+    intermediate f32 (round_intermediate=True is then refused).
+    Enqueued on ``stream`` (default: torch's current stream); no
+    synchronisation.
     """
     import torch
 
@@ -186,9 +260,10 @@ def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
         raise TypeError("y and gate must share a dtype")
     code = _torch_dtype_code(y)
     width = y.size(-1)
-    if weight.dtype != torch.float32 or weight.numel() != width or weight.dim() != 1:
-        raise TypeError("weight must be a 1-D float32 tensor with width elements "
-                        "(expand_head_scale builds one from a per-head scale)")
+    if weight.dtype != torch.float32 or weight.dim() != 1 or \
+            weight.numel() not in (width, group_size):
+        raise TypeError("weight must be a 1-D float32 tensor with width or group_size elements "
+                        "(expand_head_scale builds a per-column one from a per-head scale)")
     if not weight.is_contiguous():
         raise ValueError("weight must be contiguous")
     if out is None:
@@ -204,17 +279,18 @@ def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
         stream = torch.cuda.current_stream(y.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    flags = _flags(weight, width, group_size, round_intermediate, norm_before_gate)
     with torch.cuda.device(y.device):
-        st = ggrms_forward(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), out.data_ptr(),
-                           rows, width, group_size, sy, sg, so, float(eps), code,
-                           int(bool(round_intermediate)), stream)
+        st = ggrms_forward_ex(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), out.data_ptr(),
+                              rows, width, group_size, sy, sg, so, float(eps), code, flags,
+                              stream)
     if st != SUCCESS:
         raise GgrmsError(st)
     return out
 
 
-def plan(y, gate, weight, group_size: int, eps: float = 1e-5, round_intermediate: bool = True,
-         out=None) -> dict:
+def plan(y, gate, weight, group_size: int, eps: float = 1e-5, round_intermediate=None,
+         out=None, norm_before_gate: bool = False) -> dict:
     """The kernel forward() would launch for these tensors (no device call)."""
     code = _torch_dtype_code(y)
     width = y.size(-1)
@@ -222,9 +298,10 @@ def plan(y, gate, weight, group_size: int, eps: float = 1e-5, round_intermediate
     _, sg = _as_rows(gate, "gate")
     o = out if out is not None else y.new_empty(y.shape)
     _, so = _as_rows(o, "out")
-    st, p = ggrms_plan(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), o.data_ptr(), rows,
-                       width, group_size, sy, sg, so, float(eps), code,
-                       int(bool(round_intermediate)))
+    st, p = ggrms_plan_ex(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), o.data_ptr(), rows,
+                          width, group_size, sy, sg, so, float(eps), code,
+                          _flags(weight, width, group_size, round_intermediate,
+                                 norm_before_gate))
     if st != SUCCESS:
         raise GgrmsError(st, "ggrms_plan")
     return p

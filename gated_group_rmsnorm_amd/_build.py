@@ -28,7 +28,8 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-I", INCLUDE, "-I", CSRC]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
-LIB_HIP = ["ggrms_api.hip", "table_f32.hip", "table_f16.hip", "table_bf16.hip"]
+LIB_HIP = ["ggrms_api.hip", "table_f32.hip", "table_f16.hip", "table_bf16.hip",
+           "table_f32_nbg.hip", "table_f16_nbg.hip", "table_bf16_nbg.hip"]
 LIB_CXX = ["plan.cpp"]
 BENCH_HIP = ["bench_aux.hip"]
 

@@ -34,11 +34,11 @@ bool device_is_gfx950() {
     return st == 1;
 }
 
-const void* pick(int dtype, int kernel, int vb, int lanes, int vpt, int upb) {
+const void* pick(int dtype, bool nbg, int kernel, int vb, int lanes, int vpt, int upb) {
     switch (dtype) {
-    case GGRMS_F32: return pick_f32(kernel, vb, lanes, vpt, upb);
-    case GGRMS_F16: return pick_f16(kernel, vb, lanes, vpt, upb);
-    case GGRMS_BF16: return pick_bf16(kernel, vb, lanes, vpt, upb);
+    case GGRMS_F32: return (nbg ? pick_f32_nbg : pick_f32)(kernel, vb, lanes, vpt, upb);
+    case GGRMS_F16: return (nbg ? pick_f16_nbg : pick_f16)(kernel, vb, lanes, vpt, upb);
+    case GGRMS_BF16: return (nbg ? pick_bf16_nbg : pick_bf16)(kernel, vb, lanes, vpt, upb);
     default: return nullptr;
     }
 }
@@ -46,18 +46,19 @@ const void* pick(int dtype, int kernel, int vb, int lanes, int vpt, int upb) {
 ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_weight, void* out,
                             int64_t rows, int64_t width, int64_t group_size, int64_t y_row_stride,
                             int64_t gate_row_stride, int64_t out_row_stride, float eps,
-                            ggrms_dtype_t dtype, int round_intermediate, int force_lanes,
-                            int force_vpt, int force_upb, void* stream) {
+                            ggrms_dtype_t dtype, uint32_t flags, const ggrms_shape_t* shape,
+                            void* stream) {
     LaunchPlan lp;
     ggrms_status_t st = make_plan(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
-                                  gate_row_stride, out_row_stride, eps, (int)dtype,
-                                  round_intermediate, force_lanes, force_vpt, force_upb, &lp);
+                                  gate_row_stride, out_row_stride, eps, (int)dtype, flags, shape,
+                                  &lp);
     if (st != GGRMS_SUCCESS || lp.pub.kernel == GGRMS_KERNEL_NONE) return st;
     if (!device_is_gfx950()) return GGRMS_ERROR_NOT_SUPPORTED;
 
     const ggrms_plan_t& p = lp.pub;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const void* fn = pick((int)dtype, p.kernel, p.vector_bytes, p.lanes_per_group,
+    const bool nbg = (flags & GGRMS_FLAG_NORM_BEFORE_GATE) != 0;
+    const void* fn = pick((int)dtype, nbg, p.kernel, p.vector_bytes, p.lanes_per_group,
                           p.vectors_per_lane, p.rows_per_workgroup);
     if (!fn) return GGRMS_ERROR_NOT_SUPPORTED;
 
@@ -67,13 +68,14 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     a.sy = y_row_stride;
     a.sg = gate_row_stride;
     a.so = out_row_stride;
+    a.wgs = (flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? 0 : group_size;
     a.groups = (uint32_t)lp.groups;
     div_magic(a.groups, &a.div_m, &a.div_s);
     a.G = (uint32_t)group_size;
     a.nvec = (uint32_t)lp.nvec;
     a.Gf = (float)group_size;
     a.eps = eps;
-    a.ri = dtype == GGRMS_F32 ? 0 : round_intermediate;
+    a.ri = (dtype != GGRMS_F32 && (flags & GGRMS_FLAG_ROUND_INTERMEDIATE)) ? 1 : 0;
     const int es = lp.esize;
     const int64_t thread_per_unit = p.kernel == GGRMS_KERNEL_WIDE ? kWideBlock : p.lanes_per_group;
     const int upb = p.rows_per_workgroup;
@@ -101,15 +103,28 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
 }  // namespace
 }  // namespace ggrms
 
+extern "C" ggrms_status_t ggrms_forward_ex(const void* y, const void* gate,
+                                           const float* norm_weight, void* out, int64_t rows,
+                                           int64_t width, int64_t group_size,
+                                           int64_t y_row_stride, int64_t gate_row_stride,
+                                           int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                           uint32_t flags, const ggrms_shape_t* shape,
+                                           void* stream) {
+    return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                               gate_row_stride, out_row_stride, eps, dtype, flags, shape, stream);
+}
+
 extern "C" ggrms_status_t ggrms_forward(const void* y, const void* gate,
                                         const float* norm_weight, void* out, int64_t rows,
                                         int64_t width, int64_t group_size, int64_t y_row_stride,
                                         int64_t gate_row_stride, int64_t out_row_stride,
                                         float eps, ggrms_dtype_t dtype, int round_intermediate,
                                         void* stream) {
+    if (round_intermediate != 0 && round_intermediate != 1) return GGRMS_ERROR_INVALID_VALUE;
     return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
-                               gate_row_stride, out_row_stride, eps, dtype, round_intermediate, 0,
-                               0, 0, stream);
+                               gate_row_stride, out_row_stride, eps, dtype,
+                               round_intermediate ? GGRMS_FLAG_ROUND_INTERMEDIATE : 0u, nullptr,
+                               stream);
 }
 
 extern "C" ggrms_status_t ggrms_forward_with_shape(
@@ -117,9 +132,10 @@ extern "C" ggrms_status_t ggrms_forward_with_shape(
     int64_t width, int64_t group_size, int64_t y_row_stride, int64_t gate_row_stride,
     int64_t out_row_stride, float eps, ggrms_dtype_t dtype, int round_intermediate,
     int lanes_per_group, int vectors_per_lane, int rows_per_workgroup, void* stream) {
-    if (lanes_per_group == 0 && vectors_per_lane == 0) return GGRMS_ERROR_INVALID_VALUE;
-    if (rows_per_workgroup < 0) return GGRMS_ERROR_INVALID_VALUE;
+    if (round_intermediate != 0 && round_intermediate != 1) return GGRMS_ERROR_INVALID_VALUE;
+    const ggrms_shape_t shape = {lanes_per_group, vectors_per_lane, rows_per_workgroup};
     return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
-                               gate_row_stride, out_row_stride, eps, dtype, round_intermediate,
-                               lanes_per_group, vectors_per_lane, rows_per_workgroup, stream);
+                               gate_row_stride, out_row_stride, eps, dtype,
+                               round_intermediate ? GGRMS_FLAG_ROUND_INTERMEDIATE : 0u, &shape,
+                               stream);
 }

@@ -16,6 +16,7 @@ struct KArgs {
     const float* w;
     void* out;
     int64_t sy, sg, so;
+    int64_t wgs;      // weight offset per group: G (one weight per column) or 0 (shared)
     uint32_t units;   // (row, group) units in this launch
     uint32_t rows;    // rows in this launch
     uint32_t groups;  // groups per row
@@ -64,6 +65,7 @@ inline bool shape_supported(int kernel, int lanes, int vpt) {
 // Full launch plan: the public plan plus what the launcher needs.
 struct LaunchPlan {
     ggrms_plan_t pub;
+    uint32_t flags;
     int esize;
     int64_t groups;
     int64_t nvec;
@@ -71,22 +73,26 @@ struct LaunchPlan {
 };
 
 // Validation and kernel choice; no HIP calls.  Implemented in plan.cpp.
-// force_lanes / force_vpt = 0 / 0 picks the shape; otherwise that shape is
-// used if it is built and covers the group (GGRMS_ERROR_NOT_SUPPORTED if not).
-// force_upb = 0 picks the rows per BLOCK workgroup; otherwise it must be built
-// for the shape and the weights must allow staging.
+// `flags` are ggrms_flag_t bits.  shape == nullptr picks the shape; otherwise
+// its lanes/vectors are used if built and covering the group
+// (GGRMS_ERROR_NOT_SUPPORTED if not) and its rows_per_workgroup (0 = pick)
+// must be built for the shape and allowed by the weight's alignment.
 ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const void* out,
                          int64_t rows, int64_t width, int64_t group_size, int64_t sy,
-                         int64_t sg, int64_t so, float eps, int dtype, int ri,
-                         int force_lanes, int force_vpt, int force_upb, LaunchPlan* plan);
+                         int64_t sg, int64_t so, float eps, int dtype, uint32_t flags,
+                         const ggrms_shape_t* shape, LaunchPlan* plan);
 
 // Magic numbers for n / d with n < 2^31 and 1 <= d < 2^31:
 // q = (umulhi(n, m) + n) >> s.
 void div_magic(uint32_t d, uint32_t* m, uint32_t* s);
 
 // Kernel lookup per dtype (kernel tables); nullptr if the shape is not built.
+// (nbg selects the norm-before-gate instantiations, in their own files.)
 const void* pick_f32(int kernel, int vb, int lanes, int vpt, int upb);
 const void* pick_f16(int kernel, int vb, int lanes, int vpt, int upb);
 const void* pick_bf16(int kernel, int vb, int lanes, int vpt, int upb);
+const void* pick_f32_nbg(int kernel, int vb, int lanes, int vpt, int upb);
+const void* pick_f16_nbg(int kernel, int vb, int lanes, int vpt, int upb);
+const void* pick_bf16_nbg(int kernel, int vb, int lanes, int vpt, int upb);
 
 }  // namespace ggrms

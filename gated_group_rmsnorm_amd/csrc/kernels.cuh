@@ -250,7 +250,7 @@ enum class WSource { Global, Lds };
 // vectors (indices sl, sl+SEG, ...), computes its share, reduces with
 // `reduce`, and stores if `store_ok`.  With WSource::Lds, `wl` points at the
 // group's weights in LDS, valid once `reduce` has passed its barrier.
-template <class T, int VB, int SEG, int VPT, WSource WS, class Reduce>
+template <class T, int VB, int SEG, int VPT, bool NBG, WSource WS, class Reduce>
 __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g, uint32_t sl,
                                           bool store_ok, const float* wl, Reduce reduce) {
     using P = Packet<T, VB>;
@@ -263,7 +263,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     const W* gv =
         reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + col0);
     W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + col0);
-    const float* wp = a.w + col0;
+    const float* wp = a.w + (int64_t)g * a.wgs;
 
     W yr[VPT], gr[VPT];
     float wr[VPT][N];
@@ -277,7 +277,8 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
         if constexpr (WS == WSource::Global) load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
     }
 
-    // a = y * silu(gate) for every loaded element; lanes past the group's end
+    // Gate first: a = y * silu(gate) for every loaded element.  Norm first:
+    // a = y, and silu(gate) waits for the output.  Lanes past the group's end
     // hold a copy of its last vector and their partial sum is dropped by one
     // select per vector (no per-element predication).
     float av[VPT][N];
@@ -292,15 +293,16 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 #pragma unroll
         for (int e = 0; e < N; ++e) {
             gmin = __builtin_fminf(gmin, gf[e]);
-            const float x = yf[e] * silu_fast(gf[e]);
+            const float x = NBG ? yf[e] : yf[e] * silu_fast(gf[e]);
             av[k][e] = x;
             part = __builtin_fmaf(x, x, part);
         }
         acc += (sl + k * SEG < a.nvec) ? part : 0.0f;
     }
-    if (__builtin_expect(__any(gmin < kSiluFastMin), 0)) {
-        // Rare: a gate deep in silu's underflow range.  Redo the wave's
-        // elements with the exact form (identical bits for every other gate).
+    // Rare: a gate deep in silu's underflow range.  Redo the wave's silu with
+    // the exact form (identical bits for every other gate).
+    const bool exact_silu = __builtin_expect(__any(gmin < kSiluFastMin), 0);
+    if (!NBG && exact_silu) {
         acc = 0.0f;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
@@ -339,9 +341,20 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
             float t[N];
 #pragma unroll
             for (int e = 0; e < N; ++e) t[e] = av[k][e] * nf;
-            if constexpr (RI) P::round_trip(t);
+            if constexpr (NBG) {
+                // ((y * nf) * w) * silu(gate), every intermediate f32
+                float gf[N];
+                P::unpack(gr[k], gf);
 #pragma unroll
-            for (int e = 0; e < N; ++e) t[e] = wr[k][e] * t[e];
+                for (int e = 0; e < N; ++e) {
+                    const float sg = exact_silu ? silu_exact(gf[e]) : silu_fast(gf[e]);
+                    t[e] = (t[e] * wr[k][e]) * sg;
+                }
+            } else {
+                if constexpr (RI) P::round_trip(t);
+#pragma unroll
+                for (int e = 0; e < N; ++e) t[e] = wr[k][e] * t[e];
+            }
             res[k] = P::pack(t);
         }
 #pragma unroll
@@ -350,7 +363,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
             if (store_ok && idx < a.nvec) store_stream(ov + idx, res[k]);
         }
     };
-    if (a.ri)
+    if (!NBG && a.ri)
         finish(std::true_type{});
     else
         finish(std::false_type{});
@@ -359,15 +372,15 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 // ------------------------------------------------------------ kernels
 
 // WAVE: SEG (<= 64) lanes per unit, 256-thread workgroups, no LDS, no barrier.
-template <class T, int VB, int SEG, int VPT>
+template <class T, int VB, int SEG, int VPT, bool NBG>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
     const uint32_t t = blockIdx.x * (uint32_t)kWaveBlock + threadIdx.x;
     const uint32_t unit = t / SEG;
     if (unit >= a.units) return;  // whole segments leave together
     const uint32_t n = fast_div(unit, a.div_m, a.div_s);
-    unit_pass<T, VB, SEG, VPT, WSource::Global>(a, n, unit - n * a.groups, threadIdx.x & (SEG - 1),
-                                                true, nullptr,
-                                                [](float v) { return segment_sum<SEG>(v); });
+    unit_pass<T, VB, SEG, VPT, NBG, WSource::Global>(a, n, unit - n * a.groups,
+                                                     threadIdx.x & (SEG - 1), true, nullptr,
+                                                     [](float v) { return segment_sum<SEG>(v); });
 }
 
 // BLOCK: a unit spans SEG/64 waves; the per-wave sums meet in LDS after one
@@ -378,7 +391,7 @@ __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
 // and parked in LDS before the reduction barrier, instead of every unit
 // fetching its own copy: weight traffic from L2 falls by UPB and the L1
 // miss slots it held go back to the HBM streams.
-template <class T, int VB, int SEG, int VPT, int UPB>
+template <class T, int VB, int SEG, int VPT, int UPB, bool NBG>
 __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     constexpr int BT = SEG * UPB;
     constexpr int WPG = SEG / 64;
@@ -397,7 +410,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     constexpr int SV = UPB > 1 ? (VPT * N + 4 * UPB - 1) / (4 * UPB) : 1;
     f32x4 wst[SV];
     if constexpr (UPB > 1) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(a.w + (int64_t)g * a.G);
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.w + (int64_t)g * a.wgs);
         const uint32_t nw4 = a.G / 4;
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
@@ -406,7 +419,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
         }
     }
     constexpr WSource WS = UPB > 1 ? WSource::Lds : WSource::Global;
-    unit_pass<T, VB, SEG, VPT, WS>(a, n, g, threadIdx.x & (SEG - 1), live, wl, [&](float v) {
+    unit_pass<T, VB, SEG, VPT, NBG, WS>(a, n, g, threadIdx.x & (SEG - 1), live, wl, [&](float v) {
         const float s = segment_sum<64>(v);
         if ((threadIdx.x & 63) == 0) part[wave] = s;
         if constexpr (UPB > 1) {
@@ -428,7 +441,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
 // WIDE: one 1024-thread workgroup per unit, for groups with more vectors than
 // the BLOCK shapes hold in registers.  Pass 1 reads the group and reduces;
 // pass 2 reads it again and writes (the only path that reads inputs twice).
-template <class T, int VB>
+template <class T, int VB, bool NBG>
 __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
     using P = Packet<T, VB>;
     using W = typename P::W;
@@ -444,16 +457,16 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
     const W* gv =
         reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + col0);
     W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + col0);
-    const float* wp = a.w + col0;
+    const float* wp = a.w + (int64_t)g * a.wgs;
 
     float acc = 0.0f;
     for (uint32_t i = threadIdx.x; i < a.nvec; i += kWideBlock) {
         float yf[N], gf[N];
         P::unpack(yv[i], yf);
-        P::unpack(gv[i], gf);
+        if constexpr (!NBG) P::unpack(gv[i], gf);
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            const float x = yf[e] * silu_exact(gf[e]);
+            const float x = NBG ? yf[e] : yf[e] * silu_exact(gf[e]);
             acc = __builtin_fmaf(x, x, acc);
         }
     }
@@ -470,24 +483,30 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
         P::unpack(load_stream(yv + i), yf);
         P::unpack(load_stream(gv + i), gf);
         load_weights<N>(wp + (int64_t)i * N, wv);
+        if constexpr (NBG) {
 #pragma unroll
-        for (int e = 0; e < N; ++e) t[e] = yf[e] * silu_exact(gf[e]) * nf;
-        if (a.ri) P::round_trip(t);
+            for (int e = 0; e < N; ++e) t[e] = ((yf[e] * nf) * wv[e]) * silu_exact(gf[e]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < N; ++e) t[e] = wv[e] * t[e];
+            for (int e = 0; e < N; ++e) t[e] = yf[e] * silu_exact(gf[e]) * nf;
+            if (a.ri) P::round_trip(t);
+#pragma unroll
+            for (int e = 0; e < N; ++e) t[e] = wv[e] * t[e];
+        }
         store_stream(ov + i, P::pack(t));
     }
 }
 
 // ------------------------------------------------------------ table
 
-template <class T, int VB>
+template <class T, int VB, bool NBG>
 inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
-#define GG_W(L, V) \
-    if (lanes == L && vpt == V) return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, L, V>)
+#define GG_W(L, V)                      \
+    if (lanes == L && vpt == V)         \
+    return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, L, V, NBG>)
 #define GG_B(L, V, U)                     \
     if (lanes == L && vpt == V && upb == U) \
-    return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V, U>)
+    return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V, U, NBG>)
 #define GG_B4(L, U) GG_B(L, 1, U); GG_B(L, 2, U); GG_B(L, 3, U); GG_B(L, 4, U)
     if (kernel == GGRMS_KERNEL_WAVE) {
         if (upb != 1) return nullptr;
@@ -500,7 +519,7 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
         GG_B4(1024, 1);
     } else if (kernel == GGRMS_KERNEL_WIDE) {
         if (upb != 1) return nullptr;
-        return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB>);
+        return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB, NBG>);
     }
 #undef GG_W
 #undef GG_B
@@ -508,14 +527,14 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
     return nullptr;
 }
 
-template <class T>
+template <class T, bool NBG>
 inline const void* pick_type(int kernel, int vb, int lanes, int vpt, int upb) {
     switch (vb) {
-    case 16: return pick_vb<T, 16>(kernel, lanes, vpt, upb);
-    case 8: return pick_vb<T, 8>(kernel, lanes, vpt, upb);
-    case 4: return pick_vb<T, 4>(kernel, lanes, vpt, upb);
+    case 16: return pick_vb<T, 16, NBG>(kernel, lanes, vpt, upb);
+    case 8: return pick_vb<T, 8, NBG>(kernel, lanes, vpt, upb);
+    case 4: return pick_vb<T, 4, NBG>(kernel, lanes, vpt, upb);
     case 2:
-        if constexpr (T::kSize == 2) return pick_vb<T, 2>(kernel, lanes, vpt, upb);
+        if constexpr (T::kSize == 2) return pick_vb<T, 2, NBG>(kernel, lanes, vpt, upb);
         return nullptr;
     default: return nullptr;
     }

@@ -125,13 +125,19 @@ void div_magic(uint32_t d, uint32_t* m, uint32_t* s) {
 
 ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const void* out,
                          int64_t rows, int64_t width, int64_t group_size, int64_t sy,
-                         int64_t sg, int64_t so, float eps, int dtype, int ri,
-                         int force_lanes, int force_vpt, int force_upb, LaunchPlan* plan) {
+                         int64_t sg, int64_t so, float eps, int dtype, uint32_t flags,
+                         const ggrms_shape_t* shape, LaunchPlan* plan) {
     if (!plan) return GGRMS_ERROR_INVALID_VALUE;
     memset(plan, 0, sizeof *plan);
     if (rows < 0 || width <= 0 || group_size <= 0 || width % group_size != 0)
         return GGRMS_ERROR_INVALID_VALUE;
-    if (ri != 0 && ri != 1) return GGRMS_ERROR_INVALID_VALUE;
+    const uint32_t known = GGRMS_FLAG_ROUND_INTERMEDIATE | GGRMS_FLAG_NORM_BEFORE_GATE |
+                           GGRMS_FLAG_WEIGHT_PER_GROUP;
+    if (flags & ~known) return GGRMS_ERROR_INVALID_VALUE;
+    if ((flags & GGRMS_FLAG_ROUND_INTERMEDIATE) && (flags & GGRMS_FLAG_NORM_BEFORE_GATE))
+        return GGRMS_ERROR_INVALID_VALUE;
+    plan->flags = flags;
+    const int64_t wlen = (flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? group_size : width;
     if (!std::isfinite(eps) || eps < 0.0f) return GGRMS_ERROR_INVALID_VALUE;
     if (dtype != GGRMS_F32 && dtype != GGRMS_F16 && dtype != GGRMS_BF16)
         return GGRMS_ERROR_NOT_SUPPORTED;
@@ -150,7 +156,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     if (rows == 1) sy = sg = so = width;  // strides of a single row are never used
     int64_t ey, eg, eo, ew, row_bytes;
     if (!extent_bytes(rows, width, sy, esize, &ey) || !extent_bytes(rows, width, sg, esize, &eg) ||
-        !extent_bytes(rows, width, so, esize, &eo) || __builtin_mul_overflow(width, (int64_t)4, &ew) ||
+        !extent_bytes(rows, width, so, esize, &eo) || __builtin_mul_overflow(wlen, (int64_t)4, &ew) ||
         __builtin_mul_overflow(width, (int64_t)esize, &row_bytes))
         return GGRMS_ERROR_INVALID_VALUE;
     if (py + (uintptr_t)ey < py || pg + (uintptr_t)eg < pg || po + (uintptr_t)eo < po ||
@@ -179,10 +185,14 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     }
     const int64_t nvec = group_size * esize / vb;
     int kernel = 0, lanes = 0, vpt = 0, rule_upb = 1;
-    if (force_lanes || force_vpt) {
-        kernel = kernel_for_shape(force_lanes, force_vpt);
-        lanes = force_lanes;
-        vpt = force_vpt;
+    const int force_upb = shape ? shape->rows_per_workgroup : 0;
+    if (force_upb < 0) return GGRMS_ERROR_INVALID_VALUE;
+    if (shape) {
+        if (shape->lanes_per_group == 0 && shape->vectors_per_lane == 0)
+            return GGRMS_ERROR_INVALID_VALUE;
+        kernel = kernel_for_shape(shape->lanes_per_group, shape->vectors_per_lane);
+        lanes = shape->lanes_per_group;
+        vpt = shape->vectors_per_lane;
         if (!shape_supported(kernel, lanes, vpt)) return GGRMS_ERROR_NOT_SUPPORTED;
         if (kernel != GGRMS_KERNEL_WIDE && (int64_t)lanes * vpt < nvec)
             return GGRMS_ERROR_NOT_SUPPORTED;
@@ -245,18 +255,30 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
 
 }  // namespace ggrms
 
+extern "C" ggrms_status_t ggrms_plan_ex(const void* y, const void* gate,
+                                        const float* norm_weight, void* out, int64_t rows,
+                                        int64_t width, int64_t group_size, int64_t y_row_stride,
+                                        int64_t gate_row_stride, int64_t out_row_stride,
+                                        float eps, ggrms_dtype_t dtype, uint32_t flags,
+                                        const ggrms_shape_t* shape, ggrms_plan_t* plan) {
+    if (!plan) return GGRMS_ERROR_INVALID_VALUE;
+    ggrms::LaunchPlan lp;
+    const ggrms_status_t st = ggrms::make_plan(y, gate, norm_weight, out, rows, width, group_size,
+                                               y_row_stride, gate_row_stride, out_row_stride, eps,
+                                               (int)dtype, flags, shape, &lp);
+    if (st == GGRMS_SUCCESS) *plan = lp.pub;
+    return st;
+}
+
 extern "C" ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_weight,
                                      void* out, int64_t rows, int64_t width, int64_t group_size,
                                      int64_t y_row_stride, int64_t gate_row_stride,
                                      int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
                                      int round_intermediate, ggrms_plan_t* plan) {
-    if (!plan) return GGRMS_ERROR_INVALID_VALUE;
-    ggrms::LaunchPlan lp;
-    const ggrms_status_t st = ggrms::make_plan(y, gate, norm_weight, out, rows, width, group_size,
-                                               y_row_stride, gate_row_stride, out_row_stride, eps,
-                                               (int)dtype, round_intermediate, 0, 0, 0, &lp);
-    if (st == GGRMS_SUCCESS) *plan = lp.pub;
-    return st;
+    if (round_intermediate != 0 && round_intermediate != 1) return GGRMS_ERROR_INVALID_VALUE;
+    return ggrms_plan_ex(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                         gate_row_stride, out_row_stride, eps, dtype,
+                         round_intermediate ? GGRMS_FLAG_ROUND_INTERMEDIATE : 0u, nullptr, plan);
 }
 
 extern "C" const char* ggrms_status_string(ggrms_status_t status) {

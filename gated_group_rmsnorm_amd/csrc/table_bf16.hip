@@ -1,11 +1,11 @@
-// table_bf16.hip -- instantiates every kernel shape for one element type, so
-// the three types compile in parallel.
+// table_bf16.hip -- instantiates every kernel shape for one element
+// type and one operator (gate-first), so the six combinations compile in parallel.
 #include "kernels.cuh"
 
 namespace ggrms {
 
 const void* pick_bf16(int kernel, int vb, int lanes, int vpt, int upb) {
-    return pick_type<TBF16>(kernel, vb, lanes, vpt, upb);
+    return pick_type<TBF16, false>(kernel, vb, lanes, vpt, upb);
 }
 
 }  // namespace ggrms

@@ -1,11 +1,11 @@
-// table_f32.hip -- instantiates every kernel shape for one element type, so
-// the three types compile in parallel.
+// table_f32.hip -- instantiates every kernel shape for one element
+// type and one operator (gate-first), so the six combinations compile in parallel.
 #include "kernels.cuh"
 
 namespace ggrms {
 
 const void* pick_f32(int kernel, int vb, int lanes, int vpt, int upb) {
-    return pick_type<TF32>(kernel, vb, lanes, vpt, upb);
+    return pick_type<TF32, false>(kernel, vb, lanes, vpt, upb);
 }
 
 }  // namespace ggrms

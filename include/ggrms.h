@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GGRMS_ABI_VERSION 1
+#define GGRMS_ABI_VERSION 2
 
 /* Element type shared by y, gate and out.  The weight is always f32. */
 typedef enum {
@@ -135,6 +135,51 @@ ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_wei
                           int64_t y_row_stride, int64_t gate_row_stride,
                           int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
                           int round_intermediate, ggrms_plan_t* plan);
+
+/* Operator variants (bits of the `flags` argument of the _ex calls). */
+typedef enum {
+    /* Gate first (the default): cast gated*nf to dtype and back before the
+     * weight multiply.  Same as round_intermediate = 1. */
+    GGRMS_FLAG_ROUND_INTERMEDIATE = 1,
+    /* Norm first: out = cast(((y * nf) * w) * silu(gate)) with
+     * nf = rsqrt(sum y^2 / G + eps) and every intermediate f32 -- the
+     * operator of the page "com.microsoft.GatedRMSNorm" (Description
+     * section).  Not combinable with GGRMS_FLAG_ROUND_INTERMEDIATE. */
+    GGRMS_FLAG_NORM_BEFORE_GATE = 2,
+    /* norm_weight holds group_size values shared by every group (indexed by
+     * the column within the group), as that page's `scale` input does;
+     * without it, width values indexed by the column. */
+    GGRMS_FLAG_WEIGHT_PER_GROUP = 4
+} ggrms_flag_t;
+
+/* A kernel shape for the _ex calls (see ggrms_forward_with_shape). */
+typedef struct {
+    int32_t lanes_per_group;
+    int32_t vectors_per_lane;
+    int32_t rows_per_workgroup; /* 0: let the library choose */
+} ggrms_shape_t;
+
+/*
+ * ggrms_forward_ex -- ggrms_forward with operator flags (a ggrms_flag_t
+ * mask) instead of round_intermediate, and an optional kernel shape (NULL:
+ * the library chooses).  The weight needs width values, or group_size with
+ * GGRMS_FLAG_WEIGHT_PER_GROUP.  GGRMS_ERROR_INVALID_VALUE also for unknown
+ * flag bits or GGRMS_FLAG_ROUND_INTERMEDIATE with
+ * GGRMS_FLAG_NORM_BEFORE_GATE; GGRMS_ERROR_NOT_SUPPORTED for a shape that
+ * cannot be used (as in ggrms_forward_with_shape).
+ */
+ggrms_status_t ggrms_forward_ex(const void* y, const void* gate, const float* norm_weight,
+                                void* out, int64_t rows, int64_t width, int64_t group_size,
+                                int64_t y_row_stride, int64_t gate_row_stride,
+                                int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                uint32_t flags, const ggrms_shape_t* shape, void* stream);
+
+/* ggrms_plan for ggrms_forward_ex's arguments (no HIP call). */
+ggrms_status_t ggrms_plan_ex(const void* y, const void* gate, const float* norm_weight,
+                             void* out, int64_t rows, int64_t width, int64_t group_size,
+                             int64_t y_row_stride, int64_t gate_row_stride,
+                             int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                             uint32_t flags, const ggrms_shape_t* shape, ggrms_plan_t* plan);
 
 /*
  * ggrms_forward_with_shape -- ggrms_forward with the kernel shape chosen by

@@ -155,9 +155,11 @@ class Workload:
     def esize(self) -> int:
         return 4 if self.dtype == F32 else 2
 
-    def algorithmic_bytes(self) -> int:
-        """y, gate and out each touched once, plus the f32 weight once."""
-        return 3 * self.rows * self.width * self.esize + 4 * self.width
+    def algorithmic_bytes(self, per_group_weight: bool = False) -> int:
+        """y, gate and out each touched once, plus the f32 weight once (width
+        values, or group_size values when one weight is shared by every group)."""
+        wlen = self.group_size if per_group_weight else self.width
+        return 3 * self.rows * self.width * self.esize + 4 * wlen
 
 
 WORKLOADS = {

@@ -43,7 +43,7 @@ def test_header_symbols_exported(g):
 
 
 def test_abi_version_and_strings(g):
-    assert g.ggrms_abi_version() == 1
+    assert g.ggrms_abi_version() == 2
     for st in range(4):
         assert g.ggrms_status_string(st)
     assert g.ggrms_status_string(99) == "unknown status"
@@ -114,6 +114,64 @@ def test_interleaved_views_do_not_overlap(g):
     st, _, _ = _fwd(g, rows=8, width=100, group_size=100, y=A, gate=A + 200, out=A + 398,
                     y_row_stride=300, gate_row_stride=300, out_row_stride=300, dtype=F16)
     assert st == INVALID
+
+
+RI, NBG, PER_GROUP = 1, 2, 4
+
+
+def _plan_ex(g, flags, shape=None, **kw):
+    args = dict(y=A, gate=A + (1 << 24), norm_weight=A + (2 << 24), out=A + (3 << 24), rows=4,
+                width=256, group_size=64, y_row_stride=256, gate_row_stride=256,
+                out_row_stride=256, eps=1e-5, dtype=BF16)
+    args.update(kw)
+    st, plan = g.ggrms_plan_ex(*args.values(), flags, shape)
+    if st != OK or args["rows"] == 0:
+        # rejected (or nothing to launch): the forward entry point returns
+        # the same status without reaching the HIP runtime
+        assert g.ggrms_forward_ex(*args.values(), flags, 0, shape) == st
+    return st, plan
+
+
+@pytest.mark.parametrize("flags", [8, 16, 1 << 31, RI | NBG, RI | NBG | PER_GROUP])
+def test_invalid_flags(g, flags):
+    assert _plan_ex(g, flags)[0] == INVALID
+
+
+@pytest.mark.parametrize("flags", [0, RI, NBG, PER_GROUP, RI | PER_GROUP, NBG | PER_GROUP])
+def test_valid_flags_plan_like_the_default(g, flags):
+    """The operator variants use the same kernel shapes: only the
+    arithmetic and the weight's stride between groups differ."""
+    st, p = _plan_ex(g, flags, rows=64, width=7680, group_size=960, y_row_stride=7680,
+                     gate_row_stride=7680, out_row_stride=7680,
+                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == OK
+    st, ref = g.ggrms_plan(A, A + (1 << 26), A + (2 << 26), A + (3 << 26), 64, 7680, 960, 7680,
+                           7680, 7680, 1e-5, BF16, 1)
+    assert p == ref
+
+
+def test_per_group_weight_extent(g):
+    """A per-group weight spans group_size floats, a per-column one width
+    floats: a weight that ends 512 bytes below the top of the address space
+    holds a 64-value group weight but not a 256-column one."""
+    top = (1 << 64) - 512
+    assert _plan_ex(g, 0, norm_weight=top)[0] == INVALID
+    assert _plan_ex(g, PER_GROUP, norm_weight=top)[0] == OK
+    assert _plan_ex(g, NBG | PER_GROUP, norm_weight=top)[0] == OK
+
+
+def test_plan_ex_with_shape(g):
+    st, p = _plan_ex(g, NBG, shape=(64, 2), width=960, group_size=960, y_row_stride=960,
+                     gate_row_stride=960, out_row_stride=960)
+    assert st == OK and (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 64, 2)
+    st, p = _plan_ex(g, RI, shape=(128, 1, 2), width=960, group_size=960, y_row_stride=960,
+                     gate_row_stride=960, out_row_stride=960)
+    assert st == OK and (p["lanes_per_group"], p["rows_per_workgroup"], p["lds_bytes"]) == (128, 2, 3840)
+    assert _plan_ex(g, 0, shape=(64, 1), width=960, group_size=960, y_row_stride=960,
+                    gate_row_stride=960, out_row_stride=960)[0] == NOTSUP
+    assert _plan_ex(g, 0, shape=(0, 0))[0] == INVALID
+    assert _plan_ex(g, 0, shape=(128, 1, -1), width=1024, group_size=1024, y_row_stride=1024,
+                    gate_row_stride=1024, out_row_stride=1024)[0] == INVALID
 
 
 def _plan(g, rows, width, G, dtype, sy=None, sg=None, so=None, y=A, gate=A + (1 << 30),
@@ -255,6 +313,22 @@ int main() {
                                        rows, width, G, width + off, width, width, 1e-5f,
                                        (ggrms_dtype_t)dt, 1, &p);
         n_ok += st == GGRMS_SUCCESS;
+        const ggrms_shape_t shapes[] = {{64, 2, 0}, {128, 1, 4}, {256, 3, 2}, {1024, 0, 0},
+                                        {16, 1, 0}, {0, 0, 0}, {128, 1, -1}};
+        for (uint32_t flags = 0; flags < 9; ++flags) {
+            st = ggrms_plan_ex((void*)(base + off * 2), (void*)(base + (1u << 28)),
+                               (const float*)(base + (2u << 28) + off * 4),
+                               (void*)(base + (3u << 28)), rows, width, G, width + off, width,
+                               width, 1e-5f, (ggrms_dtype_t)dt, flags, nullptr, &p);
+            n_ok += st == GGRMS_SUCCESS;
+            for (const ggrms_shape_t& sh : shapes) {
+                st = ggrms_plan_ex((void*)(base + off * 2), (void*)(base + (1u << 28)),
+                                   (const float*)(base + (2u << 28)), (void*)(base + (3u << 28)),
+                                   rows, width, G, width + off, width, width, 1e-5f,
+                                   (ggrms_dtype_t)dt, flags, &sh, &p);
+                n_ok += st == GGRMS_SUCCESS;
+            }
+        }
     }
     printf("%ld\n", n_ok);
     return n_ok > 0 ? 0 : 1;

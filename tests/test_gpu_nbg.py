@@ -1,0 +1,285 @@
+"""GPU parity of the operator variants against the CPU oracle: norm before
+gate (page "com.microsoft.GatedRMSNorm", Description section: the RMS of y
+alone, then the scale, then silu(gate)) and a weight of group_size values
+shared by every group (that page's `scale` input), each through
+ggrms_forward_ex.
+
+Same bar as the gate-first tests: f32 within a relative 1e-5 of the oracle,
+fp16/bf16 within 2 units in the last place, NaN where the oracle has NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from gpu_util import (BF16, DT_IDS, F16, F32, FLAG_NBG, FLAG_PER_GROUP, FLAG_RI, TDT,
+                      assert_parity, check_contiguous, dev_buf, host_bits, random_case, run_gpu,
+                      say)
+
+pytestmark = pytest.mark.gpu
+
+NBG, NBG_PG = FLAG_NBG, FLAG_NBG | FLAG_PER_GROUP
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_group_rmsnorm_amd as g  # raises if libggrms.so is missing
+
+    return g
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+
+    oracle.build(force=False)
+    return oracle
+
+
+def workload_weight(w, wt):
+    """The workload's weight in the form its operator takes: the per-head
+    scale itself where the workload has one spanning a group, else the
+    per-column weight."""
+    if w.scale_len and w.scale_len == w.group_size:
+        return np.ascontiguousarray(wt[:w.group_size]), True
+    return wt, False
+
+
+@pytest.mark.parametrize("name", list(S.WORKLOADS))
+def test_workload_full_size_nbg(g, orc, name):
+    """Every configured workload at full size in the norm-first operator,
+    element by element, in the benchmark's layout; the 128-wide fp16 head
+    scale of the GDN-shaped workload is passed as the shared group weight."""
+    w = S.WORKLOADS[name]
+    ybuf, gbuf, wt, lay = S.make_inputs(w)
+    wt, per_group = workload_weight(w, wt)
+    say(f"workload {name} nbg per_group={per_group}")
+    rows, width = w.rows, w.width
+    wd = torch.from_numpy(wt).cuda()
+    if w.fused_width:
+        fd = dev_buf(ybuf, w.dtype)
+        yv, gv = fd[lay["y_offset"]:], fd[lay["gate_offset"]:]
+    else:
+        yv, gv = dev_buf(ybuf, w.dtype), dev_buf(gbuf, w.dtype)
+    od = torch.empty(rows * width, dtype=TDT[w.dtype], device="cuda")
+    flags = NBG | (FLAG_PER_GROUP if per_group else 0)
+    st = run_gpu(g, yv, gv, wd, od, rows, width, w.group_size, lay["y_row_stride"],
+                 lay["gate_row_stride"], width, w.eps, w.dtype, 0, flags=flags)
+    assert st == g.SUCCESS, g.ggrms_status_string(st)
+    torch.cuda.synchronize()
+    got = host_bits(od, w.dtype)
+    ref = orc.forward(ybuf, gbuf, wt, rows=rows, width=width, group_size=w.group_size,
+                      y_row_stride=lay["y_row_stride"], gate_row_stride=lay["gate_row_stride"],
+                      out_row_stride=width, eps=w.eps, dtype=w.dtype, y_offset=lay["y_offset"],
+                      gate_offset=lay["gate_offset"], norm_before_gate=True,
+                      weight_per_group=per_group)
+    stats = assert_parity(got, ref, w.dtype, name)
+    say(f"  {name} nbg: {stats}")
+
+
+G_SWEEP = [1, 3, 8, 24, 63, 64, 100, 128, 129, 257, 960, 1024, 2056, 4096, 7680, 32768, 32776]
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16, F32], ids=DT_IDS.get)
+@pytest.mark.parametrize("G", G_SWEEP)
+def test_nbg_group_size_sweep(g, orc, G, dtype):
+    """The norm-first operator on every kernel family (one group per lane,
+    wave segments, multi-wave workgroups with staged weights, the two-pass
+    kernel), with per-column and shared group weights."""
+    if dtype == F32 and G > 4096:
+        pytest.skip("f32 beyond G = 4096: the oracle's own sum error nears the 1e-5 bar")
+    groups = 3 if G <= 4096 else 2
+    rows = 6 if G <= 1024 else 3
+    for flags in (NBG, NBG_PG):
+        check_contiguous(g, orc, rows, G * groups, G, dtype, 0, seed=G * 5 + dtype + flags,
+                         tag=f"nbg G={G}", flags=flags)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16, F32], ids=DT_IDS.get)
+@pytest.mark.parametrize("G", [8, 100, 960, 2056, 32776])
+def test_shared_weight_equals_tiled_weight(g, orc, G, dtype):
+    """A shared group weight gives the same bits as the same values tiled
+    over every group as a per-column weight, in both operators."""
+    groups, rows = 3, 5
+    width = G * groups
+    y, gt, w = random_case(rows, width, dtype, seed=G + 3 * dtype)
+    wg = np.ascontiguousarray(w[:G])
+    yd, gd = dev_buf(y, dtype), dev_buf(gt, dtype)
+    wgd = torch.from_numpy(wg).cuda()
+    wtd = torch.from_numpy(np.tile(wg, groups)).cuda()
+    for base in ((0, FLAG_RI) if dtype != F32 else (0,)) + (FLAG_NBG,):
+        say(f"case shared weight G={G} dtype={DT_IDS[dtype]} base={base}")
+        o1, o2 = torch.empty_like(yd), torch.empty_like(yd)
+        assert run_gpu(g, yd, gd, wgd, o1, rows, width, G, width, width, width, 1e-5, dtype, 0,
+                       flags=base | FLAG_PER_GROUP) == g.SUCCESS
+        assert run_gpu(g, yd, gd, wtd, o2, rows, width, G, width, width, width, 1e-5, dtype, 0,
+                       flags=base) == g.SUCCESS
+        torch.cuda.synchronize()
+        a, b = host_bits(o1, dtype), host_bits(o2, dtype)
+        assert np.array_equal(a.view(np.uint32) if dtype == F32 else a,
+                              b.view(np.uint32) if dtype == F32 else b)
+        ref = orc.forward(y, gt, wg, rows=rows, width=width, group_size=G, y_row_stride=width,
+                          gate_row_stride=width, out_row_stride=width, eps=1e-5, dtype=dtype,
+                          round_intermediate=base & FLAG_RI,
+                          norm_before_gate=bool(base & FLAG_NBG), weight_per_group=True)
+        assert_parity(a, ref, dtype, f"shared weight base={base}")
+
+
+SHAPES = [(1, 1), (4, 1), (16, 1), (64, 1), (64, 2), (64, 4)] + \
+         [(l, v, 1) for l in (128, 256, 512, 1024) for v in (1, 4)] + \
+         [(128, v, u) for v in (1, 2) for u in (2, 4)] + [(256, 2, 2), (1024, 0)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_nbg_forced_shapes(g, orc, shape):
+    """Each kernel shape, forced, in the norm-first operator with a shared
+    group weight (the staged-weight path reads the same G values for every
+    group), on 7 rows so the last row tile is partly empty."""
+    lanes, vpt = shape[:2]
+    cap = lanes * (vpt or 8)
+    for nvec in sorted({max(1, cap), max(1, cap - 3)}):
+        G = nvec * 8
+        if G > 65536:
+            continue
+        for flags in (NBG, NBG_PG):
+            check_contiguous(g, orc, 7, G * 2, G, BF16, 0, seed=nvec + lanes + flags,
+                             shape=shape, tag=f"nbg forced {shape} G={G}", flags=flags)
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16, F32], ids=DT_IDS.get)
+def test_nbg_special_values(g, orc, dtype):
+    """NaN/inf in y (the whole group follows) and in the gate (only that
+    element: silu(gate) multiplies after the norm), zero groups, gates in
+    silu's underflow window and large gates."""
+    rows, width, G = 16, 1024, 128
+    rng = np.random.default_rng(19)
+    yv = rng.standard_normal((rows, width))
+    gv = rng.standard_normal((rows, width))
+    yv[0, 5] = np.nan
+    yv[1, 200] = np.inf
+    gv[2, 300] = np.nan
+    yv[3, :G] = 0.0
+    gv[4, :] = rng.uniform(-104, -86, width)
+    gv[5, :G] = -95.0
+    gv[6, :] = rng.uniform(80, 100, width)
+    gv[7, 7] = -np.inf
+    gv[7, 300] = np.inf
+    yv[8, G:2 * G] = 1e-30  # tiny but non-zero: nf large, products near the range's ends
+    import refs
+    y = refs.round64(yv, dtype).reshape(-1)
+    gt = refs.round64(gv, dtype).reshape(-1)
+    w = rng.uniform(0.5, 1.5, width).astype(np.float32)
+    yd, gd = dev_buf(y, dtype), dev_buf(gt, dtype)
+    for per_group in (False, True):
+        wa = np.ascontiguousarray(w[:G]) if per_group else w
+        wd = torch.from_numpy(wa).cuda()
+        for eps in (1e-5, 0.0):
+            say(f"case nbg special dtype={DT_IDS[dtype]} eps={eps} per_group={per_group}")
+            od = torch.empty_like(yd)
+            flags = NBG_PG if per_group else NBG
+            assert run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, eps, dtype, 0,
+                           flags=flags) == g.SUCCESS
+            torch.cuda.synchronize()
+            ref = orc.forward(y, gt, wa, rows=rows, width=width, group_size=G,
+                              y_row_stride=width, gate_row_stride=width, out_row_stride=width,
+                              eps=eps, dtype=dtype, norm_before_gate=True,
+                              weight_per_group=per_group)
+            assert_parity(host_bits(od, dtype), ref, dtype, f"nbg special eps={eps}")
+
+
+def test_nbg_strided_and_in_place(g, orc):
+    """Column slices of one fused buffer with padded strides, and the output
+    written over the gate, in the norm-first operator."""
+    rows, width, G, fused = 37, 4800, 100, 9856
+    buf = S.tensor(41, S.TID_Y, rows * fused, F16, ("normal", 1.0))
+    w = S.tensor(41, S.TID_W, G, F32, ("uniform", 0.5, 1.5))
+    ref = orc.forward(buf, buf, w, rows=rows, width=width, group_size=G, y_row_stride=fused,
+                      gate_row_stride=fused, out_row_stride=fused, eps=1e-5, dtype=F16,
+                      gate_offset=width, out_offset=width, norm_before_gate=True,
+                      weight_per_group=True, out=buf.copy())
+    fd = dev_buf(buf, F16)
+    wd = torch.from_numpy(w).cuda()
+    say("case nbg strided in place")
+    assert run_gpu(g, fd, fd[width:], wd, fd[width:], rows, width, G, fused, fused, fused, 1e-5,
+                   F16, 0, flags=NBG_PG) == g.SUCCESS
+    torch.cuda.synchronize()
+    assert_parity(host_bits(fd, F16), ref, F16, "nbg strided in place")
+
+
+def test_nbg_rejections(g):
+    """Round-intermediate with norm-first and unknown flag bits are refused
+    before any launch; the output is left untouched."""
+    yd = torch.ones(4 * 256, dtype=torch.bfloat16, device="cuda")
+    wd = torch.ones(256, dtype=torch.float32, device="cuda")
+    od = torch.full_like(yd, 7.0)
+    for flags in (FLAG_RI | FLAG_NBG, 8, 1 << 20):
+        assert run_gpu(g, yd, yd, wd, od, 4, 256, 64, 256, 256, 256, 1e-5, BF16, 0,
+                       flags=flags) == g.ERROR_INVALID_VALUE
+    torch.cuda.synchronize()
+    assert bool((od == 7.0).all())
+
+
+def test_nbg_graph_capture_replays(g):
+    """21 decode-sized norm-first launches (shared 960-value weight) captured
+    once and replayed with eager work between replays, each replay equal to
+    the eager result bit for bit."""
+    width, G = 7680, 960
+    layers = []
+    for layer in range(S.DECODE_LAYERS):
+        y, gt, w = random_case(1, width, BF16, seed=500 + layer)
+        layers.append((dev_buf(y, BF16), dev_buf(gt, BF16),
+                       torch.from_numpy(np.ascontiguousarray(w[:G])).cuda(),
+                       torch.empty(width, dtype=torch.bfloat16, device="cuda")))
+    torch.cuda.synchronize()
+
+    def burst(stream):
+        for yd, gd, wd, od in layers:
+            assert run_gpu(g, yd, gd, wd, od, 1, width, G, width, width, width, 1e-5, BF16, 0,
+                           stream=stream, flags=NBG_PG) == g.SUCCESS
+
+    burst(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = [o.clone() for *_, o in layers]
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cs):
+        burst(cs)
+    for rep in range(3):
+        for *_, o in layers:
+            o.fill_(0)
+        junk = torch.randn(1 << 20, device="cuda").sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert junk.isfinite()
+        for o, e in zip((o for *_, o in layers), eager):
+            assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {rep}"
+
+
+def test_torch_wrapper_nbg(g, orc):
+    """forward(norm_before_gate=True) with the per-head scale passed as is
+    (group_size values) and tiled (width values) gives the same bits and
+    matches the oracle; round_intermediate with it raises."""
+    B, T, H, C = 3, 7, 16, 128
+    width = H * C
+    fused = torch.randn(B, T, 2 * width, generator=torch.Generator().manual_seed(3)).to(torch.float16)
+    scale = (torch.rand(C, generator=torch.Generator().manual_seed(4)) + 0.5).to(torch.float16)
+    fd = fused.cuda()
+    y, gate = fd[..., :width], fd[..., width:]
+    w_head = scale.float().cuda()
+    o1 = g.forward(y, gate, w_head, C, eps=1e-6, norm_before_gate=True)
+    o2 = g.forward(y, gate, g.expand_head_scale(scale.cuda(), H), C, eps=1e-6,
+                   norm_before_gate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    yh = fused[..., :width].contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    gh = fused[..., width:].contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    ref = orc.forward(yh, gh, scale.float().numpy(), rows=B * T, width=width, group_size=C,
+                      y_row_stride=width, gate_row_stride=width, out_row_stride=width, eps=1e-6,
+                      dtype=F16, norm_before_gate=True, weight_per_group=True)
+    assert_parity(o1.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1), ref, F16,
+                  "wrapper nbg")
+    with pytest.raises(g.GgrmsError):
+        g.forward(y, gate, w_head, C, round_intermediate=True, norm_before_gate=True)
+    assert g.plan(y, gate, w_head, C, norm_before_gate=True)["kernel_name"] == "wave"
