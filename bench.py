@@ -9,9 +9,9 @@ inputs in the 256 MB last-level cache.
 
 Printed (one JSON line): whole-job HBM throughput in GB/s over the timed
 steps, the kernel's roofline figures (event-timed average launch), the
-decode latency (1 x 7680, 21 layers back to back, eager and graph-replayed,
-next to an empty kernel of the same grid), the unfused four-op chain in
-PyTorch eager timed the same ways, and the CPU oracle timed on a bounded
+decode latency (1 x 7680, 21 layers back to back issued from C, eager and
+graph-replayed, next to an empty kernel of the same grid), the unfused
+four-op chain in PyTorch eager, and the CPU oracle timed on a bounded
 sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|copy]
@@ -182,67 +182,80 @@ def bench_prefill(torch, g, S, args, shape):
 
 
 def bench_decode(torch, g, S, bursts):
-    """21 back-to-back launches (distinct layer inputs) per burst, timed with
-    events around each burst; eager and as one replayed HIP graph; next to an
-    empty kernel launched with the same grid the same ways."""
+    """21 back-to-back launches (distinct layer inputs) per burst, issued from
+    C through libggrms.so (libggrms_bench.so's loop: no interpreter between
+    launches), timed with events around each burst; eager and as one replayed
+    HIP graph; next to an empty kernel launched with the same grid the same
+    ways.  Also: the same bursts with the streaming cache hint forced (the
+    default keeps a job this small cached), and the eager burst issued from
+    Python through the ctypes binding, for context."""
     w = S.WORKLOADS[DECODE]
     L = S.DECODE_LAYERS
     layers = [Setup(torch, S, w, 1, layer) for layer in range(L)]
     aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
-    aux.ggrms_bench_empty.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    vp = ctypes.c_void_p
+    aux.ggrms_bench_decode_native.argtypes = [
+        ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+        ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+        ctypes.POINTER(ctypes.c_double)]
     plan = layers[0].plan(g)
-    blocks, threads = plan["workgroups"], plan["block_threads"]
+    ptrs = [layers[i].sets[0] for i in range(L)]
+    arr = lambda xs: (vp * L)(*xs)
+    ys = arr([p[0].data_ptr() for p in ptrs])
+    gs = arr([p[1].data_ptr() for p in ptrs])
+    ws = arr([ly.weight.data_ptr() for ly in layers])
+    outs = arr([p[2].data_ptr() for p in ptrs])
 
-    def fused_burst(stream):
+    def native(mode, flags):
+        dev, host = ctypes.c_double(), ctypes.c_double()
+        rc = aux.ggrms_bench_decode_native(ys, gs, ws, outs, L, w.width, w.group_size, w.eps,
+                                           w.dtype, flags, bursts, mode, ctypes.byref(dev),
+                                           ctypes.byref(host))
+        if rc != 0:
+            raise RuntimeError(f"ggrms_bench_decode_native mode {mode}: status {rc}")
+        return dev.value, host.value
+
+    flags = layers[0].flags
+    eager, host = native(0, flags)
+    graph, _ = native(1, flags)
+    floor_eager, floor_host = native(2, flags)
+    floor_graph, _ = native(3, flags)
+    eager_nt, _ = native(0, flags | g.FLAG_CACHE_STREAM)
+    graph_nt, _ = native(1, flags | g.FLAG_CACHE_STREAM)
+
+    def python_burst(stream):
         for ly in layers:
             ly.launch(g, 0, stream)
 
-    def empty_burst(stream):
-        for _ in range(L):
-            if aux.ggrms_bench_empty(blocks, threads, stream) != 0:
-                raise RuntimeError("empty kernel launch failed")
-
-    def timed(burst_fn):
-        stream = torch.cuda.current_stream()
-        sp = stream.cuda_stream
-        settle(torch, lambda i: burst_fn(sp), 0.1)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(bursts)]
-        torch.cuda.synchronize()
-        for a, b in evs:
-            a.record(stream)
-            burst_fn(sp)
-            b.record(stream)
-        torch.cuda.synchronize()
-        return statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3 / L
-
-    def graphed(burst_fn):
-        cs = torch.cuda.Stream()
-        graph = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=cs):
-            burst_fn(cs.cuda_stream)
-        stream = torch.cuda.current_stream()
-        settle(torch, lambda i: graph.replay(), 0.1)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(bursts)]
-        torch.cuda.synchronize()
-        for a, b in evs:
-            a.record(stream)
-            graph.replay()
-            b.record(stream)
-        torch.cuda.synchronize()
-        return statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3 / L
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    settle(torch, lambda i: python_burst(sp), 0.1)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(bursts)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        python_burst(sp)
+        b.record(stream)
+    torch.cuda.synchronize()
+    py_eager = statistics.median(a.elapsed_time(b) for a, b in evs) * 1e3 / L
 
     res = {
         "workload": w.name,
         "layers": L,
         "bursts": bursts,
-        "us_per_launch_eager": timed(fused_burst),
-        "floor_us_per_launch_eager": timed(empty_burst),
-        "us_per_launch_graph": graphed(fused_burst),
-        "floor_us_per_launch_graph": graphed(empty_burst),
-        "grid": [blocks, threads],
+        "cache_policy": "stream" if plan["streaming"] else "keep",
+        "us_per_launch_eager": eager,
+        "host_us_per_call": host,
+        "floor_us_per_launch_eager": floor_eager,
+        "floor_host_us_per_call": floor_host,
+        "us_per_launch_graph": graph,
+        "floor_us_per_launch_graph": floor_graph,
+        "us_per_launch_eager_streamed": eager_nt,
+        "us_per_launch_graph_streamed": graph_nt,
+        "us_per_launch_eager_python": py_eager,
+        "grid": [plan["workgroups"], plan["block_threads"]],
     }
     log(f"decode: {json.dumps(res)}")
     return res

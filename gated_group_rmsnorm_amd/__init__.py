@@ -29,7 +29,7 @@ import os
 
 __all__ = [
     "F32", "F16", "BF16", "FLAG_ROUND_INTERMEDIATE", "FLAG_NORM_BEFORE_GATE",
-    "FLAG_WEIGHT_PER_GROUP", "SUCCESS", "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED",
+    "FLAG_WEIGHT_PER_GROUP", "FLAG_CACHE_STREAM", "FLAG_CACHE_KEEP", "STREAM_MIN_BYTES", "SUCCESS", "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED",
     "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError", "ggrms_forward", "ggrms_forward_ex",
     "ggrms_forward_with_shape", "ggrms_plan", "ggrms_plan_ex",
     "ggrms_status_string", "ggrms_abi_version", "forward", "plan", "expand_head_scale",
@@ -38,9 +38,11 @@ __all__ = [
 
 F32, F16, BF16 = 0, 1, 2
 FLAG_ROUND_INTERMEDIATE, FLAG_NORM_BEFORE_GATE, FLAG_WEIGHT_PER_GROUP = 1, 2, 4
+FLAG_CACHE_STREAM, FLAG_CACHE_KEEP = 8, 16
+STREAM_MIN_BYTES = 4 << 20  # default policy: jobs of at least this many y+gate+out bytes stream
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
 KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide"}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libggrms.so")
@@ -66,7 +68,8 @@ class _Plan(ctypes.Structure):
                 ("lanes_per_group", ctypes.c_int32), ("vectors_per_lane", ctypes.c_int32),
                 ("block_threads", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("rows_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
-                ("workgroups", ctypes.c_int64)]
+                ("workgroups", ctypes.c_int64), ("streaming", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -225,18 +228,23 @@ def expand_head_scale(scale, heads: int):
     return s.repeat(heads).contiguous()
 
 
-def _flags(weight, width, group_size, round_intermediate, norm_before_gate) -> int:
+_CACHE_FLAGS = {None: 0, "stream": FLAG_CACHE_STREAM, "keep": FLAG_CACHE_KEEP}
+
+
+def _flags(weight, width, group_size, round_intermediate, norm_before_gate, cache=None) -> int:
     if round_intermediate is None:
         round_intermediate = not norm_before_gate
+    if cache not in _CACHE_FLAGS:
+        raise ValueError(f"cache must be None, 'stream' or 'keep', not {cache!r}")
     per_group = weight.numel() == group_size and group_size != width
     return ((FLAG_ROUND_INTERMEDIATE if round_intermediate else 0) |
             (FLAG_NORM_BEFORE_GATE if norm_before_gate else 0) |
-            (FLAG_WEIGHT_PER_GROUP if per_group else 0))
+            (FLAG_WEIGHT_PER_GROUP if per_group else 0) | _CACHE_FLAGS[cache])
 
 
 def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
             round_intermediate=None, out=None, stream=None,
-            norm_before_gate: bool = False):
+            norm_before_gate: bool = False, cache=None):
     """out = fused gated group-RMSNorm of (y, gate) with the f32 ``weight``
     over groups of ``group_size`` columns of the last axis.
 
@@ -249,6 +257,8 @@ def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
     dtype before the weight multiply.  norm_before_gate selects
     out = ((y * nf) * w) * silu(gate) with nf from y alone, every
     intermediate f32 (round_intermediate=True is then refused).
+    cache: None (the library streams jobs of at least STREAM_MIN_BYTES and
+    keeps smaller ones cached), "stream" or "keep"; results are identical.
     Enqueued on ``stream`` (default: torch's current stream); no
     synchronisation.
     """
@@ -279,7 +289,7 @@ def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
         stream = torch.cuda.current_stream(y.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    flags = _flags(weight, width, group_size, round_intermediate, norm_before_gate)
+    flags = _flags(weight, width, group_size, round_intermediate, norm_before_gate, cache)
     with torch.cuda.device(y.device):
         st = ggrms_forward_ex(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), out.data_ptr(),
                               rows, width, group_size, sy, sg, so, float(eps), code, flags,
@@ -290,7 +300,7 @@ def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
 
 
 def plan(y, gate, weight, group_size: int, eps: float = 1e-5, round_intermediate=None,
-         out=None, norm_before_gate: bool = False) -> dict:
+         out=None, norm_before_gate: bool = False, cache=None) -> dict:
     """The kernel forward() would launch for these tensors (no device call)."""
     code = _torch_dtype_code(y)
     width = y.size(-1)
@@ -301,7 +311,7 @@ def plan(y, gate, weight, group_size: int, eps: float = 1e-5, round_intermediate
     st, p = ggrms_plan_ex(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), o.data_ptr(), rows,
                           width, group_size, sy, sg, so, float(eps), code,
                           _flags(weight, width, group_size, round_intermediate,
-                                 norm_before_gate))
+                                 norm_before_gate, cache))
     if st != SUCCESS:
         raise GgrmsError(st, "ggrms_plan")
     return p

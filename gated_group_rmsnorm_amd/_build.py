@@ -51,9 +51,9 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _link(objs, out):
+def _link(objs, out, libs=()):
     tmp = out + f".tmp{os.getpid()}"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *libs])
     os.replace(tmp, out)
 
 
@@ -66,7 +66,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = dict(zip(srcs, ex.map(_compile, srcs)))
     _link([objs[s] for s in LIB_HIP + LIB_CXX], LIB)
-    _link([objs[s] for s in BENCH_HIP], BENCH_LIB)
+    # the benchmark helpers call the product library itself (found next to them)
+    _link([objs[s] for s in BENCH_HIP], BENCH_LIB,
+          ["-L", PKG, "-l:libggrms.so", "-Wl,-rpath,$ORIGIN"])
     if verbose:
         print(f"built {LIB} and {BENCH_LIB}")
     return LIB

@@ -3,11 +3,19 @@
 //   * an empty kernel taking an argument block of the same size as the
 //     normalisation kernels, launched with a caller-chosen grid: the floor
 //     that a decode launch is compared against;
+//   * decode bursts issued from C through libggrms.so's ggrms_forward_ex
+//     (eager and replayed as one HIP graph), next to the same bursts of the
+//     empty kernel, so the per-launch figure carries no interpreter overhead;
 //   * a plain 16-byte vector copy of known size: the calibration that turns
 //     the FETCH_SIZE / WRITE_SIZE counters into HBM bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <chrono>
+#include <vector>
+
+#include "ggrms.h"
 #include "ggrms_internal.h"
 
 namespace {
@@ -51,4 +59,103 @@ extern "C" int ggrms_bench_copy(const void* src, void* dst, int64_t nbytes, void
                            static_cast<hipStream_t>(stream)) == hipSuccess
                ? 0
                : 1;
+}
+
+namespace {
+
+double median_of(std::vector<double> v) {
+    std::sort(v.begin(), v.end());
+    return v.empty() ? 0.0 : v[v.size() / 2];
+}
+
+// The stream, events and graph of one measurement, released on every path.
+struct BurstRes {
+    hipStream_t s = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    ~BurstRes() {
+        if (s) hipStreamSynchronize(s);
+        if (exec) hipGraphExecDestroy(exec);
+        if (graph) hipGraphDestroy(graph);
+        if (e0) hipEventDestroy(e0);
+        if (e1) hipEventDestroy(e1);
+        if (s) hipStreamDestroy(s);
+    }
+};
+
+}  // namespace
+
+// Decode bursts: `layers` back-to-back launches over the layers' [1, width]
+// buffers, repeated `bursts` times on a stream of its own, after about 100 ms
+// of untimed bursts (the clocks settle).  mode 0: ggrms_forward_ex eager;
+// 1: the same burst captured once and replayed as a HIP graph; 2 and 3: the
+// empty kernel with the fused launch's grid, eager and graph.  Device time
+// comes from events around each burst (median burst / layers); host time is
+// the steady-clock time of enqueueing one burst (median / layers).
+// Returns 0, or a ggrms status / -1 for a HIP error.
+extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const* gate,
+                                         const float* const* w, void* const* out, int layers,
+                                         int64_t width, int64_t group_size, float eps, int dtype,
+                                         uint32_t flags, int bursts, int mode, double* dev_us,
+                                         double* host_us) {
+    if (layers <= 0 || bursts <= 0 || mode < 0 || mode > 3) return GGRMS_ERROR_INVALID_VALUE;
+    ggrms_plan_t plan;
+    const int st = ggrms_plan_ex(y[0], gate[0], w[0], out[0], 1, width, group_size, width, width,
+                                 width, eps, (ggrms_dtype_t)dtype, flags, nullptr, &plan);
+    if (st != GGRMS_SUCCESS) return st;
+    BurstRes r;
+    if (hipStreamCreate(&r.s) != hipSuccess || hipEventCreate(&r.e0) != hipSuccess ||
+        hipEventCreate(&r.e1) != hipSuccess)
+        return -1;
+    const bool empty = mode >= 2;
+    auto burst = [&]() -> int {
+        for (int l = 0; l < layers; ++l) {
+            if (empty) {
+                if (ggrms_bench_empty(plan.workgroups, plan.block_threads, r.s) != 0) return -1;
+            } else {
+                const int rc = ggrms_forward_ex(y[l], gate[l], w[l], out[l], 1, width, group_size,
+                                                width, width, width, eps, (ggrms_dtype_t)dtype,
+                                                flags, nullptr, r.s);
+                if (rc != GGRMS_SUCCESS) return rc;
+            }
+        }
+        return 0;
+    };
+    const bool graphed = mode == 1 || mode == 3;
+    if (graphed) {
+        if (hipStreamBeginCapture(r.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return -1;
+        const int rc = burst();
+        const bool ended = hipStreamEndCapture(r.s, &r.graph) == hipSuccess;
+        if (rc) return rc;
+        if (!ended || hipGraphInstantiate(&r.exec, r.graph, nullptr, nullptr, 0) != hipSuccess)
+            return -1;
+    }
+    auto run = [&]() -> int {
+        if (graphed) return hipGraphLaunch(r.exec, r.s) == hipSuccess ? 0 : -1;
+        return burst();
+    };
+    const auto t0 = std::chrono::steady_clock::now();
+    while (std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() < 0.1) {
+        for (int i = 0; i < 8; ++i)
+            if (const int rc = run()) return rc;
+        if (hipStreamSynchronize(r.s) != hipSuccess) return -1;
+    }
+    std::vector<double> dev, host;
+    for (int b = 0; b < bursts; ++b) {
+        if (hipStreamSynchronize(r.s) != hipSuccess || hipEventRecord(r.e0, r.s) != hipSuccess)
+            return -1;
+        const auto h0 = std::chrono::steady_clock::now();
+        if (const int rc = run()) return rc;
+        const auto h1 = std::chrono::steady_clock::now();
+        float ms = 0.0f;
+        if (hipEventRecord(r.e1, r.s) != hipSuccess || hipEventSynchronize(r.e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess)
+            return -1;
+        dev.push_back(ms * 1e3 / layers);
+        host.push_back(std::chrono::duration<double, std::micro>(h1 - h0).count() / layers);
+    }
+    *dev_us = median_of(dev);
+    *host_us = median_of(host);
+    return 0;
 }

@@ -87,12 +87,13 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
 void div_magic(uint32_t d, uint32_t* m, uint32_t* s);
 
 // Kernel lookup per dtype (kernel tables); nullptr if the shape is not built.
-// (nbg selects the norm-before-gate instantiations, in their own files.)
-const void* pick_f32(int kernel, int vb, int lanes, int vpt, int upb);
-const void* pick_f16(int kernel, int vb, int lanes, int vpt, int upb);
-const void* pick_bf16(int kernel, int vb, int lanes, int vpt, int upb);
-const void* pick_f32_nbg(int kernel, int vb, int lanes, int vpt, int upb);
-const void* pick_f16_nbg(int kernel, int vb, int lanes, int vpt, int upb);
-const void* pick_bf16_nbg(int kernel, int vb, int lanes, int vpt, int upb);
+// (nbg selects the norm-before-gate instantiations, in their own files; nt
+// the variant whose y/gate/out accesses carry the non-temporal hint.)
+const void* pick_f32(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
+const void* pick_f16(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
+const void* pick_bf16(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
+const void* pick_f32_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
+const void* pick_f16_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
+const void* pick_bf16_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
 
 }  // namespace ggrms

@@ -149,15 +149,24 @@ template <class T, int VB> struct Packet {
     }
 };
 
-// Streaming accesses.  y, gate and out are touched once per launch, so their
-// loads and stores carry the non-temporal hint (the nt bit): on gfx950 this
-// takes a two-read-one-write stream from ~72% to ~81% of HBM peak against
-// plain accesses.  The weight, re-read by every row, stays cached.
-template <class W> __device__ inline W load_stream(const W* p) {
-    return __builtin_nontemporal_load(p);
+// Accesses of y, gate and out.  Each is touched once per launch; with NT they
+// carry the non-temporal hint (the nt bit), which on gfx950 takes a large
+// two-read-one-write stream from ~72% to ~81% of HBM peak against plain
+// accesses.  Small jobs (decode) use plain accesses: their inputs are usually
+// still in L2 from the kernel that wrote them and their output is read next,
+// so keeping lines cached is worth more than streaming them.  The weight,
+// re-read by every row, always stays cached.
+template <bool NT, class W> __device__ inline W load_stream(const W* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
 }
-template <class W> __device__ inline void store_stream(W* p, W v) {
-    __builtin_nontemporal_store(v, p);
+template <bool NT, class W> __device__ inline void store_stream(W* p, W v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
 }
 
 // N consecutive f32 weights; p is aligned to min(16, 4N) bytes.
@@ -250,7 +259,7 @@ enum class WSource { Global, Lds };
 // vectors (indices sl, sl+SEG, ...), computes its share, reduces with
 // `reduce`, and stores if `store_ok`.  With WSource::Lds, `wl` points at the
 // group's weights in LDS, valid once `reduce` has passed its barrier.
-template <class T, int VB, int SEG, int VPT, bool NBG, WSource WS, class Reduce>
+template <class T, int VB, int SEG, int VPT, bool NBG, bool NT, WSource WS, class Reduce>
 __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g, uint32_t sl,
                                           bool store_ok, const float* wl, Reduce reduce) {
     using P = Packet<T, VB>;
@@ -272,8 +281,8 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     for (int k = 0; k < VPT; ++k) {
         const uint32_t idx = sl + k * SEG;
         ci[k] = idx < a.nvec ? idx : a.nvec - 1;
-        yr[k] = load_stream(yv + ci[k]);
-        gr[k] = load_stream(gv + ci[k]);
+        yr[k] = load_stream<NT>(yv + ci[k]);
+        gr[k] = load_stream<NT>(gv + ci[k]);
         if constexpr (WS == WSource::Global) load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
     }
 
@@ -360,7 +369,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const uint32_t idx = sl + k * SEG;
-            if (store_ok && idx < a.nvec) store_stream(ov + idx, res[k]);
+            if (store_ok && idx < a.nvec) store_stream<NT>(ov + idx, res[k]);
         }
     };
     if (!NBG && a.ri)
@@ -372,13 +381,13 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 // ------------------------------------------------------------ kernels
 
 // WAVE: SEG (<= 64) lanes per unit, 256-thread workgroups, no LDS, no barrier.
-template <class T, int VB, int SEG, int VPT, bool NBG>
+template <class T, int VB, int SEG, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
     const uint32_t t = blockIdx.x * (uint32_t)kWaveBlock + threadIdx.x;
     const uint32_t unit = t / SEG;
     if (unit >= a.units) return;  // whole segments leave together
     const uint32_t n = fast_div(unit, a.div_m, a.div_s);
-    unit_pass<T, VB, SEG, VPT, NBG, WSource::Global>(a, n, unit - n * a.groups,
+    unit_pass<T, VB, SEG, VPT, NBG, NT, WSource::Global>(a, n, unit - n * a.groups,
                                                      threadIdx.x & (SEG - 1), true, nullptr,
                                                      [](float v) { return segment_sum<SEG>(v); });
 }
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
 // and parked in LDS before the reduction barrier, instead of every unit
 // fetching its own copy: weight traffic from L2 falls by UPB and the L1
 // miss slots it held go back to the HBM streams.
-template <class T, int VB, int SEG, int VPT, int UPB, bool NBG>
+template <class T, int VB, int SEG, int VPT, int UPB, bool NBG, bool NT>
 __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     constexpr int BT = SEG * UPB;
     constexpr int WPG = SEG / 64;
@@ -419,7 +428,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
         }
     }
     constexpr WSource WS = UPB > 1 ? WSource::Lds : WSource::Global;
-    unit_pass<T, VB, SEG, VPT, NBG, WS>(a, n, g, threadIdx.x & (SEG - 1), live, wl, [&](float v) {
+    unit_pass<T, VB, SEG, VPT, NBG, NT, WS>(a, n, g, threadIdx.x & (SEG - 1), live, wl, [&](float v) {
         const float s = segment_sum<64>(v);
         if ((threadIdx.x & 63) == 0) part[wave] = s;
         if constexpr (UPB > 1) {
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
 // WIDE: one 1024-thread workgroup per unit, for groups with more vectors than
 // the BLOCK shapes hold in registers.  Pass 1 reads the group and reduces;
 // pass 2 reads it again and writes (the only path that reads inputs twice).
-template <class T, int VB, bool NBG>
+template <class T, int VB, bool NBG, bool NT>
 __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
     using P = Packet<T, VB>;
     using W = typename P::W;
@@ -480,8 +489,8 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
 
     for (uint32_t i = threadIdx.x; i < a.nvec; i += kWideBlock) {
         float yf[N], gf[N], wv[N], t[N];
-        P::unpack(load_stream(yv + i), yf);
-        P::unpack(load_stream(gv + i), gf);
+        P::unpack(load_stream<NT>(yv + i), yf);
+        P::unpack(load_stream<NT>(gv + i), gf);
         load_weights<N>(wp + (int64_t)i * N, wv);
         if constexpr (NBG) {
 #pragma unroll
@@ -493,20 +502,20 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
 #pragma unroll
             for (int e = 0; e < N; ++e) t[e] = wv[e] * t[e];
         }
-        store_stream(ov + i, P::pack(t));
+        store_stream<NT>(ov + i, P::pack(t));
     }
 }
 
 // ------------------------------------------------------------ table
 
-template <class T, int VB, bool NBG>
+template <class T, int VB, bool NBG, bool NT>
 inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
 #define GG_W(L, V)                      \
     if (lanes == L && vpt == V)         \
-    return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, L, V, NBG>)
+    return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, L, V, NBG, NT>)
 #define GG_B(L, V, U)                     \
     if (lanes == L && vpt == V && upb == U) \
-    return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V, U, NBG>)
+    return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V, U, NBG, NT>)
 #define GG_B4(L, U) GG_B(L, 1, U); GG_B(L, 2, U); GG_B(L, 3, U); GG_B(L, 4, U)
     if (kernel == GGRMS_KERNEL_WAVE) {
         if (upb != 1) return nullptr;
@@ -519,7 +528,7 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
         GG_B4(1024, 1);
     } else if (kernel == GGRMS_KERNEL_WIDE) {
         if (upb != 1) return nullptr;
-        return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB, NBG>);
+        return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB, NBG, NT>);
     }
 #undef GG_W
 #undef GG_B
@@ -527,14 +536,14 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
     return nullptr;
 }
 
-template <class T, bool NBG>
+template <class T, bool NBG, bool NT>
 inline const void* pick_type(int kernel, int vb, int lanes, int vpt, int upb) {
     switch (vb) {
-    case 16: return pick_vb<T, 16, NBG>(kernel, lanes, vpt, upb);
-    case 8: return pick_vb<T, 8, NBG>(kernel, lanes, vpt, upb);
-    case 4: return pick_vb<T, 4, NBG>(kernel, lanes, vpt, upb);
+    case 16: return pick_vb<T, 16, NBG, NT>(kernel, lanes, vpt, upb);
+    case 8: return pick_vb<T, 8, NBG, NT>(kernel, lanes, vpt, upb);
+    case 4: return pick_vb<T, 4, NBG, NT>(kernel, lanes, vpt, upb);
     case 2:
-        if constexpr (T::kSize == 2) return pick_vb<T, 2, NBG>(kernel, lanes, vpt, upb);
+        if constexpr (T::kSize == 2) return pick_vb<T, 2, NBG, NT>(kernel, lanes, vpt, upb);
         return nullptr;
     default: return nullptr;
     }

@@ -132,9 +132,12 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     if (rows < 0 || width <= 0 || group_size <= 0 || width % group_size != 0)
         return GGRMS_ERROR_INVALID_VALUE;
     const uint32_t known = GGRMS_FLAG_ROUND_INTERMEDIATE | GGRMS_FLAG_NORM_BEFORE_GATE |
-                           GGRMS_FLAG_WEIGHT_PER_GROUP;
+                           GGRMS_FLAG_WEIGHT_PER_GROUP | GGRMS_FLAG_CACHE_STREAM |
+                           GGRMS_FLAG_CACHE_KEEP;
     if (flags & ~known) return GGRMS_ERROR_INVALID_VALUE;
     if ((flags & GGRMS_FLAG_ROUND_INTERMEDIATE) && (flags & GGRMS_FLAG_NORM_BEFORE_GATE))
+        return GGRMS_ERROR_INVALID_VALUE;
+    if ((flags & GGRMS_FLAG_CACHE_STREAM) && (flags & GGRMS_FLAG_CACHE_KEEP))
         return GGRMS_ERROR_INVALID_VALUE;
     plan->flags = flags;
     const int64_t wlen = (flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? group_size : width;
@@ -250,6 +253,15 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->pub.rows_per_workgroup = upb;
     plan->pub.lds_bytes = upb > 1 ? (int32_t)(group_size * 4) : 0;
     plan->pub.workgroups = workgroups;
+    // Cache policy: stream large jobs, keep small ones cached.  The job is
+    // 3 * rows * row_bytes bytes; rows * row_bytes is at most y's extent, so
+    // it does not overflow, and comparing it with ceil(min / 3) is exact.
+    if (flags & GGRMS_FLAG_CACHE_STREAM)
+        plan->pub.streaming = 1;
+    else if (flags & GGRMS_FLAG_CACHE_KEEP)
+        plan->pub.streaming = 0;
+    else
+        plan->pub.streaming = rows * row_bytes >= (GGRMS_STREAM_MIN_BYTES + 2) / 3 ? 1 : 0;
     return GGRMS_SUCCESS;
 }
 

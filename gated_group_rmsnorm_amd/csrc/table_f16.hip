@@ -1,11 +1,13 @@
 // table_f16.hip -- instantiates every kernel shape for one element
-// type and one operator (gate-first), so the six combinations compile in parallel.
+// type and one operator (gate-first), with and without the streaming hint,
+// so the six combinations compile in parallel.
 #include "kernels.cuh"
 
 namespace ggrms {
 
-const void* pick_f16(int kernel, int vb, int lanes, int vpt, int upb) {
-    return pick_type<TF16, false>(kernel, vb, lanes, vpt, upb);
+const void* pick_f16(int kernel, int vb, int lanes, int vpt, int upb, bool nt) {
+    return nt ? pick_type<TF16, false, true>(kernel, vb, lanes, vpt, upb)
+              : pick_type<TF16, false, false>(kernel, vb, lanes, vpt, upb);
 }
 
 }  // namespace ggrms

@@ -1,11 +1,13 @@
 // table_f32_nbg.hip -- instantiates every kernel shape for one element
-// type and one operator (norm-before-gate), so the six combinations compile in parallel.
+// type and one operator (norm-before-gate), with and without the streaming
+// hint, so the six combinations compile in parallel.
 #include "kernels.cuh"
 
 namespace ggrms {
 
-const void* pick_f32_nbg(int kernel, int vb, int lanes, int vpt, int upb) {
-    return pick_type<TF32, true>(kernel, vb, lanes, vpt, upb);
+const void* pick_f32_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt) {
+    return nt ? pick_type<TF32, true, true>(kernel, vb, lanes, vpt, upb)
+              : pick_type<TF32, true, false>(kernel, vb, lanes, vpt, upb);
 }
 
 }  // namespace ggrms

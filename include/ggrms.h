@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GGRMS_ABI_VERSION 2
+#define GGRMS_ABI_VERSION 3
 
 /* Element type shared by y, gate and out.  The weight is always f32. */
 typedef enum {
@@ -123,6 +123,8 @@ typedef struct {
     int32_t rows_per_workgroup; /* BLOCK: rows of one group per workgroup (weights shared in LDS) */
     int32_t lds_bytes;        /* dynamic LDS per workgroup (the staged weights) */
     int64_t workgroups;       /* workgroups over all launches */
+    int32_t streaming;        /* 1: y/gate/out loads and stores carry the non-temporal hint */
+    int32_t reserved;         /* 0 */
 } ggrms_plan_t;
 
 /*
@@ -149,8 +151,23 @@ typedef enum {
     /* norm_weight holds group_size values shared by every group (indexed by
      * the column within the group), as that page's `scale` input does;
      * without it, width values indexed by the column. */
-    GGRMS_FLAG_WEIGHT_PER_GROUP = 4
+    GGRMS_FLAG_WEIGHT_PER_GROUP = 4,
+    /* Cache policy for y, gate and out (the weight is always cached).  By
+     * default a job whose y, gate and out views hold at least
+     * GGRMS_STREAM_MIN_BYTES together is streamed: its loads and stores carry
+     * the non-temporal hint, which keeps a large one-pass stream from
+     * evicting other data and runs it faster.  Smaller jobs (decode) use
+     * plain accesses, so inputs still cached from the kernel that wrote them
+     * are hit and the output stays cached for the kernel that reads it next.
+     * CACHE_STREAM forces the hint, CACHE_KEEP forces plain accesses; setting
+     * both is GGRMS_ERROR_INVALID_VALUE.  Results are identical either way. */
+    GGRMS_FLAG_CACHE_STREAM = 8,
+    GGRMS_FLAG_CACHE_KEEP = 16
 } ggrms_flag_t;
+
+/* Job size (bytes of y, gate and out together) from which the default cache
+ * policy streams. */
+#define GGRMS_STREAM_MIN_BYTES (4ll << 20)
 
 /* A kernel shape for the _ex calls (see ggrms_forward_with_shape). */
 typedef struct {
@@ -164,9 +181,9 @@ typedef struct {
  * mask) instead of round_intermediate, and an optional kernel shape (NULL:
  * the library chooses).  The weight needs width values, or group_size with
  * GGRMS_FLAG_WEIGHT_PER_GROUP.  GGRMS_ERROR_INVALID_VALUE also for unknown
- * flag bits or GGRMS_FLAG_ROUND_INTERMEDIATE with
- * GGRMS_FLAG_NORM_BEFORE_GATE; GGRMS_ERROR_NOT_SUPPORTED for a shape that
- * cannot be used (as in ggrms_forward_with_shape).
+ * flag bits, GGRMS_FLAG_ROUND_INTERMEDIATE with GGRMS_FLAG_NORM_BEFORE_GATE,
+ * or both cache flags; GGRMS_ERROR_NOT_SUPPORTED for a shape that cannot be
+ * used (as in ggrms_forward_with_shape).
  */
 ggrms_status_t ggrms_forward_ex(const void* y, const void* gate, const float* norm_weight,
                                 void* out, int64_t rows, int64_t width, int64_t group_size,

@@ -8,7 +8,7 @@ import synthetic as S
 F32, F16, BF16 = 0, 1, 2
 TDT = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
 DT_IDS = {F32: "f32", F16: "f16", BF16: "bf16"}
-FLAG_RI, FLAG_NBG, FLAG_PER_GROUP = 1, 2, 4
+FLAG_RI, FLAG_NBG, FLAG_PER_GROUP, FLAG_STREAM, FLAG_KEEP = 1, 2, 4, 8, 16
 
 
 def say(msg):

@@ -43,7 +43,7 @@ def test_header_symbols_exported(g):
 
 
 def test_abi_version_and_strings(g):
-    assert g.ggrms_abi_version() == 2
+    assert g.ggrms_abi_version() == 3
     for st in range(4):
         assert g.ggrms_status_string(st)
     assert g.ggrms_status_string(99) == "unknown status"
@@ -116,7 +116,7 @@ def test_interleaved_views_do_not_overlap(g):
     assert st == INVALID
 
 
-RI, NBG, PER_GROUP = 1, 2, 4
+RI, NBG, PER_GROUP, STREAM, KEEP = 1, 2, 4, 8, 16
 
 
 def _plan_ex(g, flags, shape=None, **kw):
@@ -132,22 +132,48 @@ def _plan_ex(g, flags, shape=None, **kw):
     return st, plan
 
 
-@pytest.mark.parametrize("flags", [8, 16, 1 << 31, RI | NBG, RI | NBG | PER_GROUP])
+@pytest.mark.parametrize("flags", [32, 1 << 31, RI | NBG, RI | NBG | PER_GROUP,
+                                   STREAM | KEEP, RI | STREAM | KEEP])
 def test_invalid_flags(g, flags):
     assert _plan_ex(g, flags)[0] == INVALID
 
 
-@pytest.mark.parametrize("flags", [0, RI, NBG, PER_GROUP, RI | PER_GROUP, NBG | PER_GROUP])
+@pytest.mark.parametrize("flags", [0, RI, NBG, PER_GROUP, RI | PER_GROUP, NBG | PER_GROUP,
+                                   RI | STREAM, NBG | KEEP, PER_GROUP | STREAM])
 def test_valid_flags_plan_like_the_default(g, flags):
-    """The operator variants use the same kernel shapes: only the
-    arithmetic and the weight's stride between groups differ."""
+    """The operator variants and cache policies use the same kernel shapes:
+    only the arithmetic, the weight's stride between groups and the cache
+    hint differ."""
     st, p = _plan_ex(g, flags, rows=64, width=7680, group_size=960, y_row_stride=7680,
                      gate_row_stride=7680, out_row_stride=7680,
                      gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
     assert st == OK
     st, ref = g.ggrms_plan(A, A + (1 << 26), A + (2 << 26), A + (3 << 26), 64, 7680, 960, 7680,
                            7680, 7680, 1e-5, BF16, 1)
+    # 64 rows x 7680 bf16 x 3 views = 2.9 MB: below the streaming threshold
+    assert ref["streaming"] == 0
+    assert p["streaming"] == (1 if flags & STREAM else 0)
+    p.pop("streaming"), ref.pop("streaming")
     assert p == ref
+
+
+def test_cache_policy_by_job_size(g):
+    """Jobs of at least STREAM_MIN_BYTES (y, gate and out together) stream;
+    smaller ones keep their lines cached; the flags override either way."""
+    assert g.STREAM_MIN_BYTES == 4 << 20
+    # 4 MiB exactly: 3 views x rows x width x 2 B with width 1024 -> rows = 4 MiB / 6 KiB
+    # is not an integer; use f32 width 1024 (4 KiB rows, 12 KiB per row over the views):
+    # 341 rows = 4,190,208 B (below), 342 rows = 4,202,496 B (at or above)
+    kw = dict(width=1024, group_size=1024, y_row_stride=1024, gate_row_stride=1024,
+              out_row_stride=1024, dtype=F32, gate=A + (1 << 26), norm_weight=A + (2 << 26),
+              out=A + (3 << 26))
+    assert _plan_ex(g, 0, rows=341, **kw)[1]["streaming"] == 0
+    assert _plan_ex(g, 0, rows=342, **kw)[1]["streaming"] == 1
+    assert _plan_ex(g, STREAM, rows=1, **kw)[1]["streaming"] == 1
+    assert _plan_ex(g, KEEP, rows=342, **kw)[1]["streaming"] == 0
+    # padded row strides do not count: only the [rows, width] views' bytes
+    kw.update(y_row_stride=4096, gate_row_stride=4096)
+    assert _plan_ex(g, 0, rows=341, **kw)[1]["streaming"] == 0
 
 
 def test_per_group_weight_extent(g):
@@ -210,6 +236,13 @@ def test_plans_for_the_workloads(g):
     # tiny f32, G = 64: 16 vectors
     p = _plan(g, 4, 256, 64, F32)
     assert (p["vector_bytes"], p["lanes_per_group"]) == (16, 16)
+    # cache policy: the prefill (377 MB), GDN-shaped (805 MB) and strided (7.4 MB) jobs
+    # stream; decode (77 KB) and the tiny case keep their lines cached
+    assert _plan(g, 8192, 7680, 960, BF16)["streaming"] == 1
+    assert _plan(g, 16384, 8192, 128, F16)["streaming"] == 1
+    assert _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)["streaming"] == 1
+    assert _plan(g, 1, 7680, 960, BF16)["streaming"] == 0
+    assert _plan(g, 4, 256, 64, F32)["streaming"] == 0
 
 
 def test_vector_width_follows_alignment(g):
@@ -315,7 +348,7 @@ int main() {
         n_ok += st == GGRMS_SUCCESS;
         const ggrms_shape_t shapes[] = {{64, 2, 0}, {128, 1, 4}, {256, 3, 2}, {1024, 0, 0},
                                         {16, 1, 0}, {0, 0, 0}, {128, 1, -1}};
-        for (uint32_t flags = 0; flags < 9; ++flags) {
+        for (uint32_t flags = 0; flags < 33; ++flags) {
             st = ggrms_plan_ex((void*)(base + off * 2), (void*)(base + (1u << 28)),
                                (const float*)(base + (2u << 28) + off * 4),
                                (void*)(base + (3u << 28)), rows, width, G, width + off, width,

@@ -12,8 +12,9 @@ import pytest
 import torch
 
 import synthetic as S
-from gpu_util import (BF16, DT_IDS, F16, F32, TDT, assert_parity, check_contiguous, dev_buf,
-                      host_bits, random_case, run_gpu, say, ulp_key)
+from gpu_util import (BF16, DT_IDS, F16, F32, FLAG_KEEP, FLAG_NBG, FLAG_RI, FLAG_STREAM, TDT,
+                      assert_parity, check_contiguous, dev_buf, host_bits, random_case, run_gpu,
+                      say, ulp_key)
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +120,35 @@ def test_forced_shapes_agree(g, orc, shape):
         stats = check_contiguous(g, orc, rows, G * groups, G, BF16, 1, seed=nvec + lanes,
                                  shape=shape, tag=f"forced {lanes}x{vpt} G={G}")
         assert stats["max_ulp"] <= 2
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_cache_policies_agree_bitwise(g, orc, shape):
+    """Every shape in both cache policies, both operators: the streamed
+    (non-temporal) launch matches the oracle and the cached launch gives the
+    same bits.  (These 7-row jobs run cached by default; the full-size
+    workloads run streamed.)"""
+    lanes, vpt = shape[:2]
+    nvec = max(1, lanes * (vpt or 8) - 3)
+    G = min(nvec * 8, 65536)
+    rows, groups = 7, 2
+    width = G * groups
+    y, gt, w = random_case(rows, width, BF16, seed=lanes + 31 * vpt)
+    yd, gd, wd = dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(w).cuda()
+    for op in (FLAG_RI, FLAG_NBG):
+        say(f"case cache policies {lanes}x{vpt} G={G} flags={op}")
+        outs = []
+        for cache in (FLAG_STREAM, FLAG_KEEP):
+            od = torch.full_like(yd, float("nan"))
+            assert run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, 1e-5, BF16, 0,
+                           shape, flags=op | cache) == g.SUCCESS
+            torch.cuda.synchronize()
+            outs.append(host_bits(od, BF16))
+        ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                          gate_row_stride=width, out_row_stride=width, eps=1e-5, dtype=BF16,
+                          round_intermediate=op & FLAG_RI, norm_before_gate=bool(op & FLAG_NBG))
+        assert_parity(outs[0], ref, BF16, f"streamed {lanes}x{vpt} flags={op}")
+        assert np.array_equal(outs[0], outs[1]), f"cached != streamed for {lanes}x{vpt} flags={op}"
 
 
 def test_forced_shape_matches_auto_bitwise(g):
