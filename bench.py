@@ -284,11 +284,49 @@ def bench_copy(torch, steps):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "kernel_ms_avg": ms}
 
 
+def stream_ceiling(torch, nbytes, steps, settle_s=0.1):
+    """Event-timed average launch of the plain two-read-one-write kernel
+    (libggrms_bench.so's ggrms_bench_stream3) over `nbytes` per stream, with
+    as many rotating buffer sets as keep the 256 MB Infinity Cache cold, after
+    the same warm-up and settle as the fused kernel.  Returns microseconds."""
+    aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
+    aux.ggrms_bench_stream3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p]
+    nbytes = (nbytes + 15) // 16 * 16
+    sets = min(64, max(2, math.ceil(3 * 256e6 / (3 * nbytes))))
+    bufs = [[torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(0.5)
+             for _ in range(3)] for _ in range(sets)]
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def launch(i):
+        a, b, c = bufs[i % sets]
+        if aux.ggrms_bench_stream3(a.data_ptr(), b.data_ptr(), c.data_ptr(), nbytes, sp) != 0:
+            raise RuntimeError("stream3 launch failed")
+
+    for i in range(5):
+        launch(i)
+    settle(torch, launch, settle_s)
+    a_ev = torch.cuda.Event(enable_timing=True)
+    b_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a_ev.record()
+    for i in range(steps):
+        launch(i)
+    b_ev.record()
+    torch.cuda.synchronize()
+    del bufs
+    torch.cuda.empty_cache()
+    return a_ev.elapsed_time(b_ev) * 1e3 / steps
+
+
 # (label, workload, ggrms_forward_ex flags or None for the workload's own)
 OTHER_WORKLOADS = [
     ("strided_256x4800_f16_g100", "strided_256x4800_f16_g100", None),
-    ("gdn_head_16384x8192_f16_g128", "gdn_head_16384x8192_f16_g128", None),
-    # norm first with the 128-value head scale shared by every head
+    # gate first, the 128-value head scale shared by every head (the page's
+    # [C] scale), and the same scale tiled into a per-column weight
+    ("gdn_head_16384x8192_f16_g128", "gdn_head_16384x8192_f16_g128", 4),
+    ("gdn_head_16384x8192_f16_g128_per_column_weight", "gdn_head_16384x8192_f16_g128", None),
+    # norm first with the shared head scale
     ("gdn_head_16384x8192_f16_g128_norm_first", "gdn_head_16384x8192_f16_g128", 2 | 4),
     ("prefill_8192x7680_bf16_g960_norm_first", PREFILL, 2),
 ]
@@ -305,12 +343,15 @@ def bench_workloads(torch, g, S, steps):
         _, ev_ms = time_kernel(torch, g, setup, steps, 5, settle_s=0.1)
         avg = ev_ms / steps
         nbytes = w.algorithmic_bytes(per_group_weight=bool(setup.flags & 4))
+        del setup
+        torch.cuda.empty_cache()
+        ceil_us = stream_ceiling(torch, w.rows * w.width * w.esize, steps)
         out[label] = {"kernel_us_avg": avg * 1e3,
                       "gbs": nbytes / (avg * 1e-3) / 1e9,
                       "frac_of_peak": nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                      "rows_per_s": w.rows / (avg * 1e-3)}
-        del setup
-        torch.cuda.empty_cache()
+                      "rows_per_s": w.rows / (avg * 1e-3),
+                      "stream_ceiling_us": ceil_us,
+                      "frac_of_stream_ceiling": ceil_us / (avg * 1e3)}
     log(f"workloads: {json.dumps(out)}")
     return out
 
@@ -500,12 +541,14 @@ def main():
     pre = bench_prefill(torch, g, S, args, shape)
     if args.only == "prefill":
         return
+    w = pre["workload"]
+    ceil_us = stream_ceiling(torch, w.rows * w.width * w.esize, args.steps, args.settle_ms / 1e3)
+    log(f"stream ceiling at the prefill's bytes: {ceil_us:.2f} us per launch")
     decode = bench_decode(torch, g, S, args.decode_bursts)
     others = bench_workloads(torch, g, S, max(20, args.steps // 4))
     unfused = bench_unfused(torch, S, 100)
     cpu = None if args.no_cpu_baseline else cpu_baseline(S, args.cpu_seconds)
 
-    w = pre["workload"]
     nbytes = pre["bytes"]
     value = args.steps * nbytes / pre["wall_s"] / 1e9
     achieved = nbytes / (pre["kernel_ms_avg"] * 1e-3) / 1e9
@@ -531,7 +574,12 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic_figure(),
                      "algorithmic_bytes_per_launch": nbytes,
-                     "kernel_us_avg": round(pre["kernel_ms_avg"] * 1e3, 2)},
+                     "kernel_us_avg": round(pre["kernel_ms_avg"] * 1e3, 2),
+                     # the plain two-read-one-write kernel moving the same three streams
+                     "stream_ceiling_us": round(ceil_us, 2),
+                     "stream_ceiling_frac": round(3 * w.rows * w.width * w.esize / (ceil_us * 1e-6)
+                                                  / 1e9 / PEAK_HBM_GBS, 4),
+                     "frac_of_stream_ceiling": round(ceil_us / (pre["kernel_ms_avg"] * 1e3), 4)},
         "cpu_baseline": cpu,
         "decode": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in decode.items()},
         "other_workloads": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in others.items()},

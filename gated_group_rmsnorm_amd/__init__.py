@@ -69,7 +69,7 @@ class _Plan(ctypes.Structure):
                 ("block_threads", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("rows_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("streaming", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("piece_bytes", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:

@@ -7,7 +7,11 @@
 //     (eager and replayed as one HIP graph), next to the same bursts of the
 //     empty kernel, so the per-launch figure carries no interpreter overhead;
 //   * a plain 16-byte vector copy of known size: the calibration that turns
-//     the FETCH_SIZE / WRITE_SIZE counters into HBM bytes.
+//     the FETCH_SIZE / WRITE_SIZE counters into HBM bytes;
+//   * the simplest kernel that moves a workload's bytes: two streams read and
+//     one written, 16-byte non-temporal accesses, two vectors per lane (the
+//     fastest plain form in a sweep of vector counts and cache hints) -- the
+//     practical ceiling the fused kernel is compared against.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,6 +33,29 @@ __global__ __launch_bounds__(256) void ggrms_bench_copy_kernel(const u32x4* __re
                                                                uint64_t n) {
     const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
     if (i < n) dst[i] = src[i];
+}
+
+// c = a ^ b over n 16-byte vectors; each wave takes 128 consecutive vectors,
+// two per lane, loads all four before its two stores.
+__global__ __launch_bounds__(256) void ggrms_bench_stream3_kernel(const u32x4* __restrict__ a,
+                                                                  const u32x4* __restrict__ b,
+                                                                  u32x4* __restrict__ c,
+                                                                  uint64_t n) {
+    const uint64_t base = ((uint64_t)blockIdx.x * 4u + (threadIdx.x >> 6)) * 128u + (threadIdx.x & 63);
+    u32x4 x[2], y[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint64_t i = base + 64u * k;
+        if (i < n) {
+            x[k] = __builtin_nontemporal_load(a + i);
+            y[k] = __builtin_nontemporal_load(b + i);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint64_t i = base + 64u * k;
+        if (i < n) __builtin_nontemporal_store(x[k] ^ y[k], c + i);
+    }
 }
 
 }  // namespace
@@ -55,6 +82,27 @@ extern "C" int ggrms_bench_copy(const void* src, void* dst, int64_t nbytes, void
     args[0] = &s;
     args[1] = &d;
     return hipLaunchKernel(reinterpret_cast<const void*>(&ggrms_bench_copy_kernel),
+                           dim3((uint32_t)blocks), dim3(256), args, 0,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
+               ? 0
+               : 1;
+}
+
+// c = a ^ b over nbytes per buffer (a multiple of 16; 16-byte aligned
+// pointers): two reads and one write of nbytes each.
+extern "C" int ggrms_bench_stream3(const void* a, const void* b, void* c, int64_t nbytes,
+                                   void* stream) {
+    if (nbytes <= 0 || nbytes % 16 || (uintptr_t)a % 16 || (uintptr_t)b % 16 ||
+        (uintptr_t)c % 16)
+        return 1;
+    const uint64_t n = (uint64_t)nbytes / 16;
+    const uint64_t blocks = (n + 511) / 512;
+    if (blocks > 0xFFFFFFFFull) return 1;
+    const u32x4* pa = static_cast<const u32x4*>(a);
+    const u32x4* pb = static_cast<const u32x4*>(b);
+    u32x4* pc = static_cast<u32x4*>(c);
+    void* args[] = {&pa, &pb, &pc, (void*)&n};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&ggrms_bench_stream3_kernel),
                            dim3((uint32_t)blocks), dim3(256), args, 0,
                            static_cast<hipStream_t>(stream)) == hipSuccess
                ? 0

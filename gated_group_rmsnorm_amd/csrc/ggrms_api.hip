@@ -34,11 +34,12 @@ bool device_is_gfx950() {
     return st == 1;
 }
 
-const void* pick(int dtype, bool nbg, bool nt, int kernel, int vb, int lanes, int vpt, int upb) {
+const void* pick(int dtype, bool nbg, bool nt, int kernel, int vb, int pb, int lanes, int vpt,
+                 int upb) {
     switch (dtype) {
-    case GGRMS_F32: return (nbg ? pick_f32_nbg : pick_f32)(kernel, vb, lanes, vpt, upb, nt);
-    case GGRMS_F16: return (nbg ? pick_f16_nbg : pick_f16)(kernel, vb, lanes, vpt, upb, nt);
-    case GGRMS_BF16: return (nbg ? pick_bf16_nbg : pick_bf16)(kernel, vb, lanes, vpt, upb, nt);
+    case GGRMS_F32: return (nbg ? pick_f32_nbg : pick_f32)(kernel, vb, pb, lanes, vpt, upb, nt);
+    case GGRMS_F16: return (nbg ? pick_f16_nbg : pick_f16)(kernel, vb, pb, lanes, vpt, upb, nt);
+    case GGRMS_BF16: return (nbg ? pick_bf16_nbg : pick_bf16)(kernel, vb, pb, lanes, vpt, upb, nt);
     default: return nullptr;
     }
 }
@@ -59,7 +60,8 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool nbg = (flags & GGRMS_FLAG_NORM_BEFORE_GATE) != 0;
     const void* fn = pick((int)dtype, nbg, p.streaming != 0, p.kernel, p.vector_bytes,
-                          p.lanes_per_group, p.vectors_per_lane, p.rows_per_workgroup);
+                          p.piece_bytes, p.lanes_per_group, p.vectors_per_lane,
+                          p.rows_per_workgroup);
     if (!fn) return GGRMS_ERROR_NOT_SUPPORTED;
 
     if (rows == 1) y_row_stride = gate_row_stride = out_row_stride = width;

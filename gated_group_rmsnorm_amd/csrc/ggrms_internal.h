@@ -88,12 +88,13 @@ void div_magic(uint32_t d, uint32_t* m, uint32_t* s);
 
 // Kernel lookup per dtype (kernel tables); nullptr if the shape is not built.
 // (nbg selects the norm-before-gate instantiations, in their own files; nt
-// the variant whose y/gate/out accesses carry the non-temporal hint.)
-const void* pick_f32(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
-const void* pick_f16(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
-const void* pick_bf16(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
-const void* pick_f32_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
-const void* pick_f16_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
-const void* pick_bf16_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt);
+// the variant whose y/gate/out accesses carry the non-temporal hint; pb the
+// piece bytes: vb for group-aligned vectors, 2/4/8 for packed groups.)
+const void* pick_f32(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt);
+const void* pick_f16(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt);
+const void* pick_bf16(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt);
+const void* pick_f32_nbg(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt);
+const void* pick_f16_nbg(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt);
+const void* pick_bf16_nbg(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt);
 
 }  // namespace ggrms

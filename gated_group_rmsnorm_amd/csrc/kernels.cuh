@@ -255,36 +255,96 @@ __device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t s) {
 // from global memory, or the workgroup staged the group's weights in LDS.
 enum class WSource { Global, Lds };
 
+// A PB-byte piece of a VB-byte vector (PB < VB), written alone.
+template <int PB, class W> __device__ inline void store_piece(char* p, const W& v, int piece) {
+    if constexpr (PB == 8) {
+        const u32x2 h = piece ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]};
+        *reinterpret_cast<u32x2*>(p) = h;
+    } else if constexpr (PB == 4) {
+        *reinterpret_cast<u32*>(p) = v[piece];
+    } else {
+        *reinterpret_cast<u16*>(p) = (u16)(v[piece >> 1] >> (16 * (piece & 1)));
+    }
+}
+template <bool NT, int PB, class W>
+__device__ inline void store_piece_stream(char* p, const W& v, int piece) {
+    if constexpr (!NT) {
+        store_piece<PB>(p, v, piece);
+    } else if constexpr (PB == 8) {
+        const u32x2 h = piece ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]};
+        __builtin_nontemporal_store(h, reinterpret_cast<u32x2*>(p));
+    } else if constexpr (PB == 4) {
+        __builtin_nontemporal_store(v[piece], reinterpret_cast<u32*>(p));
+    } else {
+        __builtin_nontemporal_store((u16)(v[piece >> 1] >> (16 * (piece & 1))),
+                                    reinterpret_cast<u16*>(p));
+    }
+}
+
 // Lane `sl` of the SEG lanes that own the unit (row n, group g) loads VPT
 // vectors (indices sl, sl+SEG, ...), computes its share, reduces with
 // `reduce`, and stores if `store_ok`.  With WSource::Lds, `wl` points at the
 // group's weights in LDS, valid once `reduce` has passed its barrier.
-template <class T, int VB, int SEG, int VPT, bool NBG, bool NT, WSource WS, class Reduce>
+//
+// PB == VB: every group starts on a vector boundary and spans a.nvec whole
+// vectors.  PB < VB (packed): the group's byte length is not a multiple of
+// the 16-byte vector but the rows are, so vectors are counted from the row's
+// start and the unit takes the vectors that hold any of its elements; a
+// vector on a group boundary also holds a neighbour's elements, which are
+// left out of the sum and not written: such a vector is stored in PB-byte
+// pieces (PB = gcd(group bytes, 16), so a group boundary never splits a
+// piece).  Reads stay inside the row; every element is written by exactly
+// one unit.
+template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT, WSource WS, class Reduce>
 __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g, uint32_t sl,
                                           bool store_ok, const float* wl, Reduce reduce) {
     using P = Packet<T, VB>;
     using W = typename P::W;
     constexpr int N = P::N;
     using S = typename VecWord<T::kSize>::type;  // element storage
+    constexpr bool kPacked = PB < VB;
+    static_assert(!kPacked || (VB == 16 && WS == WSource::Global), "packed: 16-byte vectors");
+    // With three or more vectors per lane the per-lane weights are loaded
+    // after the reduction, so they are not live at the same time as the
+    // inputs: 4 vectors drop from ~140 to ~110 VGPRs (3 -> 4 waves per SIMD;
+    // 512 x 4 runs 14-18% faster) and the 1024-lane shape, capped at 128
+    // VGPRs, no longer spills.  Narrower shapes keep the early loads, which
+    // overlap the input stream.
+    constexpr bool kLateWeights = WS == WSource::Global && VPT >= 3;
 
     const int64_t col0 = (int64_t)g * a.G;
-    const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy + col0);
+    const int64_t cbase = kPacked ? 0 : col0;  // column of vector 0
+    const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy + cbase);
     const W* gv =
-        reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + col0);
-    W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + col0);
-    const float* wp = a.w + (int64_t)g * a.wgs;
+        reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + cbase);
+    W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + cbase);
+    const float* wp = kPacked ? a.w : a.w + (int64_t)g * a.wgs;
+    // vectors of this unit: v0 .. v0 + nv - 1 (packed: those holding any of
+    // columns col0 .. col0 + G - 1)
+    uint32_t v0 = 0, nv = a.nvec;
+    if constexpr (kPacked) {
+        v0 = (uint32_t)(col0 / N);
+        nv = (uint32_t)((col0 + a.G + N - 1) / N) - v0;
+    }
 
     W yr[VPT], gr[VPT];
     float wr[VPT][N];
     uint32_t ci[VPT];
+    int32_t rel[VPT];  // packed: column of the vector's first element minus col0
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const uint32_t idx = sl + k * SEG;
-        ci[k] = idx < a.nvec ? idx : a.nvec - 1;
+        ci[k] = v0 + (idx < nv ? idx : nv - 1);
+        rel[k] = kPacked ? (int32_t)((int64_t)ci[k] * N - col0) : 0;
         yr[k] = load_stream<NT>(yv + ci[k]);
         gr[k] = load_stream<NT>(gv + ci[k]);
-        if constexpr (WS == WSource::Global) load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
+        if constexpr (WS == WSource::Global && !kLateWeights)
+            load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
     }
+    // whether element e of vector k belongs to the unit (always, unless packed)
+    auto owned = [&](int k, int e) {
+        return !kPacked || (uint32_t)(rel[k] + e) < a.G;
+    };
 
     // Gate first: a = y * silu(gate) for every loaded element.  Norm first:
     // a = y, and silu(gate) waits for the output.  Lanes past the group's end
@@ -304,9 +364,10 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
             gmin = __builtin_fminf(gmin, gf[e]);
             const float x = NBG ? yf[e] : yf[e] * silu_fast(gf[e]);
             av[k][e] = x;
-            part = __builtin_fmaf(x, x, part);
+            const float xx = __builtin_fmaf(x, x, part);
+            part = owned(k, e) ? xx : part;
         }
-        acc += (sl + k * SEG < a.nvec) ? part : 0.0f;
+        acc += (sl + k * SEG < nv) ? part : 0.0f;
     }
     // Rare: a gate deep in silu's underflow range.  Redo the wave's silu with
     // the exact form (identical bits for every other gate).
@@ -323,9 +384,10 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
             for (int e = 0; e < N; ++e) {
                 const float x = yf[e] * silu_exact(gf[e]);
                 av[k][e] = x;
-                part = __builtin_fmaf(x, x, part);
+                const float xx = __builtin_fmaf(x, x, part);
+                part = owned(k, e) ? xx : part;
             }
-            acc += (sl + k * SEG < a.nvec) ? part : 0.0f;
+            acc += (sl + k * SEG < nv) ? part : 0.0f;
         }
     }
 
@@ -333,7 +395,10 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     const float nf = 1.0f / __builtin_sqrtf(m2 / a.Gf + a.eps);
     if constexpr (WS == WSource::Lds) {
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) load_weights<N>(wl + ci[k] * N, wr[k]);
+        for (int k = 0; k < VPT; ++k) load_weights<N>(wl + ci[k] * N, wr[k]);  // v0 == 0 here
+    } else if constexpr (kLateWeights) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
     }
 
     // Wait for every load (the weights included) before the first store:
@@ -369,7 +434,19 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const uint32_t idx = sl + k * SEG;
-            if (store_ok && idx < a.nvec) store_stream<NT>(ov + idx, res[k]);
+            if (!store_ok || idx >= nv) continue;
+            if constexpr (kPacked) {
+                if (rel[k] < 0 || rel[k] + N > (int32_t)a.G) {
+                    // a vector on a group boundary: only this unit's pieces
+                    constexpr int PE = PB / T::kSize;
+                    char* base = reinterpret_cast<char*>(ov + v0 + idx);
+#pragma unroll
+                    for (int q = 0; q < VB / PB; ++q)
+                        if (owned(k, q * PE)) store_piece_stream<NT, PB>(base + q * PB, res[k], q);
+                    continue;
+                }
+            }
+            store_stream<NT>(ov + v0 + idx, res[k]);
         }
     };
     if (!NBG && a.ri)
@@ -381,13 +458,13 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 // ------------------------------------------------------------ kernels
 
 // WAVE: SEG (<= 64) lanes per unit, 256-thread workgroups, no LDS, no barrier.
-template <class T, int VB, int SEG, int VPT, bool NBG, bool NT>
+template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
     const uint32_t t = blockIdx.x * (uint32_t)kWaveBlock + threadIdx.x;
     const uint32_t unit = t / SEG;
     if (unit >= a.units) return;  // whole segments leave together
     const uint32_t n = fast_div(unit, a.div_m, a.div_s);
-    unit_pass<T, VB, SEG, VPT, NBG, NT, WSource::Global>(a, n, unit - n * a.groups,
+    unit_pass<T, VB, PB, SEG, VPT, NBG, NT, WSource::Global>(a, n, unit - n * a.groups,
                                                      threadIdx.x & (SEG - 1), true, nullptr,
                                                      [](float v) { return segment_sum<SEG>(v); });
 }
@@ -400,7 +477,7 @@ __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
 // and parked in LDS before the reduction barrier, instead of every unit
 // fetching its own copy: weight traffic from L2 falls by UPB and the L1
 // miss slots it held go back to the HBM streams.
-template <class T, int VB, int SEG, int VPT, int UPB, bool NBG, bool NT>
+template <class T, int VB, int PB, int SEG, int VPT, int UPB, bool NBG, bool NT>
 __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     constexpr int BT = SEG * UPB;
     constexpr int WPG = SEG / 64;
@@ -428,7 +505,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
         }
     }
     constexpr WSource WS = UPB > 1 ? WSource::Lds : WSource::Global;
-    unit_pass<T, VB, SEG, VPT, NBG, NT, WS>(a, n, g, threadIdx.x & (SEG - 1), live, wl, [&](float v) {
+    unit_pass<T, VB, PB, SEG, VPT, NBG, NT, WS>(a, n, g, threadIdx.x & (SEG - 1), live, wl, [&](float v) {
         const float s = segment_sum<64>(v);
         if ((threadIdx.x & 63) == 0) part[wave] = s;
         if constexpr (UPB > 1) {
@@ -508,25 +585,30 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
 
 // ------------------------------------------------------------ table
 
-template <class T, int VB, bool NBG, bool NT>
+// PB == VB: group-aligned vectors; PB < VB (VB == 16): packed groups, built
+// for every WAVE shape and for the BLOCK shapes with one row per workgroup.
+template <class T, int VB, int PB, bool NBG, bool NT>
 inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
+    constexpr bool kPacked = PB < VB;
 #define GG_W(L, V)                      \
     if (lanes == L && vpt == V)         \
-    return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, L, V, NBG, NT>)
+    return reinterpret_cast<const void*>(&ggrms_wave_kernel<T, VB, PB, L, V, NBG, NT>)
 #define GG_B(L, V, U)                     \
     if (lanes == L && vpt == V && upb == U) \
-    return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, L, V, U, NBG, NT>)
+    return reinterpret_cast<const void*>(&ggrms_block_kernel<T, VB, PB, L, V, U, NBG, NT>)
 #define GG_B4(L, U) GG_B(L, 1, U); GG_B(L, 2, U); GG_B(L, 3, U); GG_B(L, 4, U)
     if (kernel == GGRMS_KERNEL_WAVE) {
         if (upb != 1) return nullptr;
         GG_W(1, 1); GG_W(2, 1); GG_W(4, 1); GG_W(8, 1); GG_W(16, 1); GG_W(32, 1);
         GG_W(64, 1); GG_W(64, 2); GG_W(64, 3); GG_W(64, 4);
     } else if (kernel == GGRMS_KERNEL_BLOCK) {
-        GG_B4(128, 1); GG_B4(128, 2); GG_B4(128, 4);
-        GG_B4(256, 1); GG_B4(256, 2);
-        GG_B4(512, 1);
-        GG_B4(1024, 1);
+        GG_B4(128, 1); GG_B4(256, 1); GG_B4(512, 1); GG_B4(1024, 1);
+        if constexpr (!kPacked) {
+            GG_B4(128, 2); GG_B4(128, 4);
+            GG_B4(256, 2);
+        }
     } else if (kernel == GGRMS_KERNEL_WIDE) {
+        if constexpr (kPacked) return nullptr;
         if (upb != 1) return nullptr;
         return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB, NBG, NT>);
     }
@@ -536,14 +618,27 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
     return nullptr;
 }
 
+// vb: vector bytes; pb: piece bytes (== vb for group-aligned vectors, 2, 4 or
+// 8 with vb == 16 for packed groups).
 template <class T, bool NBG, bool NT>
-inline const void* pick_type(int kernel, int vb, int lanes, int vpt, int upb) {
-    switch (vb) {
-    case 16: return pick_vb<T, 16, NBG, NT>(kernel, lanes, vpt, upb);
-    case 8: return pick_vb<T, 8, NBG, NT>(kernel, lanes, vpt, upb);
-    case 4: return pick_vb<T, 4, NBG, NT>(kernel, lanes, vpt, upb);
+inline const void* pick_type(int kernel, int vb, int pb, int lanes, int vpt, int upb) {
+    if (pb == vb) {
+        switch (vb) {
+        case 16: return pick_vb<T, 16, 16, NBG, NT>(kernel, lanes, vpt, upb);
+        case 8: return pick_vb<T, 8, 8, NBG, NT>(kernel, lanes, vpt, upb);
+        case 4: return pick_vb<T, 4, 4, NBG, NT>(kernel, lanes, vpt, upb);
+        case 2:
+            if constexpr (T::kSize == 2) return pick_vb<T, 2, 2, NBG, NT>(kernel, lanes, vpt, upb);
+            return nullptr;
+        default: return nullptr;
+        }
+    }
+    if (vb != 16) return nullptr;
+    switch (pb) {
+    case 8: return pick_vb<T, 16, 8, NBG, NT>(kernel, lanes, vpt, upb);
+    case 4: return pick_vb<T, 16, 4, NBG, NT>(kernel, lanes, vpt, upb);
     case 2:
-        if constexpr (T::kSize == 2) return pick_vb<T, 2, NBG, NT>(kernel, lanes, vpt, upb);
+        if constexpr (T::kSize == 2) return pick_vb<T, 16, 2, NBG, NT>(kernel, lanes, vpt, upb);
         return nullptr;
     default: return nullptr;
     }

@@ -52,24 +52,29 @@ int64_t round_up_pow2(int64_t x) {
     return p;
 }
 
+// Largest packed group, in 16-byte vectors (512 lanes x 4 vectors); wider
+// groups keep the narrower vectors.
+constexpr int64_t kMaxPackedVectors = 2048;
+
 int kernel_for_shape(int lanes, int vpt) {
     if (vpt == 0) return GGRMS_KERNEL_WIDE;
     return lanes <= 64 ? GGRMS_KERNEL_WAVE : GGRMS_KERNEL_BLOCK;
 }
 
 // Kernel shape for a group of nvec vectors, and the rows of one group a
-// BLOCK workgroup takes (1 means no weight staging).  The table comes from a
-// sweep of every built shape on gfx950 at ~377 MB per launch (8192-row bf16
-// jobs over group widths 8..32768, plus fp16 and f32 spot checks), timed
-// after the clocks settle:
+// BLOCK workgroup takes (1 means no weight staging).  The table comes from
+// sweeps of every built shape on gfx950 at ~377 MB per launch (bf16 jobs over
+// group widths 8..32768, plus fp16 and f32 spot checks), timed after the
+// clocks settle:
 //   * up to 64 vectors: one vector per lane, the smallest power-of-two lane
 //     segment, several groups per wave (WAVE kernel, 77-80% of HBM peak);
 //   * 65-96: one wave, two vectors per lane (74%; 128 lanes idle too many);
-//   * 97-512: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
-//     workgroup sharing staged weights (79-81%); 4 rows only with one vector
+//   * 97-768: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
+//     workgroup sharing staged weights (78-81%); 4 rows only with one vector
 //     per lane, since the staging registers cost occupancy at 2+;
-//   * 513-4096: 256-1024 lanes x 4 vectors, one row per workgroup (staging
-//     at 4 vectors per lane measured 57% against 76% without);
+//   * 769-4096: 256-1024 lanes x 3-4 vectors, one row per workgroup (staging
+//     at 4 vectors per lane measured 46-59% against 77% without); three
+//     vectors where they cover the group with fewer idle lanes;
 //   * wider groups loop over the row twice (WIDE).
 struct ShapeRule {
     int64_t max_nvec;
@@ -82,8 +87,11 @@ const ShapeRule kRules[] = {
     {256, GGRMS_KERNEL_BLOCK, 256, 1, 2},
     {384, GGRMS_KERNEL_BLOCK, 128, 3, 2},
     {512, GGRMS_KERNEL_BLOCK, 256, 2, 2},
+    {768, GGRMS_KERNEL_BLOCK, 256, 3, 2},
     {1024, GGRMS_KERNEL_BLOCK, 256, 4, 1},
+    {1536, GGRMS_KERNEL_BLOCK, 512, 3, 1},
     {2048, GGRMS_KERNEL_BLOCK, 512, 4, 1},
+    {3072, GGRMS_KERNEL_BLOCK, 1024, 3, 1},
     {4096, GGRMS_KERNEL_BLOCK, 1024, 4, 1},
 };
 
@@ -186,7 +194,30 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
             break;
         }
     }
-    const int64_t nvec = group_size * esize / vb;
+    int64_t nvec = group_size * esize / vb;
+    int pb = vb;
+    // Packed groups: the group's byte length is not a multiple of 16 but the
+    // rows are 16-byte aligned and a multiple of 16 bytes long, so 16-byte
+    // vectors counted from the row start never leave the row.  A unit takes
+    // the vectors holding any of its elements -- at most
+    // ceil((16 - pb + group bytes) / 16), since group starts fall on
+    // multiples of pb = gcd(group bytes, 16) -- and stores boundary vectors in
+    // pb-byte pieces.  Only with a per-column weight (its vectors then line up
+    // with the data's) and groups of more than one vector.
+    const int64_t gbytes = group_size * esize;
+    if (vb < 16 && gbytes > 16 && row_bytes % 16 == 0 && py % 16 == 0 && pg % 16 == 0 &&
+        po % 16 == 0 && by % 16 == 0 && bg % 16 == 0 && bo % 16 == 0 && pw % 16 == 0 &&
+        !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP)) {
+        int64_t gcd = 16;
+        while (gbytes % gcd) gcd >>= 1;
+        const int64_t nvp = (16 - gcd + gbytes + 15) / 16;
+        if (nvp <= kMaxPackedVectors) {
+            vb = 16;
+            pb = (int)gcd;
+            nvec = nvp;
+        }
+    }
+    const bool packed = pb < vb;
     int kernel = 0, lanes = 0, vpt = 0, rule_upb = 1;
     const int force_upb = shape ? shape->rows_per_workgroup : 0;
     if (force_upb < 0) return GGRMS_ERROR_INVALID_VALUE;
@@ -206,12 +237,13 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     } else {
         choose_shape(nvec, &kernel, &lanes, &vpt, &rule_upb);
     }
+    if (packed && kernel == GGRMS_KERNEL_WIDE) return GGRMS_ERROR_NOT_SUPPORTED;  // not built
 
     const int64_t groups = plan->groups;
     // Rows of one group per BLOCK workgroup: the group's weights are staged
     // once in LDS with 16-byte loads, so the weight must be 16-byte aligned
     // and the group a multiple of 4 floats; no more rows than the job has.
-    const bool can_stage = pw % 16 == 0 && group_size % 4 == 0;
+    const bool can_stage = pw % 16 == 0 && group_size % 4 == 0 && !packed;
     int upb = 1;
     if (force_upb) {
         if (!rows_per_workgroup_supported(kernel, lanes, force_upb) ||
@@ -246,6 +278,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->rows_per_launch = rows_per_launch;
     plan->pub.kernel = kernel;
     plan->pub.vector_bytes = vb;
+    plan->pub.piece_bytes = pb;
     plan->pub.lanes_per_group = lanes;
     plan->pub.vectors_per_lane = vpt;
     plan->pub.block_threads = block;

@@ -5,9 +5,9 @@
 
 namespace ggrms {
 
-const void* pick_bf16(int kernel, int vb, int lanes, int vpt, int upb, bool nt) {
-    return nt ? pick_type<TBF16, false, true>(kernel, vb, lanes, vpt, upb)
-              : pick_type<TBF16, false, false>(kernel, vb, lanes, vpt, upb);
+const void* pick_bf16(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt) {
+    return nt ? pick_type<TBF16, false, true>(kernel, vb, pb, lanes, vpt, upb)
+              : pick_type<TBF16, false, false>(kernel, vb, pb, lanes, vpt, upb);
 }
 
 }  // namespace ggrms

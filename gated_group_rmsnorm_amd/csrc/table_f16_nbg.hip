@@ -5,9 +5,9 @@
 
 namespace ggrms {
 
-const void* pick_f16_nbg(int kernel, int vb, int lanes, int vpt, int upb, bool nt) {
-    return nt ? pick_type<TF16, true, true>(kernel, vb, lanes, vpt, upb)
-              : pick_type<TF16, true, false>(kernel, vb, lanes, vpt, upb);
+const void* pick_f16_nbg(int kernel, int vb, int pb, int lanes, int vpt, int upb, bool nt) {
+    return nt ? pick_type<TF16, true, true>(kernel, vb, pb, lanes, vpt, upb)
+              : pick_type<TF16, true, false>(kernel, vb, pb, lanes, vpt, upb);
 }
 
 }  // namespace ggrms

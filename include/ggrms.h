@@ -115,7 +115,7 @@ typedef enum {
 
 typedef struct {
     int32_t kernel;           /* a ggrms_kernel_t */
-    int32_t vector_bytes;     /* bytes per y/gate/out load and store (16, 8, 4 or 2) */
+    int32_t vector_bytes;     /* bytes per y/gate/out load (16, 8, 4 or 2) */
     int32_t lanes_per_group;  /* lanes that share one (row, group) */
     int32_t vectors_per_lane; /* vectors each lane holds per group (0 for WIDE: it loops) */
     int32_t block_threads;    /* threads per workgroup */
@@ -124,8 +124,23 @@ typedef struct {
     int32_t lds_bytes;        /* dynamic LDS per workgroup (the staged weights) */
     int64_t workgroups;       /* workgroups over all launches */
     int32_t streaming;        /* 1: y/gate/out loads and stores carry the non-temporal hint */
-    int32_t reserved;         /* 0 */
+    int32_t piece_bytes;      /* == vector_bytes when every group starts on a vector
+                                 boundary; 2, 4 or 8 for packed groups (see below) */
 } ggrms_plan_t;
+
+/*
+ * Vector width.  Every y/gate/out access is a vector of the widest size
+ * (16, 8, 4 or 2 bytes) that the three base pointers, their row strides, the
+ * group's byte length and the weight's alignment allow.  When the group's
+ * byte length is not a multiple of 16 (say 100 fp16 values, 200 bytes) but
+ * more than 16, and the rows are: every base pointer and row stride and the
+ * weight 16-byte aligned, width * element size a multiple of 16, one weight
+ * per column -- the groups are "packed": 16-byte vectors are counted from
+ * the start of the row, a vector on a group boundary is read by both groups
+ * (each uses its own elements) and written in pieces of
+ * piece_bytes = gcd(group bytes, 16), so no element is written twice and no
+ * read leaves the row.
+ */
 
 /*
  * ggrms_plan -- run ggrms_forward's argument checks and kernel choice

@@ -230,9 +230,12 @@ def test_plans_for_the_workloads(g):
     # 16384x8192 fp16, G = 128: 16 vectors -> 16-lane segments, four groups per wave
     p = _plan(g, 16384, 8192, 128, F16)
     assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 16, 16, 1)
-    # 256x4800 fp16 slices of a [256, 9856] buffer, G = 100: 200-byte groups -> 8-byte vectors
+    # 256x4800 fp16 slices of a [256, 9856] buffer, G = 100: 200-byte groups in 9600-byte
+    # rows -> packed: 16-byte vectors from the row start, boundary vectors in 8-byte pieces;
+    # a group touches at most ceil((8 + 200) / 16) = 13 vectors -> 16-lane segments
     p = _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)
-    assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"]) == ("wave", 8, 32)
+    assert (p["kernel_name"], p["vector_bytes"], p["piece_bytes"], p["lanes_per_group"]) == \
+        ("wave", 16, 8, 16)
     # tiny f32, G = 64: 16 vectors
     p = _plan(g, 4, 256, 64, F32)
     assert (p["vector_bytes"], p["lanes_per_group"]) == (16, 16)
@@ -243,6 +246,74 @@ def test_plans_for_the_workloads(g):
     assert _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)["streaming"] == 1
     assert _plan(g, 1, 7680, 960, BF16)["streaming"] == 0
     assert _plan(g, 4, 256, 64, F32)["streaming"] == 0
+
+
+@pytest.mark.parametrize("G,dtype,pb,nvec", [
+    (100, F16, 8, 13),     # 200-byte groups
+    (99, BF16, 2, 14),     # 198 bytes: gcd 2, up to 14 bytes before the first boundary
+    (50, BF16, 4, 7),      # 100 bytes
+    (9, BF16, 2, 2),       # 18 bytes: just over one vector
+    (5, F32, 4, 2),        # 20 bytes
+    (1001, F32, 4, 251),
+    (8191, F16, 2, 1025),  # BLOCK 512 x 3 (packed groups keep one row per workgroup)
+])
+def test_packed_groups_plan(g, G, dtype, pb, nvec):
+    """Groups whose byte length is not a multiple of 16, in rows that are:
+    16-byte vectors, pieces of gcd(group bytes, 16), one row per workgroup,
+    a shape covering the worst-aligned group."""
+    width = 16 * G
+    p = _plan(g, 7, width, G, dtype)
+    assert (p["vector_bytes"], p["piece_bytes"], p["rows_per_workgroup"]) == (16, pb, 1)
+    assert p["lanes_per_group"] * p["vectors_per_lane"] >= nvec
+    assert p["lanes_per_group"] * p["vectors_per_lane"] < 2 * nvec or p["lanes_per_group"] == 1
+
+
+def test_packed_groups_need_aligned_rows(g):
+    """The packed path only when every row is 16-byte aligned and a multiple
+    of 16 bytes long, the weight is per column and 16-byte aligned, and a
+    group is more than one vector and at most 2048 vectors; otherwise the
+    widest vector the group allows."""
+    G = 100
+    ok = _plan(g, 7, 16 * G, G, F16)
+    assert (ok["vector_bytes"], ok["piece_bytes"]) == (16, 8)
+    # rows of 3 groups: 600 bytes, not a multiple of 16
+    assert (_plan(g, 7, 3 * G, G, F16)["vector_bytes"], _plan(g, 7, 3 * G, G, F16)["piece_bytes"]) == (8, 8)
+    # a base pointer only 8-byte aligned; a row stride that breaks 16-byte rows
+    assert _plan(g, 7, 16 * G, G, F16, y=A + 8)["vector_bytes"] == 8
+    assert _plan(g, 7, 16 * G, G, F16, sg=16 * G + 4)["vector_bytes"] == 8
+    # ... but a single row ignores its strides
+    assert _plan(g, 1, 16 * G, G, F16, sg=16 * G + 4)["piece_bytes"] == 8
+    # weight only 8-byte aligned: 4-byte vectors (two fp16 values, two 4-byte weights)
+    p = _plan(g, 7, 16 * G, G, F16, w=A + (2 << 30) + 8)
+    assert (p["vector_bytes"], p["piece_bytes"]) == (4, 4)
+    # one weight per group position (shared by every group)
+    st, p = _plan_ex(g, PER_GROUP, rows=7, width=16 * G, group_size=G, y_row_stride=16 * G,
+                     gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
+                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == OK and p["vector_bytes"] == 8
+    # groups of at most one vector (14 bytes)
+    assert _plan(g, 7, 16 * 7, 7, BF16)["vector_bytes"] == 2
+    # 16381 bf16 = 32762 bytes: 2049 vectors, above the packed limit
+    p = _plan(g, 3, 16 * 16381, 16381, BF16)
+    assert (p["vector_bytes"], p["kernel_name"]) == (2, "wide")
+    # forced shapes: WIDE and staged rows are not built packed
+    st, _ = _plan_ex(g, RI, shape=(1024, 0), rows=7, width=16 * G, group_size=G,
+                     y_row_stride=16 * G, gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
+                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == NOTSUP
+    st, _ = _plan_ex(g, RI, shape=(16, 1, 2), rows=7, width=16 * G, group_size=G,
+                     y_row_stride=16 * G, gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
+                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == NOTSUP
+    # a covering shape can be forced; one that does not cover 13 vectors cannot
+    st, p = _plan_ex(g, RI, shape=(64, 1), rows=7, width=16 * G, group_size=G,
+                     y_row_stride=16 * G, gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
+                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == OK and (p["lanes_per_group"], p["piece_bytes"]) == (64, 8)
+    st, _ = _plan_ex(g, RI, shape=(8, 1), rows=7, width=16 * G, group_size=G,
+                     y_row_stride=16 * G, gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
+                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == NOTSUP
 
 
 def test_vector_width_follows_alignment(g):
@@ -274,8 +345,13 @@ def test_kernel_family_by_group_width(g):
         2048: ("block", 256, 1, 2),   # 256
         2056: ("block", 128, 3, 2),   # 257
         4096: ("block", 256, 2, 2),   # 512
+        5120: ("block", 256, 3, 2),   # 640
+        6144: ("block", 256, 3, 2),   # 768
+        6152: ("block", 256, 4, 1),   # 769
         7680: ("block", 256, 4, 1),   # 960
+        12288: ("block", 512, 3, 1),  # 1536
         16384: ("block", 512, 4, 1),  # 2048
+        24576: ("block", 1024, 3, 1),  # 3072
         32768: ("block", 1024, 4, 1),
         32776: ("wide", 1024, 0, 1),
     }

@@ -187,6 +187,81 @@ def test_shape_rejections(g):
                        shape) == want
 
 
+# ------------------------------------------------------------ packed groups
+
+PACKED_CASES = [(100, F16), (100, BF16), (99, BF16), (97, F16), (50, BF16), (9, BF16), (10, F16),
+                (63, BF16), (65, F16), (127, BF16), (129, BF16), (250, F16), (1001, BF16),
+                (2047, F16), (8191, BF16), (5, F32), (7, F32), (25, F32), (99, F32), (1001, F32)]
+
+
+def _plan_of(g, yd, gd, wd, od, rows, width, G, sy, sg, so, dtype, flags):
+    st, p = g.ggrms_plan_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od.data_ptr(), rows,
+                            width, G, sy, sg, so, 1e-5, dtype, flags)
+    assert st == g.SUCCESS
+    return p
+
+
+@pytest.mark.parametrize("G,dtype", PACKED_CASES,
+                         ids=[f"G{G}-{DT_IDS[d]}" for G, d in PACKED_CASES])
+def test_packed_groups(g, orc, G, dtype):
+    """Groups whose byte length is not a multiple of 16, in rows that are (16
+    groups per row): 16-byte vectors counted from the row start, vectors on
+    a group boundary stored in pieces.  Both operators; the out rows are
+    padded by 16 bytes and guarded on both sides, and everything outside the
+    [rows, width] view must keep its sentinel."""
+    groups, rows = 16, (5 if G <= 1001 else 3)
+    width = G * groups
+    esz = 4 if dtype == F32 else 2
+    pad = 16 // esz
+    so = width + pad
+    guard = 64
+    y, gt, w = random_case(rows, width, dtype, seed=G * 3 + dtype)
+    canary = {F32: np.float32(-1234.5), F16: np.uint16(0x7BFF), BF16: np.uint16(0x4B4B)}[dtype]
+    ob = np.full(guard + (rows - 1) * so + width + guard, canary, dtype=S.storage_dtype(dtype))
+    yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+    view = np.zeros(ob.shape, dtype=bool)
+    for r in range(rows):
+        view[guard + r * so: guard + r * so + width] = True
+    for flags in ((FLAG_RI,) if dtype != F32 else (0,)) + (FLAG_NBG,):
+        say(f"case packed G={G} dtype={DT_IDS[dtype]} flags={flags}")
+        od = dev_buf(ob, dtype)
+        p = _plan_of(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, dtype, flags)
+        assert p["vector_bytes"] == 16 and p["piece_bytes"] < 16, p
+        assert run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5, dtype,
+                       0, flags=flags) == g.SUCCESS
+        torch.cuda.synchronize()
+        got = host_bits(od, dtype)
+        ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                          gate_row_stride=width, out_row_stride=so, eps=1e-5, dtype=dtype,
+                          round_intermediate=flags & FLAG_RI, norm_before_gate=bool(flags & FLAG_NBG),
+                          out=ob.copy(), out_offset=guard)
+        assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
+            "packed stores touched elements outside the view"
+        assert_parity(got[view], ref[view], dtype, f"packed G={G} flags={flags}")
+
+
+def test_packed_in_place_over_the_gate(g, orc):
+    """The strided layout (y and gate column slices of one fused fp16 buffer,
+    200-byte groups) normalised in place over the gate: a vector on a group
+    boundary is read by two units while each writes its own pieces."""
+    rows, width, G, fused = 64, 4800, 100, 9856
+    buf = S.tensor(91, S.TID_Y, rows * fused, F16, ("normal", 1.0))
+    w = S.tensor(91, S.TID_W, width, F32, ("uniform", 0.5, 1.5))
+    ref = orc.forward(buf, buf, w, rows=rows, width=width, group_size=G, y_row_stride=fused,
+                      gate_row_stride=fused, out_row_stride=fused, eps=1e-5, dtype=F16,
+                      round_intermediate=1, gate_offset=width, out_offset=width, out=buf.copy())
+    fd = dev_buf(buf, F16)
+    wd = torch.from_numpy(w).cuda()
+    p = _plan_of(g, fd, fd[width:], wd, fd[width:], rows, width, G, fused, fused, fused, F16,
+                 FLAG_RI)
+    assert (p["vector_bytes"], p["piece_bytes"]) == (16, 8)
+    say("case packed in place over the gate")
+    assert run_gpu(g, fd, fd[width:], wd, fd[width:], rows, width, G, fused, fused, fused, 1e-5,
+                   F16, 1) == g.SUCCESS
+    torch.cuda.synchronize()
+    assert_parity(host_bits(fd, F16), ref, F16, "packed in place")
+
+
 # ------------------------------------------------------------ rows and layout
 
 @pytest.mark.parametrize("rows", [0, 1, 2, 3, 257])
