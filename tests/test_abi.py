@@ -316,6 +316,29 @@ def test_packed_groups_need_aligned_rows(g):
     assert st == NOTSUP
 
 
+def test_rows_split_over_launches(g):
+    """A grid that would pass 2^31 threads is split by rows: with 1024
+    threads per group (BLOCK 1024 x 1 or WIDE, forced) a launch takes at most
+    2^21 groups."""
+    rows, G = (1 << 21) + 3, 8
+    for shape in ((1024, 1), (1024, 0)):
+        st, p = _plan_ex(g, RI, shape=shape, rows=rows, width=G, group_size=G, y_row_stride=G,
+                         gate_row_stride=G, out_row_stride=G, gate=A + (1 << 26),
+                         norm_weight=A + (2 << 26), out=A + (3 << 26))
+        assert st == OK
+        assert (p["launches"], p["workgroups"], p["block_threads"]) == (2, rows, 1024), shape
+    # two groups per row: 2^20 rows per launch
+    st, p = _plan_ex(g, RI, shape=(1024, 1), rows=(1 << 20) + 1, width=2 * G, group_size=G,
+                     y_row_stride=2 * G, gate_row_stride=2 * G, out_row_stride=2 * G,
+                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == OK and (p["launches"], p["workgroups"]) == (2, 2 * ((1 << 20) + 1))
+    # just below the limit: one launch
+    st, p = _plan_ex(g, RI, shape=(1024, 1), rows=1 << 21, width=G, group_size=G,
+                     y_row_stride=G, gate_row_stride=G, out_row_stride=G, gate=A + (1 << 26),
+                     norm_weight=A + (2 << 26), out=A + (3 << 26))
+    assert st == OK and p["launches"] == 1
+
+
 def test_vector_width_follows_alignment(g):
     assert _plan(g, 4, 256, 64, BF16)["vector_bytes"] == 16
     assert _plan(g, 4, 256, 64, BF16, y=A + 8)["vector_bytes"] == 8

@@ -276,6 +276,28 @@ def test_row_counts(g, orc, rows):
     check_contiguous(g, orc, rows, 4800, 100, F16, 1, seed=rows + 1, tag=f"rows={rows}")
 
 
+@pytest.mark.parametrize("shape", [(1024, 1, 1), (1024, 0)], ids=["block1024x1", "wide"])
+def test_rows_split_over_launches(g, orc, shape):
+    """A job whose grid would pass 2^31 threads goes out as several launches
+    split by rows: 2^21 + 3 rows of one 8-value bf16 group with a forced
+    1024-thread-per-group shape are two launches; every row, on both sides of
+    the split, matches the oracle."""
+    rows, G = (1 << 21) + 3, 8
+    y, gt, w = random_case(rows, G, BF16, seed=2021)
+    yd, gd, wd = dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(w).cuda()
+    od = torch.empty_like(yd)
+    st, p = g.ggrms_plan_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od.data_ptr(), rows, G,
+                            G, G, G, G, 1e-5, BF16, FLAG_RI, shape)
+    assert st == g.SUCCESS and p["launches"] == 2, p
+    say(f"case rows split over launches shape={shape}")
+    assert run_gpu(g, yd, gd, wd, od, rows, G, G, G, G, G, 1e-5, BF16, 1, shape) == g.SUCCESS
+    torch.cuda.synchronize()
+    ref = orc.forward(y, gt, w, rows=rows, width=G, group_size=G, y_row_stride=G,
+                      gate_row_stride=G, out_row_stride=G, eps=1e-5, dtype=BF16,
+                      round_intermediate=1)
+    assert_parity(host_bits(od, BF16), ref, BF16, f"split launches {shape}")
+
+
 @pytest.mark.parametrize("dtype", [BF16, F16, F32], ids=DT_IDS.get)
 @pytest.mark.parametrize("offs", [(0, 0, 0), (1, 0, 0), (0, 3, 0), (0, 0, 1), (2, 6, 4), (4, 4, 4)])
 @pytest.mark.parametrize("pad", [0, 1, 3, 8])
