@@ -14,7 +14,8 @@ graph-replayed, next to an empty kernel of the same grid), the unfused
 four-op chain in PyTorch eager, and the CPU oracle timed on a bounded
 sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|copy]
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+                  [--only prefill|decode|copy|workloads|unfused|shapes]
 """
 from __future__ import annotations
 
@@ -59,8 +60,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for this long after the warmup steps")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads", "unfused"],
-                    default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads", "unfused",
+                                       "shapes"], default=None)
     ap.add_argument("--decode-bursts", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -284,18 +285,24 @@ def bench_copy(torch, steps):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "kernel_ms_avg": ms}
 
 
-def stream_ceiling(torch, nbytes, steps, settle_s=0.1):
+def stream_ceiling(torch, nbytes, steps, settle_s=0.1, fill="random"):
     """Event-timed average launch of the plain two-read-one-write kernel
     (libggrms_bench.so's ggrms_bench_stream3) over `nbytes` per stream, with
     as many rotating buffer sets as keep the 256 MB Infinity Cache cold, after
-    the same warm-up and settle as the fused kernel.  Returns microseconds."""
+    the same warm-up and settle as the fused kernel.  The buffers hold random
+    normal f32 values like the fused kernel's inputs (fill="constant": 0.5
+    everywhere; the HBM rate depends slightly on the bits moved).  Returns
+    microseconds."""
     aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
     aux.ggrms_bench_stream3.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_void_p]
     nbytes = (nbytes + 15) // 16 * 16
     sets = min(64, max(2, math.ceil(3 * 256e6 / (3 * nbytes))))
-    bufs = [[torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(0.5)
-             for _ in range(3)] for _ in range(sets)]
+    def buf():
+        t = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+        return t.normal_() if fill == "random" else t.fill_(0.5)
+
+    bufs = [[buf() for _ in range(3)] for _ in range(sets)]
     sp = torch.cuda.current_stream().cuda_stream
 
     def launch(i):
@@ -353,6 +360,100 @@ def bench_workloads(torch, g, S, steps):
                       "stream_ceiling_us": ceil_us,
                       "frac_of_stream_ceiling": ceil_us / (avg * 1e3)}
     log(f"workloads: {json.dumps(out)}")
+    return out
+
+
+# Model-shaped jobs at the prefill's size (~125.8 MB per stream): (label,
+# dtype, group size, width, ggrms_forward_ex flags[, row stride]).  Group sizes of Mamba-2
+# mixers (d_inner / n_groups for 8 or fewer groups), per-head norms with a
+# shared head weight, both operators, the three element types.
+SHAPES = [
+    ("bf16 G960 gate first (the prefill workload)", 2, 960, 7680, 1),
+    ("bf16 G960 norm first", 2, 960, 7680, 2),
+    ("fp16 G960 gate first", 1, 960, 7680, 1),
+    ("f32 G960 gate first", 0, 960, 7680, 0),
+    ("f32 G960 norm first", 0, 960, 7680, 2),
+    ("bf16 G1024, 8 groups of a 8192-wide row", 2, 1024, 8192, 1),
+    ("bf16 G2048, 8 groups of a 16384-wide row", 2, 2048, 16384, 1),
+    ("bf16 G3584, 2 groups of a 7168-wide row", 2, 3584, 7168, 1),
+    ("bf16 G5120, one group per row", 2, 5120, 5120, 1),
+    ("bf16 G8192, one group per row", 2, 8192, 8192, 1),
+    ("fp16 G128 heads, per-column weight", 1, 128, 8192, 0),
+    ("bf16 G128, 60 groups of a 7680-wide row, per-column weight", 2, 128, 7680, 1),
+    ("bf16 G128, 64 groups of a 8192-wide row, per-column weight", 2, 128, 8192, 1),
+    ("fp16 G128 heads, shared head weight", 1, 128, 8192, 4),
+    ("fp16 G128 heads, norm first, shared head weight", 1, 128, 8192, 6),
+    ("fp16 G256 heads, shared head weight", 1, 256, 8192, 4),
+    ("f32 G128 heads, shared head weight", 0, 128, 4096, 4),
+    ("fp16 G100 packed groups, per-column weight", 1, 100, 4800, 1),
+    # the same groups in rows padded by 4 elements: rows not 16-byte aligned,
+    # so the whole group falls back to 8-byte vectors
+    ("fp16 G100 in padded rows (8-byte vectors)", 1, 100, 4800, 1, 4804),
+]
+
+
+def bench_shapes(torch, g, steps):
+    """The fused kernel on model-shaped jobs of ~377 MB (three streams of
+    125,829,120 B each, three rotating sets, random normal inputs), each next
+    to the plain two-read-one-write kernel moving the same bytes."""
+    tb = 125829120
+    sets = 3
+    raw = [[torch.empty(tb, dtype=torch.uint8, device="cuda") for _ in range(3)] for _ in range(sets)]
+    weight = torch.rand(16384, device="cuda") + 0.5
+    sp = torch.cuda.current_stream().cuda_stream
+    tdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}
+    ceil_us = stream_ceiling(torch, tb, steps)
+    const_us = stream_ceiling(torch, tb, steps, fill="constant")
+    log(f"plain two-read-one-write kernel at 3 x {tb} B: {ceil_us:.2f} us on random data, "
+        f"{const_us:.2f} us on constant data")
+    out = {"stream_ceiling_us": ceil_us, "stream_ceiling_constant_data_us": const_us,
+           "shapes": []}
+    for label, dt, G, width, flags, *pad in SHAPES:
+        esz = 4 if dt == 0 else 2
+        stride = pad[0] if pad else width
+        rows = tb // esz // stride
+        views = []
+        for y, gt, o in raw:
+            yv, gv = y.view(tdt[dt]), gt.view(tdt[dt])
+            yv.normal_()
+            gv.normal_()
+            views.append((yv, gv, o.view(tdt[dt])))
+
+        def launch(i):
+            y, gt, o = views[i % sets]
+            st = g.ggrms_forward_ex(y.data_ptr(), gt.data_ptr(), weight.data_ptr(), o.data_ptr(),
+                                    rows, width, G, stride, stride, stride, 1e-5, dt, flags, sp)
+            if st != 0:
+                raise RuntimeError(f"{label}: {g.ggrms_status_string(st)}")
+
+        for i in range(5):
+            launch(i)
+        settle(torch, launch, 0.1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(steps):
+            launch(i)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        nbytes = 3 * rows * width * esz
+        st, p = g.ggrms_plan_ex(views[0][0].data_ptr(), views[0][1].data_ptr(), weight.data_ptr(),
+                                views[0][2].data_ptr(), rows, width, G, stride, stride, stride,
+                                1e-5, dt, flags)
+        rec = {"label": label, "rows": rows, "width": width, "row_stride": stride,
+               "group_size": G, "flags": flags,
+               "us": round(us, 2), "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+               "frac_of_stream_ceiling": round(ceil_us * nbytes / (3 * tb) / us, 4),
+               "shape": f"{p['kernel_name']} {p['lanes_per_group']}x{p['vectors_per_lane']} "
+                        f"rows/wg {p['rows_per_workgroup']} vector {p['vector_bytes']} B"
+                        f" piece {p['piece_bytes']} B"}
+        out["shapes"].append(rec)
+        log(f"{label:50s} {rec['shape']:40s} {us:8.2f} us {rec['frac_of_peak']:.3f} of peak "
+            f"{rec['frac_of_stream_ceiling']:.3f} of the plain stream")
+    del raw
+    torch.cuda.empty_cache()
     return out
 
 
@@ -536,6 +637,9 @@ def main():
         return
     if args.only == "unfused":
         bench_unfused(torch, S, 100)
+        return
+    if args.only == "shapes":
+        print(json.dumps(bench_shapes(torch, g, min(args.steps, 300))), flush=True)
         return
 
     pre = bench_prefill(torch, g, S, args, shape)

@@ -76,6 +76,7 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     a.G = (uint32_t)group_size;
     a.nvec = (uint32_t)lp.nvec;
     a.Gf = (float)group_size;
+    a.Ginv = (float)(1.0 / (double)group_size);
     a.eps = eps;
     a.ri = (dtype != GGRMS_F32 && (flags & GGRMS_FLAG_ROUND_INTERMEDIATE)) ? 1 : 0;
     const int es = lp.esize;

@@ -25,6 +25,7 @@ struct KArgs {
     uint32_t G;       // group size in elements
     uint32_t nvec;    // vectors per group
     float Gf;         // (float)G
+    float Ginv;       // 1/G rounded to f32 (the normaliser multiplies by it)
     float eps;
     int32_t ri;       // round the intermediate (16-bit types only)
 };

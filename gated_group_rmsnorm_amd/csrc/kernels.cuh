@@ -39,6 +39,7 @@ namespace ggrms {
 
 using u16 = unsigned short;
 using u32 = unsigned int;
+typedef u16 u16x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -197,6 +198,33 @@ template <int N> __device__ inline void load_weights(const float* p, float (&w)[
 // some gate of the wave is below kSiluFastMin.
 constexpr float kSiluFastMin = -87.0f;
 
+// Whether some gate is below kSiluFastMin, from the raw bits: for negative
+// numbers the sign-magnitude pattern, read as an unsigned integer of the
+// element's width, grows with the magnitude, so the lane keeps the largest
+// pattern of its gate words (one packed 16-bit maximum per two bf16/fp16
+// gates, no widening) and compares it with the pattern of -87 at the end.
+// A NaN with its sign bit set also selects the exact form, which gives it
+// the same result.
+template <class T> __device__ inline u32 gate_max_word(u32 acc, u32 w) {
+    if constexpr (T::kSize == 4)
+        return acc > w ? acc : w;
+    else
+        return __builtin_bit_cast(u32, __builtin_elementwise_max(__builtin_bit_cast(u16x2, acc),
+                                                                  __builtin_bit_cast(u16x2, w)));
+}
+template <class T> struct FastMinBits;  // bit pattern of kSiluFastMin (-87)
+template <> struct FastMinBits<TF32> { static constexpr u32 v = 0xC2AE0000u; };
+template <> struct FastMinBits<TBF16> { static constexpr u32 v = 0xC2AEu; };
+template <> struct FastMinBits<TF16> { static constexpr u32 v = 0xD570u; };
+template <class T> __device__ inline bool gate_below_fast_min(u32 acc) {
+    if constexpr (T::kSize == 4) {
+        return acc > FastMinBits<T>::v;
+    } else {
+        const u32 lo = acc & 0xFFFFu, hi = acc >> 16;
+        return (lo > hi ? lo : hi) > FastMinBits<T>::v;
+    }
+}
+
 __device__ inline float silu_fast(float x) {
     const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
     return x * __builtin_amdgcn_rcpf(1.0f + e);
@@ -244,6 +272,20 @@ template <int SEG> __device__ inline float segment_sum(float v) {
 // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): gfx9 encoding (vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) -- waits for vector memory only.
 constexpr int kWaitVmcnt0 = 0x0F70;
+
+// nf = 1/sqrt(m2/G + eps): the mean and eps in one fused multiply-add with
+// 1/G rounded once on the host, then v_rsq_f32 (about 1 ulp).  The result is
+// within a few f32 ulp of the correctly rounded steps (divide, add, square
+// root, divide), for a few VALU operations instead of ~35 IEEE-exact ones
+// per lane.  An argument below FLT_MIN is scaled by 2^64 first and the
+// result by 2^32, so tiny means are not flushed; 0 gives +inf, inf gives 0,
+// NaN stays NaN.
+__device__ inline float norm_factor(float m2, float ginv, float eps) {
+    const float v = __builtin_fmaf(m2, ginv, eps);
+    const bool tiny = v < 0x1p-126f;
+    const float r = __builtin_amdgcn_rsqf(tiny ? v * 0x1p64f : v);
+    return tiny ? r * 0x1p32f : r;
+}
 
 __device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t s) {
     return (__umulhi(n, m) + n) >> s;
@@ -347,22 +389,31 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     };
 
     // Gate first: a = y * silu(gate) for every loaded element.  Norm first:
-    // a = y, and silu(gate) waits for the output.  Lanes past the group's end
+    // a = y, and silu(gate) is kept for the output.  Lanes past the group's end
     // hold a copy of its last vector and their partial sum is dropped by one
     // select per vector (no per-element predication).
     float av[VPT][N];
+    // norm first: silu(gate), computed here (before the reduction, while
+    // other waves' loads are in flight) rather than after it
+    float sgv[NBG ? VPT : 1][N];
     float acc = 0.0f;
-    float gmin = __builtin_inff();
+    unsigned gmax = 0;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         float yf[N], gf[N];
         P::unpack(yr[k], yf);
         P::unpack(gr[k], gf);
+        if constexpr (VB <= 4) {
+            gmax = gate_max_word<T>(gmax, (unsigned)gr[k]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VB / 4; ++i) gmax = gate_max_word<T>(gmax, gr[k][i]);
+        }
         float part = 0.0f;
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            gmin = __builtin_fminf(gmin, gf[e]);
             const float x = NBG ? yf[e] : yf[e] * silu_fast(gf[e]);
+            if constexpr (NBG) sgv[k][e] = silu_fast(gf[e]);
             av[k][e] = x;
             const float xx = __builtin_fmaf(x, x, part);
             part = owned(k, e) ? xx : part;
@@ -371,7 +422,16 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     }
     // Rare: a gate deep in silu's underflow range.  Redo the wave's silu with
     // the exact form (identical bits for every other gate).
-    const bool exact_silu = __builtin_expect(__any(gmin < kSiluFastMin), 0);
+    const bool exact_silu = __builtin_expect(__any(gate_below_fast_min<T>(gmax)), 0);
+    if (NBG && exact_silu) {
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            float gf[N];
+            P::unpack(gr[k], gf);
+#pragma unroll
+            for (int e = 0; e < N; ++e) sgv[k][e] = silu_exact(gf[e]);
+        }
+    }
     if (!NBG && exact_silu) {
         acc = 0.0f;
 #pragma unroll
@@ -392,7 +452,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     }
 
     const float m2 = reduce(acc);
-    const float nf = 1.0f / __builtin_sqrtf(m2 / a.Gf + a.eps);
+    const float nf = norm_factor(m2, a.Ginv, a.eps);
     if constexpr (WS == WSource::Lds) {
 #pragma unroll
         for (int k = 0; k < VPT; ++k) load_weights<N>(wl + ci[k] * N, wr[k]);  // v0 == 0 here
@@ -417,13 +477,8 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
             for (int e = 0; e < N; ++e) t[e] = av[k][e] * nf;
             if constexpr (NBG) {
                 // ((y * nf) * w) * silu(gate), every intermediate f32
-                float gf[N];
-                P::unpack(gr[k], gf);
 #pragma unroll
-                for (int e = 0; e < N; ++e) {
-                    const float sg = exact_silu ? silu_exact(gf[e]) : silu_fast(gf[e]);
-                    t[e] = (t[e] * wr[k][e]) * sg;
-                }
+                for (int e = 0; e < N; ++e) t[e] = (t[e] * wr[k][e]) * sgv[k][e];
             } else {
                 if constexpr (RI) P::round_trip(t);
 #pragma unroll
@@ -562,7 +617,7 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
     float m2 = 0.0f;
 #pragma unroll
     for (int i = 0; i < kWideBlock / 64; ++i) m2 += part[i];
-    const float nf = 1.0f / __builtin_sqrtf(m2 / a.Gf + a.eps);
+    const float nf = norm_factor(m2, a.Ginv, a.eps);
 
     for (uint32_t i = threadIdx.x; i < a.nvec; i += kWideBlock) {
         float yf[N], gf[N], wv[N], t[N];
