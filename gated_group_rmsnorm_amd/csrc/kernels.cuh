@@ -12,7 +12,11 @@
 // VALU ops per element), so the design is about moving bytes:
 //   * every y/gate/out access is a VB-byte vector (16 B when alignment allows),
 //     one vector per lane per step, so a wave instruction covers a contiguous
-//     64*VB-byte run;
+//     64*VB-byte run; groups whose byte length is not a multiple of 16 in
+//     rows that are keep 16-byte vectors counted from the row start
+//     ("packed", boundary vectors stored in PB-byte pieces);
+//   * large jobs stream y/gate/out with the non-temporal hint, small ones
+//     (decode) keep their lines cached (the NT template argument);
 //   * a unit is read once into registers; its reduction happens in registers
 //     and the outputs are written from the same registers (single pass);
 //   * lanes past the end of a group re-load the group's last vector (an L1/L2
@@ -24,7 +28,10 @@
 //     combine the partial sums;
 //   * every lane of a group ends with a bit-identical m2 (the same additions
 //     in the same order), so nf is uniform over the group and the result is
-//     deterministic run to run.
+//     deterministic run to run;
+//   * VALU work is kept low (it runs about half busy at the HBM rate): one
+//     exp and one reciprocal per silu, the normaliser as a fused multiply-add
+//     and v_rsq_f32, the silu-underflow test on raw gate bits.
 // Nothing here uses MFMA: there is no contraction to feed it.
 #pragma once
 
