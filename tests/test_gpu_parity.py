@@ -569,3 +569,13 @@ def test_torch_wrapper(g, orc):
         g.forward(fd[..., :width:2], gate[..., :width // 2], wt[:width // 2], C)
     with pytest.raises(TypeError):
         g.forward(y, gate, wt.half(), C)
+    # cache policy: this 61 KB job keeps its lines cached by default; forcing
+    # either policy gives the same bits, and a wrong name is refused
+    assert g.plan(y, gate, wt, C, eps=1e-6, round_intermediate=False)["streaming"] == 0
+    assert g.plan(y, gate, wt, C, eps=1e-6, round_intermediate=False, cache="stream")["streaming"] == 1
+    for cache in ("stream", "keep"):
+        o2 = g.forward(y, gate, wt, C, eps=1e-6, round_intermediate=False, cache=cache)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), cache
+    with pytest.raises(ValueError):
+        g.forward(y, gate, wt, C, cache="bypass")
