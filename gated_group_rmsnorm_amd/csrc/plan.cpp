@@ -68,8 +68,8 @@ int kernel_for_shape(int lanes, int vpt) {
 // clocks settle:
 //   * up to 64 vectors: one vector per lane, the smallest power-of-two lane
 //     segment, several groups per wave (WAVE kernel, 77-80% of HBM peak);
-//   * 65-96: one wave, two vectors per lane (74%; 128 lanes idle too many);
-//   * 97-768: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
+//   * 65-72: one wave, two vectors per lane (65-74%, the same as 128 lanes);
+//   * 73-768: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
 //     workgroup sharing staged weights (78-81%); 4 rows only with one vector
 //     per lane, since the staging registers cost occupancy at 2+;
 //   * 769-4096: 256-1024 lanes x 3-4 vectors, one row per workgroup (staging
@@ -81,7 +81,8 @@ struct ShapeRule {
     int kernel, lanes, vpt, upb;
 };
 const ShapeRule kRules[] = {
-    {96, GGRMS_KERNEL_WAVE, 64, 2, 1},
+    {72, GGRMS_KERNEL_WAVE, 64, 2, 1},
+    {96, GGRMS_KERNEL_BLOCK, 128, 1, 2},
     {128, GGRMS_KERNEL_BLOCK, 128, 1, 4},
     {192, GGRMS_KERNEL_BLOCK, 128, 2, 2},
     {256, GGRMS_KERNEL_BLOCK, 256, 1, 2},

@@ -361,7 +361,9 @@ def test_kernel_family_by_group_width(g):
         8: ("wave", 1, 1, 1),         # 1 vector: a group per lane
         64: ("wave", 8, 1, 1),
         512: ("wave", 64, 1, 1),      # 64
-        640: ("wave", 64, 2, 1),      # 80
+        576: ("wave", 64, 2, 1),      # 72
+        640: ("block", 128, 1, 2),    # 80
+        768: ("block", 128, 1, 2),    # 96
         960: ("block", 128, 1, 4),    # 120
         1032: ("block", 128, 2, 4 // 2),  # 129
         1536: ("block", 128, 2, 2),   # 192
