@@ -519,10 +519,11 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 
 // ------------------------------------------------------------ kernels
 
-// WAVE: SEG (<= 64) lanes per unit, 256-thread workgroups, no LDS, no barrier.
+// WAVE: SEG (<= 64) lanes per unit, workgroups of 64 or 256 threads (the
+// launch's choice), no LDS, no barrier.
 template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
-    const uint32_t t = blockIdx.x * (uint32_t)kWaveBlock + threadIdx.x;
+    const uint32_t t = blockIdx.x * (uint32_t)blockDim.x + threadIdx.x;
     const uint32_t unit = t / SEG;
     if (unit >= a.units) return;  // whole segments leave together
     const uint32_t n = fast_div(unit, a.div_m, a.div_s);

@@ -256,7 +256,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         while (upb > 1 && (rows < upb || !rows_per_workgroup_supported(kernel, lanes, upb)))
             upb >>= 1;
     }
-    int block = kWaveBlock;
+    int block = (flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? kWaveBlockOneWave : kWaveBlock;
     if (kernel == GGRMS_KERNEL_BLOCK) block = lanes * upb;
     if (kernel == GGRMS_KERNEL_WIDE) block = kWideBlock;
     // Units per launch stay below 2^31 and so do threads per launch, so the

@@ -53,7 +53,9 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: int, what: str = "") 
         gn, rn = np.isnan(g64), np.isnan(r64)
         assert np.array_equal(gn, rn), f"{what}: NaN positions differ ({int((gn != rn).sum())})"
         ok = ~rn
-        err = np.abs(g64[ok] - r64[ok])
+        # equal values (infinities included) differ by 0, not by inf - inf
+        with np.errstate(invalid="ignore"):
+            err = np.where(g64[ok] == r64[ok], 0.0, np.abs(g64[ok] - r64[ok]))
         lim = 1e-5 * np.abs(r64[ok])
         # a zero reference needs a zero (or an underflowed f32 subnormal) result
         lim = np.where(r64[ok] == 0, 2.0 ** -126, lim)

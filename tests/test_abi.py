@@ -230,6 +230,13 @@ def test_plans_for_the_workloads(g):
     # 16384x8192 fp16, G = 128: 16 vectors -> 16-lane segments, four groups per wave
     p = _plan(g, 16384, 8192, 128, F16)
     assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 16, 16, 1)
+    # a weight per column: 4-wave workgroups (4 x 16 groups); the head scale shared by
+    # every group: one wave per workgroup (16384 * 64 / 4 workgroups)
+    assert (p["block_threads"], p["workgroups"]) == (256, 16384 * 64 // 16)
+    st, p = _plan_ex(g, PER_GROUP, rows=16384, width=8192, group_size=128, y_row_stride=8192,
+                     gate_row_stride=8192, out_row_stride=8192, dtype=F16, gate=A + (1 << 30),
+                     norm_weight=A + (2 << 30), out=A + (3 << 30))
+    assert st == OK and (p["block_threads"], p["workgroups"]) == (64, 16384 * 64 // 4)
     # 256x4800 fp16 slices of a [256, 9856] buffer, G = 100: 200-byte groups in 9600-byte
     # rows -> packed: 16-byte vectors from the row start, boundary vectors in 8-byte pieces;
     # a group touches at most ceil((8 + 200) / 16) = 13 vectors -> 16-lane segments
