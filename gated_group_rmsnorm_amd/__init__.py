@@ -42,7 +42,7 @@ FLAG_CACHE_STREAM, FLAG_CACHE_KEEP = 8, 16
 STREAM_MIN_BYTES = 4 << 20  # default policy: jobs of at least this many y+gate+out bytes stream
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
 KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide"}
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libggrms.so")
@@ -69,7 +69,7 @@ class _Plan(ctypes.Structure):
                 ("block_threads", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("rows_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("streaming", ctypes.c_int32),
-                ("piece_bytes", ctypes.c_int32)]
+                ("piece_bytes", ctypes.c_int32), ("tile_order", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:

@@ -44,6 +44,21 @@ const void* pick(int dtype, bool nbg, bool nt, int kernel, int vb, int pb, int l
     }
 }
 
+// The XCD-banded order's fields of KArgs for a launch over r rows.
+void set_band(const LaunchPlan& lp, int64_t r, KArgs* a) {
+    a->xband = lp.xband ? 1u : 0u;
+    int64_t R, C;
+    launch_tiles(lp, r, &R, &C);
+    a->xc = (uint32_t)C;
+    div_magic(a->xc, &a->xc_m, &a->xc_s);
+    a->xfullk = (uint32_t)(R / kXcds * C);
+    a->xfullrows = (uint32_t)(R / kXcds * kXcds);
+    a->xrr = (uint32_t)(R % kXcds ? R % kXcds : 1);
+    div_magic(a->xrr, &a->xrr_m, &a->xrr_s);
+    a->xq2 = (uint32_t)(R % kXcds * C / kXcds);
+    a->xr2 = (uint32_t)(R % kXcds * C % kXcds);
+}
+
 ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_weight, void* out,
                             int64_t rows, int64_t width, int64_t group_size, int64_t y_row_stride,
                             int64_t gate_row_stride, int64_t out_row_stride, float eps,
@@ -80,8 +95,6 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     a.eps = eps;
     a.ri = (dtype != GGRMS_F32 && (flags & GGRMS_FLAG_ROUND_INTERMEDIATE)) ? 1 : 0;
     const int es = lp.esize;
-    const int64_t thread_per_unit = p.kernel == GGRMS_KERNEL_WIDE ? kWideBlock : p.lanes_per_group;
-    const int upb = p.rows_per_workgroup;
 
     for (int64_t r0 = 0; r0 < rows; r0 += lp.rows_per_launch) {
         const int64_t r = rows - r0 < lp.rows_per_launch ? rows - r0 : lp.rows_per_launch;
@@ -90,11 +103,8 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
         a.out = static_cast<char*>(out) + r0 * out_row_stride * es;
         a.units = (uint32_t)(r * lp.groups);
         a.rows = (uint32_t)r;
-        int64_t blocks;
-        if (p.kernel == GGRMS_KERNEL_BLOCK)
-            blocks = (r + upb - 1) / upb * lp.groups;  // row tiles x groups
-        else
-            blocks = ((int64_t)a.units * thread_per_unit + p.block_threads - 1) / p.block_threads;
+        const int64_t blocks = launch_workgroups(lp, r);
+        set_band(lp, r, &a);
         void* args[] = {&a};
         if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3((uint32_t)p.block_threads), args,
                             (size_t)p.lds_bytes, s) != hipSuccess)

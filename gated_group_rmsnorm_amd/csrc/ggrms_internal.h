@@ -28,19 +28,41 @@ struct KArgs {
     float Ginv;       // 1/G rounded to f32 (the normaliser multiplies by it)
     float eps;
     int32_t ri;       // round the intermediate (16-bit types only)
+    // XCD-banded tile order (xband set; WAVE with one-wave workgroups, and
+    // BLOCK).  A tile is one workgroup's work: WAVE, 64 / lanes consecutive
+    // groups of one row; BLOCK, one group of a row tile of UPB rows.  The
+    // launch's R x C tiles (R rows or row tiles, C tile columns) are taken in
+    // blocks of 8 rows; inside a block, numbered column-major, XCD x takes
+    // the C tiles x*C .. x*C + C-1, i.e. a band of about C/8 columns of 8 rows.
+    // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
+    // b % 8) and all XCDs move through the blocks at the same pace, so the
+    // tiles in flight still cover a contiguous run of rows -- the HBM access
+    // pattern of the row-major order -- while each XCD reads the weights of
+    // only its band, which then stay in its L2 and its CUs' L1.  The last
+    // R % 8 rows form a short block, shared out the same way.
+    uint32_t xband;
+    uint32_t xc, xc_m, xc_s;        // C and its magic numbers
+    uint32_t xfullk;                // workgroups per XCD in the full blocks: (R / 8) * C
+    uint32_t xfullrows;             // rows in the full blocks: (R / 8) * 8
+    uint32_t xrr, xrr_m, xrr_s;     // rows in the short block (R % 8; 1 if none) and magic
+    uint32_t xq2, xr2;              // short block's tiles (R % 8) * C: / 8 and % 8
 };
+
+// Workgroups are dealt to XCDs in turn on the 8-XCD part.
+constexpr uint32_t kXcds = 8;
 
 // Supported shapes.  WAVE: lanes in {1..64} (powers of two); vectors per lane
 // 1 for lanes < 64, 1..4 for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
 // vectors per lane 1..4.  WIDE: 1024 lanes, vectors per lane 0 (it loops over
-// the group).  A WAVE workgroup is 256 threads (4 waves), or a single wave
-// when every group shares one weight vector (the kernel takes its size from
-// the launch): there a wave's slot is freed the moment it retires, instead
-// of waiting for the slowest wave of its workgroup, which keeps more loads
-// in flight -- 0.83 against 0.815 of HBM peak on 128-wide fp16 groups.  With
-// a weight per column the 4-wave form is ahead (0.77 against 0.76).
+// the group).  A WAVE workgroup is a single wave or 4 waves (the kernel takes
+// its size from the launch).  One wave's slot is freed the moment it
+// retires, instead of waiting for the slowest wave of its workgroup, which
+// keeps more loads in flight (128-wide fp16 groups sharing one weight: 0.83
+// against 0.815 of HBM peak); 4 waves are kept for small jobs of packed
+// groups (see the planner).
 constexpr int kWaveBlock = 256;
 constexpr int kWaveBlockOneWave = 64;
+constexpr int64_t kWaveFourMaxWaves = 4096;  // 4 waves per SIMD on 256 CUs
 constexpr int kWideBlock = 1024;
 
 // Rows of one group per BLOCK workgroup (the workgroup stays <= 512 threads).
@@ -77,7 +99,48 @@ struct LaunchPlan {
     int64_t groups;
     int64_t nvec;
     int64_t rows_per_launch;  // rows handled by each launch (the last one may have fewer)
+    bool xband;               // XCD-banded tile order (KArgs::xband)
 };
+
+// WAVE: groups one wave covers (lanes <= 64).
+inline int64_t wave_groups_per_wave(int lanes) { return 64 / lanes; }
+
+// Tile rows and tile columns of one launch over r rows (see KArgs::xband);
+// a WAVE tile is one wave.
+inline void launch_tiles(const LaunchPlan& lp, int64_t r, int64_t* R, int64_t* C) {
+    const ggrms_plan_t& p = lp.pub;
+    if (p.kernel == GGRMS_KERNEL_BLOCK) {
+        *R = (r + p.rows_per_workgroup - 1) / p.rows_per_workgroup;
+        *C = lp.groups;
+    } else if (p.kernel == GGRMS_KERNEL_WIDE) {  // one unit per workgroup, row-major only
+        *R = r;
+        *C = lp.groups;
+    } else {
+        const int64_t gpw = wave_groups_per_wave(p.lanes_per_group);
+        *R = r;
+        *C = (lp.groups + gpw - 1) / gpw;
+    }
+}
+
+// Workgroups of one launch over r rows.
+inline int64_t launch_workgroups(const LaunchPlan& lp, int64_t r) {
+    const ggrms_plan_t& p = lp.pub;
+    switch (p.kernel) {
+    case GGRMS_KERNEL_BLOCK:
+        return (r + p.rows_per_workgroup - 1) / p.rows_per_workgroup * lp.groups;
+    case GGRMS_KERNEL_WAVE: {
+        if (lp.xband) {  // one wave per tile, tiles of one row
+            int64_t R, C;
+            launch_tiles(lp, r, &R, &C);
+            return R * C;
+        }
+        const int64_t threads = r * lp.groups * p.lanes_per_group;  // units in a row-major run
+        return (threads + p.block_threads - 1) / p.block_threads;
+    }
+    case GGRMS_KERNEL_WIDE: return r * lp.groups;
+    default: return 0;
+    }
+}
 
 // Validation and kernel choice; no HIP calls.  Implemented in plan.cpp.
 // `flags` are ggrms_flag_t bits.  shape == nullptr picks the shape; otherwise

@@ -519,23 +519,55 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 
 // ------------------------------------------------------------ kernels
 
+// Tile (row or row tile rt, tile column c) of workgroup blockIdx.x in the
+// XCD-banded order (KArgs::xband): XCD x = b % 8 takes, in each block of 8
+// rows numbered column-major, the tiles x*C .. x*C + C-1, block after block;
+// then its share of the short block of the last R % 8 rows.  A bijection of
+// the launch's workgroups onto its R x C tiles.
+__device__ inline void xcd_band_tile(const KArgs& a, uint32_t& rt, uint32_t& c) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t x = b % kXcds, k = b / kXcds;
+    if (k < a.xfullk) {
+        const uint32_t blk = fast_div(k, a.xc_m, a.xc_s);
+        const uint32_t idx = x * a.xc + (k - blk * a.xc);
+        c = idx / kXcds;
+        rt = blk * kXcds + idx % kXcds;
+    } else {
+        const uint32_t idx = x * a.xq2 + (x < a.xr2 ? x : a.xr2) + (k - a.xfullk);
+        c = fast_div(idx, a.xrr_m, a.xrr_s);
+        rt = a.xfullrows + (idx - c * a.xrr);
+    }
+}
+
 // WAVE: SEG (<= 64) lanes per unit, workgroups of 64 or 256 threads (the
-// launch's choice), no LDS, no barrier.
+// launch's choice), no LDS, no barrier.  Row-major order: each wave takes
+// the next 64 / SEG units of the (row, group) sequence.  XCD-banded order
+// (one wave per workgroup): the wave takes 64 / SEG consecutive groups of one
+// row.
 template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
-    const uint32_t t = blockIdx.x * (uint32_t)blockDim.x + threadIdx.x;
-    const uint32_t unit = t / SEG;
-    if (unit >= a.units) return;  // whole segments leave together
-    const uint32_t n = fast_div(unit, a.div_m, a.div_s);
-    unit_pass<T, VB, PB, SEG, VPT, NBG, NT, WSource::Global>(a, n, unit - n * a.groups,
-                                                     threadIdx.x & (SEG - 1), true, nullptr,
-                                                     [](float v) { return segment_sum<SEG>(v); });
+    uint32_t n, g;
+    if (a.xband) {
+        uint32_t c;
+        xcd_band_tile(a, n, c);
+        g = c * (64 / SEG) + threadIdx.x / SEG;
+        if (g >= a.groups) return;  // the row's last tile may be partial
+    } else {
+        const uint32_t unit = (blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) / SEG;
+        if (unit >= a.units) return;  // whole segments leave together
+        n = fast_div(unit, a.div_m, a.div_s);
+        g = unit - n * a.groups;
+    }
+    unit_pass<T, VB, PB, SEG, VPT, NBG, NT, WSource::Global>(a, n, g, threadIdx.x & (SEG - 1),
+                                                             true, nullptr,
+                                                             [](float v) { return segment_sum<SEG>(v); });
 }
 
 // BLOCK: a unit spans SEG/64 waves; the per-wave sums meet in LDS after one
 // barrier and every wave adds them in the same order.  A workgroup holds UPB
-// units: UPB consecutive rows of one group (workgroup b = row tile b / groups,
-// group b % groups).  With UPB > 1 the group's f32 weights are fetched once
+// units: UPB consecutive rows of one group (row-major order: workgroup b
+// takes row tile b / groups, group b % groups; or the XCD-banded order).
+// With UPB > 1 the group's f32 weights are fetched once
 // per workgroup -- contiguous 16-byte loads spread over all its threads --
 // and parked in LDS before the reduction barrier, instead of every unit
 // fetching its own copy: weight traffic from L2 falls by UPB and the L1
@@ -547,8 +579,15 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     constexpr int N = Packet<T, VB>::N;
     __shared__ float part[BT / 64];
     extern __shared__ __attribute__((aligned(16))) float wl[];  // a.G floats when UPB > 1
-    const uint32_t tile = fast_div(blockIdx.x, a.div_m, a.div_s);
-    const uint32_t g = blockIdx.x - tile * a.groups;
+    // row tile and group: row-major (the groups of a row tile in turn) or
+    // XCD-banded (KArgs::xband)
+    uint32_t tile, g;
+    if (a.xband) {
+        xcd_band_tile(a, tile, g);
+    } else {
+        tile = fast_div(blockIdx.x, a.div_m, a.div_s);
+        g = blockIdx.x - tile * a.groups;
+    }
     const uint32_t u = threadIdx.x / SEG;
     uint32_t n = tile * UPB + u;
     const bool live = n < a.rows;

@@ -142,8 +142,13 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         return GGRMS_ERROR_INVALID_VALUE;
     const uint32_t known = GGRMS_FLAG_ROUND_INTERMEDIATE | GGRMS_FLAG_NORM_BEFORE_GATE |
                            GGRMS_FLAG_WEIGHT_PER_GROUP | GGRMS_FLAG_CACHE_STREAM |
-                           GGRMS_FLAG_CACHE_KEEP;
+                           GGRMS_FLAG_CACHE_KEEP | GGRMS_FLAG_ORDER_ROWS |
+                           GGRMS_FLAG_ORDER_BANDED | GGRMS_FLAG_WAVE_ONE | GGRMS_FLAG_WAVE_FOUR;
     if (flags & ~known) return GGRMS_ERROR_INVALID_VALUE;
+    if (((flags & GGRMS_FLAG_ORDER_ROWS) && (flags & GGRMS_FLAG_ORDER_BANDED)) ||
+        ((flags & GGRMS_FLAG_WAVE_ONE) && (flags & GGRMS_FLAG_WAVE_FOUR)) ||
+        ((flags & GGRMS_FLAG_ORDER_BANDED) && (flags & GGRMS_FLAG_WAVE_FOUR)))
+        return GGRMS_ERROR_INVALID_VALUE;
     if ((flags & GGRMS_FLAG_ROUND_INTERMEDIATE) && (flags & GGRMS_FLAG_NORM_BEFORE_GATE))
         return GGRMS_ERROR_INVALID_VALUE;
     if ((flags & GGRMS_FLAG_CACHE_STREAM) && (flags & GGRMS_FLAG_CACHE_KEEP))
@@ -256,24 +261,48 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         while (upb > 1 && (rows < upb || !rows_per_workgroup_supported(kernel, lanes, upb)))
             upb >>= 1;
     }
-    int block = (flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? kWaveBlockOneWave : kWaveBlock;
+    plan->pub.kernel = kernel;
+    plan->pub.lanes_per_group = lanes;
+    plan->pub.rows_per_workgroup = upb;
+    // WAVE workgroups: one wave, except for a small job of packed groups
+    // (at most 4 waves per SIMD), where 4-wave workgroups spread the waves
+    // evenly over each CU's four SIMDs and the VALU work that follows the
+    // loads ends sooner (the 256 x 4800 fp16 strided job: 3.8 against 4.2 us;
+    // from 512 rows one wave is ahead).
+    int64_t lane_count;  // WAVE only; rows * groups fits (it is at most y's extent)
+    if (__builtin_mul_overflow(rows * groups, (int64_t)lanes, &lane_count)) lane_count = INT64_MAX;
+    const int64_t waves = lane_count / 64 + (lane_count % 64 != 0);
+    bool four = kernel == GGRMS_KERNEL_WAVE && packed && waves <= kWaveFourMaxWaves;
+    if (flags & (GGRMS_FLAG_WAVE_ONE | GGRMS_FLAG_ORDER_BANDED)) four = false;
+    if (kernel == GGRMS_KERNEL_WAVE && (flags & GGRMS_FLAG_WAVE_FOUR)) four = true;
+    int block = four ? kWaveBlock : kWaveBlockOneWave;
+    plan->pub.block_threads = block;
+    // Tile order: XCD-banded when each group has its own weights and the
+    // row-major order would not keep every XCD on a fixed set of columns
+    // (tile columns per row not a multiple of 8); it takes one-wave WAVE
+    // workgroups.
+    int64_t R1, C1;
+    launch_tiles(*plan, rows, &R1, &C1);
+    plan->xband = kernel != GGRMS_KERNEL_WIDE && !four && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) &&
+                  C1 % kXcds != 0;
+    if (flags & GGRMS_FLAG_ORDER_ROWS) plan->xband = false;
+    if ((flags & GGRMS_FLAG_ORDER_BANDED) && kernel != GGRMS_KERNEL_WIDE) plan->xband = true;
     if (kernel == GGRMS_KERNEL_BLOCK) block = lanes * upb;
     if (kernel == GGRMS_KERNEL_WIDE) block = kWideBlock;
-    // Units per launch stay below 2^31 and so do threads per launch, so the
-    // kernels index with 32-bit integers; larger jobs are split by rows.
-    const int64_t thread_per_unit = kernel == GGRMS_KERNEL_WIDE ? kWideBlock : lanes;
-    const int64_t max_units = ((int64_t)1 << 31) / thread_per_unit;
-    int64_t rows_per_launch = max_units / groups;
+    plan->pub.block_threads = block;
+    // Threads per row of the grid.  Each launch stays within 2^31 threads
+    // (so within 2^31 units and tiles too) and the kernels index with 32-bit
+    // integers; larger jobs are split by rows.
+    int64_t row_threads = groups * (kernel == GGRMS_KERNEL_WIDE ? kWideBlock : lanes);
+    if (kernel == GGRMS_KERNEL_WAVE && plan->xband) row_threads = C1 * kWaveBlockOneWave;
+    int64_t rows_per_launch = ((int64_t)1 << 31) / row_threads;
     if (rows_per_launch < 1) return GGRMS_ERROR_INVALID_VALUE;  // one row alone too large
     if (rows_per_launch > rows) rows_per_launch = rows;
     const int64_t launches = (rows + rows_per_launch - 1) / rows_per_launch;
     int64_t workgroups = 0;
     for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
         const int64_t r = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
-        if (kernel == GGRMS_KERNEL_BLOCK)
-            workgroups += (r + upb - 1) / upb * groups;
-        else
-            workgroups += (r * groups * thread_per_unit + block - 1) / block;
+        workgroups += launch_workgroups(*plan, r);
     }
     plan->nvec = nvec;
     plan->rows_per_launch = rows_per_launch;
@@ -287,6 +316,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->pub.rows_per_workgroup = upb;
     plan->pub.lds_bytes = upb > 1 ? (int32_t)(group_size * 4) : 0;
     plan->pub.workgroups = workgroups;
+    plan->pub.tile_order = plan->xband ? 1 : 0;
     // Cache policy: stream large jobs, keep small ones cached.  The job is
     // 3 * rows * row_bytes bytes; rows * row_bytes is at most y's extent, so
     // it does not overflow, and comparing it with ceil(min / 3) is exact.

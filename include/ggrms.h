@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GGRMS_ABI_VERSION 3
+#define GGRMS_ABI_VERSION 4
 
 /* Element type shared by y, gate and out.  The weight is always f32. */
 typedef enum {
@@ -131,6 +131,8 @@ typedef struct {
     int32_t streaming;        /* 1: y/gate/out loads and stores carry the non-temporal hint */
     int32_t piece_bytes;      /* == vector_bytes when every group starts on a vector
                                  boundary; 2, 4 or 8 for packed groups (see below) */
+    int32_t tile_order;       /* order in which workgroups take the job's tiles:
+                                 0 row-major, 1 XCD-banded (see below) */
 } ggrms_plan_t;
 
 /*
@@ -145,6 +147,17 @@ typedef struct {
  * (each uses its own elements) and written in pieces of
  * piece_bytes = gcd(group bytes, 16), so no element is written twice and no
  * read leaves the row.
+ */
+
+/*
+ * Tile order.  Row-major: workgroup b takes the b-th tile (WAVE: the next
+ * units of the (row, group) sequence; BLOCK: row tile b / groups, group
+ * b % groups).  XCD-banded, chosen when every group has its own weights and
+ * a row's tiles are not a multiple of 8: the tiles are taken in blocks of 8
+ * rows, and the part's 8 XCDs (workgroup b runs on XCD b % 8) each take a
+ * band of about 1/8 of the columns of every block, so each XCD reads the
+ * weights of its band only, while the tiles in flight still cover a
+ * contiguous run of rows.  Results are identical in either order.
  */
 
 /*
@@ -182,7 +195,19 @@ typedef enum {
      * CACHE_STREAM forces the hint, CACHE_KEEP forces plain accesses; setting
      * both is GGRMS_ERROR_INVALID_VALUE.  Results are identical either way. */
     GGRMS_FLAG_CACHE_STREAM = 8,
-    GGRMS_FLAG_CACHE_KEEP = 16
+    GGRMS_FLAG_CACHE_KEEP = 16,
+    /* Launch controls, for tuning and cross-checks; results are identical
+     * whatever they select.  ORDER_ROWS / ORDER_BANDED force the tile order
+     * (plan field tile_order; BANDED has no effect on WIDE).  WAVE_ONE /
+     * WAVE_FOUR force WAVE workgroups of one or four waves (by default one,
+     * but four for small jobs of packed groups).  The banded order takes
+     * one-wave WAVE workgroups.  ORDER_ROWS with ORDER_BANDED, WAVE_ONE
+     * with WAVE_FOUR and ORDER_BANDED with WAVE_FOUR are
+     * GGRMS_ERROR_INVALID_VALUE. */
+    GGRMS_FLAG_ORDER_ROWS = 32,
+    GGRMS_FLAG_ORDER_BANDED = 64,
+    GGRMS_FLAG_WAVE_ONE = 128,
+    GGRMS_FLAG_WAVE_FOUR = 256
 } ggrms_flag_t;
 
 /* Job size (bytes of y, gate and out together) from which the default cache

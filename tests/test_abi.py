@@ -43,7 +43,7 @@ def test_header_symbols_exported(g):
 
 
 def test_abi_version_and_strings(g):
-    assert g.ggrms_abi_version() == 3
+    assert g.ggrms_abi_version() == 4
     for st in range(4):
         assert g.ggrms_status_string(st)
     assert g.ggrms_status_string(99) == "unknown status"
@@ -117,6 +117,7 @@ def test_interleaved_views_do_not_overlap(g):
 
 
 RI, NBG, PER_GROUP, STREAM, KEEP = 1, 2, 4, 8, 16
+ROWS, BANDED, WAVE1, WAVE4 = 32, 64, 128, 256
 
 
 def _plan_ex(g, flags, shape=None, **kw):
@@ -132,8 +133,9 @@ def _plan_ex(g, flags, shape=None, **kw):
     return st, plan
 
 
-@pytest.mark.parametrize("flags", [32, 1 << 31, RI | NBG, RI | NBG | PER_GROUP,
-                                   STREAM | KEEP, RI | STREAM | KEEP])
+@pytest.mark.parametrize("flags", [512, 1 << 31, RI | NBG, RI | NBG | PER_GROUP,
+                                   STREAM | KEEP, RI | STREAM | KEEP, ROWS | BANDED,
+                                   WAVE1 | WAVE4, BANDED | WAVE4, RI | ROWS | BANDED])
 def test_invalid_flags(g, flags):
     assert _plan_ex(g, flags)[0] == INVALID
 
@@ -155,6 +157,58 @@ def test_valid_flags_plan_like_the_default(g, flags):
     assert p["streaming"] == (1 if flags & STREAM else 0)
     p.pop("streaming"), ref.pop("streaming")
     assert p == ref
+
+
+def test_tile_order_and_wave_workgroups(g):
+    """The XCD-banded order is taken when every group has its own weights and a
+    row's tiles are not a multiple of 8; WAVE workgroups are one wave, except for
+    small jobs of packed groups; the launch controls force either."""
+    kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
+
+    def plan(flags, rows, width, G, dtype=BF16, stride=None, **more):
+        st, p = _plan_ex(g, flags, rows=rows, width=width, group_size=G,
+                         y_row_stride=stride or width, gate_row_stride=stride or width,
+                         out_row_stride=width, dtype=dtype, **{**kw, **more})
+        assert st == OK, (flags, rows, width, G)
+        return p
+
+    # 60 groups of 128 bf16 per row, 4 per wave: 15 waves per row -> banded, one tile per wave
+    p = plan(RI, 8192, 7680, 128)
+    assert (p["kernel_name"], p["tile_order"], p["block_threads"], p["workgroups"]) == \
+        ("wave", 1, 64, 8192 * 15)
+    # the same groups sharing one weight: row-major, one wave per workgroup
+    p = plan(RI | PER_GROUP, 8192, 7680, 128)
+    assert (p["tile_order"], p["block_threads"], p["workgroups"]) == (0, 64, 8192 * 60 // 4)
+    # forced row-major order and 4-wave workgroups
+    p = plan(RI | ROWS | WAVE4, 8192, 7680, 128)
+    assert (p["tile_order"], p["block_threads"], p["workgroups"]) == (0, 256, 8192 * 60 // 16)
+    # a partial last tile per row: 7 groups of 128 -> 2 waves per row, the second half idle
+    p = plan(RI, 100, 896, 128)
+    assert (p["tile_order"], p["workgroups"]) == (1, 100 * 2)
+    # BLOCK, 10 groups of 768 bf16 (2 rows per workgroup): banded over 32 x 10 tiles
+    p = plan(RI, 64, 7680, 768)
+    assert (p["kernel_name"], p["rows_per_workgroup"], p["tile_order"], p["workgroups"]) == \
+        ("block", 2, 1, 32 * 10)
+    # 8 groups of 960: a multiple of 8 tiles per row -> row-major; banded if forced
+    assert plan(RI, 8192, 7680, 960)["tile_order"] == 0
+    p = plan(RI | BANDED, 8192, 7680, 960)
+    assert (p["tile_order"], p["workgroups"]) == (1, 8192 // 4 * 8)
+    # WIDE is always row-major
+    assert plan(RI | BANDED, 4, 3 * 40960, 40960)["tile_order"] == 0
+    # packed groups: small jobs (<= 4096 waves) take 4-wave workgroups in row-major order,
+    # larger ones one wave, banded (12 waves per row)
+    fused = dict(y=A, gate=A + 9600)
+    p = plan(RI, 256, 4800, 100, F16, stride=9856, **fused)
+    assert (p["piece_bytes"], p["block_threads"], p["tile_order"]) == (8, 256, 0)
+    p = plan(RI, 1024, 4800, 100, F16, stride=9856, **fused)
+    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 1, 1024 * 12)
+    p = plan(RI | BANDED, 256, 4800, 100, F16, stride=9856, **fused)
+    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 1, 256 * 12)
+    p = plan(RI | WAVE1, 256, 4800, 100, F16, stride=9856, **fused)
+    assert (p["block_threads"], p["tile_order"]) == (64, 1)
+    # one row: banded over the row's tiles (XCD x takes a run of columns)
+    p = plan(RI, 1, 7680, 128)
+    assert (p["tile_order"], p["workgroups"]) == (1, 15)
 
 
 def test_cache_policy_by_job_size(g):
@@ -230,19 +284,22 @@ def test_plans_for_the_workloads(g):
     # 16384x8192 fp16, G = 128: 16 vectors -> 16-lane segments, four groups per wave
     p = _plan(g, 16384, 8192, 128, F16)
     assert (p["kernel_name"], p["vector_bytes"], p["lanes_per_group"], p["vectors_per_lane"]) == ("wave", 16, 16, 1)
-    # a weight per column: 4-wave workgroups (4 x 16 groups); the head scale shared by
-    # every group: one wave per workgroup (16384 * 64 / 4 workgroups)
-    assert (p["block_threads"], p["workgroups"]) == (256, 16384 * 64 // 16)
+    # one wave per workgroup (4 groups each), row-major: a row's 16 waves are a multiple
+    # of 8, so every XCD already keeps to two of them (a weight per column); with the head
+    # scale shared by every group the order does not matter either
+    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (64, 16384 * 16, 0)
     st, p = _plan_ex(g, PER_GROUP, rows=16384, width=8192, group_size=128, y_row_stride=8192,
                      gate_row_stride=8192, out_row_stride=8192, dtype=F16, gate=A + (1 << 30),
                      norm_weight=A + (2 << 30), out=A + (3 << 30))
-    assert st == OK and (p["block_threads"], p["workgroups"]) == (64, 16384 * 64 // 4)
+    assert st == OK and (p["block_threads"], p["workgroups"], p["tile_order"]) == (64, 16384 * 16, 0)
     # 256x4800 fp16 slices of a [256, 9856] buffer, G = 100: 200-byte groups in 9600-byte
     # rows -> packed: 16-byte vectors from the row start, boundary vectors in 8-byte pieces;
     # a group touches at most ceil((8 + 200) / 16) = 13 vectors -> 16-lane segments
     p = _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)
     assert (p["kernel_name"], p["vector_bytes"], p["piece_bytes"], p["lanes_per_group"]) == \
         ("wave", 16, 8, 16)
+    # a small job of packed groups (3072 waves): 4-wave workgroups, row-major
+    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (256, 256 * 48 * 16 // 256, 0)
     # tiny f32, G = 64: 16 vectors
     p = _plan(g, 4, 256, 64, F32)
     assert (p["vector_bytes"], p["lanes_per_group"]) == (16, 16)

@@ -209,13 +209,13 @@ def test_nbg_strided_and_in_place(g, orc):
 
 
 def test_nbg_rejections(g):
-    """Round-intermediate with norm-first, both cache policies at once and
-    unknown flag bits are refused before any launch; the output is left
-    untouched."""
+    """Round-intermediate with norm-first, both cache policies at once, both
+    tile orders or both WAVE workgroup sizes at once, and unknown flag bits
+    are refused before any launch; the output is left untouched."""
     yd = torch.ones(4 * 256, dtype=torch.bfloat16, device="cuda")
     wd = torch.ones(256, dtype=torch.float32, device="cuda")
     od = torch.full_like(yd, 7.0)
-    for flags in (FLAG_RI | FLAG_NBG, 8 | 16, 32, 1 << 20):
+    for flags in (FLAG_RI | FLAG_NBG, 8 | 16, 32 | 64, 128 | 256, 512, 1 << 20):
         assert run_gpu(g, yd, yd, wd, od, 4, 256, 64, 256, 256, 256, 1e-5, BF16, 0,
                        flags=flags) == g.ERROR_INVALID_VALUE
     torch.cuda.synchronize()
