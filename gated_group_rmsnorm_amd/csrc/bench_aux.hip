@@ -9,9 +9,12 @@
 //   * a plain 16-byte vector copy of known size: the calibration that turns
 //     the FETCH_SIZE / WRITE_SIZE counters into HBM bytes;
 //   * the simplest kernel that moves a workload's bytes: two streams read and
-//     one written, 16-byte non-temporal accesses, two vectors per lane (the
-//     fastest plain form in a sweep of vector counts and cache hints) -- the
-//     practical ceiling the fused kernel is compared against.
+//     one written, 16-byte non-temporal accesses, one vector per lane,
+//     one-wave workgroups (the fastest plain form in a sweep of vectors per
+//     lane 1-4, workgroups of 64-1024 threads and cache hints: 0.82-0.83 of
+//     HBM peak at 377 MB, against 0.80-0.81 with 2 vectors per lane in
+//     256-thread workgroups) -- the practical ceiling the fused kernel is
+//     compared against.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,26 +38,17 @@ __global__ __launch_bounds__(256) void ggrms_bench_copy_kernel(const u32x4* __re
     if (i < n) dst[i] = src[i];
 }
 
-// c = a ^ b over n 16-byte vectors; each wave takes 128 consecutive vectors,
-// two per lane, loads all four before its two stores.
-__global__ __launch_bounds__(256) void ggrms_bench_stream3_kernel(const u32x4* __restrict__ a,
-                                                                  const u32x4* __restrict__ b,
-                                                                  u32x4* __restrict__ c,
-                                                                  uint64_t n) {
-    const uint64_t base = ((uint64_t)blockIdx.x * 4u + (threadIdx.x >> 6)) * 128u + (threadIdx.x & 63);
-    u32x4 x[2], y[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint64_t i = base + 64u * k;
-        if (i < n) {
-            x[k] = __builtin_nontemporal_load(a + i);
-            y[k] = __builtin_nontemporal_load(b + i);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint64_t i = base + 64u * k;
-        if (i < n) __builtin_nontemporal_store(x[k] ^ y[k], c + i);
+// c = a ^ b over n 16-byte vectors; a one-wave workgroup takes 64
+// consecutive vectors, one per lane.
+__global__ __launch_bounds__(64) void ggrms_bench_stream3_kernel(const u32x4* __restrict__ a,
+                                                                 const u32x4* __restrict__ b,
+                                                                 u32x4* __restrict__ c,
+                                                                 uint64_t n) {
+    const uint64_t i = (uint64_t)blockIdx.x * 64u + threadIdx.x;
+    if (i < n) {
+        const u32x4 x = __builtin_nontemporal_load(a + i);
+        const u32x4 y = __builtin_nontemporal_load(b + i);
+        __builtin_nontemporal_store(x ^ y, c + i);
     }
 }
 
@@ -96,14 +90,14 @@ extern "C" int ggrms_bench_stream3(const void* a, const void* b, void* c, int64_
         (uintptr_t)c % 16)
         return 1;
     const uint64_t n = (uint64_t)nbytes / 16;
-    const uint64_t blocks = (n + 511) / 512;
-    if (blocks > 0xFFFFFFFFull) return 1;
+    const uint64_t blocks = (n + 63) / 64;
+    if (blocks > 0xFFFFFFFFull / 64) return 1;  // work-items must fit in 32 bits
     const u32x4* pa = static_cast<const u32x4*>(a);
     const u32x4* pb = static_cast<const u32x4*>(b);
     u32x4* pc = static_cast<u32x4*>(c);
     void* args[] = {&pa, &pb, &pc, (void*)&n};
     return hipLaunchKernel(reinterpret_cast<const void*>(&ggrms_bench_stream3_kernel),
-                           dim3((uint32_t)blocks), dim3(256), args, 0,
+                           dim3((uint32_t)blocks), dim3(64), args, 0,
                            static_cast<hipStream_t>(stream)) == hipSuccess
                ? 0
                : 1;

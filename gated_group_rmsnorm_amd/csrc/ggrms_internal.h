@@ -28,9 +28,9 @@ struct KArgs {
     float Ginv;       // 1/G rounded to f32 (the normaliser multiplies by it)
     float eps;
     int32_t ri;       // round the intermediate (16-bit types only)
-    // XCD-banded tile order (xband set; WAVE with one-wave workgroups, and
-    // BLOCK).  A tile is one workgroup's work: WAVE, 64 / lanes consecutive
-    // groups of one row; BLOCK, one group of a row tile of UPB rows.  The
+    // XCD-banded tile order (xband set; WAVE and BLOCK).  A tile is one
+    // workgroup's work: WAVE, threads / lanes consecutive groups of one row;
+    // BLOCK, one group of a row tile of UPB rows.  The
     // launch's R x C tiles (R rows or row tiles, C tile columns) are taken in
     // blocks of 8 rows; inside a block, numbered column-major, XCD x takes
     // the C tiles x*C .. x*C + C-1, i.e. a band of about C/8 columns of 8 rows.
@@ -55,14 +55,9 @@ constexpr uint32_t kXcds = 8;
 // 1 for lanes < 64, 1..4 for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
 // vectors per lane 1..4.  WIDE: 1024 lanes, vectors per lane 0 (it loops over
 // the group).  A WAVE workgroup is a single wave or 4 waves (the kernel takes
-// its size from the launch).  One wave's slot is freed the moment it
-// retires, instead of waiting for the slowest wave of its workgroup, which
-// keeps more loads in flight (128-wide fp16 groups sharing one weight: 0.83
-// against 0.815 of HBM peak); 4 waves are kept for small jobs of packed
-// groups (see the planner).
+// its size from the launch; the planner's rule says which).
 constexpr int kWaveBlock = 256;
 constexpr int kWaveBlockOneWave = 64;
-constexpr int64_t kWaveFourMaxWaves = 4096;  // 4 waves per SIMD on 256 CUs
 constexpr int kWideBlock = 1024;
 
 // Rows of one group per BLOCK workgroup (the workgroup stays <= 512 threads).
@@ -102,8 +97,8 @@ struct LaunchPlan {
     bool xband;               // XCD-banded tile order (KArgs::xband)
 };
 
-// WAVE: groups one wave covers (lanes <= 64).
-inline int64_t wave_groups_per_wave(int lanes) { return 64 / lanes; }
+// WAVE: groups one workgroup covers (lanes <= 64).
+inline int64_t wave_groups_per_workgroup(int lanes, int threads) { return threads / lanes; }
 
 // Tile rows and tile columns of one launch over r rows (see KArgs::xband);
 // a WAVE tile is one wave.
@@ -116,7 +111,7 @@ inline void launch_tiles(const LaunchPlan& lp, int64_t r, int64_t* R, int64_t* C
         *R = r;
         *C = lp.groups;
     } else {
-        const int64_t gpw = wave_groups_per_wave(p.lanes_per_group);
+        const int64_t gpw = wave_groups_per_workgroup(p.lanes_per_group, p.block_threads);
         *R = r;
         *C = (lp.groups + gpw - 1) / gpw;
     }
@@ -129,7 +124,7 @@ inline int64_t launch_workgroups(const LaunchPlan& lp, int64_t r) {
     case GGRMS_KERNEL_BLOCK:
         return (r + p.rows_per_workgroup - 1) / p.rows_per_workgroup * lp.groups;
     case GGRMS_KERNEL_WAVE: {
-        if (lp.xband) {  // one wave per tile, tiles of one row
+        if (lp.xband) {  // one workgroup per tile, tiles of one row
             int64_t R, C;
             launch_tiles(lp, r, &R, &C);
             return R * C;

@@ -540,17 +540,17 @@ __device__ inline void xcd_band_tile(const KArgs& a, uint32_t& rt, uint32_t& c) 
 }
 
 // WAVE: SEG (<= 64) lanes per unit, workgroups of 64 or 256 threads (the
-// launch's choice), no LDS, no barrier.  Row-major order: each wave takes
-// the next 64 / SEG units of the (row, group) sequence.  XCD-banded order
-// (one wave per workgroup): the wave takes 64 / SEG consecutive groups of one
-// row.
+// launch's choice), no LDS, no barrier.  Row-major order: each workgroup
+// takes the next threads / SEG units of the (row, group) sequence.
+// XCD-banded order: the workgroup takes threads / SEG consecutive groups of
+// one row.
 template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
     uint32_t n, g;
     if (a.xband) {
         uint32_t c;
         xcd_band_tile(a, n, c);
-        g = c * (64 / SEG) + threadIdx.x / SEG;
+        g = c * (blockDim.x / SEG) + threadIdx.x / SEG;
         if (g >= a.groups) return;  // the row's last tile may be partial
     } else {
         const uint32_t unit = (blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) / SEG;

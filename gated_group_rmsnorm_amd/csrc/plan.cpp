@@ -67,10 +67,11 @@ int kernel_for_shape(int lanes, int vpt) {
 // group widths 8..32768, plus fp16 and f32 spot checks), timed after the
 // clocks settle:
 //   * up to 64 vectors: one vector per lane, the smallest power-of-two lane
-//     segment, several groups per wave (WAVE kernel, 77-80% of HBM peak);
-//   * 65-72: one wave, two vectors per lane (65-74%, the same as 128 lanes);
-//   * 73-768: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
-//     workgroup sharing staged weights (78-81%); 4 rows only with one vector
+//     segment, several groups per wave (WAVE kernel, 80-83% of HBM peak);
+//   * 65-80: one wave, two vectors per lane (67-77%; 128 lanes: 64-75%);
+//   * 81-96: two waves, one vector per lane, one row per workgroup (79-80%);
+//   * 97-768: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
+//     workgroup sharing staged weights (75-81%); 4 rows only with one vector
 //     per lane, since the staging registers cost occupancy at 2+;
 //   * 769-4096: 256-1024 lanes x 3-4 vectors, one row per workgroup (staging
 //     at 4 vectors per lane measured 46-59% against 77% without); three
@@ -81,8 +82,8 @@ struct ShapeRule {
     int kernel, lanes, vpt, upb;
 };
 const ShapeRule kRules[] = {
-    {72, GGRMS_KERNEL_WAVE, 64, 2, 1},
-    {96, GGRMS_KERNEL_BLOCK, 128, 1, 2},
+    {80, GGRMS_KERNEL_WAVE, 64, 2, 1},
+    {96, GGRMS_KERNEL_BLOCK, 128, 1, 1},
     {128, GGRMS_KERNEL_BLOCK, 128, 1, 4},
     {192, GGRMS_KERNEL_BLOCK, 128, 2, 2},
     {256, GGRMS_KERNEL_BLOCK, 256, 1, 2},
@@ -146,8 +147,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
                            GGRMS_FLAG_ORDER_BANDED | GGRMS_FLAG_WAVE_ONE | GGRMS_FLAG_WAVE_FOUR;
     if (flags & ~known) return GGRMS_ERROR_INVALID_VALUE;
     if (((flags & GGRMS_FLAG_ORDER_ROWS) && (flags & GGRMS_FLAG_ORDER_BANDED)) ||
-        ((flags & GGRMS_FLAG_WAVE_ONE) && (flags & GGRMS_FLAG_WAVE_FOUR)) ||
-        ((flags & GGRMS_FLAG_ORDER_BANDED) && (flags & GGRMS_FLAG_WAVE_FOUR)))
+        ((flags & GGRMS_FLAG_WAVE_ONE) && (flags & GGRMS_FLAG_WAVE_FOUR)))
         return GGRMS_ERROR_INVALID_VALUE;
     if ((flags & GGRMS_FLAG_ROUND_INTERMEDIATE) && (flags & GGRMS_FLAG_NORM_BEFORE_GATE))
         return GGRMS_ERROR_INVALID_VALUE;
@@ -264,27 +264,28 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->pub.kernel = kernel;
     plan->pub.lanes_per_group = lanes;
     plan->pub.rows_per_workgroup = upb;
-    // WAVE workgroups: one wave, except for a small job of packed groups
-    // (at most 4 waves per SIMD), where 4-wave workgroups spread the waves
-    // evenly over each CU's four SIMDs and the VALU work that follows the
-    // loads ends sooner (the 256 x 4800 fp16 strided job: 3.8 against 4.2 us;
-    // from 512 rows one wave is ahead).
-    int64_t lane_count;  // WAVE only; rows * groups fits (it is at most y's extent)
-    if (__builtin_mul_overflow(rows * groups, (int64_t)lanes, &lane_count)) lane_count = INT64_MAX;
-    const int64_t waves = lane_count / 64 + (lane_count % 64 != 0);
-    bool four = kernel == GGRMS_KERNEL_WAVE && packed && waves <= kWaveFourMaxWaves;
-    if (flags & (GGRMS_FLAG_WAVE_ONE | GGRMS_FLAG_ORDER_BANDED)) four = false;
+    // WAVE workgroups: one wave for 16-byte vectors, whose slot is freed the
+    // moment it retires (128-wide groups: 0.83 against 0.79 of HBM peak with
+    // four); four waves for narrower vectors, which need 2-4x the workgroups
+    // for the same bytes (4-byte vectors: 96 against 107 us with one), and for
+    // packed groups, whose extra VALU work after the loads ends sooner when
+    // each CU's four SIMDs hold one wave of every workgroup (the 256 x 4800
+    // fp16 strided job: 3.8 against 4.2 us).
+    bool four = kernel == GGRMS_KERNEL_WAVE && (packed || vb < 16);
+    if (flags & GGRMS_FLAG_WAVE_ONE) four = false;
     if (kernel == GGRMS_KERNEL_WAVE && (flags & GGRMS_FLAG_WAVE_FOUR)) four = true;
     int block = four ? kWaveBlock : kWaveBlockOneWave;
     plan->pub.block_threads = block;
     // Tile order: XCD-banded when each group has its own weights and the
-    // row-major order would not keep every XCD on a fixed set of columns
-    // (tile columns per row not a multiple of 8); it takes one-wave WAVE
-    // workgroups.
+    // row-major order would not keep every XCD on a fixed set of columns --
+    // i.e. unless a row is a whole multiple of 8 workgroups (row-major WAVE
+    // workgroups take a linear run of units, so rows line up with them only
+    // if the groups per workgroup divide the row).
     int64_t R1, C1;
     launch_tiles(*plan, rows, &R1, &C1);
-    plan->xband = kernel != GGRMS_KERNEL_WIDE && !four && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) &&
-                  C1 % kXcds != 0;
+    const int64_t gpw = kernel == GGRMS_KERNEL_WAVE ? wave_groups_per_workgroup(lanes, block) : 1;
+    plan->xband = kernel != GGRMS_KERNEL_WIDE && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) &&
+                  groups % (kXcds * gpw) != 0;
     if (flags & GGRMS_FLAG_ORDER_ROWS) plan->xband = false;
     if ((flags & GGRMS_FLAG_ORDER_BANDED) && kernel != GGRMS_KERNEL_WIDE) plan->xband = true;
     if (kernel == GGRMS_KERNEL_BLOCK) block = lanes * upb;
@@ -294,7 +295,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     // (so within 2^31 units and tiles too) and the kernels index with 32-bit
     // integers; larger jobs are split by rows.
     int64_t row_threads = groups * (kernel == GGRMS_KERNEL_WIDE ? kWideBlock : lanes);
-    if (kernel == GGRMS_KERNEL_WAVE && plan->xband) row_threads = C1 * kWaveBlockOneWave;
+    if (kernel == GGRMS_KERNEL_WAVE && plan->xband) row_threads = C1 * block;
     int64_t rows_per_launch = ((int64_t)1 << 31) / row_threads;
     if (rows_per_launch < 1) return GGRMS_ERROR_INVALID_VALUE;  // one row alone too large
     if (rows_per_launch > rows) rows_per_launch = rows;

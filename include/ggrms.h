@@ -199,11 +199,10 @@ typedef enum {
     /* Launch controls, for tuning and cross-checks; results are identical
      * whatever they select.  ORDER_ROWS / ORDER_BANDED force the tile order
      * (plan field tile_order; BANDED has no effect on WIDE).  WAVE_ONE /
-     * WAVE_FOUR force WAVE workgroups of one or four waves (by default one,
-     * but four for small jobs of packed groups).  The banded order takes
-     * one-wave WAVE workgroups.  ORDER_ROWS with ORDER_BANDED, WAVE_ONE
-     * with WAVE_FOUR and ORDER_BANDED with WAVE_FOUR are
-     * GGRMS_ERROR_INVALID_VALUE. */
+     * WAVE_FOUR force WAVE workgroups of one or four waves (by default one
+     * for 16-byte vectors, four for narrower vectors and packed groups;
+     * no effect on BLOCK and WIDE).  ORDER_ROWS with ORDER_BANDED and
+     * WAVE_ONE with WAVE_FOUR are GGRMS_ERROR_INVALID_VALUE. */
     GGRMS_FLAG_ORDER_ROWS = 32,
     GGRMS_FLAG_ORDER_BANDED = 64,
     GGRMS_FLAG_WAVE_ONE = 128,

@@ -135,7 +135,7 @@ def _plan_ex(g, flags, shape=None, **kw):
 
 @pytest.mark.parametrize("flags", [512, 1 << 31, RI | NBG, RI | NBG | PER_GROUP,
                                    STREAM | KEEP, RI | STREAM | KEEP, ROWS | BANDED,
-                                   WAVE1 | WAVE4, BANDED | WAVE4, RI | ROWS | BANDED])
+                                   WAVE1 | WAVE4, RI | ROWS | BANDED, RI | WAVE1 | WAVE4])
 def test_invalid_flags(g, flags):
     assert _plan_ex(g, flags)[0] == INVALID
 
@@ -160,9 +160,10 @@ def test_valid_flags_plan_like_the_default(g, flags):
 
 
 def test_tile_order_and_wave_workgroups(g):
-    """The XCD-banded order is taken when every group has its own weights and a
-    row's tiles are not a multiple of 8; WAVE workgroups are one wave, except for
-    small jobs of packed groups; the launch controls force either."""
+    """WAVE workgroups are one wave for 16-byte vectors and four waves for
+    narrower vectors and packed groups; the XCD-banded order is taken when every
+    group has its own weights and a row's tiles (one per workgroup) are not a
+    multiple of 8; the launch controls force either."""
     kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
 
     def plan(flags, rows, width, G, dtype=BF16, stride=None, **more):
@@ -176,36 +177,52 @@ def test_tile_order_and_wave_workgroups(g):
     p = plan(RI, 8192, 7680, 128)
     assert (p["kernel_name"], p["tile_order"], p["block_threads"], p["workgroups"]) == \
         ("wave", 1, 64, 8192 * 15)
-    # the same groups sharing one weight: row-major, one wave per workgroup
+    # the same groups sharing one weight: row-major
     p = plan(RI | PER_GROUP, 8192, 7680, 128)
     assert (p["tile_order"], p["block_threads"], p["workgroups"]) == (0, 64, 8192 * 60 // 4)
-    # forced row-major order and 4-wave workgroups
+    # forced row-major order and 4-wave workgroups: a row-major run of 16 units each
     p = plan(RI | ROWS | WAVE4, 8192, 7680, 128)
     assert (p["tile_order"], p["block_threads"], p["workgroups"]) == (0, 256, 8192 * 60 // 16)
-    # a partial last tile per row: 7 groups of 128 -> 2 waves per row, the second half idle
+    # forced banded with 4-wave workgroups: tiles of 16 groups, 4 per row (the last 3/4 full)
+    p = plan(RI | BANDED | WAVE4, 8192, 7680, 128)
+    assert (p["tile_order"], p["block_threads"], p["workgroups"]) == (1, 256, 8192 * 4)
+    # a partial last tile per row: 7 groups of 128 -> 2 waves per row, the second 3/4 full
     p = plan(RI, 100, 896, 128)
     assert (p["tile_order"], p["workgroups"]) == (1, 100 * 2)
-    # BLOCK, 10 groups of 768 bf16 (2 rows per workgroup): banded over 32 x 10 tiles
-    p = plan(RI, 64, 7680, 768)
+    # 8-byte vectors (rows padded by 4 bf16): 4-wave workgroups of 8 groups; 60 groups are
+    # 7.5 of them, so row-major workgroups would straddle rows -> banded, 8 tiles per row
+    # (the last half full)
+    p = plan(RI, 1024, 7680, 128, stride=7684)
+    assert (p["vector_bytes"], p["block_threads"], p["tile_order"], p["workgroups"]) == \
+        (8, 256, 1, 1024 * 8)
+    # 64 such groups: exactly 8 workgroups per row -> row-major
+    p = plan(RI, 1024, 8192, 128, stride=8196)
+    assert (p["vector_bytes"], p["block_threads"], p["tile_order"], p["workgroups"]) == \
+        (8, 256, 0, 1024 * 8)
+    # 4-byte vectors: 64 lanes per group, 4 groups per workgroup, 15 tiles -> banded
+    p = plan(RI, 1024, 7680, 128, stride=7682)
+    assert (p["vector_bytes"], p["block_threads"], p["tile_order"], p["workgroups"]) == \
+        (4, 256, 1, 1024 * 15)
+    # BLOCK, 9 groups of 832 bf16 (4 rows per workgroup): banded over 16 x 9 tiles
+    p = plan(RI, 64, 7488, 832)
     assert (p["kernel_name"], p["rows_per_workgroup"], p["tile_order"], p["workgroups"]) == \
-        ("block", 2, 1, 32 * 10)
+        ("block", 4, 1, 16 * 9)
     # 8 groups of 960: a multiple of 8 tiles per row -> row-major; banded if forced
     assert plan(RI, 8192, 7680, 960)["tile_order"] == 0
     p = plan(RI | BANDED, 8192, 7680, 960)
     assert (p["tile_order"], p["workgroups"]) == (1, 8192 // 4 * 8)
     # WIDE is always row-major
     assert plan(RI | BANDED, 4, 3 * 40960, 40960)["tile_order"] == 0
-    # packed groups: small jobs (<= 4096 waves) take 4-wave workgroups in row-major order,
-    # larger ones one wave, banded (12 waves per row)
+    # packed groups (200-byte groups of the strided layout): 4-wave workgroups of 16
+    # groups, 3 per row -> banded; one wave if forced
     fused = dict(y=A, gate=A + 9600)
     p = plan(RI, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["piece_bytes"], p["block_threads"], p["tile_order"]) == (8, 256, 0)
-    p = plan(RI, 1024, 4800, 100, F16, stride=9856, **fused)
-    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 1, 1024 * 12)
-    p = plan(RI | BANDED, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 1, 256 * 12)
+    assert (p["piece_bytes"], p["block_threads"], p["tile_order"], p["workgroups"]) == \
+        (8, 256, 1, 256 * 3)
     p = plan(RI | WAVE1, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["block_threads"], p["tile_order"]) == (64, 1)
+    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 1, 256 * 12)
+    p = plan(RI | ROWS, 256, 4800, 100, F16, stride=9856, **fused)
+    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (256, 0, 256 * 48 * 16 // 256)
     # one row: banded over the row's tiles (XCD x takes a run of columns)
     p = plan(RI, 1, 7680, 128)
     assert (p["tile_order"], p["workgroups"]) == (1, 15)
@@ -298,8 +315,8 @@ def test_plans_for_the_workloads(g):
     p = _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)
     assert (p["kernel_name"], p["vector_bytes"], p["piece_bytes"], p["lanes_per_group"]) == \
         ("wave", 16, 8, 16)
-    # a small job of packed groups (3072 waves): 4-wave workgroups, row-major
-    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (256, 256 * 48 * 16 // 256, 0)
+    # packed groups: 4-wave workgroups of 16 groups, 3 per row -> banded
+    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (256, 256 * 3, 1)
     # tiny f32, G = 64: 16 vectors
     p = _plan(g, 4, 256, 64, F32)
     assert (p["vector_bytes"], p["lanes_per_group"]) == (16, 16)
@@ -426,8 +443,10 @@ def test_kernel_family_by_group_width(g):
         64: ("wave", 8, 1, 1),
         512: ("wave", 64, 1, 1),      # 64
         576: ("wave", 64, 2, 1),      # 72
-        640: ("block", 128, 1, 2),    # 80
-        768: ("block", 128, 1, 2),    # 96
+        640: ("wave", 64, 2, 1),      # 80
+        648: ("block", 128, 1, 1),    # 81
+        768: ("block", 128, 1, 1),    # 96
+        776: ("block", 128, 1, 4),    # 97
         960: ("block", 128, 1, 4),    # 120
         1032: ("block", 128, 2, 4 // 2),  # 129
         1536: ("block", 128, 2, 2),   # 192

@@ -44,30 +44,35 @@ def orc():
 CASES = [
     (BF16, 128, 60, 37, FLAG_RI),     # WAVE 16 lanes: 15 tiles per row, 4 full 8-row blocks + 5
     (BF16, 128, 7, 9, FLAG_RI),       # 2 tiles per row, the second 3/4 full
+    (BF16, 128, 60, 13, FLAG_RI, 4),  # 8-byte vectors (rows padded): 4-wave workgroups
+    (BF16, 128, 60, 11, FLAG_RI, 2),  # 4-byte vectors
     (BF16, 8, 100, 19, FLAG_RI),      # WAVE 1 lane: 64 groups per wave, second tile 36/64 full
     (BF16, 512, 9, 17, FLAG_RI),      # WAVE 64 x 1
     (BF16, 576, 13, 11, FLAG_RI),     # WAVE 64 x 2
-    (BF16, 768, 10, 33, FLAG_RI),     # BLOCK 128 x 1, 2 rows per workgroup: 17 row tiles
+    (BF16, 768, 10, 19, FLAG_RI),     # BLOCK 128 x 1, one row per workgroup
+    (BF16, 832, 9, 33, FLAG_RI),      # BLOCK 128 x 1, 4 rows per workgroup: 9 row tiles
     (BF16, 1280, 6, 20, FLAG_RI),     # BLOCK 128 x 2, 2 rows per workgroup
     (BF16, 4096, 3, 8, FLAG_RI),      # BLOCK 256 x 2, one full block
     (F32, 64, 20, 10, 0),             # f32, 16 lanes
     (F16, 128, 60, 12, FLAG_NBG),     # norm first, per-column weight
-    (F16, 100, 48, 300, FLAG_RI),     # packed groups (200 bytes): 4-wave workgroups by default
-    (F16, 100, 48, 1100, FLAG_RI),    # packed groups, a larger job: banded by default
+    (F16, 100, 48, 300, FLAG_RI),     # packed groups (200 bytes): banded 4-wave workgroups
+    (F16, 100, 48, 1100, FLAG_RI),    # packed groups, a larger job
     (BF16, 128, 60, 21, FLAG_RI | FLAG_PER_GROUP),  # shared weight: row-major by default
 ]
-VARIANTS = [ROWS, ROWS | WAVE4, ROWS | WAVE1, BANDED, BANDED | WAVE1, WAVE1, WAVE4]
+VARIANTS = [ROWS, ROWS | WAVE4, ROWS | WAVE1, BANDED, BANDED | WAVE1, BANDED | WAVE4, WAVE1, WAVE4]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{DT_IDS[c[0]]}-G{c[1]}x{c[2]}-r{c[3]}-f{c[4]}")
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{DT_IDS[c[0]]}-G{c[1]}x{c[2]}-r{c[3]}-f{c[4]}"
+                         + (f"-pad{c[5]}" if len(c) > 5 else ""))
 def test_tile_orders_agree_bitwise(g, orc, case):
-    dtype, G, groups, rows, op = case
+    dtype, G, groups, rows, op = case[:5]
     width = G * groups
+    sin = width + (case[5] if len(case) > 5 else 0)  # y/gate row stride: padding narrows the vectors
     esz = 4 if dtype == F32 else 2
     pad = 16 // esz
     so = width + pad
     guard = 64
-    y, gt, w = random_case(rows, width, dtype, seed=G + 7 * groups + rows)
+    y, gt, w = random_case(rows, sin, dtype, seed=G + 7 * groups + rows)
     if op & FLAG_PER_GROUP:
         w = np.ascontiguousarray(w[:G])
     yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
@@ -83,21 +88,21 @@ def test_tile_orders_agree_bitwise(g, orc, case):
         od = dev_buf(ob, dtype)
         # (WAVE_ONE / WAVE_FOUR do nothing for BLOCK launches; nothing here is refused)
         st, p = g.ggrms_plan_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od[guard:].data_ptr(),
-                                rows, width, G, width, width, so, 1e-5, dtype, flags)
+                                rows, width, G, sin, sin, so, 1e-5, dtype, flags)
         assert st == g.SUCCESS, f"flags={flags}: {g.ggrms_status_string(st)}"
         say(f"case order {DT_IDS[dtype]} G={G} groups={groups} rows={rows} flags={flags} "
             f"kernel={p['kernel_name']} lanes={p['lanes_per_group']} block={p['block_threads']} "
             f"order={p['tile_order']} workgroups={p['workgroups']}")
         st = g.ggrms_forward_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od[guard:].data_ptr(),
-                                rows, width, G, width, width, so, 1e-5, dtype, flags, sp)
+                                rows, width, G, sin, sin, so, 1e-5, dtype, flags, sp)
         assert st == g.SUCCESS, g.ggrms_status_string(st)
         torch.cuda.synchronize()
         got = host_bits(od, dtype)
         assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
             f"flags={flags}: wrote outside the view"
         outs[extra] = (got, p["tile_order"], p["block_threads"])
-    ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
-                      gate_row_stride=width, out_row_stride=so, eps=1e-5, dtype=dtype,
+    ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=sin,
+                      gate_row_stride=sin, out_row_stride=so, eps=1e-5, dtype=dtype,
                       round_intermediate=op & FLAG_RI, norm_before_gate=bool(op & FLAG_NBG),
                       weight_per_group=bool(op & FLAG_PER_GROUP), out=ob.copy(), out_offset=guard)
     base = outs[0][0]
