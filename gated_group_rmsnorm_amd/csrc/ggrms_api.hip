@@ -44,21 +44,6 @@ const void* pick(int dtype, bool nbg, bool nt, int kernel, int vb, int pb, int l
     }
 }
 
-// The XCD-banded order's fields of KArgs for a launch over r rows.
-void set_band(const LaunchPlan& lp, int64_t r, KArgs* a) {
-    a->xband = lp.xband ? 1u : 0u;
-    int64_t R, C;
-    launch_tiles(lp, r, &R, &C);
-    a->xc = (uint32_t)C;
-    div_magic(a->xc, &a->xc_m, &a->xc_s);
-    a->xfullk = (uint32_t)(R / kXcds * C);
-    a->xfullrows = (uint32_t)(R / kXcds * kXcds);
-    a->xrr = (uint32_t)(R % kXcds ? R % kXcds : 1);
-    div_magic(a->xrr, &a->xrr_m, &a->xrr_s);
-    a->xq2 = (uint32_t)(R % kXcds * C / kXcds);
-    a->xr2 = (uint32_t)(R % kXcds * C % kXcds);
-}
-
 ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_weight, void* out,
                             int64_t rows, int64_t width, int64_t group_size, int64_t y_row_stride,
                             int64_t gate_row_stride, int64_t out_row_stride, float eps,
@@ -85,15 +70,22 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     a.sy = y_row_stride;
     a.sg = gate_row_stride;
     a.so = out_row_stride;
-    a.wgs = (flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? 0 : group_size;
     a.groups = (uint32_t)lp.groups;
-    div_magic(a.groups, &a.div_m, &a.div_s);
+    uint32_t div_s = 0, xc_s = 0;
+    div_magic(a.groups, &a.div_m, &div_s);
     a.G = (uint32_t)group_size;
     a.nvec = (uint32_t)lp.nvec;
-    a.Gf = (float)group_size;
     a.Ginv = (float)(1.0 / (double)group_size);
     a.eps = eps;
-    a.ri = (dtype != GGRMS_F32 && (flags & GGRMS_FLAG_ROUND_INTERMEDIATE)) ? 1 : 0;
+    // tile columns of the banded order (the same for every launch of the job)
+    int64_t R, C;
+    launch_tiles(lp, lp.rows_per_launch, &R, &C);
+    (void)R;
+    a.xc = (uint32_t)C;
+    div_magic(a.xc, &a.xc_m, &xc_s);
+    a.bits = (div_s << kBitDivShift) | (xc_s << kBitXcShift) |
+             ((dtype != GGRMS_F32 && (flags & GGRMS_FLAG_ROUND_INTERMEDIATE)) ? kBitRound : 0u) |
+             ((flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? kBitShared : 0u) | (lp.xband ? kBitBand : 0u);
     const int es = lp.esize;
 
     for (int64_t r0 = 0; r0 < rows; r0 += lp.rows_per_launch) {
@@ -101,10 +93,8 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
         a.y = static_cast<const char*>(y) + r0 * y_row_stride * es;
         a.gate = static_cast<const char*>(gate) + r0 * gate_row_stride * es;
         a.out = static_cast<char*>(out) + r0 * out_row_stride * es;
-        a.units = (uint32_t)(r * lp.groups);
         a.rows = (uint32_t)r;
         const int64_t blocks = launch_workgroups(lp, r);
-        set_band(lp, r, &a);
         void* args[] = {&a};
         if (hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3((uint32_t)p.block_threads), args,
                             (size_t)p.lds_bytes, s) != hipSuccess)

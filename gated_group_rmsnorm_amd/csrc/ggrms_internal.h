@@ -9,44 +9,51 @@
 namespace ggrms {
 
 // Kernel arguments, passed by value.  Pointers already include the row
-// offset of the launch chunk.  Strides are in elements.
+// offset of the launch chunk.  Strides are in elements.  Kept to 96 bytes:
+// the HIP runtime enqueues a launch whose arguments fit in 96 bytes ~0.5 us
+// faster than one with 128 or more (2.8 against 3.3-3.6 us of host time per
+// launch, which is what a decode step's launches cost), so whatever the
+// kernels can derive (units, the weight's stride between groups, the banded
+// order's block sizes) is derived on the device, and the flags and shifts
+// share one word.
+//
+// XCD-banded tile order (kBitBand; WAVE and BLOCK).  A tile is one
+// workgroup's work: WAVE, threads / lanes consecutive groups of one row;
+// BLOCK, one group of a row tile of UPB rows.  The launch's R x C tiles (R
+// rows or row tiles, C = xc tile columns) are taken in blocks of 8 rows;
+// inside a block, numbered column-major, XCD x takes the C tiles x*C ..
+// x*C + C-1, i.e. a band of about C/8 columns of 8 rows.  Workgroups are dealt
+// to the 8 XCDs in turn (workgroup b runs on XCD b % 8) and all XCDs move
+// through the blocks at the same pace, so the tiles in flight still cover a
+// contiguous run of rows -- the HBM access pattern of the row-major order --
+// while each XCD reads the weights of only its band, which then stay in its
+// L2 and its CUs' L1.  The last R % 8 rows form a short block, shared out the
+// same way.
 struct KArgs {
     const void* y;
     const void* gate;
     const float* w;
     void* out;
     int64_t sy, sg, so;
-    int64_t wgs;      // weight offset per group: G (one weight per column) or 0 (shared)
-    uint32_t units;   // (row, group) units in this launch
     uint32_t rows;    // rows in this launch
     uint32_t groups;  // groups per row
-    uint32_t div_m;   // magic multiplier for x / groups
-    uint32_t div_s;   // shift for x / groups
     uint32_t G;       // group size in elements
     uint32_t nvec;    // vectors per group
-    float Gf;         // (float)G
+    uint32_t div_m;   // magic multiplier for x / groups (shift in bits)
+    uint32_t xc;      // banded order: tile columns C
+    uint32_t xc_m;    // magic multiplier for x / C (shift in bits)
     float Ginv;       // 1/G rounded to f32 (the normaliser multiplies by it)
     float eps;
-    int32_t ri;       // round the intermediate (16-bit types only)
-    // XCD-banded tile order (xband set; WAVE and BLOCK).  A tile is one
-    // workgroup's work: WAVE, threads / lanes consecutive groups of one row;
-    // BLOCK, one group of a row tile of UPB rows.  The
-    // launch's R x C tiles (R rows or row tiles, C tile columns) are taken in
-    // blocks of 8 rows; inside a block, numbered column-major, XCD x takes
-    // the C tiles x*C .. x*C + C-1, i.e. a band of about C/8 columns of 8 rows.
-    // Workgroups are dealt to the 8 XCDs in turn (workgroup b runs on XCD
-    // b % 8) and all XCDs move through the blocks at the same pace, so the
-    // tiles in flight still cover a contiguous run of rows -- the HBM access
-    // pattern of the row-major order -- while each XCD reads the weights of
-    // only its band, which then stay in its L2 and its CUs' L1.  The last
-    // R % 8 rows form a short block, shared out the same way.
-    uint32_t xband;
-    uint32_t xc, xc_m, xc_s;        // C and its magic numbers
-    uint32_t xfullk;                // workgroups per XCD in the full blocks: (R / 8) * C
-    uint32_t xfullrows;             // rows in the full blocks: (R / 8) * 8
-    uint32_t xrr, xrr_m, xrr_s;     // rows in the short block (R % 8; 1 if none) and magic
-    uint32_t xq2, xr2;              // short block's tiles (R % 8) * C: / 8 and % 8
+    uint32_t bits;    // kBit* fields below
 };
+static_assert(sizeof(KArgs) == 96, "kernel arguments must stay within 96 bytes");
+
+// KArgs::bits
+constexpr uint32_t kBitDivShift = 0;      // 5 bits: shift for x / groups
+constexpr uint32_t kBitXcShift = 5;       // 5 bits: shift for x / C
+constexpr uint32_t kBitRound = 1u << 10;  // round the intermediate (16-bit types only)
+constexpr uint32_t kBitShared = 1u << 11; // one weight vector shared by every group
+constexpr uint32_t kBitBand = 1u << 12;   // XCD-banded tile order
 
 // Workgroups are dealt to XCDs in turn on the 8-XCD part.
 constexpr uint32_t kXcds = 8;

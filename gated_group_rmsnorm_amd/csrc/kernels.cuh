@@ -298,6 +298,35 @@ __device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t s) {
     return (__umulhi(n, m) + n) >> s;
 }
 
+// Fields of KArgs::bits, and what the kernels derive from the arguments.
+__device__ inline uint32_t div_shift(const KArgs& a) { return (a.bits >> kBitDivShift) & 31u; }
+__device__ inline uint32_t xc_shift(const KArgs& a) { return (a.bits >> kBitXcShift) & 31u; }
+__device__ inline bool round_intermediate(const KArgs& a) { return (a.bits & kBitRound) != 0; }
+__device__ inline bool banded(const KArgs& a) { return (a.bits & kBitBand) != 0; }
+// the weight's offset between groups: G (one weight per column) or 0 (shared)
+__device__ inline int64_t weight_group_stride(const KArgs& a) {
+    return (a.bits & kBitShared) ? 0 : (int64_t)a.G;
+}
+__device__ inline uint32_t row_div(const KArgs& a, uint32_t x) {  // x / groups
+    return fast_div(x, a.div_m, div_shift(a));
+}
+
+// Magic numbers for x / d, d = 1..7 (the short block of the banded order),
+// by the same round-up method as the host's: l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1.
+struct SmallMagic { uint32_t m[8], s[8]; };
+constexpr SmallMagic small_magic() {
+    SmallMagic r{};
+    for (uint32_t d = 1; d < 8; ++d) {
+        uint32_t l = 0;
+        while ((1u << l) < d) ++l;
+        r.m[d] = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+        r.s[d] = l;
+    }
+    return r;
+}
+constexpr SmallMagic kSmallMagic = small_magic();
+
 // ------------------------------------------------------------ one unit
 
 // Where the output multiply takes its weights from: each lane loads its own
@@ -367,7 +396,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     const W* gv =
         reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + cbase);
     W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + cbase);
-    const float* wp = kPacked ? a.w : a.w + (int64_t)g * a.wgs;
+    const float* wp = kPacked ? a.w : a.w + (int64_t)g * weight_group_stride(a);
     // vectors of this unit: v0 .. v0 + nv - 1 (packed: those holding any of
     // columns col0 .. col0 + G - 1)
     uint32_t v0 = 0, nv = a.nvec;
@@ -511,7 +540,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
             store_stream<NT>(ov + v0 + idx, res[k]);
         }
     };
-    if (!NBG && a.ri)
+    if (!NBG && round_intermediate(a))
         finish(std::true_type{});
     else
         finish(std::false_type{});
@@ -520,22 +549,27 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 // ------------------------------------------------------------ kernels
 
 // Tile (row or row tile rt, tile column c) of workgroup blockIdx.x in the
-// XCD-banded order (KArgs::xband): XCD x = b % 8 takes, in each block of 8
-// rows numbered column-major, the tiles x*C .. x*C + C-1, block after block;
-// then its share of the short block of the last R % 8 rows.  A bijection of
-// the launch's workgroups onto its R x C tiles.
-__device__ inline void xcd_band_tile(const KArgs& a, uint32_t& rt, uint32_t& c) {
+// XCD-banded order over R x C tiles (C = KArgs::xc): XCD x = b % 8 takes, in
+// each block of 8 rows numbered column-major, the tiles x*C .. x*C + C-1,
+// block after block; then its share of the short block of the last R % 8
+// rows.  A bijection of the launch's R * C workgroups onto its tiles.
+__device__ inline void xcd_band_tile(const KArgs& a, uint32_t R, uint32_t& rt, uint32_t& c) {
     const uint32_t b = blockIdx.x;
     const uint32_t x = b % kXcds, k = b / kXcds;
-    if (k < a.xfullk) {
-        const uint32_t blk = fast_div(k, a.xc_m, a.xc_s);
-        const uint32_t idx = x * a.xc + (k - blk * a.xc);
+    const uint32_t C = a.xc;
+    const uint32_t fullk = (R / kXcds) * C;  // each XCD's workgroups in the full blocks
+    if (k < fullk) {
+        const uint32_t blk = fast_div(k, a.xc_m, xc_shift(a));
+        const uint32_t idx = x * C + (k - blk * C);
         c = idx / kXcds;
         rt = blk * kXcds + idx % kXcds;
     } else {
-        const uint32_t idx = x * a.xq2 + (x < a.xr2 ? x : a.xr2) + (k - a.xfullk);
-        c = fast_div(idx, a.xrr_m, a.xrr_s);
-        rt = a.xfullrows + (idx - c * a.xrr);
+        const uint32_t rr = R % kXcds;  // >= 1 here
+        const uint32_t t2 = rr * C;     // tiles of the short block
+        const uint32_t q2 = t2 / kXcds, r2 = t2 % kXcds;
+        const uint32_t idx = x * q2 + (x < r2 ? x : r2) + (k - fullk);
+        c = fast_div(idx, kSmallMagic.m[rr], kSmallMagic.s[rr]);
+        rt = (R - rr) + (idx - c * rr);
     }
 }
 
@@ -547,15 +581,15 @@ __device__ inline void xcd_band_tile(const KArgs& a, uint32_t& rt, uint32_t& c) 
 template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
     uint32_t n, g;
-    if (a.xband) {
+    if (banded(a)) {
         uint32_t c;
-        xcd_band_tile(a, n, c);
+        xcd_band_tile(a, a.rows, n, c);
         g = c * (blockDim.x / SEG) + threadIdx.x / SEG;
         if (g >= a.groups) return;  // the row's last tile may be partial
     } else {
         const uint32_t unit = (blockIdx.x * (uint32_t)blockDim.x + threadIdx.x) / SEG;
-        if (unit >= a.units) return;  // whole segments leave together
-        n = fast_div(unit, a.div_m, a.div_s);
+        if (unit >= a.rows * a.groups) return;  // whole segments leave together
+        n = row_div(a, unit);
         g = unit - n * a.groups;
     }
     unit_pass<T, VB, PB, SEG, VPT, NBG, NT, WSource::Global>(a, n, g, threadIdx.x & (SEG - 1),
@@ -582,10 +616,10 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     // row tile and group: row-major (the groups of a row tile in turn) or
     // XCD-banded (KArgs::xband)
     uint32_t tile, g;
-    if (a.xband) {
-        xcd_band_tile(a, tile, g);
+    if (banded(a)) {
+        xcd_band_tile(a, (a.rows + UPB - 1) / UPB, tile, g);
     } else {
-        tile = fast_div(blockIdx.x, a.div_m, a.div_s);
+        tile = row_div(a, blockIdx.x);
         g = blockIdx.x - tile * a.groups;
     }
     const uint32_t u = threadIdx.x / SEG;
@@ -598,7 +632,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     constexpr int SV = UPB > 1 ? (VPT * N + 4 * UPB - 1) / (4 * UPB) : 1;
     f32x4 wst[SV];
     if constexpr (UPB > 1) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(a.w + (int64_t)g * a.wgs);
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.w + (int64_t)g * weight_group_stride(a));
         const uint32_t nw4 = a.G / 4;
 #pragma unroll
         for (int i = 0; i < SV; ++i) {
@@ -638,14 +672,14 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
     __shared__ float part[kWideBlock / 64];
 
     const uint32_t unit = blockIdx.x;
-    const uint32_t n = fast_div(unit, a.div_m, a.div_s);
+    const uint32_t n = row_div(a, unit);
     const uint32_t g = unit - n * a.groups;
     const int64_t col0 = (int64_t)g * a.G;
     const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy + col0);
     const W* gv =
         reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg + col0);
     W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so + col0);
-    const float* wp = a.w + (int64_t)g * a.wgs;
+    const float* wp = a.w + (int64_t)g * weight_group_stride(a);
 
     float acc = 0.0f;
     for (uint32_t i = threadIdx.x; i < a.nvec; i += kWideBlock) {
@@ -677,7 +711,7 @@ __global__ __launch_bounds__(kWideBlock) void ggrms_wide_kernel(KArgs a) {
         } else {
 #pragma unroll
             for (int e = 0; e < N; ++e) t[e] = yf[e] * silu_exact(gf[e]) * nf;
-            if (a.ri) P::round_trip(t);
+            if (round_intermediate(a)) P::round_trip(t);
 #pragma unroll
             for (int e = 0; e < N; ++e) t[e] = wv[e] * t[e];
         }
