@@ -70,9 +70,11 @@ int kernel_for_shape(int lanes, int vpt) {
 //     segment, several groups per wave (WAVE kernel, 80-83% of HBM peak);
 //   * 65-80: one wave, two vectors per lane (67-77%; 128 lanes: 64-75%);
 //   * 81-96: two waves, one vector per lane, one row per workgroup (79-80%);
-//   * 97-768: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
-//     workgroup sharing staged weights (75-81%); 4 rows only with one vector
+//   * 97-512: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
+//     workgroup sharing staged weights (78-81%); 4 rows only with one vector
 //     per lane, since the staging registers cost occupancy at 2+;
+//   * 513-768: 256 lanes x 3 vectors, one row per workgroup (75-76%; 2 rows:
+//     72-75%);
 //   * 769-4096: 256-1024 lanes x 3-4 vectors, one row per workgroup (staging
 //     at 4 vectors per lane measured 46-59% against 77% without); three
 //     vectors where they cover the group with fewer idle lanes;
@@ -89,7 +91,7 @@ const ShapeRule kRules[] = {
     {256, GGRMS_KERNEL_BLOCK, 256, 1, 2},
     {384, GGRMS_KERNEL_BLOCK, 128, 3, 2},
     {512, GGRMS_KERNEL_BLOCK, 256, 2, 2},
-    {768, GGRMS_KERNEL_BLOCK, 256, 3, 2},
+    {768, GGRMS_KERNEL_BLOCK, 256, 3, 1},
     {1024, GGRMS_KERNEL_BLOCK, 256, 4, 1},
     {1536, GGRMS_KERNEL_BLOCK, 512, 3, 1},
     {2048, GGRMS_KERNEL_BLOCK, 512, 4, 1},

@@ -453,8 +453,8 @@ def test_kernel_family_by_group_width(g):
         2048: ("block", 256, 1, 2),   # 256
         2056: ("block", 128, 3, 2),   # 257
         4096: ("block", 256, 2, 2),   # 512
-        5120: ("block", 256, 3, 2),   # 640
-        6144: ("block", 256, 3, 2),   # 768
+        5120: ("block", 256, 3, 1),   # 640
+        6144: ("block", 256, 3, 1),   # 768
         6152: ("block", 256, 4, 1),   # 769
         7680: ("block", 256, 4, 1),   # 960
         12288: ("block", 512, 3, 1),  # 1536
