@@ -157,6 +157,14 @@ template <class T, int VB> struct Packet {
     }
 };
 
+// 32-bit word i of a VB-byte vector (VB >= 4).
+template <int VB, class W> __device__ inline uint32_t word_of(const W& v, int i) {
+    if constexpr (VB == 4)
+        return (uint32_t)v;
+    else
+        return v[i];
+}
+
 // Accesses of y, gate and out.  Each is touched once per launch; with NT they
 // carry the non-temporal hint (the nt bit), which on gfx950 takes a large
 // two-read-one-write stream from ~72% to ~81% of HBM peak against plain
@@ -242,6 +250,37 @@ __device__ inline float silu_exact(float x) {
     const float d = 1.0f + e;
     const float sc = d > 0x1p64f ? 0x1p-64f : 1.0f;
     return (x * sc) * __builtin_amdgcn_rcpf(d * sc);
+}
+
+// -0.0f that the compiler cannot see through (a v_mov of the bit pattern),
+// so that fma(x, b, nz) is kept as an FMA instead of being folded into a
+// multiply.
+__device__ inline float opaque_neg_zero() {
+    float z;
+    asm("v_mov_b32 %0, 0x80000000" : "=v"(z));
+    return z;
+}
+
+// f32(half h of the fp16 pair `word`) * b, rounded once, as fma(x, b, -0):
+// gfx950 issues it as one v_fma_mix_f32, which widens the 16-bit operand
+// exactly inside the FMA and so saves the separate v_cvt_f32_f16 of each fp16
+// operand; the addend -0 leaves every product -- a zero's sign included -- as
+// the f32 multiply of the widened value gives it.  The compiler emits the
+// instruction itself, so its hazard checks cover it (a transcendental's result
+// read by the next VALU instruction needs a wait state).  gfx950 has no bf16
+// form.
+__device__ inline float mul_f16(uint32_t word, int h, float b, float nz) {
+    const _Float16 x = __builtin_bit_cast(_Float16, (u16)(h ? word >> 16 : word & 0xFFFFu));
+    return __builtin_fmaf((float)x, b, nz);
+}
+
+// silu_fast of half h of an fp16 pair, and y * silu(gate) for element h of
+// the pairs yw, gw, with the widening folded into the multiplies: the same
+// operations in the same order as y * silu_fast(gate) on widened values.
+__device__ inline float gated_f16(uint32_t yw, uint32_t gw, int h, float nz) {
+    const float e = __builtin_amdgcn_exp2f(mul_f16(gw, h, -1.4426950408889634f, nz));
+    const float s = mul_f16(gw, h, __builtin_amdgcn_rcpf(1.0f + e), nz);
+    return mul_f16(yw, h, s, nz);
 }
 
 // DPP move with all rows and banks enabled.
@@ -434,11 +473,16 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     float sgv[NBG ? VPT : 1][N];
     float acc = 0.0f;
     unsigned gmax = 0;
+    // fp16 gate first: the widening folded into the multiplies (mul_f16)
+    constexpr bool kMix = std::is_same<T, TF16>::value && VB >= 4 && !NBG;
+    const float nz = kMix ? opaque_neg_zero() : 0.0f;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         float yf[N], gf[N];
-        P::unpack(yr[k], yf);
-        P::unpack(gr[k], gf);
+        if constexpr (!kMix) {
+            P::unpack(yr[k], yf);
+            P::unpack(gr[k], gf);
+        }
         if constexpr (VB <= 4) {
             gmax = gate_max_word<T>(gmax, (unsigned)gr[k]);
         } else {
@@ -448,7 +492,11 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
         float part = 0.0f;
 #pragma unroll
         for (int e = 0; e < N; ++e) {
-            const float x = NBG ? yf[e] : yf[e] * silu_fast(gf[e]);
+            float x;
+            if constexpr (kMix)
+                x = gated_f16(word_of<VB>(yr[k], e / 2), word_of<VB>(gr[k], e / 2), e & 1, nz);
+            else
+                x = NBG ? yf[e] : yf[e] * silu_fast(gf[e]);
             if constexpr (NBG) sgv[k][e] = silu_fast(gf[e]);
             av[k][e] = x;
             const float xx = __builtin_fmaf(x, x, part);
@@ -515,6 +563,12 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
                 // ((y * nf) * w) * silu(gate), every intermediate f32
 #pragma unroll
                 for (int e = 0; e < N; ++e) t[e] = (t[e] * wr[k][e]) * sgv[k][e];
+            } else if constexpr (RI && kMix) {
+                // cast to fp16, then weight * f32(cast) with the widening folded in
+                const W h = P::pack(t);
+#pragma unroll
+                for (int e = 0; e < N; ++e)
+                    t[e] = mul_f16(word_of<VB>(h, e / 2), e & 1, wr[k][e], nz);
             } else {
                 if constexpr (RI) P::round_trip(t);
 #pragma unroll
