@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import refs
 import synthetic as S
 from gpu_util import (BF16, DT_IDS, F16, F32, FLAG_KEEP, FLAG_NBG, FLAG_RI, FLAG_STREAM, TDT,
                       assert_parity, check_contiguous, dev_buf, host_bits, random_case, run_gpu,
@@ -79,6 +80,33 @@ def test_workload_full_size(g, orc, name, ri):
 
 # ------------------------------------------------------------ group sizes
 
+def _wide_f32_against_exact(g, orc, G):
+    """f32 groups wider than 4096: the oracle's sequential f32 sum may be off
+    by up to (G/2 + 16) * 2^-24 relative, which nears the 1e-5 bar, so the GPU
+    is held to the exact result instead -- the unfused chain from library
+    routines in float64 (tests/refs.py), times the weight -- within the same
+    1e-5; the oracle is held to the exact result within its own bound."""
+    rows, groups = 3, 2
+    width = G * groups
+    say(f"case wide f32 G={G} against the float64 chain")
+    y, gt, w = random_case(rows, width, F32, seed=G * 7 + F32)
+    yd, gd, wd = dev_buf(y, F32), dev_buf(gt, F32), torch.from_numpy(w).cuda()
+    od = torch.empty_like(yd)
+    assert run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, 1e-5, F32,
+                   0) == g.SUCCESS
+    torch.cuda.synchronize()
+    got = host_bits(od, F32).reshape(rows, width).astype(np.float64)
+    t = refs.chain_fp64(y.reshape(rows, width).astype(np.float64),
+                        gt.reshape(rows, width).astype(np.float64), G, float(np.float32(1e-5)))
+    ref = w.astype(np.float64)[None, :] * t
+    rel = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-38)
+    assert rel.max() <= 1e-5, f"G={G}: GPU off the exact result by {rel.max():.3e} relative"
+    o = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                    gate_row_stride=width, out_row_stride=width, eps=1e-5, dtype=F32,
+                    round_intermediate=0)
+    refs.check_f32(o.reshape(rows, width), t, w.astype(np.float64)[None, :], G)
+
+
 G_SWEEP = [1, 2, 3, 4, 7, 8, 12, 16, 24, 63, 64, 65, 97, 100, 127, 128, 129, 200, 255, 256, 257,
            512, 960, 1000, 1024, 1032, 2048, 2056, 4096, 7680, 8192, 16384, 32768, 32776, 65536]
 
@@ -90,7 +118,8 @@ def test_group_size_sweep(g, orc, G, dtype):
     not a multiple of the vector or the wave width and groups too wide for
     registers (two-pass kernel)."""
     if dtype == F32 and G > 4096:
-        pytest.skip("f32 beyond G = 4096: the oracle's own sum error nears the 1e-5 bar")
+        _wide_f32_against_exact(g, orc, G)
+        return
     groups = 3 if G <= 4096 else 2
     rows = 5 if G <= 1024 else 3
     for ri in ((0, 1) if dtype != F32 else (0,)):
