@@ -60,8 +60,8 @@ constexpr uint32_t kXcds = 8;
 
 // Supported shapes.  WAVE: lanes in {1..64} (powers of two); vectors per lane
 // 1 for lanes < 64, 1..4 for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
-// vectors per lane 1..4.  WIDE: 1024 lanes, vectors per lane 0 (it loops over
-// the group).  A WAVE workgroup is a single wave or 4 waves (the kernel takes
+// vectors per lane 1..4, and 6 with 256 lanes.  WIDE: 1024 lanes, vectors per
+// lane 0 (it loops over the group).  A WAVE workgroup is a single wave or 4 waves (the kernel takes
 // its size from the launch; the planner's rule says which).
 constexpr int kWaveBlock = 256;
 constexpr int kWaveBlockOneWave = 64;
@@ -84,8 +84,8 @@ inline bool shape_supported(int kernel, int lanes, int vpt) {
                 lanes == 32) &&
                vpt == 1;
     case GGRMS_KERNEL_BLOCK:
-        return (lanes == 128 || lanes == 256 || lanes == 512 || lanes == 1024) && vpt >= 1 &&
-               vpt <= 4;
+        return (lanes == 128 || lanes == 256 || lanes == 512 || lanes == 1024) &&
+               ((vpt >= 1 && vpt <= 4) || (lanes == 256 && vpt == 6));
     case GGRMS_KERNEL_WIDE:
         return lanes == kWideBlock;
     default:

@@ -793,6 +793,7 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
         GG_W(64, 1); GG_W(64, 2); GG_W(64, 3); GG_W(64, 4);
     } else if (kernel == GGRMS_KERNEL_BLOCK) {
         GG_B4(128, 1); GG_B4(256, 1); GG_B4(512, 1); GG_B4(1024, 1);
+        GG_B(256, 6, 1);
         if constexpr (!kPacked) {
             GG_B4(128, 2); GG_B4(128, 4);
             GG_B4(256, 2);

@@ -75,9 +75,11 @@ int kernel_for_shape(int lanes, int vpt) {
 //     per lane, since the staging registers cost occupancy at 2+;
 //   * 513-768: 256 lanes x 3 vectors, one row per workgroup (75-76%; 2 rows:
 //     72-75%);
-//   * 769-4096: 256-1024 lanes x 3-4 vectors, one row per workgroup (staging
-//     at 4 vectors per lane measured 46-59% against 77% without); three
-//     vectors where they cover the group with fewer idle lanes;
+//   * 769-4096: 256-1024 lanes x 3-6 vectors, one row per workgroup (staging
+//     at 4 vectors per lane measured 46-59% against 77% without); fewer waves
+//     with more vectors each where the registers allow (1025-1536: 256 x 6,
+//     0.75 against 0.67-0.71 for 512 x 3; 6 vectors take 163 VGPRs, 8 took
+//     218 and lost to 512 x 4 and 1024 x 4);
 //   * wider groups loop over the row twice (WIDE).
 struct ShapeRule {
     int64_t max_nvec;
@@ -93,7 +95,7 @@ const ShapeRule kRules[] = {
     {512, GGRMS_KERNEL_BLOCK, 256, 2, 2},
     {768, GGRMS_KERNEL_BLOCK, 256, 3, 1},
     {1024, GGRMS_KERNEL_BLOCK, 256, 4, 1},
-    {1536, GGRMS_KERNEL_BLOCK, 512, 3, 1},
+    {1536, GGRMS_KERNEL_BLOCK, 256, 6, 1},
     {2048, GGRMS_KERNEL_BLOCK, 512, 4, 1},
     {3072, GGRMS_KERNEL_BLOCK, 1024, 3, 1},
     {4096, GGRMS_KERNEL_BLOCK, 1024, 4, 1},

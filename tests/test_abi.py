@@ -457,7 +457,8 @@ def test_kernel_family_by_group_width(g):
         6144: ("block", 256, 3, 1),   # 768
         6152: ("block", 256, 4, 1),   # 769
         7680: ("block", 256, 4, 1),   # 960
-        12288: ("block", 512, 3, 1),  # 1536
+        12288: ("block", 256, 6, 1),  # 1536
+        12296: ("block", 512, 4, 1),  # 1537
         16384: ("block", 512, 4, 1),  # 2048
         24576: ("block", 1024, 3, 1),  # 3072
         32768: ("block", 1024, 4, 1),

@@ -131,7 +131,7 @@ def test_group_size_sweep(g, orc, G, dtype):
 SHAPES = [(1, 1), (2, 1), (4, 1), (8, 1), (16, 1), (32, 1), (64, 1), (64, 2), (64, 3), (64, 4)] + \
          [(l, v, 1) for l in (128, 256, 512, 1024) for v in (1, 2, 3, 4)] + \
          [(128, v, u) for v in (1, 2, 3, 4) for u in (2, 4)] + [(256, v, 2) for v in (1, 2, 3, 4)] + \
-         [(1024, 0)]
+         [(256, 6, 1), (1024, 0)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
