@@ -607,6 +607,31 @@ def traffic_figure():
         return None
 
 
+def run_environment(torch, w) -> dict:
+    """Where and with what the line was measured: device, runtime, host."""
+    props = torch.cuda.get_device_properties(0)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"device": props.name, "arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__,
+            "host_cpu": cpu_model, "host_cores": os.cpu_count(),
+            "seed": w.seed, "library_abi": g_abi_version()}
+
+
+def g_abi_version() -> int:
+    import gated_group_rmsnorm_amd as g
+
+    return g.ggrms_abi_version()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -689,6 +714,7 @@ def main():
         "other_workloads": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in others.items()},
         "unfused_chain_torch_eager": {k: round(v, 3) for k, v in unfused.items()},
         "kernel": pre["plan"],
+        "env": run_environment(torch, w),
     }
     print(json.dumps(line), flush=True)
 
