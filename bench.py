@@ -159,6 +159,25 @@ def time_kernel(torch, g, setup, steps, warmup, shape=None, settle_s=0.2):
     return wall, start.elapsed_time(end)
 
 
+def per_launch_percentiles(torch, g, setup, shape, launches=200):
+    """p10 / p50 / p90 of single launches, each between its own pair of HIP
+    events on the launch stream (after the timed loop, outside it; the
+    rotating input sets keep every launch's inputs out of the caches)."""
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        setup.launch(g, i, sp, shape)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    pick = lambda q: round(us[min(len(us) - 1, int(q * len(us)))], 2)
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "launches": launches}
+
+
 def bench_prefill(torch, g, S, args, shape):
     w = S.WORKLOADS[PREFILL]
     nbytes = w.algorithmic_bytes()
@@ -174,6 +193,7 @@ def bench_prefill(torch, g, S, args, shape):
         "bytes": nbytes,
         "wall_s": wall,
         "kernel_ms_avg": avg_ms,
+        "per_launch_us": per_launch_percentiles(torch, g, setup, shape),
         "plan": plan,
         "sets": sets,
     }
@@ -704,6 +724,8 @@ def main():
                      "traffic": traffic_figure(),
                      "algorithmic_bytes_per_launch": nbytes,
                      "kernel_us_avg": round(pre["kernel_ms_avg"] * 1e3, 2),
+                     # single launches, each between its own events
+                     "kernel_us_per_launch": pre["per_launch_us"],
                      # the plain two-read-one-write kernel moving the same three streams
                      "stream_ceiling_us": round(ceil_us, 2),
                      "stream_ceiling_frac": round(3 * w.rows * w.width * w.esize / (ceil_us * 1e-6)
