@@ -605,7 +605,51 @@ def cpu_baseline(S, seconds):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{rows} of the 8192 rows of {w.name}, {reps} passes in {el:.1f} s "
                       f"(single-threaded C, one host core)",
-            "rows_per_s": round(reps * rows / el, 1)}
+            "rows_per_s": round(reps * rows / el, 1),
+            "all_cores": cpu_baseline_all_cores(S, y, gt, wt, rows, max(2.0, seconds / 3))}
+
+
+def cpu_baseline_all_cores(S, y, gt, wt, rows, seconds):
+    """The same oracle function on the same rows, the rows split across all
+    the host cores this process may use (one thread each; the C call runs
+    without the interpreter lock), repeated for about `seconds`."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+
+    w = S.WORKLOADS[PREFILL]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, rows))
+    bounds = np.linspace(0, rows, cores + 1).astype(int)
+    y2, g2 = y.reshape(rows, w.width), gt.reshape(rows, w.width)
+
+    def part(i):
+        r0, r1 = bounds[i], bounds[i + 1]
+        oracle.forward(np.ascontiguousarray(y2[r0:r1]).reshape(-1),
+                       np.ascontiguousarray(g2[r0:r1]).reshape(-1), wt, rows=r1 - r0,
+                       width=w.width, group_size=w.group_size, y_row_stride=w.width,
+                       gate_row_stride=w.width, out_row_stride=w.width, eps=w.eps,
+                       dtype=w.dtype, round_intermediate=w.round_intermediate)
+
+    sample_bytes = 3 * rows * w.width * w.esize + 4 * w.width
+    reps = 0
+    with cf.ThreadPoolExecutor(cores) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(part, range(cores)))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(reps * sample_bytes / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle x cores",
+            "sample": f"the same {rows} rows split over {cores} threads, {reps} passes in "
+                      f"{el:.1f} s"}
 
 
 def traffic_figure():
