@@ -31,7 +31,11 @@
 //     deterministic run to run;
 //   * VALU work is kept low (it runs about half busy at the HBM rate): one
 //     exp and one reciprocal per silu, the normaliser as a fused multiply-add
-//     and v_rsq_f32, the silu-underflow test on raw gate bits.
+//     and v_rsq_f32, the silu-underflow test on raw gate bits, and fp16
+//     operands multiplied without a separate widening (v_fma_mix_f32);
+//   * which workgroup takes which rows and groups (row-major or XCD-banded
+//     order, WAVE workgroups of one or four waves) is a launch argument and
+//     changes no result bit.
 // Nothing here uses MFMA: there is no contraction to feed it.
 #pragma once
 
