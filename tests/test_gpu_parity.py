@@ -427,6 +427,44 @@ def test_strided_equals_contiguous(g):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype,G,groups,flags", [(BF16, 960, 8, FLAG_RI), (F16, 128, 64, 0),
+                                                   (F16, 128, 64, FLAG_NBG)],
+                         ids=["bf16-g960", "f16-g128", "f16-g128-nbg"])
+def test_shards_equal_the_whole(g, dtype, G, groups, flags):
+    """How the op would shard over GPUs, on one GPU: every (row, group) unit is
+    independent, so launching it on shards -- column slices on group boundaries
+    with the matching slice of the weight (tensor parallel over the
+    intermediate axis), or blocks of rows (data / sequence parallel) -- writes
+    exactly the bits of the whole launch, with no exchange between shards."""
+    rows = 96
+    width = G * groups
+    y, gt, w = random_case(rows, width, dtype, seed=G + groups + flags)
+    yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+    whole = torch.empty_like(yd)
+    assert run_gpu(g, yd, gd, wd, whole, rows, width, G, width, width, width, 1e-5, dtype, 0,
+                   flags=flags) == g.SUCCESS
+    for tp in (2, 8):  # column shards of groups // tp groups each
+        out = torch.full_like(yd, float("nan"))
+        sw = width // tp
+        for r in range(tp):
+            c0 = r * sw
+            assert run_gpu(g, yd[c0:], gd[c0:], wd[c0:], out[c0:], rows, sw, G, width, width,
+                           width, 1e-5, dtype, 0, flags=flags) == g.SUCCESS
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if dtype != F32 else out,
+                           whole.view(torch.int16) if dtype != F32 else whole), f"tp={tp}"
+    for dp in (3, 4):  # row shards
+        out = torch.full_like(yd, float("nan"))
+        bounds = [rows * i // dp for i in range(dp + 1)]
+        for r0, r1 in zip(bounds[:-1], bounds[1:]):
+            assert run_gpu(g, yd[r0 * width:], gd[r0 * width:], wd, out[r0 * width:], r1 - r0,
+                           width, G, width, width, width, 1e-5, dtype, 0,
+                           flags=flags) == g.SUCCESS
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if dtype != F32 else out,
+                           whole.view(torch.int16) if dtype != F32 else whole), f"dp={dp}"
+
+
 def test_deterministic(g):
     w = S.WORKLOADS["mamba2_prefill_8192x7680_bf16_g960"]
     rows = 1024
