@@ -38,7 +38,11 @@
  * ggrms_forward only enqueues work on `stream` and returns (the page's
  * "Enqueues" entry point); results are ready when the stream reaches that
  * point.  Faults inside the kernel surface at the caller's next
- * synchronisation with that stream.
+ * synchronisation with that stream.  A call may be captured into a HIP graph
+ * (stream capture) and replayed: it allocates nothing, waits for nothing and
+ * enqueues nothing but its kernel launches, whose arguments are fixed at
+ * capture.  The current device's architecture is queried on the first call
+ * on that device and cached.
  */
 #ifndef GGRMS_H
 #define GGRMS_H
