@@ -29,8 +29,9 @@ import os
 
 __all__ = [
     "F32", "F16", "BF16", "FLAG_ROUND_INTERMEDIATE", "FLAG_NORM_BEFORE_GATE",
-    "FLAG_WEIGHT_PER_GROUP", "FLAG_CACHE_STREAM", "FLAG_CACHE_KEEP", "STREAM_MIN_BYTES", "SUCCESS", "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED",
-    "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError", "ggrms_forward", "ggrms_forward_ex",
+    "FLAG_WEIGHT_PER_GROUP", "FLAG_CACHE_STREAM", "FLAG_CACHE_KEEP", "FLAG_ORDER_ROWS",
+    "FLAG_ORDER_BANDED", "FLAG_WAVE_ONE", "FLAG_WAVE_FOUR", "STREAM_MIN_BYTES", "SUCCESS",
+    "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED", "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError", "ggrms_forward", "ggrms_forward_ex",
     "ggrms_forward_with_shape", "ggrms_plan", "ggrms_plan_ex",
     "ggrms_status_string", "ggrms_abi_version", "forward", "plan", "expand_head_scale",
     "library_path",
@@ -39,6 +40,8 @@ __all__ = [
 F32, F16, BF16 = 0, 1, 2
 FLAG_ROUND_INTERMEDIATE, FLAG_NORM_BEFORE_GATE, FLAG_WEIGHT_PER_GROUP = 1, 2, 4
 FLAG_CACHE_STREAM, FLAG_CACHE_KEEP = 8, 16
+# launch controls (tile order, WAVE workgroup size); results are identical whatever they select
+FLAG_ORDER_ROWS, FLAG_ORDER_BANDED, FLAG_WAVE_ONE, FLAG_WAVE_FOUR = 32, 64, 128, 256
 STREAM_MIN_BYTES = 4 << 20  # default policy: jobs of at least this many y+gate+out bytes stream
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
 KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide"}

@@ -61,8 +61,9 @@ constexpr uint32_t kXcds = 8;
 // Supported shapes.  WAVE: lanes in {1..64} (powers of two); vectors per lane
 // 1 for lanes < 64, 1..4 for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
 // vectors per lane 1..4, and 6 with 256 lanes.  WIDE: 1024 lanes, vectors per
-// lane 0 (it loops over the group).  A WAVE workgroup is a single wave or 4 waves (the kernel takes
-// its size from the launch; the planner's rule says which).
+// lane 0 (it loops over the group).  A WAVE workgroup is a single wave or 4
+// waves (the kernel takes its size from the launch; the planner's rule says
+// which).
 constexpr int kWaveBlock = 256;
 constexpr int kWaveBlockOneWave = 64;
 constexpr int kWideBlock = 1024;
@@ -101,14 +102,14 @@ struct LaunchPlan {
     int64_t groups;
     int64_t nvec;
     int64_t rows_per_launch;  // rows handled by each launch (the last one may have fewer)
-    bool xband;               // XCD-banded tile order (KArgs::xband)
+    bool xband;               // XCD-banded tile order (kBitBand)
 };
 
 // WAVE: groups one workgroup covers (lanes <= 64).
 inline int64_t wave_groups_per_workgroup(int lanes, int threads) { return threads / lanes; }
 
-// Tile rows and tile columns of one launch over r rows (see KArgs::xband);
-// a WAVE tile is one wave.
+// Tile rows and tile columns of one launch over r rows (the banded order's R
+// and C, described above KArgs); a WAVE tile is one workgroup.
 inline void launch_tiles(const LaunchPlan& lp, int64_t r, int64_t* R, int64_t* C) {
     const ggrms_plan_t& p = lp.pub;
     if (p.kernel == GGRMS_KERNEL_BLOCK) {

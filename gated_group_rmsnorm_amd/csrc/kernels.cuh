@@ -672,7 +672,7 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     __shared__ float part[BT / 64];
     extern __shared__ __attribute__((aligned(16))) float wl[];  // a.G floats when UPB > 1
     // row tile and group: row-major (the groups of a row tile in turn) or
-    // XCD-banded (KArgs::xband)
+    // XCD-banded (kBitBand)
     uint32_t tile, g;
     if (banded(a)) {
         xcd_band_tile(a, (a.rows + UPB - 1) / UPB, tile, g);

@@ -157,7 +157,8 @@ typedef struct {
  * Tile order.  Row-major: workgroup b takes the b-th tile (WAVE: the next
  * units of the (row, group) sequence; BLOCK: row tile b / groups, group
  * b % groups).  XCD-banded, chosen when every group has its own weights and
- * a row's tiles are not a multiple of 8: the tiles are taken in blocks of 8
+ * a row does not split into a multiple of 8 full tiles (WIDE launches are
+ * always row-major): the tiles are taken in blocks of 8
  * rows, and the part's 8 XCDs (workgroup b runs on XCD b % 8) each take a
  * band of about 1/8 of the columns of every block, so each XCD reads the
  * weights of its band only, while the tiles in flight still cover a
@@ -255,7 +256,7 @@ ggrms_status_t ggrms_plan_ex(const void* y, const void* gate, const float* norm_
  *   lanes_per_group   1, 2, 4, ..., 64 (WAVE kernel) or 128, 256, 512, 1024
  *                     (BLOCK kernel; 1024 with vectors_per_lane = 0 is WIDE)
  *   vectors_per_lane  1 for lanes < 64; 1..4 for 64 lanes or the BLOCK
- *                     kernel; 0 for WIDE
+ *                     kernel (also 6 with 256 lanes); 0 for WIDE
  *   rows_per_workgroup  0 to let the library choose; 1; or, for the BLOCK
  *                     kernel, 2 or 4 with 128 lanes and 2 with 256 lanes (the
  *                     workgroup's rows share one group, whose weights are

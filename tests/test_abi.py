@@ -49,6 +49,35 @@ def test_abi_version_and_strings(g):
     assert g.ggrms_status_string(99) == "unknown status"
 
 
+def _header_constants():
+    """NAME -> value of every enumerator and integer #define in ggrms.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    consts = {n: int(v) for n, v in re.findall(r"\b(GGRMS_[A-Z0-9_]+)\s*=\s*(\d+)\s*[,}\n]", text)}
+    for n, v in re.findall(r"#define\s+(GGRMS_[A-Z0-9_]+)\s+(.+)", text):
+        m = re.fullmatch(r"\(?(\d+)(?:ll)?(?:\s*<<\s*(\d+))?\)?", v.strip())
+        if m:  # an integer literal, possibly shifted
+            consts[n] = int(m[1]) << int(m[2] or 0)
+    return consts
+
+
+def test_binding_constants_match_header(g):
+    """Every enumerator and integer macro of the header has the same value in
+    the Python binding (named without the GGRMS_ prefix, or, for the kernel
+    ids, as keys of KERNEL_NAMES)."""
+    consts = _header_constants()
+    assert len(consts) >= 22, sorted(consts)
+    for name, value in consts.items():
+        short = name[len("GGRMS_"):]
+        if short.startswith("KERNEL_"):
+            assert g.KERNEL_NAMES[value] == short[len("KERNEL_"):].lower(), name
+        elif short == "ABI_VERSION":
+            assert g.ABI_VERSION == value == g.ggrms_abi_version()
+        else:
+            assert getattr(g, short) == value, f"{name} = {value} in the header"
+            assert short in g.__all__, short
+    assert set(g.KERNEL_NAMES) == {v for n, v in consts.items() if n.startswith("GGRMS_KERNEL_")}
+
+
 def _fwd(g, **kw):
     args = dict(y=A, gate=A + (1 << 24), norm_weight=A + (2 << 24), out=A + (3 << 24), rows=4,
                 width=256, group_size=64, y_row_stride=256, gate_row_stride=256,
