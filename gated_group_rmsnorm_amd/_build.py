@@ -44,10 +44,12 @@ def _run(cmd):
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     path = os.path.join(CSRC, src)
+    # the product library exports its C ABI only (GGRMS_API in ggrms.h)
+    vis = ["-fvisibility=hidden"] if src in LIB_HIP + LIB_CXX else []
     if src.endswith(".hip"):
-        _run([HIPCC, *HIP_FLAGS, "-c", path, "-o", obj])
+        _run([HIPCC, *HIP_FLAGS, *vis, "-c", path, "-o", obj])
     else:
-        _run(["g++", *CXX_FLAGS, "-c", path, "-o", obj])
+        _run(["g++", *CXX_FLAGS, *vis, "-c", path, "-o", obj])
     return obj
 
 
@@ -65,7 +67,8 @@ def build(verbose: bool = False) -> str:
     srcs = LIB_HIP + LIB_CXX + BENCH_HIP
     with cf.ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = dict(zip(srcs, ex.map(_compile, srcs)))
-    _link([objs[s] for s in LIB_HIP + LIB_CXX], LIB)
+    _link([objs[s] for s in LIB_HIP + LIB_CXX], LIB,
+          [f"-Wl,--version-script={os.path.join(CSRC, 'libggrms.map')}"])
     # the benchmark helpers call the product library itself (found next to them)
     _link([objs[s] for s in BENCH_HIP], BENCH_LIB,
           ["-L", PKG, "-l:libggrms.so", "-Wl,-rpath,$ORIGIN"])

@@ -55,6 +55,14 @@ extern "C" {
 
 #define GGRMS_ABI_VERSION 4
 
+/* The library exports these functions and nothing else (it is built with
+ * hidden visibility). */
+#if defined(__GNUC__)
+#define GGRMS_API __attribute__((visibility("default")))
+#else
+#define GGRMS_API
+#endif
+
 /* Element type shared by y, gate and out.  The weight is always f32. */
 typedef enum {
     GGRMS_F32 = 0,  /* IEEE binary32 */
@@ -108,11 +116,11 @@ typedef enum {
  * current device is checked (GGRMS_ERROR_NOT_SUPPORTED unless gfx950) and
  * the kernels are launched (GGRMS_ERROR_LAUNCH if the runtime refuses one).
  */
-ggrms_status_t ggrms_forward(const void* y, const void* gate, const float* norm_weight,
-                             void* out, int64_t rows, int64_t width, int64_t group_size,
-                             int64_t y_row_stride, int64_t gate_row_stride,
-                             int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
-                             int round_intermediate, void* stream);
+GGRMS_API ggrms_status_t ggrms_forward(const void* y, const void* gate, const float* norm_weight,
+                                       void* out, int64_t rows, int64_t width, int64_t group_size,
+                                       int64_t y_row_stride, int64_t gate_row_stride,
+                                       int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                       int round_intermediate, void* stream);
 
 /* Which kernel ggrms_forward would launch for a set of arguments. */
 typedef enum {
@@ -170,11 +178,11 @@ typedef struct {
  * without touching the device; fills *plan on GGRMS_SUCCESS.  Makes no HIP
  * call, so it works on a host without a GPU.
  */
-ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_weight,
-                          void* out, int64_t rows, int64_t width, int64_t group_size,
-                          int64_t y_row_stride, int64_t gate_row_stride,
-                          int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
-                          int round_intermediate, ggrms_plan_t* plan);
+GGRMS_API ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_weight,
+                                    void* out, int64_t rows, int64_t width, int64_t group_size,
+                                    int64_t y_row_stride, int64_t gate_row_stride,
+                                    int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                    int round_intermediate, ggrms_plan_t* plan);
 
 /* Operator variants (bits of the `flags` argument of the _ex calls). */
 typedef enum {
@@ -234,18 +242,20 @@ typedef struct {
  * or both cache flags; GGRMS_ERROR_NOT_SUPPORTED for a shape that cannot be
  * used (as in ggrms_forward_with_shape).
  */
-ggrms_status_t ggrms_forward_ex(const void* y, const void* gate, const float* norm_weight,
-                                void* out, int64_t rows, int64_t width, int64_t group_size,
-                                int64_t y_row_stride, int64_t gate_row_stride,
-                                int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
-                                uint32_t flags, const ggrms_shape_t* shape, void* stream);
+GGRMS_API ggrms_status_t ggrms_forward_ex(const void* y, const void* gate, const float* norm_weight,
+                                          void* out, int64_t rows, int64_t width,
+                                          int64_t group_size, int64_t y_row_stride,
+                                          int64_t gate_row_stride, int64_t out_row_stride,
+                                          float eps, ggrms_dtype_t dtype, uint32_t flags,
+                                          const ggrms_shape_t* shape, void* stream);
 
 /* ggrms_plan for ggrms_forward_ex's arguments (no HIP call). */
-ggrms_status_t ggrms_plan_ex(const void* y, const void* gate, const float* norm_weight,
-                             void* out, int64_t rows, int64_t width, int64_t group_size,
-                             int64_t y_row_stride, int64_t gate_row_stride,
-                             int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
-                             uint32_t flags, const ggrms_shape_t* shape, ggrms_plan_t* plan);
+GGRMS_API ggrms_status_t ggrms_plan_ex(const void* y, const void* gate, const float* norm_weight,
+                                       void* out, int64_t rows, int64_t width, int64_t group_size,
+                                       int64_t y_row_stride, int64_t gate_row_stride,
+                                       int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                       uint32_t flags, const ggrms_shape_t* shape,
+                                       ggrms_plan_t* plan);
 
 /*
  * ggrms_forward_with_shape -- ggrms_forward with the kernel shape chosen by
@@ -271,20 +281,20 @@ ggrms_status_t ggrms_plan_ex(const void* y, const void* gate, const float* norm_
  * built, whose lanes_per_group * vectors_per_lane vectors do not cover one
  * group, or whose rows_per_workgroup cannot be used.
  */
-ggrms_status_t ggrms_forward_with_shape(const void* y, const void* gate,
-                                        const float* norm_weight, void* out, int64_t rows,
-                                        int64_t width, int64_t group_size,
-                                        int64_t y_row_stride, int64_t gate_row_stride,
-                                        int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
-                                        int round_intermediate, int lanes_per_group,
-                                        int vectors_per_lane, int rows_per_workgroup,
-                                        void* stream);
+GGRMS_API ggrms_status_t ggrms_forward_with_shape(const void* y, const void* gate,
+                                                  const float* norm_weight, void* out, int64_t rows,
+                                                  int64_t width, int64_t group_size,
+                                                  int64_t y_row_stride, int64_t gate_row_stride,
+                                                  int64_t out_row_stride, float eps,
+                                                  ggrms_dtype_t dtype, int round_intermediate,
+                                                  int lanes_per_group, int vectors_per_lane,
+                                                  int rows_per_workgroup, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
-const char* ggrms_status_string(ggrms_status_t status);
+GGRMS_API const char* ggrms_status_string(ggrms_status_t status);
 
 /* GGRMS_ABI_VERSION of the loaded library. */
-int ggrms_abi_version(void);
+GGRMS_API int ggrms_abi_version(void);
 
 #ifdef __cplusplus
 }

@@ -35,11 +35,14 @@ def test_header_symbols_exported(g):
     lib = ctypes.CDLL(g.library_path())
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ggrms.h but not exported"
+    # the dynamic symbol table holds the header's functions and nothing else
+    # (no internal C++ symbols, no kernel handles)
     out = subprocess.run(["nm", "-D", "--defined-only", g.library_path()], capture_output=True,
                          text=True, check=True).stdout
-    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
-    public = {n for n in exported if n.startswith("ggrms_")}
-    assert public == set(names), f"exported but undeclared: {public - set(names)}"
+    exported = {l.split()[-1] for l in out.splitlines() if len(l.split()) == 3}
+    assert exported == set(names), (f"exported but undeclared: {sorted(exported - set(names))[:5]}; "
+                                    f"declared but not exported: {sorted(set(names) - exported)}")
+    assert all(l.split()[1] == "T" for l in out.splitlines() if len(l.split()) == 3)
 
 
 def test_abi_version_and_strings(g):
