@@ -71,8 +71,9 @@ int kernel_for_shape(int lanes, int vpt) {
 //   * 65-80: one wave, two vectors per lane (67-77%; 128 lanes: 64-75%);
 //   * 81-96: two waves, one vector per lane, one row per workgroup (79-80%);
 //   * 97-512: 128 or 256 lanes with 1-3 vectors each and 2-4 rows per
-//     workgroup sharing staged weights (78-81%); 4 rows only with one vector
-//     per lane, since the staging registers cost occupancy at 2+;
+//     workgroup sharing staged weights (73-82%): 4 rows for 105-128 and
+//     145-192 vectors, 2 elsewhere (1-2% apart at the band edges); never 4
+//     at three vectors per lane, where the staging registers cost occupancy;
 //   * 513-768: 256 lanes x 3 vectors, one row per workgroup (75-76%; 2 rows:
 //     72-75%);
 //   * 769-4096: 256-1024 lanes x 3-6 vectors, one row per workgroup (staging
@@ -88,8 +89,10 @@ struct ShapeRule {
 const ShapeRule kRules[] = {
     {80, GGRMS_KERNEL_WAVE, 64, 2, 1},
     {96, GGRMS_KERNEL_BLOCK, 128, 1, 1},
+    {104, GGRMS_KERNEL_BLOCK, 128, 1, 2},
     {128, GGRMS_KERNEL_BLOCK, 128, 1, 4},
-    {192, GGRMS_KERNEL_BLOCK, 128, 2, 2},
+    {144, GGRMS_KERNEL_BLOCK, 128, 2, 2},
+    {192, GGRMS_KERNEL_BLOCK, 128, 2, 4},
     {256, GGRMS_KERNEL_BLOCK, 256, 1, 2},
     {384, GGRMS_KERNEL_BLOCK, 128, 3, 2},
     {512, GGRMS_KERNEL_BLOCK, 256, 2, 2},

@@ -235,10 +235,14 @@ def test_tile_order_and_wave_workgroups(g):
     p = plan(RI, 1024, 7680, 128, stride=7682)
     assert (p["vector_bytes"], p["block_threads"], p["tile_order"], p["workgroups"]) == \
         (4, 256, 1, 1024 * 15)
-    # BLOCK, 9 groups of 832 bf16 (4 rows per workgroup): banded over 16 x 9 tiles
-    p = plan(RI, 64, 7488, 832)
+    # BLOCK, 9 groups of 896 bf16 (4 rows per workgroup): banded over 16 x 9 tiles
+    p = plan(RI, 64, 8064, 896)
     assert (p["kernel_name"], p["rows_per_workgroup"], p["tile_order"], p["workgroups"]) == \
         ("block", 4, 1, 16 * 9)
+    # 9 groups of 832 (2 rows per workgroup): 32 x 9 tiles
+    p = plan(RI, 64, 7488, 832)
+    assert (p["kernel_name"], p["rows_per_workgroup"], p["tile_order"], p["workgroups"]) == \
+        ("block", 2, 1, 32 * 9)
     # 8 groups of 960: a multiple of 8 tiles per row -> row-major; banded if forced
     assert plan(RI, 8192, 7680, 960)["tile_order"] == 0
     p = plan(RI | BANDED, 8192, 7680, 960)
@@ -478,10 +482,14 @@ def test_kernel_family_by_group_width(g):
         640: ("wave", 64, 2, 1),      # 80
         648: ("block", 128, 1, 1),    # 81
         768: ("block", 128, 1, 1),    # 96
-        776: ("block", 128, 1, 4),    # 97
+        776: ("block", 128, 1, 2),    # 97
+        832: ("block", 128, 1, 2),    # 104
+        840: ("block", 128, 1, 4),    # 105
         960: ("block", 128, 1, 4),    # 120
-        1032: ("block", 128, 2, 4 // 2),  # 129
-        1536: ("block", 128, 2, 2),   # 192
+        1032: ("block", 128, 2, 2),   # 129
+        1152: ("block", 128, 2, 2),   # 144
+        1160: ("block", 128, 2, 4),   # 145
+        1536: ("block", 128, 2, 4),   # 192
         2048: ("block", 256, 1, 2),   # 256
         2056: ("block", 128, 3, 2),   # 257
         4096: ("block", 256, 2, 2),   # 512

@@ -50,8 +50,10 @@ CASES = [
     (BF16, 512, 9, 17, FLAG_RI),      # WAVE 64 x 1
     (BF16, 576, 13, 11, FLAG_RI),     # WAVE 64 x 2
     (BF16, 768, 10, 19, FLAG_RI),     # BLOCK 128 x 1, one row per workgroup
-    (BF16, 832, 9, 33, FLAG_RI),      # BLOCK 128 x 1, 4 rows per workgroup: 9 row tiles
-    (BF16, 1280, 6, 20, FLAG_RI),     # BLOCK 128 x 2, 2 rows per workgroup
+    (BF16, 896, 9, 33, FLAG_RI),      # BLOCK 128 x 1, 4 rows per workgroup: 9 row tiles
+    (BF16, 832, 9, 33, FLAG_RI),      # BLOCK 128 x 1, 2 rows per workgroup: 17 row tiles
+    (BF16, 1280, 6, 20, FLAG_RI),     # BLOCK 128 x 2, 4 rows per workgroup
+    (BF16, 1088, 6, 20, FLAG_RI),     # BLOCK 128 x 2, 2 rows per workgroup
     (BF16, 4096, 3, 8, FLAG_RI),      # BLOCK 256 x 2, one full block
     (F32, 64, 20, 10, 0),             # f32, 16 lanes
     (F16, 128, 60, 12, FLAG_NBG),     # norm first, per-column weight
