@@ -12,8 +12,8 @@
  *     nf    = rsqrt(m2 / G + eps)                        eps added after the mean
  *     out[n,col] = cast(f32(norm_weight[col]) * f32(cast(gated*nf, y.dtype)), out.dtype)
  *
- * This is the norm_before_gate = False branch of the Mamba-2 mixer's gated
- * RMSNorm; one launch replaces the four-op chain (widen, silu-gate, group
+ * This computes the Mamba-2 mixer's gated RMSNorm in its norm_before_gate =
+ * False form; one launch replaces the four-op chain (widen, silu-gate, group
  * RMSNorm, weight multiply and narrow) the page's intro describes.  With
  * round_intermediate = 0 the intermediate cast(gated*nf, y.dtype) is skipped
  * and every intermediate stays f32 until the final store (the mode that the

@@ -21,10 +21,11 @@
  * and narrows only at the store, as the page "com.microsoft.GatedRMSNorm"
  * (Description section) puts it for its own operator.
  *
- * That page's operator itself normalises before gating,
- *     Y = X * rsqrt(mean(X^2) + eps) * scale * SiLU(gate),
- * with `scale` holding one value per column of a group, shared by every group
- * (Inputs table).  It is available with GGRMS_ORACLE_NORM_BEFORE_GATE and
+ * That page's operator itself normalises before gating: the group's
+ * normaliser comes from the input alone, nf = 1/sqrt(mean_j y_j^2 + eps), and
+ * out = y * nf * w * silu(gate) with every intermediate in f32, where its
+ * weight holds one value per column of a group, shared by every group (Inputs
+ * table).  It is available with GGRMS_ORACLE_NORM_BEFORE_GATE and
  * GGRMS_ORACLE_WEIGHT_PER_GROUP (which also applies to the gate-first form).
  *
  * Readings where the pages say nothing (each is listed in the design notes):

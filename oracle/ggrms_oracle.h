@@ -22,7 +22,7 @@ enum { GGRMS_ORACLE_F32 = 0, GGRMS_ORACLE_F16 = 1, GGRMS_ORACLE_BF16 = 2 };
 /* Flags of ggrms_oracle_forward_ex. */
 enum {
     GGRMS_ORACLE_ROUND_INTERMEDIATE = 1, /* gate-first: cast gated*nf before the weight */
-    GGRMS_ORACLE_NORM_BEFORE_GATE = 2,   /* Y = X*rsqrt(mean(X^2)+eps)*w*silu(gate) */
+    GGRMS_ORACLE_NORM_BEFORE_GATE = 2,   /* out = y * nf(y) * w * silu(gate), all f32 */
     GGRMS_ORACLE_WEIGHT_PER_GROUP = 4    /* weight has group_size values shared by all groups */
 };
 

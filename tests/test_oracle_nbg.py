@@ -1,9 +1,11 @@
 """Pins for the oracle's norm-before-gate operator and per-group weight (CPU).
 
-The "com.microsoft.GatedRMSNorm" page (Description section) defines
-Y = X * rsqrt(mean(X^2) + eps) * scale * SiLU(gate), every intermediate f32,
-only the store narrowing, with `scale` holding one value per column of a
-group shared by every group (Inputs table).  The oracle's
+The "com.microsoft.GatedRMSNorm" page (Description section) defines an
+operator that takes the group's normaliser from the input alone,
+nf = 1/sqrt(mean_j y_j^2 + eps), and multiplies y * nf by the weight and by
+silu(gate), every intermediate in f32 and only the store narrowing; its
+weight holds one value per column of a group, shared by every group (Inputs
+table).  The oracle's
 WEIGHT_PER_GROUP flag also applies to the gate-first operator.
 """
 import numpy as np
