@@ -599,3 +599,49 @@ int main() {
                     str(drv), os.path.join(csrc, "plan.cpp"), "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+C_CLIENT = r"""
+#include <stdint.h>
+#include <stdio.h>
+#include "ggrms.h"
+
+int main(void) {
+    /* fake, 256-byte aligned device addresses: planning makes no HIP call */
+    const void* y = (const void*)(uintptr_t)0x100000;
+    const void* gate = (const void*)(uintptr_t)0x4100000;
+    const float* w = (const float*)(uintptr_t)0x8100000;
+    void* out = (void*)(uintptr_t)0xc100000;
+    ggrms_plan_t p;
+    ggrms_status_t st = ggrms_plan(y, gate, w, out, 8192, 7680, 960, 7680, 7680, 7680, 1e-5f,
+                                   GGRMS_BF16, 1, &p);
+    /* rejected before any HIP call: width is not a multiple of the group */
+    ggrms_status_t bad = ggrms_forward(y, gate, w, out, 4, 1000, 960, 1000, 1000, 1000, 1e-5f,
+                                       GGRMS_BF16, 1, NULL);
+    printf("%d %d %d %d %d %lld %d %s\n", ggrms_abi_version(), (int)st, p.kernel,
+           p.lanes_per_group, p.rows_per_workgroup, (long long)p.workgroups, (int)bad,
+           ggrms_status_string(bad));
+    return st == GGRMS_SUCCESS && bad == GGRMS_ERROR_INVALID_VALUE ? 0 : 1;
+}
+"""
+
+
+@pytest.mark.parametrize("compiler", [["gcc", "-x", "c", "-std=c99"], ["g++", "-x", "c++", "-std=c++11"]],
+                         ids=["c99", "c++11"])
+def test_c_client_builds_and_links(g, tmp_path, compiler):
+    """The header is plain C (and C++): a client compiled with -pedantic
+    -Werror links against the library and plans the prefill job through the
+    C ABI alone."""
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(g.library_path())
+    subprocess.run([*compiler, "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-x", "none",
+                    "-L", libdir, "-l:libggrms.so", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                   check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    fields = r.stdout.split()
+    assert fields[:7] == [str(g.ABI_VERSION), "0", "2", "128", "4", str(8192 // 4 * 8), "1"], r.stdout
+    assert " ".join(fields[7:]) == g.ggrms_status_string(1)
