@@ -104,7 +104,9 @@ typedef enum {
  *                 multiply; 0: keep it f32.  For GGRMS_F32 both are identical.
  *   stream        a hipStream_t, or NULL for the null stream.
  *
- * Every element pointer must be aligned to its element size.
+ * The buffers and the stream belong to the calling thread's current HIP
+ * device, which is the device that is checked and launched on.  Every
+ * element pointer must be aligned to its element size.
  *
  * Returns GGRMS_SUCCESS once the work is enqueued.  Argument checks run
  * before any HIP call: GGRMS_ERROR_INVALID_VALUE for a negative rows, a
