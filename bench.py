@@ -178,6 +178,16 @@ def per_launch_percentiles(torch, g, setup, shape, launches=200):
     return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "launches": launches}
 
 
+class _OneSet:
+    """A Setup whose launches all use input set 0."""
+
+    def __init__(self, setup):
+        self.setup = setup
+
+    def launch(self, g, i, stream, shape=None):
+        self.setup.launch(g, 0, stream, shape)
+
+
 def bench_prefill(torch, g, S, args, shape):
     w = S.WORKLOADS[PREFILL]
     nbytes = w.algorithmic_bytes()
@@ -193,6 +203,7 @@ def bench_prefill(torch, g, S, args, shape):
         "bytes": nbytes,
         "wall_s": wall,
         "kernel_ms_avg": avg_ms,
+        "setup": setup,
         "per_launch_us": per_launch_percentiles(torch, g, setup, shape),
         "plan": plan,
         "sets": sets,
@@ -735,6 +746,13 @@ def main():
     if args.only == "prefill":
         return
     w = pre["workload"]
+    # warm: every launch on the same input set, which the 256 MB Infinity
+    # Cache then partly holds (reported apart; the headline rate is cold; not
+    # part of the --only prefill run that the kernel trace covers)
+    _, warm_ms = time_kernel(torch, g, _OneSet(pre["setup"]), args.steps, args.warmup, shape,
+                             args.settle_ms / 1e3)
+    log(f"prefill, one input set reused: {warm_ms * 1e3 / args.steps:.2f} us per launch")
+    del pre["setup"]  # release the prefill's input sets before the other workloads
     ceil_us = stream_ceiling(torch, w.rows * w.width * w.esize, args.steps, args.settle_ms / 1e3)
     log(f"stream ceiling at the prefill's bytes: {ceil_us:.2f} us per launch")
     decode = bench_decode(torch, g, S, args.decode_bursts)
@@ -774,7 +792,9 @@ def main():
                      "stream_ceiling_us": round(ceil_us, 2),
                      "stream_ceiling_frac": round(3 * w.rows * w.width * w.esize / (ceil_us * 1e-6)
                                                   / 1e9 / PEAK_HBM_GBS, 4),
-                     "frac_of_stream_ceiling": round(ceil_us / (pre["kernel_ms_avg"] * 1e3), 4)},
+                     "frac_of_stream_ceiling": round(ceil_us / (pre["kernel_ms_avg"] * 1e3), 4),
+                     # the same launch with one input set reused (partly cached): not the rate
+                     "warm_one_input_set_us": round(warm_ms * 1e3 / args.steps, 2)},
         "cpu_baseline": cpu,
         "decode": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in decode.items()},
         "other_workloads": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in others.items()},
