@@ -1,8 +1,10 @@
 """Fused gated group-RMSNorm for AMD Instinct MI355X (gfx950).
 
-A thin ctypes binding over ``libggrms.so`` (C ABI in ``include/ggrms.h``).
-Every step of the computation runs in the library's HIP kernels; this
-module only marshals arguments.  PyTorch supplies device memory and the
+A thin ctypes binding over ``libggrms.so`` (C ABI in ``include/ggrms.h``;
+launch controls for tuning in ``include/ggrms_tuning.h``).  Every step of
+the computation runs in the library's HIP kernels; this module only marshals
+arguments (and widens a 16-bit weight exactly to the f32 the library
+takes).  PyTorch supplies device memory and the
 current stream.  There is no fallback: if the library is missing, importing
 the binding raises.
 
@@ -31,21 +33,23 @@ __all__ = [
     "F32", "F16", "BF16", "FLAG_ROUND_INTERMEDIATE", "FLAG_NORM_BEFORE_GATE",
     "FLAG_WEIGHT_PER_GROUP", "FLAG_CACHE_STREAM", "FLAG_CACHE_KEEP", "FLAG_ORDER_ROWS",
     "FLAG_ORDER_BANDED", "FLAG_WAVE_ONE", "FLAG_WAVE_FOUR", "STREAM_MIN_BYTES", "SUCCESS",
-    "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED", "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError", "ggrms_forward", "ggrms_forward_ex",
-    "ggrms_forward_with_shape", "ggrms_plan", "ggrms_plan_ex",
-    "ggrms_status_string", "ggrms_abi_version", "forward", "plan", "expand_head_scale",
-    "library_path",
+    "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED", "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError",
+    "ggrms_forward", "ggrms_forward_ex", "ggrms_forward_tuned", "ggrms_plan", "ggrms_plan_ex",
+    "ggrms_plan_tuned", "ggrms_status_string", "ggrms_abi_version", "forward", "plan",
+    "expand_head_scale", "library_path",
 ]
 
 F32, F16, BF16 = 0, 1, 2
+# operator flags (include/ggrms.h)
 FLAG_ROUND_INTERMEDIATE, FLAG_NORM_BEFORE_GATE, FLAG_WEIGHT_PER_GROUP = 1, 2, 4
+# launch controls (include/ggrms_tuning.h; the _tuned calls only): cache policy, tile
+# order, WAVE workgroup size.  Results are identical whatever they select.
 FLAG_CACHE_STREAM, FLAG_CACHE_KEEP = 8, 16
-# launch controls (tile order, WAVE workgroup size); results are identical whatever they select
 FLAG_ORDER_ROWS, FLAG_ORDER_BANDED, FLAG_WAVE_ONE, FLAG_WAVE_FOUR = 32, 64, 128, 256
 STREAM_MIN_BYTES = 4 << 20  # default policy: jobs of at least this many y+gate+out bytes stream
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
 KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide"}
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libggrms.so")
@@ -63,7 +67,7 @@ class GgrmsError(RuntimeError):
 
 class _Shape(ctypes.Structure):
     _fields_ = [("lanes_per_group", ctypes.c_int32), ("vectors_per_lane", ctypes.c_int32),
-                ("rows_per_workgroup", ctypes.c_int32)]
+                ("rows_per_workgroup", ctypes.c_int32), ("vector_bytes", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
@@ -85,15 +89,18 @@ def _load() -> ctypes.CDLL:
     fwd = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32]
     L.ggrms_forward.argtypes = fwd + [vp]
     L.ggrms_forward.restype = i32
-    L.ggrms_forward_with_shape.argtypes = fwd + [i32, i32, i32, vp]
-    L.ggrms_forward_with_shape.restype = i32
     L.ggrms_plan.argtypes = fwd + [ctypes.POINTER(_Plan)]
     L.ggrms_plan.restype = i32
-    fwd_ex = fwd[:-1] + [ctypes.c_uint32, ctypes.POINTER(_Shape)]
+    fwd_ex = fwd[:-1] + [ctypes.c_uint32]
     L.ggrms_forward_ex.argtypes = fwd_ex + [vp]
     L.ggrms_forward_ex.restype = i32
     L.ggrms_plan_ex.argtypes = fwd_ex + [ctypes.POINTER(_Plan)]
     L.ggrms_plan_ex.restype = i32
+    fwd_tuned = fwd_ex + [ctypes.POINTER(_Shape)]
+    L.ggrms_forward_tuned.argtypes = fwd_tuned + [vp]
+    L.ggrms_forward_tuned.restype = i32
+    L.ggrms_plan_tuned.argtypes = fwd_tuned + [ctypes.POINTER(_Plan)]
+    L.ggrms_plan_tuned.restype = i32
     L.ggrms_status_string.argtypes = [i32]
     L.ggrms_status_string.restype = ctypes.c_char_p
     L.ggrms_abi_version.argtypes = []
@@ -119,51 +126,61 @@ def ggrms_forward(y: int, gate: int, norm_weight: int, out: int, rows: int, widt
                               round_intermediate, stream)
 
 
-def ggrms_forward_with_shape(y: int, gate: int, norm_weight: int, out: int, rows: int,
-                             width: int, group_size: int, y_row_stride: int,
-                             gate_row_stride: int, out_row_stride: int, eps: float, dtype: int,
-                             round_intermediate: int, lanes_per_group: int,
-                             vectors_per_lane: int, stream: int,
-                             rows_per_workgroup: int = 0) -> int:
-    """ggrms_forward with a caller-chosen kernel shape; returns the status."""
-    return _lib.ggrms_forward_with_shape(y, gate, norm_weight, out, rows, width, group_size,
-                                         y_row_stride, gate_row_stride, out_row_stride, eps,
-                                         dtype, round_intermediate, lanes_per_group,
-                                         vectors_per_lane, rows_per_workgroup, stream)
-
-
 def _shape_arg(shape):
+    """None, or (lanes, vectors[, rows per workgroup[, vector bytes]]) as a ggrms_shape_t."""
     if shape is None:
         return None
-    lanes, vpt = shape[0], shape[1]
-    upb = shape[2] if len(shape) > 2 else 0
-    return ctypes.byref(_Shape(lanes, vpt, upb))
+    f = list(shape) + [0] * (4 - len(shape))
+    return ctypes.byref(_Shape(*f[:4]))
+
+
+def _plan_dict(p) -> dict:
+    d = {f: getattr(p, f) for f, _ in _Plan._fields_}
+    d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
+    return d
 
 
 def ggrms_forward_ex(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
                      group_size: int, y_row_stride: int, gate_row_stride: int,
-                     out_row_stride: int, eps: float, dtype: int, flags: int, stream: int,
-                     shape=None) -> int:
-    """The C entry point with operator flags and an optional (lanes, vectors[, rows
-    per workgroup]) shape; returns the status."""
+                     out_row_stride: int, eps: float, dtype: int, flags: int, stream: int) -> int:
+    """The C entry point with operator flags (FLAG_ROUND_INTERMEDIATE,
+    FLAG_NORM_BEFORE_GATE, FLAG_WEIGHT_PER_GROUP); returns the status."""
     return _lib.ggrms_forward_ex(y, gate, norm_weight, out, rows, width, group_size,
                                  y_row_stride, gate_row_stride, out_row_stride, eps, dtype, flags,
-                                 _shape_arg(shape), stream)
+                                 stream)
+
+
+def ggrms_forward_tuned(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
+                        group_size: int, y_row_stride: int, gate_row_stride: int,
+                        out_row_stride: int, eps: float, dtype: int, flags: int, stream: int,
+                        shape=None) -> int:
+    """ggrms_forward_ex with launch controls: flags may also hold the FLAG_CACHE_*,
+    FLAG_ORDER_* and FLAG_WAVE_* bits, and shape = (lanes, vectors[, rows per
+    workgroup[, vector bytes]]) forces the kernel shape; returns the status."""
+    return _lib.ggrms_forward_tuned(y, gate, norm_weight, out, rows, width, group_size,
+                                    y_row_stride, gate_row_stride, out_row_stride, eps, dtype,
+                                    flags, _shape_arg(shape), stream)
+
+
+def ggrms_plan_tuned(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
+                     group_size: int, y_row_stride: int, gate_row_stride: int,
+                     out_row_stride: int, eps: float, dtype: int, flags: int, shape=None):
+    """(status, plan dict or None) for ggrms_forward_tuned's arguments; no device call."""
+    p = _Plan()
+    st = _lib.ggrms_plan_tuned(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                               gate_row_stride, out_row_stride, eps, dtype, flags,
+                               _shape_arg(shape), ctypes.byref(p))
+    return (st, _plan_dict(p)) if st == SUCCESS else (st, None)
 
 
 def ggrms_plan_ex(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
                   group_size: int, y_row_stride: int, gate_row_stride: int, out_row_stride: int,
-                  eps: float, dtype: int, flags: int, shape=None):
+                  eps: float, dtype: int, flags: int):
     """(status, plan dict or None) for ggrms_forward_ex's arguments; no device call."""
     p = _Plan()
     st = _lib.ggrms_plan_ex(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
-                            gate_row_stride, out_row_stride, eps, dtype, flags,
-                            _shape_arg(shape), ctypes.byref(p))
-    if st != SUCCESS:
-        return st, None
-    d = {f: getattr(p, f) for f, _ in _Plan._fields_}
-    d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
-    return st, d
+                            gate_row_stride, out_row_stride, eps, dtype, flags, ctypes.byref(p))
+    return (st, _plan_dict(p)) if st == SUCCESS else (st, None)
 
 
 def ggrms_plan(y: int, gate: int, norm_weight: int, out: int, rows: int, width: int,
@@ -174,11 +191,7 @@ def ggrms_plan(y: int, gate: int, norm_weight: int, out: int, rows: int, width: 
     st = _lib.ggrms_plan(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
                          gate_row_stride, out_row_stride, eps, dtype, round_intermediate,
                          ctypes.byref(p))
-    if st != SUCCESS:
-        return st, None
-    d = {f: getattr(p, f) for f, _ in _Plan._fields_}
-    d["kernel_name"] = KERNEL_NAMES.get(d["kernel"], "?")
-    return st, d
+    return (st, _plan_dict(p)) if st == SUCCESS else (st, None)
 
 
 def ggrms_status_string(status: int) -> str:
@@ -231,6 +244,30 @@ def expand_head_scale(scale, heads: int):
     return s.repeat(heads).contiguous()
 
 
+def _weight_f32(weight, width: int, group_size: int):
+    """The weight as the library takes it: a contiguous 1-D f32 tensor of
+    width values (one per column) or group_size values (shared by every
+    group).  Accepted spellings, after the Inputs table of the page
+    "com.microsoft.GatedRMSNorm" (scale shaped (C), (1, C) or (C, 1)): 1-D,
+    or 2-D with one axis of length 1; f32 as is, fp16/bf16 widened exactly
+    (a copy per call: callers that repeat a call should widen once)."""
+    import torch
+
+    shape = tuple(weight.shape)
+    if not (len(shape) == 1 or (len(shape) == 2 and 1 in shape)):
+        raise ValueError(f"weight must be shaped (n), (1, n) or (n, 1), not {shape}")
+    if weight.numel() not in (width, group_size):
+        raise ValueError(f"weight has {weight.numel()} values; needs width ({width}) or "
+                         f"group_size ({group_size})")
+    if weight.dtype not in (torch.float32, torch.float16, torch.bfloat16):
+        raise TypeError(f"unsupported weight dtype {weight.dtype}; use float32, float16 or "
+                        "bfloat16")
+    w = weight.reshape(-1)
+    if w.dtype != torch.float32:
+        w = w.float()  # every fp16 / bf16 value is an f32 value: exact
+    return w if w.is_contiguous() else w.contiguous()
+
+
 _CACHE_FLAGS = {None: 0, "stream": FLAG_CACHE_STREAM, "keep": FLAG_CACHE_KEEP}
 
 
@@ -248,14 +285,15 @@ def _flags(weight, width, group_size, round_intermediate, norm_before_gate, cach
 def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
             round_intermediate=None, out=None, stream=None,
             norm_before_gate: bool = False, cache=None):
-    """out = fused gated group-RMSNorm of (y, gate) with the f32 ``weight``
-    over groups of ``group_size`` columns of the last axis.
+    """out = fused gated group-RMSNorm of (y, gate) with ``weight`` over groups
+    of ``group_size`` columns of the last axis.
 
     y and gate: same shape (..., width), same dtype (f32/f16/bf16), on the
     GPU, unit stride in the last axis (they may be strided column slices of
-    one fused buffer).  weight: f32 with width values (one per column) or
-    group_size values (shared by every group).  out (optional) must match
-    y's shape and dtype; it is allocated like y when omitted.
+    one fused buffer).  weight: width values (one per column) or group_size
+    values (shared by every group), shaped (n), (1, n) or (n, 1), in f32 or
+    (widened exactly to f32 here) fp16/bf16.  out (optional) must match y's
+    shape and dtype; it is allocated like y when omitted.
     round_intermediate (default: on for gate first) casts gated*nf to the
     dtype before the weight multiply.  norm_before_gate selects
     out = ((y * nf) * w) * silu(gate) with nf from y alone, every
@@ -273,18 +311,13 @@ def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
         raise TypeError("y and gate must share a dtype")
     code = _torch_dtype_code(y)
     width = y.size(-1)
-    if weight.dtype != torch.float32 or weight.dim() != 1 or \
-            weight.numel() not in (width, group_size):
-        raise TypeError("weight must be a 1-D float32 tensor with width or group_size elements "
-                        "(expand_head_scale builds a per-column one from a per-head scale)")
-    if not weight.is_contiguous():
-        raise ValueError("weight must be contiguous")
     if out is None:
         out = torch.empty(y.shape, dtype=y.dtype, device=y.device)
     elif out.shape != y.shape or out.dtype != y.dtype:
         raise ValueError("out must have y's shape and dtype")
     if not (y.is_cuda and gate.is_cuda and weight.is_cuda and out.is_cuda):
         raise ValueError("all tensors must be on the GPU")
+    weight = _weight_f32(weight, width, group_size)
     rows, sy = _as_rows(y, "y")
     _, sg = _as_rows(gate, "gate")
     _, so = _as_rows(out, "out")
@@ -293,10 +326,10 @@ def forward(y, gate, weight, group_size: int, eps: float = 1e-5,
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     flags = _flags(weight, width, group_size, round_intermediate, norm_before_gate, cache)
+    call = ggrms_forward_tuned if cache is not None else ggrms_forward_ex
     with torch.cuda.device(y.device):
-        st = ggrms_forward_ex(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), out.data_ptr(),
-                              rows, width, group_size, sy, sg, so, float(eps), code, flags,
-                              stream)
+        st = call(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), out.data_ptr(), rows, width,
+                  group_size, sy, sg, so, float(eps), code, flags, stream)
     if st != SUCCESS:
         raise GgrmsError(st)
     return out
@@ -311,10 +344,11 @@ def plan(y, gate, weight, group_size: int, eps: float = 1e-5, round_intermediate
     _, sg = _as_rows(gate, "gate")
     o = out if out is not None else y.new_empty(y.shape)
     _, so = _as_rows(o, "out")
-    st, p = ggrms_plan_ex(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), o.data_ptr(), rows,
-                          width, group_size, sy, sg, so, float(eps), code,
-                          _flags(weight, width, group_size, round_intermediate,
-                                 norm_before_gate, cache))
+    weight = _weight_f32(weight, width, group_size)
+    st, p = ggrms_plan_tuned(y.data_ptr(), gate.data_ptr(), weight.data_ptr(), o.data_ptr(), rows,
+                             width, group_size, sy, sg, so, float(eps), code,
+                             _flags(weight, width, group_size, round_intermediate,
+                                    norm_before_gate, cache))
     if st != SUCCESS:
         raise GgrmsError(st, "ggrms_plan")
     return p

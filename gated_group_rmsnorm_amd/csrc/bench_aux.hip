@@ -3,8 +3,9 @@
 //   * an empty kernel taking an argument block of the same size as the
 //     normalisation kernels, launched with a caller-chosen grid: the floor
 //     that a decode launch is compared against;
-//   * decode bursts issued from C through libggrms.so's ggrms_forward_ex
-//     (eager and replayed as one HIP graph), next to the same bursts of the
+//   * decode bursts issued from C through libggrms.so's ggrms_forward_tuned
+//     (eager and replayed as one HIP graph; the library's own launch
+//     choice unless the caller forces a shape), next to the same bursts of the
 //     empty kernel, so the per-launch figure carries no interpreter overhead;
 //   * a plain 16-byte vector copy of known size: the calibration that turns
 //     the FETCH_SIZE / WRITE_SIZE counters into HBM bytes;
@@ -24,6 +25,7 @@
 
 #include "ggrms.h"
 #include "ggrms_internal.h"
+#include "ggrms_tuning.h"
 
 namespace {
 
@@ -130,7 +132,8 @@ struct BurstRes {
 
 // Decode bursts: `layers` back-to-back launches over the layers' [1, width]
 // buffers, repeated `bursts` times on a stream of its own, after about 100 ms
-// of untimed bursts (the clocks settle).  mode 0: ggrms_forward_ex eager;
+// of untimed bursts (the clocks settle), with `flags` and `shape` (NULL: the
+// library's choice) passed to ggrms_forward_tuned.  mode 0: eager;
 // 1: the same burst captured once and replayed as a HIP graph; 2 and 3: the
 // empty kernel with the fused launch's grid, eager and graph.  Device time
 // comes from events around each burst (median burst / layers); host time is
@@ -139,12 +142,12 @@ struct BurstRes {
 extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const* gate,
                                          const float* const* w, void* const* out, int layers,
                                          int64_t width, int64_t group_size, float eps, int dtype,
-                                         uint32_t flags, int bursts, int mode, double* dev_us,
-                                         double* host_us) {
+                                         uint32_t flags, const ggrms_shape_t* shape,
+                                         int bursts, int mode, double* dev_us, double* host_us) {
     if (layers <= 0 || bursts <= 0 || mode < 0 || mode > 3) return GGRMS_ERROR_INVALID_VALUE;
     ggrms_plan_t plan;
-    const int st = ggrms_plan_ex(y[0], gate[0], w[0], out[0], 1, width, group_size, width, width,
-                                 width, eps, (ggrms_dtype_t)dtype, flags, nullptr, &plan);
+    const int st = ggrms_plan_tuned(y[0], gate[0], w[0], out[0], 1, width, group_size, width,
+                                    width, width, eps, (ggrms_dtype_t)dtype, flags, shape, &plan);
     if (st != GGRMS_SUCCESS) return st;
     BurstRes r;
     if (hipStreamCreate(&r.s) != hipSuccess || hipEventCreate(&r.e0) != hipSuccess ||
@@ -156,9 +159,9 @@ extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const
             if (empty) {
                 if (ggrms_bench_empty(plan.workgroups, plan.block_threads, r.s) != 0) return -1;
             } else {
-                const int rc = ggrms_forward_ex(y[l], gate[l], w[l], out[l], 1, width, group_size,
-                                                width, width, width, eps, (ggrms_dtype_t)dtype,
-                                                flags, nullptr, r.s);
+                const int rc = ggrms_forward_tuned(y[l], gate[l], w[l], out[l], 1, width,
+                                                   group_size, width, width, width, eps,
+                                                   (ggrms_dtype_t)dtype, flags, shape, r.s);
                 if (rc != GGRMS_SUCCESS) return rc;
             }
         }

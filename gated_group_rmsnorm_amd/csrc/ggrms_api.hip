@@ -14,6 +14,7 @@
 
 #include "ggrms.h"
 #include "ggrms_internal.h"
+#include "ggrms_tuning.h"
 
 namespace ggrms {
 namespace {
@@ -106,15 +107,27 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
 }  // namespace
 }  // namespace ggrms
 
+extern "C" ggrms_status_t ggrms_forward_tuned(const void* y, const void* gate,
+                                              const float* norm_weight, void* out, int64_t rows,
+                                              int64_t width, int64_t group_size,
+                                              int64_t y_row_stride, int64_t gate_row_stride,
+                                              int64_t out_row_stride, float eps,
+                                              ggrms_dtype_t dtype, uint32_t flags,
+                                              const ggrms_shape_t* shape, void* stream) {
+    return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                               gate_row_stride, out_row_stride, eps, dtype, flags, shape, stream);
+}
+
 extern "C" ggrms_status_t ggrms_forward_ex(const void* y, const void* gate,
                                            const float* norm_weight, void* out, int64_t rows,
                                            int64_t width, int64_t group_size,
                                            int64_t y_row_stride, int64_t gate_row_stride,
                                            int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
-                                           uint32_t flags, const ggrms_shape_t* shape,
-                                           void* stream) {
+                                           uint32_t flags, void* stream) {
+    if (flags & ~ggrms::kOperatorFlags) return GGRMS_ERROR_INVALID_VALUE;
     return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
-                               gate_row_stride, out_row_stride, eps, dtype, flags, shape, stream);
+                               gate_row_stride, out_row_stride, eps, dtype, flags, nullptr,
+                               stream);
 }
 
 extern "C" ggrms_status_t ggrms_forward(const void* y, const void* gate,
@@ -127,18 +140,5 @@ extern "C" ggrms_status_t ggrms_forward(const void* y, const void* gate,
     return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
                                gate_row_stride, out_row_stride, eps, dtype,
                                round_intermediate ? GGRMS_FLAG_ROUND_INTERMEDIATE : 0u, nullptr,
-                               stream);
-}
-
-extern "C" ggrms_status_t ggrms_forward_with_shape(
-    const void* y, const void* gate, const float* norm_weight, void* out, int64_t rows,
-    int64_t width, int64_t group_size, int64_t y_row_stride, int64_t gate_row_stride,
-    int64_t out_row_stride, float eps, ggrms_dtype_t dtype, int round_intermediate,
-    int lanes_per_group, int vectors_per_lane, int rows_per_workgroup, void* stream) {
-    if (round_intermediate != 0 && round_intermediate != 1) return GGRMS_ERROR_INVALID_VALUE;
-    const ggrms_shape_t shape = {lanes_per_group, vectors_per_lane, rows_per_workgroup};
-    return ggrms::forward_impl(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
-                               gate_row_stride, out_row_stride, eps, dtype,
-                               round_intermediate ? GGRMS_FLAG_ROUND_INTERMEDIATE : 0u, &shape,
                                stream);
 }

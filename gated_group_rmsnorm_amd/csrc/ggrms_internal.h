@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "ggrms.h"
+#include "ggrms_tuning.h"
 
 namespace ggrms {
 
@@ -145,11 +146,21 @@ inline int64_t launch_workgroups(const LaunchPlan& lp, int64_t r) {
     }
 }
 
+// Operator flags the _ex calls take; the _tuned calls also take the
+// ggrms_tuning_flag_t bits.
+constexpr uint32_t kOperatorFlags =
+    GGRMS_FLAG_ROUND_INTERMEDIATE | GGRMS_FLAG_NORM_BEFORE_GATE | GGRMS_FLAG_WEIGHT_PER_GROUP;
+constexpr uint32_t kTuningFlags = GGRMS_FLAG_CACHE_STREAM | GGRMS_FLAG_CACHE_KEEP |
+                                  GGRMS_FLAG_ORDER_ROWS | GGRMS_FLAG_ORDER_BANDED |
+                                  GGRMS_FLAG_WAVE_ONE | GGRMS_FLAG_WAVE_FOUR;
+
 // Validation and kernel choice; no HIP calls.  Implemented in plan.cpp.
-// `flags` are ggrms_flag_t bits.  shape == nullptr picks the shape; otherwise
-// its lanes/vectors are used if built and covering the group
-// (GGRMS_ERROR_NOT_SUPPORTED if not) and its rows_per_workgroup (0 = pick)
-// must be built for the shape and allowed by the weight's alignment.
+// `flags` are ggrms_flag_t and ggrms_tuning_flag_t bits.  shape == nullptr
+// picks everything; otherwise its vector_bytes (0 = widest allowed) must be
+// allowed by the alignment, its lanes/vectors (both 0 = pick) must be built
+// and cover the group (GGRMS_ERROR_NOT_SUPPORTED if not), and its
+// rows_per_workgroup (0 = pick) must be built for the shape and allowed by
+// the weight's alignment.
 ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const void* out,
                          int64_t rows, int64_t width, int64_t group_size, int64_t sy,
                          int64_t sg, int64_t so, float eps, int dtype, uint32_t flags,

@@ -1,12 +1,9 @@
-// kernels.cuh -- gfx950 (CDNA4) device code of the fused gated group-RMSNorm.
-//
-// Per (row n, group g) unit of G contiguous columns, col = g*G + j (the page
-// "gated_group_rmsnorm", math block):
-//   a_j  = f32(y) * silu(f32(gate))                      (widen, gate)
-//   m2   = sum_j a_j^2                                    (group reduction, f32)
-//   nf   = rsqrt(m2 / G + eps)                            (eps after the mean)
-//   out  = cast(w[col] * f32(cast(a_j * nf, dtype)), dtype) with the inner cast
-//          only when round_intermediate is set.
+// ggrms_kernels.hpp -- gfx950 (CDNA4) kernels of the fused gated
+// group-RMSNorm: how each launch shape maps (row, group) units onto lanes,
+// loads them, combines their sums and stores them.  The per-unit arithmetic
+// (widen, gate, sum of squares, normaliser, casts, weight) is the epilogue in
+// ggrms_epilogue.hpp, which these kernels call on units they load from global
+// memory.
 //
 // The op is HBM-bound (two 16-bit input streams and one output stream; a few
 // VALU ops per element), so the design is about moving bytes:
@@ -31,8 +28,9 @@
 //     deterministic run to run;
 //   * VALU work is kept low (it runs about half busy at the HBM rate): one
 //     exp and one reciprocal per silu, the normaliser as a fused multiply-add
-//     and v_rsq_f32, the silu-underflow test on raw gate bits, and fp16
-//     operands multiplied without a separate widening (v_fma_mix_f32);
+//     and v_rsq_f32, the silu-underflow test on raw gate bits, fp16 operands
+//     multiplied without a separate widening (v_fma_mix_f32), and packed
+//     groups leaving a neighbour's elements out with one select per piece;
 //   * which workgroup takes which rows and groups (row-major or XCD-banded
 //     order, WAVE workgroups of one or four waves) is a launch argument and
 //     changes no result bit.
@@ -44,130 +42,10 @@
 
 #include <type_traits>
 
+#include "ggrms_epilogue.hpp"
 #include "ggrms_internal.h"
 
 namespace ggrms {
-
-using u16 = unsigned short;
-using u32 = unsigned int;
-typedef u16 u16x2 __attribute__((ext_vector_type(2)));
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// Element types.  kSize = bytes per element.
-struct TF32 { static constexpr int kSize = 4; };
-struct TF16 { static constexpr int kSize = 2; };
-struct TBF16 { static constexpr int kSize = 2; };
-
-// Storage word for a VB-byte vector.
-template <int VB> struct VecWord;
-template <> struct VecWord<16> { using type = u32x4; };
-template <> struct VecWord<8> { using type = u32x2; };
-template <> struct VecWord<4> { using type = u32; };
-template <> struct VecWord<2> { using type = u16; };
-
-// ------------------------------------------------------------ conversions
-// 16-bit -> f32 widening is exact.  f32 -> 16-bit narrowing uses the gfx950
-// conversion instructions (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32), which round
-// to nearest even under the default mode and keep subnormals.
-
-template <class T> struct Cvt;
-
-template <> struct Cvt<TF32> {
-    static constexpr int kPerWord = 1;
-    __device__ static inline void unpack_word(u32 w, float* f) { f[0] = __uint_as_float(w); }
-    __device__ static inline u32 pack_word(const float* f) { return __float_as_uint(f[0]); }
-    __device__ static inline void round_trip(float*) {}
-};
-
-template <> struct Cvt<TBF16> {
-    static constexpr int kPerWord = 2;
-    __device__ static inline void unpack_word(u32 w, float* f) {
-        f[0] = __uint_as_float(w << 16);
-        f[1] = __uint_as_float(w & 0xFFFF0000u);
-    }
-    __device__ static inline u32 pack_word(const float* f) {
-        f32x2 v = {f[0], f[1]};
-        return __builtin_bit_cast(u32, __builtin_convertvector(v, bf16x2));
-    }
-    __device__ static inline float unpack_half(u16 h) { return __uint_as_float((u32)h << 16); }
-    __device__ static inline u16 pack_half(float f) {
-        return __builtin_bit_cast(u16, (__bf16)f);
-    }
-    __device__ static inline void round_trip(float* f) { unpack_word(pack_word(f), f); }
-};
-
-template <> struct Cvt<TF16> {
-    static constexpr int kPerWord = 2;
-    __device__ static inline void unpack_word(u32 w, float* f) {
-        f32x2 v = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
-        f[0] = v.x;
-        f[1] = v.y;
-    }
-    __device__ static inline u32 pack_word(const float* f) {
-        f32x2 v = {f[0], f[1]};
-        return __builtin_bit_cast(u32, __builtin_convertvector(v, f16x2));
-    }
-    __device__ static inline float unpack_half(u16 h) {
-        return (float)__builtin_bit_cast(_Float16, h);
-    }
-    __device__ static inline u16 pack_half(float f) {
-        return __builtin_bit_cast(u16, (_Float16)f);
-    }
-    __device__ static inline void round_trip(float* f) { unpack_word(pack_word(f), f); }
-};
-
-// A VB-byte vector of T: N elements.
-template <class T, int VB> struct Packet {
-    static constexpr int N = VB / T::kSize;
-    using W = typename VecWord<VB>::type;
-
-    __device__ static inline void unpack(const W& v, float (&f)[N]) {
-        if constexpr (VB == 2) {
-            f[0] = Cvt<T>::unpack_half(v);
-        } else if constexpr (VB == 4) {
-            Cvt<T>::unpack_word(v, f);
-        } else {
-#pragma unroll
-            for (int i = 0; i < VB / 4; ++i) Cvt<T>::unpack_word(v[i], f + i * Cvt<T>::kPerWord);
-        }
-    }
-
-    __device__ static inline W pack(const float (&f)[N]) {
-        if constexpr (VB == 2) {
-            return Cvt<T>::pack_half(f[0]);
-        } else if constexpr (VB == 4) {
-            return Cvt<T>::pack_word(f);
-        } else {
-            W v;
-#pragma unroll
-            for (int i = 0; i < VB / 4; ++i) v[i] = Cvt<T>::pack_word(f + i * Cvt<T>::kPerWord);
-            return v;
-        }
-    }
-
-    // cast to T and back, element-wise
-    __device__ static inline void round_trip(float (&f)[N]) {
-        if constexpr (VB == 2) {
-            f[0] = Cvt<T>::unpack_half(Cvt<T>::pack_half(f[0]));
-        } else {
-#pragma unroll
-            for (int i = 0; i < N; i += Cvt<T>::kPerWord) Cvt<T>::round_trip(f + i);
-        }
-    }
-};
-
-// 32-bit word i of a VB-byte vector (VB >= 4).
-template <int VB, class W> __device__ inline uint32_t word_of(const W& v, int i) {
-    if constexpr (VB == 4)
-        return (uint32_t)v;
-    else
-        return v[i];
-}
 
 // Accesses of y, gate and out.  Each is touched once per launch; with NT they
 // carry the non-temporal hint (the nt bit), which on gfx950 takes a large
@@ -205,137 +83,9 @@ template <int N> __device__ inline void load_weights(const float* p, float (&w)[
     }
 }
 
-// ------------------------------------------------------------ arithmetic
-
-// silu(x) = x / (1 + e^-x): e^-x by v_exp_f32 (2^t with t = -x*log2 e), the
-// reciprocal by v_rcp_f32, five VALU operations.  The reciprocal is only
-// trusted while its result is a normal number, i.e. while 1 + e^-x < 2^126
-// (x > -87.33); below that it may flush to zero where the quotient is a tiny
-// non-zero number.  silu_exact scales both operands by 2^-64 once the
-// denominator passes 2^64, which keeps the reciprocal normal and changes no
-// bits elsewhere (power-of-two scalings are exact); kernels take it only when
-// some gate of the wave is below kSiluFastMin.
-constexpr float kSiluFastMin = -87.0f;
-
-// Whether some gate is below kSiluFastMin, from the raw bits: for negative
-// numbers the sign-magnitude pattern, read as an unsigned integer of the
-// element's width, grows with the magnitude, so the lane keeps the largest
-// pattern of its gate words (one packed 16-bit maximum per two bf16/fp16
-// gates, no widening) and compares it with the pattern of -87 at the end.
-// A NaN with its sign bit set also selects the exact form, which gives it
-// the same result.
-template <class T> __device__ inline u32 gate_max_word(u32 acc, u32 w) {
-    if constexpr (T::kSize == 4)
-        return acc > w ? acc : w;
-    else
-        return __builtin_bit_cast(u32, __builtin_elementwise_max(__builtin_bit_cast(u16x2, acc),
-                                                                  __builtin_bit_cast(u16x2, w)));
-}
-template <class T> struct FastMinBits;  // bit pattern of kSiluFastMin (-87)
-template <> struct FastMinBits<TF32> { static constexpr u32 v = 0xC2AE0000u; };
-template <> struct FastMinBits<TBF16> { static constexpr u32 v = 0xC2AEu; };
-template <> struct FastMinBits<TF16> { static constexpr u32 v = 0xD570u; };
-template <class T> __device__ inline bool gate_below_fast_min(u32 acc) {
-    if constexpr (T::kSize == 4) {
-        return acc > FastMinBits<T>::v;
-    } else {
-        const u32 lo = acc & 0xFFFFu, hi = acc >> 16;
-        return (lo > hi ? lo : hi) > FastMinBits<T>::v;
-    }
-}
-
-__device__ inline float silu_fast(float x) {
-    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
-    return x * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-__device__ inline float silu_exact(float x) {
-    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
-    const float d = 1.0f + e;
-    const float sc = d > 0x1p64f ? 0x1p-64f : 1.0f;
-    return (x * sc) * __builtin_amdgcn_rcpf(d * sc);
-}
-
-// -0.0f that the compiler cannot see through (a v_mov of the bit pattern),
-// so that fma(x, b, nz) is kept as an FMA instead of being folded into a
-// multiply.
-__device__ inline float opaque_neg_zero() {
-    float z;
-    asm("v_mov_b32 %0, 0x80000000" : "=v"(z));
-    return z;
-}
-
-// f32(half h of the fp16 pair `word`) * b, rounded once, as fma(x, b, -0):
-// gfx950 issues it as one v_fma_mix_f32, which widens the 16-bit operand
-// exactly inside the FMA and so saves the separate v_cvt_f32_f16 of each fp16
-// operand; the addend -0 leaves every product -- a zero's sign included -- as
-// the f32 multiply of the widened value gives it.  The compiler emits the
-// instruction itself, so its hazard checks cover it (a transcendental's result
-// read by the next VALU instruction needs a wait state).  gfx950 has no bf16
-// form.
-__device__ inline float mul_f16(uint32_t word, int h, float b, float nz) {
-    const _Float16 x = __builtin_bit_cast(_Float16, (u16)(h ? word >> 16 : word & 0xFFFFu));
-    return __builtin_fmaf((float)x, b, nz);
-}
-
-// silu_fast of half h of an fp16 pair, and y * silu(gate) for element h of
-// the pairs yw, gw, with the widening folded into the multiplies: the same
-// operations in the same order as y * silu_fast(gate) on widened values.
-__device__ inline float gated_f16(uint32_t yw, uint32_t gw, int h, float nz) {
-    const float e = __builtin_amdgcn_exp2f(mul_f16(gw, h, -1.4426950408889634f, nz));
-    const float s = mul_f16(gw, h, __builtin_amdgcn_rcpf(1.0f + e), nz);
-    return mul_f16(yw, h, s, nz);
-}
-
-// DPP move with all rows and banks enabled.
-template <int CTRL> __device__ inline float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ inline float readlane(float v, int lane) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
-}
-
-// Sum over aligned segments of SEG lanes (SEG a power of two, <= 64).  Every
-// lane of a segment gets the same bits.  Steps: swap neighbours, swap pairs
-// (quad_perm), mirror within 8 (row_half_mirror), mirror within 16
-// (row_mirror); then whole 16-lane rows are combined with v_readlane.
-template <int SEG> __device__ inline float segment_sum(float v) {
-    if constexpr (SEG >= 2) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    if constexpr (SEG >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    if constexpr (SEG >= 8) v += dpp<0x141>(v);  // row_half_mirror
-    if constexpr (SEG >= 16) v += dpp<0x140>(v); // row_mirror
-    if constexpr (SEG == 32) {
-        const float r0 = readlane(v, 0), r1 = readlane(v, 16);
-        const float r2 = readlane(v, 32), r3 = readlane(v, 48);
-        v = (threadIdx.x & 32) ? (r2 + r3) : (r0 + r1);
-    }
-    if constexpr (SEG == 64) {
-        const float r0 = readlane(v, 0), r1 = readlane(v, 16);
-        const float r2 = readlane(v, 32), r3 = readlane(v, 48);
-        v = (r0 + r1) + (r2 + r3);
-    }
-    return v;
-}
-
 // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): gfx9 encoding (vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) -- waits for vector memory only.
 constexpr int kWaitVmcnt0 = 0x0F70;
-
-// nf = 1/sqrt(m2/G + eps): the mean and eps in one fused multiply-add with
-// 1/G rounded once on the host, then v_rsq_f32 (about 1 ulp).  The result is
-// within a few f32 ulp of the correctly rounded steps (divide, add, square
-// root, divide), for a few VALU operations instead of ~35 IEEE-exact ones
-// per lane.  An argument below FLT_MIN is scaled by 2^64 first and the
-// result by 2^32, so tiny means are not flushed; 0 gives +inf, inf gives 0,
-// NaN stays NaN.
-__device__ inline float norm_factor(float m2, float ginv, float eps) {
-    const float v = __builtin_fmaf(m2, ginv, eps);
-    const bool tiny = v < 0x1p-126f;
-    const float r = __builtin_amdgcn_rsqf(tiny ? v * 0x1p64f : v);
-    return tiny ? r * 0x1p32f : r;
-}
 
 __device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t s) {
     return (__umulhi(n, m) + n) >> s;
@@ -403,9 +153,10 @@ __device__ inline void store_piece_stream(char* p, const W& v, int piece) {
 }
 
 // Lane `sl` of the SEG lanes that own the unit (row n, group g) loads VPT
-// vectors (indices sl, sl+SEG, ...), computes its share, reduces with
-// `reduce`, and stores if `store_ok`.  With WSource::Lds, `wl` points at the
-// group's weights in LDS, valid once `reduce` has passed its barrier.
+// vectors (indices sl, sl+SEG, ...), runs the epilogue's per-unit steps on
+// them, sums its share with `reduce`, and stores if `store_ok`.  With
+// WSource::Lds, `wl` points at the group's weights in LDS, valid once
+// `reduce` has passed its barrier.
 //
 // PB == VB: every group starts on a vector boundary and spans a.nvec whole
 // vectors.  PB < VB (packed): the group's byte length is not a multiple of
@@ -424,6 +175,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     constexpr int N = P::N;
     using S = typename VecWord<T::kSize>::type;  // element storage
     constexpr bool kPacked = PB < VB;
+    constexpr int PE = PB / T::kSize;  // elements per piece
     static_assert(!kPacked || (VB == 16 && WS == WSource::Global), "packed: 16-byte vectors");
     // With three or more vectors per lane the per-lane weights are loaded
     // after the reduction, so they are not live at the same time as the
@@ -462,83 +214,13 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
         if constexpr (WS == WSource::Global && !kLateWeights)
             load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
     }
-    // whether element e of vector k belongs to the unit (always, unless packed)
-    auto owned = [&](int k, int e) {
-        return !kPacked || (uint32_t)(rel[k] + e) < a.G;
-    };
+    // whether piece q of vector k belongs to the unit (packed groups only)
+    auto owned = [&](int k, int q) { return (uint32_t)(rel[k] + q * PE) < a.G; };
+    // lanes past the group's end hold a copy of its last vector
+    auto live = [&](int k) { return sl + k * SEG < nv; };
 
-    // Gate first: a = y * silu(gate) for every loaded element.  Norm first:
-    // a = y, and silu(gate) is kept for the output.  Lanes past the group's end
-    // hold a copy of its last vector and their partial sum is dropped by one
-    // select per vector (no per-element predication).
-    float av[VPT][N];
-    // norm first: silu(gate), computed here (before the reduction, while
-    // other waves' loads are in flight) rather than after it
-    float sgv[NBG ? VPT : 1][N];
-    float acc = 0.0f;
-    unsigned gmax = 0;
-    // fp16 gate first: the widening folded into the multiplies (mul_f16)
-    constexpr bool kMix = std::is_same<T, TF16>::value && VB >= 4 && !NBG;
-    const float nz = kMix ? opaque_neg_zero() : 0.0f;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        float yf[N], gf[N];
-        if constexpr (!kMix) {
-            P::unpack(yr[k], yf);
-            P::unpack(gr[k], gf);
-        }
-        if constexpr (VB <= 4) {
-            gmax = gate_max_word<T>(gmax, (unsigned)gr[k]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < VB / 4; ++i) gmax = gate_max_word<T>(gmax, gr[k][i]);
-        }
-        float part = 0.0f;
-#pragma unroll
-        for (int e = 0; e < N; ++e) {
-            float x;
-            if constexpr (kMix)
-                x = gated_f16(word_of<VB>(yr[k], e / 2), word_of<VB>(gr[k], e / 2), e & 1, nz);
-            else
-                x = NBG ? yf[e] : yf[e] * silu_fast(gf[e]);
-            if constexpr (NBG) sgv[k][e] = silu_fast(gf[e]);
-            av[k][e] = x;
-            const float xx = __builtin_fmaf(x, x, part);
-            part = owned(k, e) ? xx : part;
-        }
-        acc += (sl + k * SEG < nv) ? part : 0.0f;
-    }
-    // Rare: a gate deep in silu's underflow range.  Redo the wave's silu with
-    // the exact form (identical bits for every other gate).
-    const bool exact_silu = __builtin_expect(__any(gate_below_fast_min<T>(gmax)), 0);
-    if (NBG && exact_silu) {
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            float gf[N];
-            P::unpack(gr[k], gf);
-#pragma unroll
-            for (int e = 0; e < N; ++e) sgv[k][e] = silu_exact(gf[e]);
-        }
-    }
-    if (!NBG && exact_silu) {
-        acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            float yf[N], gf[N];
-            P::unpack(yr[k], yf);
-            P::unpack(gr[k], gf);
-            float part = 0.0f;
-#pragma unroll
-            for (int e = 0; e < N; ++e) {
-                const float x = yf[e] * silu_exact(gf[e]);
-                av[k][e] = x;
-                const float xx = __builtin_fmaf(x, x, part);
-                part = owned(k, e) ? xx : part;
-            }
-            acc += (sl + k * SEG < nv) ? part : 0.0f;
-        }
-    }
-
+    epi::LaneUnit<T, VB, VPT, NBG> L;
+    const float acc = epi::gate_and_square<T, VB, PB, VPT, NBG>(yr, gr, L, live, owned);
     const float m2 = reduce(acc);
     const float nf = norm_factor(m2, a.Ginv, a.eps);
     if constexpr (WS == WSource::Lds) {
@@ -555,31 +237,9 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     // completion between the wave's stores.  The builtin form lets the
     // compiler's wait insertion see the wait.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    auto finish = [&](auto ri_tag) {
-        constexpr bool RI = decltype(ri_tag)::value;
+    auto store = [&](auto ri_tag) {
         W res[VPT];
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            float t[N];
-#pragma unroll
-            for (int e = 0; e < N; ++e) t[e] = av[k][e] * nf;
-            if constexpr (NBG) {
-                // ((y * nf) * w) * silu(gate), every intermediate f32
-#pragma unroll
-                for (int e = 0; e < N; ++e) t[e] = (t[e] * wr[k][e]) * sgv[k][e];
-            } else if constexpr (RI && kMix) {
-                // cast to fp16, then weight * f32(cast) with the widening folded in
-                const W h = P::pack(t);
-#pragma unroll
-                for (int e = 0; e < N; ++e)
-                    t[e] = mul_f16(word_of<VB>(h, e / 2), e & 1, wr[k][e], nz);
-            } else {
-                if constexpr (RI) P::round_trip(t);
-#pragma unroll
-                for (int e = 0; e < N; ++e) t[e] = wr[k][e] * t[e];
-            }
-            res[k] = P::pack(t);
-        }
+        epi::finish<decltype(ri_tag)::value>(L, nf, wr, res);
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const uint32_t idx = sl + k * SEG;
@@ -587,11 +247,10 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
             if constexpr (kPacked) {
                 if (rel[k] < 0 || rel[k] + N > (int32_t)a.G) {
                     // a vector on a group boundary: only this unit's pieces
-                    constexpr int PE = PB / T::kSize;
                     char* base = reinterpret_cast<char*>(ov + v0 + idx);
 #pragma unroll
                     for (int q = 0; q < VB / PB; ++q)
-                        if (owned(k, q * PE)) store_piece_stream<NT, PB>(base + q * PB, res[k], q);
+                        if (owned(k, q)) store_piece_stream<NT, PB>(base + q * PB, res[k], q);
                     continue;
                 }
             }
@@ -599,9 +258,9 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
         }
     };
     if (!NBG && round_intermediate(a))
-        finish(std::true_type{});
+        store(std::true_type{});
     else
-        finish(std::false_type{});
+        store(std::false_type{});
 }
 
 // ------------------------------------------------------------ kernels

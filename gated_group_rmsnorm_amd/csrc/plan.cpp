@@ -46,6 +46,25 @@ bool views_overlap(uintptr_t a, int64_t sa, uintptr_t b, int64_t sb, int64_t row
     return false;
 }
 
+// Whether a [rows, len-byte] view at a with byte row stride sa (>= len when
+// rows > 1) shares any byte with the range [b, b + nb).  Exact: row i covers
+// [a + i*sa, a + i*sa + len), and some row meets the range iff an integer i in
+// [0, rows) has b - a - len < i*sa < b + nb - a.
+bool view_meets_range(uintptr_t a, int64_t sa, int64_t rows, int64_t len, int64_t ext_a,
+                      uintptr_t b, int64_t nb) {
+    if (a + (uintptr_t)ext_a <= b || b + (uintptr_t)nb <= a) return false;
+    if (rows == 1) return true;
+    const int64_t D = (int64_t)(b - a);  // |D| < 2^63: both ranges fit the address space
+    // smallest i with i*sa > D - len, largest i with i*sa < D + nb
+    const int64_t lo = D - len;
+    int64_t i0 = lo >= 0 ? lo / sa + 1 : -((-lo) / sa);
+    const int64_t hi = D + nb;
+    int64_t i1 = hi > 0 ? (hi - 1) / sa : -((-hi) / sa) - 1;
+    if (i0 < 0) i0 = 0;
+    if (i1 > rows - 1) i1 = rows - 1;
+    return i0 <= i1;
+}
+
 int64_t round_up_pow2(int64_t x) {
     int64_t p = 1;
     while (p < x) p <<= 1;
@@ -148,11 +167,13 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     memset(plan, 0, sizeof *plan);
     if (rows < 0 || width <= 0 || group_size <= 0 || width % group_size != 0)
         return GGRMS_ERROR_INVALID_VALUE;
-    const uint32_t known = GGRMS_FLAG_ROUND_INTERMEDIATE | GGRMS_FLAG_NORM_BEFORE_GATE |
-                           GGRMS_FLAG_WEIGHT_PER_GROUP | GGRMS_FLAG_CACHE_STREAM |
-                           GGRMS_FLAG_CACHE_KEEP | GGRMS_FLAG_ORDER_ROWS |
-                           GGRMS_FLAG_ORDER_BANDED | GGRMS_FLAG_WAVE_ONE | GGRMS_FLAG_WAVE_FOUR;
-    if (flags & ~known) return GGRMS_ERROR_INVALID_VALUE;
+    if (flags & ~(kOperatorFlags | kTuningFlags)) return GGRMS_ERROR_INVALID_VALUE;
+    if (shape && (shape->lanes_per_group < 0 || shape->vectors_per_lane < 0 ||
+                  shape->rows_per_workgroup < 0 ||
+                  (shape->vector_bytes != 0 && shape->vector_bytes != 2 &&
+                   shape->vector_bytes != 4 && shape->vector_bytes != 8 &&
+                   shape->vector_bytes != 16)))
+        return GGRMS_ERROR_INVALID_VALUE;
     if (((flags & GGRMS_FLAG_ORDER_ROWS) && (flags & GGRMS_FLAG_ORDER_BANDED)) ||
         ((flags & GGRMS_FLAG_WAVE_ONE) && (flags & GGRMS_FLAG_WAVE_FOUR)))
         return GGRMS_ERROR_INVALID_VALUE;
@@ -194,15 +215,23 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         return GGRMS_ERROR_INVALID_VALUE;
     if (!alias_g && views_overlap(po, bo, pg, bg, rows, row_bytes, eo, eg))
         return GGRMS_ERROR_INVALID_VALUE;
+    // Every row reads the weight, so out must not share a byte with it.
+    if (view_meets_range(po, bo, rows, row_bytes, eo, pw, ew)) return GGRMS_ERROR_INVALID_VALUE;
 
     // Widest vector every access can use: the three views' base pointers and
-    // row strides, the group's byte length, and the matching weight loads.
+    // row strides, the group's byte length, and the matching weight loads
+    // (or the caller's vector width, if those allow it).
+    auto vector_fits = [&](int cand) {
+        const int64_t wal = cand / esize * 4 < 16 ? cand / esize * 4 : 16;
+        return py % cand == 0 && pg % cand == 0 && po % cand == 0 && by % cand == 0 &&
+               bg % cand == 0 && bo % cand == 0 && (group_size * esize) % cand == 0 &&
+               pw % wal == 0;
+    };
+    const int force_vb = shape ? shape->vector_bytes : 0;
+    if (force_vb && force_vb < esize) return GGRMS_ERROR_NOT_SUPPORTED;
     int vb = esize;
     for (int cand = 16; cand > esize; cand >>= 1) {
-        const int64_t wal = cand / esize * 4 < 16 ? cand / esize * 4 : 16;
-        if (py % cand == 0 && pg % cand == 0 && po % cand == 0 && (by % cand == 0) &&
-            (bg % cand == 0) && (bo % cand == 0) && (group_size * esize) % cand == 0 &&
-            pw % wal == 0) {
+        if (vector_fits(cand) && (!force_vb || cand == force_vb)) {
             vb = cand;
             break;
         }
@@ -218,7 +247,8 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     // pb-byte pieces.  Only with a per-column weight (its vectors then line up
     // with the data's) and groups of more than one vector.
     const int64_t gbytes = group_size * esize;
-    if (vb < 16 && gbytes > 16 && row_bytes % 16 == 0 && py % 16 == 0 && pg % 16 == 0 &&
+    if (vb < 16 && (!force_vb || force_vb == 16) && gbytes > 16 && row_bytes % 16 == 0 &&
+        py % 16 == 0 && pg % 16 == 0 &&
         po % 16 == 0 && by % 16 == 0 && bg % 16 == 0 && bo % 16 == 0 && pw % 16 == 0 &&
         !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP)) {
         int64_t gcd = 16;
@@ -230,13 +260,11 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
             nvec = nvp;
         }
     }
+    if (force_vb && vb != force_vb) return GGRMS_ERROR_NOT_SUPPORTED;
     const bool packed = pb < vb;
     int kernel = 0, lanes = 0, vpt = 0, rule_upb = 1;
     const int force_upb = shape ? shape->rows_per_workgroup : 0;
-    if (force_upb < 0) return GGRMS_ERROR_INVALID_VALUE;
-    if (shape) {
-        if (shape->lanes_per_group == 0 && shape->vectors_per_lane == 0)
-            return GGRMS_ERROR_INVALID_VALUE;
+    if (shape && (shape->lanes_per_group != 0 || shape->vectors_per_lane != 0)) {
         kernel = kernel_for_shape(shape->lanes_per_group, shape->vectors_per_lane);
         lanes = shape->lanes_per_group;
         vpt = shape->vectors_per_lane;
@@ -339,12 +367,13 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
 
 }  // namespace ggrms
 
-extern "C" ggrms_status_t ggrms_plan_ex(const void* y, const void* gate,
-                                        const float* norm_weight, void* out, int64_t rows,
-                                        int64_t width, int64_t group_size, int64_t y_row_stride,
-                                        int64_t gate_row_stride, int64_t out_row_stride,
-                                        float eps, ggrms_dtype_t dtype, uint32_t flags,
-                                        const ggrms_shape_t* shape, ggrms_plan_t* plan) {
+extern "C" ggrms_status_t ggrms_plan_tuned(const void* y, const void* gate,
+                                           const float* norm_weight, void* out, int64_t rows,
+                                           int64_t width, int64_t group_size,
+                                           int64_t y_row_stride, int64_t gate_row_stride,
+                                           int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
+                                           uint32_t flags, const ggrms_shape_t* shape,
+                                           ggrms_plan_t* plan) {
     if (!plan) return GGRMS_ERROR_INVALID_VALUE;
     ggrms::LaunchPlan lp;
     const ggrms_status_t st = ggrms::make_plan(y, gate, norm_weight, out, rows, width, group_size,
@@ -354,15 +383,26 @@ extern "C" ggrms_status_t ggrms_plan_ex(const void* y, const void* gate,
     return st;
 }
 
+extern "C" ggrms_status_t ggrms_plan_ex(const void* y, const void* gate,
+                                        const float* norm_weight, void* out, int64_t rows,
+                                        int64_t width, int64_t group_size, int64_t y_row_stride,
+                                        int64_t gate_row_stride, int64_t out_row_stride,
+                                        float eps, ggrms_dtype_t dtype, uint32_t flags,
+                                        ggrms_plan_t* plan) {
+    if (flags & ~ggrms::kOperatorFlags) return GGRMS_ERROR_INVALID_VALUE;
+    return ggrms_plan_tuned(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                            gate_row_stride, out_row_stride, eps, dtype, flags, nullptr, plan);
+}
+
 extern "C" ggrms_status_t ggrms_plan(const void* y, const void* gate, const float* norm_weight,
                                      void* out, int64_t rows, int64_t width, int64_t group_size,
                                      int64_t y_row_stride, int64_t gate_row_stride,
                                      int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
                                      int round_intermediate, ggrms_plan_t* plan) {
     if (round_intermediate != 0 && round_intermediate != 1) return GGRMS_ERROR_INVALID_VALUE;
-    return ggrms_plan_ex(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
-                         gate_row_stride, out_row_stride, eps, dtype,
-                         round_intermediate ? GGRMS_FLAG_ROUND_INTERMEDIATE : 0u, nullptr, plan);
+    return ggrms_plan_tuned(y, gate, norm_weight, out, rows, width, group_size, y_row_stride,
+                            gate_row_stride, out_row_stride, eps, dtype,
+                            round_intermediate ? GGRMS_FLAG_ROUND_INTERMEDIATE : 0u, nullptr, plan);
 }
 
 extern "C" const char* ggrms_status_string(ggrms_status_t status) {

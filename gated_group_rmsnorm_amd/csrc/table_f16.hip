@@ -1,7 +1,7 @@
 // table_f16.hip -- instantiates every kernel shape for one element
 // type and one operator (gate-first), with and without the streaming hint,
 // so the six combinations compile in parallel.
-#include "kernels.cuh"
+#include "ggrms_kernels.hpp"
 
 namespace ggrms {
 

@@ -29,15 +29,16 @@
  * Layout.  y, gate and out are row-major [rows, width] views with unit column
  * stride and their own row strides, so y and gate may be column slices of one
  * fused in-projection buffer (the page's Parallelization section reads strided
- * views directly).  Rows are tokens of one or more sequences, flattened
- * (the page's "standalone varlen op"); leading axes fold into rows.
+ * views directly).  Rows are tokens of one or more sequences of any lengths,
+ * flattened into one axis (the page's intro: the op stands alone and takes
+ * variable-length batches); leading axes fold into rows.
  *
  * Threading and ownership.  The caller owns every buffer.  The library
  * allocates nothing, frees nothing, keeps no pointer after a call returns,
  * never synchronises, and is safe to call from several threads at once.
- * ggrms_forward only enqueues work on `stream` and returns (the page's
- * "Enqueues" entry point); results are ready when the stream reaches that
- * point.  Faults inside the kernel surface at the caller's next
+ * ggrms_forward only enqueues work on `stream` and returns (as the page's
+ * Functions section describes its GPU entry point); results are ready when
+ * the stream reaches that point.  Faults inside the kernel surface at the caller's next
  * synchronisation with that stream.  A call may be captured into a HIP graph
  * (stream capture) and replayed: it allocates nothing, waits for nothing and
  * enqueues nothing but its kernel launches, whose arguments are fixed at
@@ -53,10 +54,11 @@
 extern "C" {
 #endif
 
-#define GGRMS_ABI_VERSION 4
+#define GGRMS_ABI_VERSION 5
 
-/* The library exports these functions and nothing else (it is built with
- * hidden visibility). */
+/* The library exports the functions declared here and in ggrms_tuning.h
+ * (launch controls for tuning and cross-checks) and nothing else (it is
+ * built with hidden visibility). */
 #if defined(__GNUC__)
 #define GGRMS_API __attribute__((visibility("default")))
 #else
@@ -91,7 +93,8 @@ typedef enum {
  *                 view of `dtype`; every element of the view is written,
  *                 nothing outside it is touched.  out may be exactly y or
  *                 exactly gate (same pointer and same row stride: in place);
- *                 any other overlap with y or gate is rejected.
+ *                 any other overlap with y or gate, and any overlap with
+ *                 norm_weight (which every row reads), is rejected.
  *   rows          number of rows (tokens), >= 0.  rows == 0 enqueues nothing.
  *   width         columns per row, > 0, a multiple of group_size.
  *   group_size    columns per normalisation group (G), > 0.
@@ -114,9 +117,10 @@ typedef enum {
  * when rows > 0, a row stride < width when rows > 1, a misaligned pointer,
  * round_intermediate other than 0 or 1, a NaN, infinite or negative eps,
  * extents that overflow 64-bit addressing, or a disallowed overlap of out
- * with y or gate; GGRMS_ERROR_NOT_SUPPORTED for an unknown dtype.  Then the
- * current device is checked (GGRMS_ERROR_NOT_SUPPORTED unless gfx950) and
- * the kernels are launched (GGRMS_ERROR_LAUNCH if the runtime refuses one).
+ * with y, gate or norm_weight; GGRMS_ERROR_NOT_SUPPORTED for an unknown
+ * dtype.  Then the current device is checked (GGRMS_ERROR_NOT_SUPPORTED
+ * unless gfx950) and the kernels are launched (GGRMS_ERROR_LAUNCH if the
+ * runtime refuses one).
  */
 GGRMS_API ggrms_status_t ggrms_forward(const void* y, const void* gate, const float* norm_weight,
                                        void* out, int64_t rows, int64_t width, int64_t group_size,
@@ -142,7 +146,8 @@ typedef struct {
     int32_t rows_per_workgroup; /* BLOCK: rows of one group per workgroup (weights shared in LDS) */
     int32_t lds_bytes;        /* dynamic LDS per workgroup (the staged weights) */
     int64_t workgroups;       /* workgroups over all launches */
-    int32_t streaming;        /* 1: y/gate/out loads and stores carry the non-temporal hint */
+    int32_t streaming;        /* 1: y/gate/out loads and stores carry the non-temporal hint
+                                 (the default for jobs of at least GGRMS_STREAM_MIN_BYTES) */
     int32_t piece_bytes;      /* == vector_bytes when every group starts on a vector
                                  boundary; 2, 4 or 8 for packed groups (see below) */
     int32_t tile_order;       /* order in which workgroups take the job's tiles:
@@ -199,98 +204,40 @@ typedef enum {
     /* norm_weight holds group_size values shared by every group (indexed by
      * the column within the group), as that page's `scale` input does;
      * without it, width values indexed by the column. */
-    GGRMS_FLAG_WEIGHT_PER_GROUP = 4,
-    /* Cache policy for y, gate and out (the weight is always cached).  By
-     * default a job whose y, gate and out views hold at least
-     * GGRMS_STREAM_MIN_BYTES together is streamed: its loads and stores carry
-     * the non-temporal hint, which keeps a large one-pass stream from
-     * evicting other data and runs it faster.  Smaller jobs (decode) use
-     * plain accesses, so inputs still cached from the kernel that wrote them
-     * are hit and the output stays cached for the kernel that reads it next.
-     * CACHE_STREAM forces the hint, CACHE_KEEP forces plain accesses; setting
-     * both is GGRMS_ERROR_INVALID_VALUE.  Results are identical either way. */
-    GGRMS_FLAG_CACHE_STREAM = 8,
-    GGRMS_FLAG_CACHE_KEEP = 16,
-    /* Launch controls, for tuning and cross-checks; results are identical
-     * whatever they select.  ORDER_ROWS / ORDER_BANDED force the tile order
-     * (plan field tile_order; BANDED has no effect on WIDE).  WAVE_ONE /
-     * WAVE_FOUR force WAVE workgroups of one or four waves (by default one
-     * for 16-byte vectors, four for narrower vectors and packed groups;
-     * no effect on BLOCK and WIDE).  ORDER_ROWS with ORDER_BANDED and
-     * WAVE_ONE with WAVE_FOUR are GGRMS_ERROR_INVALID_VALUE. */
-    GGRMS_FLAG_ORDER_ROWS = 32,
-    GGRMS_FLAG_ORDER_BANDED = 64,
-    GGRMS_FLAG_WAVE_ONE = 128,
-    GGRMS_FLAG_WAVE_FOUR = 256
+    GGRMS_FLAG_WEIGHT_PER_GROUP = 4
 } ggrms_flag_t;
 
-/* Job size (bytes of y, gate and out together) from which the default cache
- * policy streams. */
+/* Cache policy.  y, gate and out are each touched once per call.  A job
+ * whose y, gate and out views hold at least GGRMS_STREAM_MIN_BYTES together
+ * is streamed: its loads and stores carry the non-temporal hint, which keeps
+ * a large one-pass stream from evicting other data and runs it faster.
+ * Smaller jobs (decode) use plain accesses, so inputs still cached from the
+ * kernel that wrote them are hit and the output stays cached for the kernel
+ * that reads it next.  The weight is always cached.  Results do not depend
+ * on the policy. */
 #define GGRMS_STREAM_MIN_BYTES (4ll << 20)
 
-/* A kernel shape for the _ex calls (see ggrms_forward_with_shape). */
-typedef struct {
-    int32_t lanes_per_group;
-    int32_t vectors_per_lane;
-    int32_t rows_per_workgroup; /* 0: let the library choose */
-} ggrms_shape_t;
-
 /*
- * ggrms_forward_ex -- ggrms_forward with operator flags (a ggrms_flag_t
- * mask) instead of round_intermediate, and an optional kernel shape (NULL:
- * the library chooses).  The weight needs width values, or group_size with
- * GGRMS_FLAG_WEIGHT_PER_GROUP.  GGRMS_ERROR_INVALID_VALUE also for unknown
- * flag bits, GGRMS_FLAG_ROUND_INTERMEDIATE with GGRMS_FLAG_NORM_BEFORE_GATE,
- * or both cache flags; GGRMS_ERROR_NOT_SUPPORTED for a shape that cannot be
- * used (as in ggrms_forward_with_shape).
+ * ggrms_forward_ex -- ggrms_forward with operator flags (a mask of
+ * ggrms_flag_t) instead of round_intermediate.  The weight needs width
+ * values, or group_size with GGRMS_FLAG_WEIGHT_PER_GROUP.
+ * GGRMS_ERROR_INVALID_VALUE also for unknown flag bits (including the launch
+ * controls of ggrms_tuning.h, which only ggrms_forward_tuned takes) and for
+ * GGRMS_FLAG_ROUND_INTERMEDIATE with GGRMS_FLAG_NORM_BEFORE_GATE.
  */
 GGRMS_API ggrms_status_t ggrms_forward_ex(const void* y, const void* gate, const float* norm_weight,
                                           void* out, int64_t rows, int64_t width,
                                           int64_t group_size, int64_t y_row_stride,
                                           int64_t gate_row_stride, int64_t out_row_stride,
                                           float eps, ggrms_dtype_t dtype, uint32_t flags,
-                                          const ggrms_shape_t* shape, void* stream);
+                                          void* stream);
 
 /* ggrms_plan for ggrms_forward_ex's arguments (no HIP call). */
 GGRMS_API ggrms_status_t ggrms_plan_ex(const void* y, const void* gate, const float* norm_weight,
                                        void* out, int64_t rows, int64_t width, int64_t group_size,
                                        int64_t y_row_stride, int64_t gate_row_stride,
                                        int64_t out_row_stride, float eps, ggrms_dtype_t dtype,
-                                       uint32_t flags, const ggrms_shape_t* shape,
-                                       ggrms_plan_t* plan);
-
-/*
- * ggrms_forward_with_shape -- ggrms_forward with the kernel shape chosen by
- * the caller instead of by the library, for tuning and for cross-checking
- * the kernel families against each other.  Same arguments, semantics and
- * results as ggrms_forward, plus:
- *
- *   lanes_per_group   1, 2, 4, ..., 64 (WAVE kernel) or 128, 256, 512, 1024
- *                     (BLOCK kernel; 1024 with vectors_per_lane = 0 is WIDE)
- *   vectors_per_lane  1 for lanes < 64; 1..4 for 64 lanes or the BLOCK
- *                     kernel (also 6 with 256 lanes); 0 for WIDE
- *   rows_per_workgroup  0 to let the library choose; 1; or, for the BLOCK
- *                     kernel, 2 or 4 with 128 lanes and 2 with 256 lanes (the
- *                     workgroup's rows share one group, whose weights are
- *                     staged once in LDS; needs a 16-byte aligned weight and
- *                     group_size % 4 == 0)
- *
- * The vector width still follows the pointers' alignment.  For packed
- * groups (see "Vector width" above) the shape must cover the vectors of the
- * worst-aligned group, WIDE is not built and rows_per_workgroup must be 0 or
- * 1.  Returns GGRMS_ERROR_INVALID_VALUE for lanes and vectors both 0 (use
- * ggrms_forward), and GGRMS_ERROR_NOT_SUPPORTED for a shape that is not
- * built, whose lanes_per_group * vectors_per_lane vectors do not cover one
- * group, or whose rows_per_workgroup cannot be used.
- */
-GGRMS_API ggrms_status_t ggrms_forward_with_shape(const void* y, const void* gate,
-                                                  const float* norm_weight, void* out, int64_t rows,
-                                                  int64_t width, int64_t group_size,
-                                                  int64_t y_row_stride, int64_t gate_row_stride,
-                                                  int64_t out_row_stride, float eps,
-                                                  ggrms_dtype_t dtype, int round_intermediate,
-                                                  int lanes_per_group, int vectors_per_lane,
-                                                  int rows_per_workgroup, void* stream);
+                                       uint32_t flags, ggrms_plan_t* plan);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 GGRMS_API const char* ggrms_status_string(ggrms_status_t status);

@@ -79,19 +79,22 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: int, what: str = "") 
 def run_gpu(g, y, gate, w, out, rows, width, G, sy, sg, so, eps, dtype, ri, shape=None,
             stream=None, flags=None):
     """y/gate/out: device tensors (already offset views allowed); returns the
-    status.  flags (a mask of FLAG_*) selects ggrms_forward_ex instead of
-    ggrms_forward / ggrms_forward_with_shape; ri is then ignored."""
+    status.  No flags and no shape: ggrms_forward.  Operator flags only
+    (FLAG_RI, FLAG_NBG, FLAG_PER_GROUP): ggrms_forward_ex.  Launch controls
+    among the flags, or a forced shape (lanes, vectors[, rows per
+    workgroup[, vector bytes]]): ggrms_forward_tuned, with ri as FLAG_RI when
+    flags is None."""
     s = (stream or torch.cuda.current_stream()).cuda_stream
-    if flags is not None:
-        return g.ggrms_forward_ex(y.data_ptr(), gate.data_ptr(), w.data_ptr(), out.data_ptr(),
-                                  rows, width, G, sy, sg, so, eps, dtype, flags, s, shape)
-    if shape is None:
+    if flags is None and shape is None:
         return g.ggrms_forward(y.data_ptr(), gate.data_ptr(), w.data_ptr(), out.data_ptr(), rows,
                                width, G, sy, sg, so, eps, dtype, ri, s)
-    upb = shape[2] if len(shape) > 2 else 0
-    return g.ggrms_forward_with_shape(y.data_ptr(), gate.data_ptr(), w.data_ptr(), out.data_ptr(),
-                                      rows, width, G, sy, sg, so, eps, dtype, ri, shape[0],
-                                      shape[1], s, upb)
+    if flags is None:
+        flags = FLAG_RI if ri else 0
+    if shape is None and not flags & ~(FLAG_RI | FLAG_NBG | FLAG_PER_GROUP):
+        return g.ggrms_forward_ex(y.data_ptr(), gate.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                  rows, width, G, sy, sg, so, eps, dtype, flags, s)
+    return g.ggrms_forward_tuned(y.data_ptr(), gate.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                 rows, width, G, sy, sg, so, eps, dtype, flags, s, shape)
 
 
 def random_case(rows, width, dtype, seed, dist=("normal", 1.0), gate_dist=None):
@@ -105,7 +108,7 @@ def random_case(rows, width, dtype, seed, dist=("normal", 1.0), gate_dist=None):
 def check_contiguous(g, orc, rows, width, G, dtype, ri, seed, eps=1e-5, shape=None,
                      dist=("normal", 1.0), gate_dist=None, tag="", flags=None):
     """One contiguous [rows, width] case through the GPU and the oracle.
-    With flags (FLAG_* mask) the case goes through ggrms_forward_ex and, for
+    With flags (FLAG_* mask) the case goes through ggrms_forward_tuned and, for
     FLAG_PER_GROUP, the weight is the first G values of the drawn one."""
     say(f"case {tag} rows={rows} width={width} G={G} dtype={DT_IDS[dtype]} ri={ri} "
         f"flags={flags} shape={shape}")

@@ -1,6 +1,6 @@
-"""The C ABI on the CPU: the library loads, exports what include/ggrms.h
-declares, rejects bad arguments before any HIP call, and plans kernels as
-documented.  Nothing here launches a kernel or needs a GPU."""
+"""The C ABI on the CPU: the library loads, exports what include/ggrms.h and
+include/ggrms_tuning.h declare, rejects bad arguments before any HIP call, and
+plans kernels as documented.  Nothing here launches a kernel or needs a GPU."""
 import ctypes
 import os
 import re
@@ -10,6 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ggrms.h")
+TUNING_HEADER = os.path.join(ROOT, "include", "ggrms_tuning.h")
+HEADERS = (HEADER, TUNING_HEADER)
 
 F32, F16, BF16 = 0, 1, 2
 OK, INVALID, NOTSUP = 0, 1, 2
@@ -23,8 +25,8 @@ def g():
     return g
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(headers=HEADERS):
+    text = "".join(open(h).read() for h in headers)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(ggrms_[a-z_]+)\s*\(", text)))
 
@@ -32,6 +34,9 @@ def _declared_functions():
 def test_header_symbols_exported(g):
     names = _declared_functions()
     assert {"ggrms_forward", "ggrms_plan", "ggrms_status_string", "ggrms_abi_version"} <= set(names)
+    # the launch controls live in the tuning header only
+    assert set(_declared_functions((TUNING_HEADER,))) == {"ggrms_forward_tuned", "ggrms_plan_tuned"}
+    assert not {"ggrms_forward_tuned", "ggrms_plan_tuned"} & set(_declared_functions((HEADER,)))
     lib = ctypes.CDLL(g.library_path())
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ggrms.h but not exported"
@@ -46,15 +51,15 @@ def test_header_symbols_exported(g):
 
 
 def test_abi_version_and_strings(g):
-    assert g.ggrms_abi_version() == 4
+    assert g.ggrms_abi_version() == 5
     for st in range(4):
         assert g.ggrms_status_string(st)
     assert g.ggrms_status_string(99) == "unknown status"
 
 
-def _header_constants():
-    """NAME -> value of every enumerator and integer #define in ggrms.h."""
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+def _header_constants(headers=HEADERS):
+    """NAME -> value of every enumerator and integer #define in the headers."""
+    text = re.sub(r"/\*.*?\*/", "", "".join(open(h).read() for h in headers), flags=re.S)
     consts = {n: int(v) for n, v in re.findall(r"\b(GGRMS_[A-Z0-9_]+)\s*=\s*(\d+)\s*[,}\n]", text)}
     for n, v in re.findall(r"#define\s+(GGRMS_[A-Z0-9_]+)\s+(.+)", text):
         m = re.fullmatch(r"\(?(\d+)(?:ll)?(?:\s*<<\s*(\d+))?\)?", v.strip())
@@ -64,11 +69,15 @@ def _header_constants():
 
 
 def test_binding_constants_match_header(g):
-    """Every enumerator and integer macro of the header has the same value in
+    """Every enumerator and integer macro of the headers has the same value in
     the Python binding (named without the GGRMS_ prefix, or, for the kernel
     ids, as keys of KERNEL_NAMES)."""
     consts = _header_constants()
     assert len(consts) >= 22, sorted(consts)
+    tuning = _header_constants((TUNING_HEADER,))
+    assert {n for n in tuning if n.startswith("GGRMS_FLAG_")} == {
+        "GGRMS_FLAG_CACHE_STREAM", "GGRMS_FLAG_CACHE_KEEP", "GGRMS_FLAG_ORDER_ROWS",
+        "GGRMS_FLAG_ORDER_BANDED", "GGRMS_FLAG_WAVE_ONE", "GGRMS_FLAG_WAVE_FOUR"}
     for name, value in consts.items():
         short = name[len("GGRMS_"):]
         if short.startswith("KERNEL_"):
@@ -104,6 +113,10 @@ BAD = [
     # out overlapping an input other than exactly in place
     dict(out=A + 2), dict(out=A, out_row_stride=512),
     dict(out=A + (1 << 24) + 64),
+    # out overlapping the weight (which every row reads): at its start, ending in it,
+    # and a strided out whose second row meets it
+    dict(out=A + (2 << 24)), dict(out=A + (2 << 24) - 2046),
+    dict(out=A + (2 << 24) - 2048 - 256, out_row_stride=1024),
     # extents that overflow 64-bit addressing
     dict(rows=1 << 40, y_row_stride=1 << 40, gate_row_stride=1 << 40, out_row_stride=1 << 40),
 ]
@@ -152,17 +165,58 @@ RI, NBG, PER_GROUP, STREAM, KEEP = 1, 2, 4, 8, 16
 ROWS, BANDED, WAVE1, WAVE4 = 32, 64, 128, 256
 
 
+TUNING = STREAM | KEEP | ROWS | BANDED | WAVE1 | WAVE4
+
+
 def _plan_ex(g, flags, shape=None, **kw):
+    """ggrms_plan_tuned (ggrms_plan_ex when no launch control is set: both must
+    agree), checking that the forward entry points return the same status
+    wherever it rejects the arguments."""
     args = dict(y=A, gate=A + (1 << 24), norm_weight=A + (2 << 24), out=A + (3 << 24), rows=4,
                 width=256, group_size=64, y_row_stride=256, gate_row_stride=256,
                 out_row_stride=256, eps=1e-5, dtype=BF16)
     args.update(kw)
-    st, plan = g.ggrms_plan_ex(*args.values(), flags, shape)
+    st, plan = g.ggrms_plan_tuned(*args.values(), flags, shape)
+    if shape is None and not flags & TUNING:
+        st_ex, plan_ex = g.ggrms_plan_ex(*args.values(), flags)
+        assert (st_ex, plan_ex) == (st, plan)
     if st != OK or args["rows"] == 0:
         # rejected (or nothing to launch): the forward entry point returns
         # the same status without reaching the HIP runtime
-        assert g.ggrms_forward_ex(*args.values(), flags, 0, shape) == st
+        assert g.ggrms_forward_tuned(*args.values(), flags, 0, shape) == st
+        if shape is None and not flags & TUNING:
+            assert g.ggrms_forward_ex(*args.values(), flags, 0) == st
     return st, plan
+
+
+def test_weight_in_the_gap_of_a_strided_out(g):
+    """A weight (1024 bytes here) that lies between two rows (512 bytes each)
+    of a strided out shares no byte with it: allowed; one byte further and
+    a row meets it."""
+    W = A + (2 << 24)
+    # rows 4096 bytes apart: row 0 ends 1536 bytes before the weight, row 1 starts after it
+    st_plan, _, _ = _fwd(g, out=W - 2048, out_row_stride=2048, rows=2)
+    assert st_plan == OK
+    # row 0 ends exactly where the weight starts
+    st_plan, _, _ = _fwd(g, out=W - 512, out_row_stride=2048, rows=2)
+    assert st_plan == OK
+    st_plan, _, _ = _fwd(g, out=W - 510, out_row_stride=2048, rows=2)
+    assert st_plan == INVALID
+    # row 1 starts exactly where the weight ends, or one element earlier
+    st_plan, _, _ = _fwd(g, out=W + 1024 - 4096, out_row_stride=2048, rows=2)
+    assert st_plan == OK
+    st_plan, _, _ = _fwd(g, out=W + 1022 - 4096, out_row_stride=2048, rows=2)
+    assert st_plan == INVALID
+
+
+@pytest.mark.parametrize("flags", [STREAM, KEEP, ROWS, BANDED, WAVE1, WAVE4, RI | STREAM])
+def test_ex_calls_refuse_launch_controls(g, flags):
+    """The launch controls belong to the _tuned calls; the _ex calls reject
+    them like unknown bits."""
+    args = (A, A + (1 << 24), A + (2 << 24), A + (3 << 24), 4, 256, 64, 256, 256, 256, 1e-5, BF16)
+    assert g.ggrms_plan_ex(*args, flags)[0] == INVALID
+    assert g.ggrms_forward_ex(*args, flags, 0) == INVALID
+    assert g.ggrms_plan_tuned(*args, flags)[0] == OK
 
 
 @pytest.mark.parametrize("flags", [512, 1 << 31, RI | NBG, RI | NBG | PER_GROUP,
@@ -302,9 +356,40 @@ def test_plan_ex_with_shape(g):
     assert st == OK and (p["lanes_per_group"], p["rows_per_workgroup"], p["lds_bytes"]) == (128, 2, 3840)
     assert _plan_ex(g, 0, shape=(64, 1), width=960, group_size=960, y_row_stride=960,
                     gate_row_stride=960, out_row_stride=960)[0] == NOTSUP
-    assert _plan_ex(g, 0, shape=(0, 0))[0] == INVALID
+    # all zero: the library's own choice
+    assert _plan_ex(g, 0, shape=(0, 0)) == _plan_ex(g, 0)
     assert _plan_ex(g, 0, shape=(128, 1, -1), width=1024, group_size=1024, y_row_stride=1024,
                     gate_row_stride=1024, out_row_stride=1024)[0] == INVALID
+    for bad in ((-1, 1), (64, -1), (64, 1, 0, 3), (64, 1, 0, 32), (64, 1, 0, -16)):
+        assert _plan_ex(g, 0, shape=bad)[0] == INVALID, bad
+
+
+def test_plan_with_vector_bytes(g):
+    """A forced vector width: the table's shape for the vectors it gives, or
+    the forced lanes and vectors; refused where the alignment or the element
+    size does not allow it."""
+    kw = dict(rows=1, width=7680, group_size=960, y_row_stride=7680, gate_row_stride=7680,
+              out_row_stride=7680, gate=A + (1 << 26), norm_weight=A + (2 << 26),
+              out=A + (3 << 26))
+    want = {16: ("block", 128, 1), 8: ("block", 256, 1), 4: ("block", 256, 2)}
+    for vb, (kern, lanes, vpt) in want.items():
+        st, p = _plan_ex(g, RI, shape=(0, 0, 0, vb), **kw)
+        assert st == OK and (p["vector_bytes"], p["piece_bytes"]) == (vb, vb), vb
+        assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"]) == (kern, lanes, vpt)
+    st, p = _plan_ex(g, RI, shape=(512, 1, 0, 4), **kw)
+    assert st == OK and (p["lanes_per_group"], p["workgroups"], p["block_threads"]) == (512, 8, 512)
+    # 2-byte vectors of f32 are smaller than an element; 16-byte vectors need 16-byte views
+    assert _plan_ex(g, 0, shape=(0, 0, 0, 2), dtype=F32)[0] == NOTSUP
+    assert _plan_ex(g, RI, shape=(0, 0, 0, 16), **{**kw, "y": A + 8})[0] == NOTSUP
+    # a forced width below 16 never packs: 100 fp16 (200 bytes) in 8-byte vectors
+    pk = dict(rows=7, width=1600, group_size=100, y_row_stride=1600, gate_row_stride=1600,
+              out_row_stride=1600, dtype=F16, gate=A + (1 << 26), norm_weight=A + (2 << 26),
+              out=A + (3 << 26))
+    assert _plan_ex(g, RI, **pk)[1]["piece_bytes"] == 8
+    st, p = _plan_ex(g, RI, shape=(0, 0, 0, 8), **pk)
+    assert st == OK and (p["vector_bytes"], p["piece_bytes"], p["lanes_per_group"]) == (8, 8, 32)
+    st, p = _plan_ex(g, RI, shape=(0, 0, 0, 16), **pk)
+    assert st == OK and (p["vector_bytes"], p["piece_bytes"]) == (16, 8)
 
 
 def _plan(g, rows, width, G, dtype, sy=None, sg=None, so=None, y=A, gate=A + (1 << 30),
@@ -558,6 +643,7 @@ def test_planner_host_sanitizers(tmp_path):
 #include <cstdio>
 #include <initializer_list>
 #include "ggrms.h"
+#include "ggrms_tuning.h"
 int main() {
     const int64_t Gs[] = {1, 2, 3, 7, 8, 63, 64, 65, 100, 128, 960, 4096, 7680, 32768, 65536};
     const uintptr_t base = 1u << 20;
@@ -571,21 +657,30 @@ int main() {
                                        rows, width, G, width + off, width, width, 1e-5f,
                                        (ggrms_dtype_t)dt, 1, &p);
         n_ok += st == GGRMS_SUCCESS;
-        const ggrms_shape_t shapes[] = {{64, 2, 0}, {128, 1, 4}, {256, 3, 2}, {1024, 0, 0},
-                                        {16, 1, 0}, {0, 0, 0}, {128, 1, -1}};
-        for (uint32_t flags = 0; flags < 33; ++flags) {
+        const ggrms_shape_t shapes[] = {{64, 2, 0, 0}, {128, 1, 4, 0}, {256, 3, 2, 0},
+                                        {1024, 0, 0, 0}, {16, 1, 0, 0}, {0, 0, 0, 0},
+                                        {128, 1, -1, 0}, {0, 0, 0, 8}, {0, 0, 0, 4},
+                                        {512, 1, 0, 4}, {0, 0, 0, 3}, {64, 1, 0, 16}};
+        for (uint32_t flags = 0; flags < 520; flags += (flags < 40 ? 1 : 31)) {
             st = ggrms_plan_ex((void*)(base + off * 2), (void*)(base + (1u << 28)),
                                (const float*)(base + (2u << 28) + off * 4),
                                (void*)(base + (3u << 28)), rows, width, G, width + off, width,
-                               width, 1e-5f, (ggrms_dtype_t)dt, flags, nullptr, &p);
+                               width, 1e-5f, (ggrms_dtype_t)dt, flags, &p);
             n_ok += st == GGRMS_SUCCESS;
             for (const ggrms_shape_t& sh : shapes) {
-                st = ggrms_plan_ex((void*)(base + off * 2), (void*)(base + (1u << 28)),
-                                   (const float*)(base + (2u << 28)), (void*)(base + (3u << 28)),
-                                   rows, width, G, width + off, width, width, 1e-5f,
-                                   (ggrms_dtype_t)dt, flags, &sh, &p);
+                st = ggrms_plan_tuned((void*)(base + off * 2), (void*)(base + (1u << 28)),
+                                      (const float*)(base + (2u << 28)),
+                                      (void*)(base + (3u << 28)), rows, width, G, width + off,
+                                      width, width, 1e-5f, (ggrms_dtype_t)dt, flags, &sh, &p);
                 n_ok += st == GGRMS_SUCCESS;
             }
+            // out over the weight, and over the gap of a strided row
+            st = ggrms_plan_ex((void*)(base + off * 2), (void*)(base + (1u << 28)),
+                               (const float*)(base + (2u << 28)),
+                               (void*)(base + (2u << 28) - 2 * width * (off + 1)), rows, width,
+                               G, width + off, width, 3 * width, 1e-5f, (ggrms_dtype_t)dt,
+                               flags & 7, &p);
+            n_ok += st == GGRMS_SUCCESS;
         }
     }
     printf("%ld\n", n_ok);
@@ -645,3 +740,29 @@ def test_c_client_builds_and_links(g, tmp_path, compiler):
     fields = r.stdout.split()
     assert fields[:7] == [str(g.ABI_VERSION), "0", "2", "128", "4", str(8192 // 4 * 8), "1"], r.stdout
     assert " ".join(fields[7:]) == g.ggrms_status_string(1)
+
+
+def test_weight_spellings_for_the_torch_wrapper(g):
+    """forward()'s weight handling on the CPU: (n), (1, n) and (n, 1) in f32,
+    fp16 or bf16 become the same contiguous f32 vector (16-bit values widen
+    exactly); other shapes, lengths and dtypes are refused."""
+    import torch
+
+    base = torch.arange(1, 129, dtype=torch.float32) / 64  # exact in fp16 and bf16
+    for t in (base, base.reshape(1, 128), base.reshape(128, 1), base.half(),
+              base.bfloat16().reshape(1, 128), base.reshape(128, 1).half()):
+        w = g._weight_f32(t, 1024, 128)
+        assert w.dtype == torch.float32 and w.dim() == 1 and w.is_contiguous()
+        assert torch.equal(w, base), tuple(t.shape)
+    # a non-contiguous column of a wider tensor is copied out
+    wide = torch.stack([base, -base], dim=1)  # [128, 2]
+    assert torch.equal(g._weight_f32(wide[:, :1], 1024, 128), base)
+    assert g._weight_f32(torch.ones(1024), 1024, 128).numel() == 1024
+    with pytest.raises(ValueError):
+        g._weight_f32(base.reshape(2, 64), 1024, 128)
+    with pytest.raises(ValueError):
+        g._weight_f32(base.reshape(1, 1, 128), 1024, 128)
+    with pytest.raises(ValueError):
+        g._weight_f32(base[:100], 1024, 128)
+    with pytest.raises(TypeError):
+        g._weight_f32(base.double(), 1024, 128)

@@ -2,7 +2,8 @@
 gate (page "com.microsoft.GatedRMSNorm", Description section: the RMS of y
 alone, then the scale, then silu(gate)) and a weight of group_size values
 shared by every group (that page's `scale` input), each through
-ggrms_forward_ex.
+ggrms_forward_ex (ggrms_forward_tuned where a shape or a launch control is
+forced).
 
 Same bar as the gate-first tests: f32 within a relative 1e-5 of the oracle,
 fp16/bf16 within 2 units in the last place, NaN where the oracle has NaN.
@@ -256,17 +257,22 @@ def test_nbg_rejections(g):
     assert bool((od == 7.0).all())
 
 
-def test_nbg_graph_capture_replays(g):
+def test_nbg_graph_capture_replays(g, orc):
     """21 decode-sized norm-first launches (shared 960-value weight) captured
-    once and replayed with eager work between replays, each replay equal to
-    the eager result bit for bit."""
+    once and replayed with eager work between replays: every layer of the
+    eager burst meets the bar against the oracle, and each replay equals the
+    eager result bit for bit."""
     width, G = 7680, 960
-    layers = []
+    layers, refs_ = [], []
     for layer in range(S.DECODE_LAYERS):
         y, gt, w = random_case(1, width, BF16, seed=500 + layer)
-        layers.append((dev_buf(y, BF16), dev_buf(gt, BF16),
-                       torch.from_numpy(np.ascontiguousarray(w[:G])).cuda(),
+        wg = np.ascontiguousarray(w[:G])
+        layers.append((dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(wg).cuda(),
                        torch.empty(width, dtype=torch.bfloat16, device="cuda")))
+        refs_.append(orc.forward(y, gt, wg, rows=1, width=width, group_size=G,
+                                 y_row_stride=width, gate_row_stride=width, out_row_stride=width,
+                                 eps=1e-5, dtype=BF16, round_intermediate=0,
+                                 norm_before_gate=True, weight_per_group=True))
     torch.cuda.synchronize()
 
     def burst(stream):
@@ -277,6 +283,8 @@ def test_nbg_graph_capture_replays(g):
     burst(torch.cuda.current_stream())
     torch.cuda.synchronize()
     eager = [o.clone() for *_, o in layers]
+    for layer, (e, ref) in enumerate(zip(eager, refs_)):
+        assert_parity(host_bits(e, BF16), ref, BF16, f"norm-first decode layer {layer}")
     graph = torch.cuda.CUDAGraph()
     cs = torch.cuda.Stream()
     with torch.cuda.graph(graph, stream=cs):

@@ -89,13 +89,13 @@ def test_tile_orders_agree_bitwise(g, orc, case):
         flags = op | extra
         od = dev_buf(ob, dtype)
         # (WAVE_ONE / WAVE_FOUR do nothing for BLOCK launches; nothing here is refused)
-        st, p = g.ggrms_plan_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od[guard:].data_ptr(),
+        st, p = g.ggrms_plan_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od[guard:].data_ptr(),
                                 rows, width, G, sin, sin, so, 1e-5, dtype, flags)
         assert st == g.SUCCESS, f"flags={flags}: {g.ggrms_status_string(st)}"
         say(f"case order {DT_IDS[dtype]} G={G} groups={groups} rows={rows} flags={flags} "
             f"kernel={p['kernel_name']} lanes={p['lanes_per_group']} block={p['block_threads']} "
             f"order={p['tile_order']} workgroups={p['workgroups']}")
-        st = g.ggrms_forward_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od[guard:].data_ptr(),
+        st = g.ggrms_forward_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od[guard:].data_ptr(),
                                 rows, width, G, sin, sin, so, 1e-5, dtype, flags, sp)
         assert st == g.SUCCESS, g.ggrms_status_string(st)
         torch.cuda.synchronize()

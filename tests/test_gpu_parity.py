@@ -208,13 +208,50 @@ def test_shape_rejections(g):
     wd = torch.ones(960, dtype=torch.float32, device="cuda")
     od = torch.empty_like(yd)
     # 64 lanes x 1 vector cannot cover 120 vectors; 48 lanes is not built;
-    # rows per workgroup only for 128- and 256-lane groups
+    # rows per workgroup only for 128- and 256-lane groups; negative fields and
+    # vector widths other than 2-16 bytes are invalid; 16-byte vectors need
+    # 16-byte aligned views
     for shape, want in (((64, 1), g.ERROR_NOT_SUPPORTED), ((48, 1), g.ERROR_NOT_SUPPORTED),
-                        ((64, 5), g.ERROR_NOT_SUPPORTED), ((0, 0), g.ERROR_INVALID_VALUE),
+                        ((64, 5), g.ERROR_NOT_SUPPORTED), ((-1, 1), g.ERROR_INVALID_VALUE),
+                        ((0, 0, 0, 32), g.ERROR_INVALID_VALUE),
+                        ((0, 0, 0, 12), g.ERROR_INVALID_VALUE),
                         ((64, 2, 2), g.ERROR_NOT_SUPPORTED), ((512, 1, 2), g.ERROR_NOT_SUPPORTED),
                         ((128, 1, 3), g.ERROR_NOT_SUPPORTED), ((128, 1, 8), g.ERROR_NOT_SUPPORTED)):
         assert run_gpu(g, yd, yd, wd, od, 4, 960, 960, 960, 960, 960, 1e-5, BF16, 1,
                        shape) == want
+    assert run_gpu(g, yd[1:], yd[1:], wd, od[1:], 3, 960, 960, 960, 960, 960, 1e-5, BF16, 1,
+                   (0, 0, 0, 16)) == g.ERROR_NOT_SUPPORTED
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("rows,width,G,dtype", [(1, 7680, 960, BF16), (37, 7680, 960, BF16),
+                                                 (19, 1024, 128, F16), (11, 4800, 100, F16),
+                                                 (5, 640, 64, F32)],
+                         ids=["decode-bf16", "rows-bf16", "heads-f16", "g100-f16", "f32"])
+def test_forced_vector_widths(g, orc, rows, width, G, dtype):
+    """Every vector width the views allow, forced through the tuning entry
+    point (the table's shape for the resulting vector count), meets the bar
+    against the oracle in both operators."""
+    y, gt, w = random_case(rows, width, dtype, seed=4242 + G)
+    yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+    for vb in (16, 8, 4, 2):
+        if vb < (4 if dtype == F32 else 2):
+            continue
+        for flags in (FLAG_RI, FLAG_NBG):
+            od = torch.empty_like(yd)
+            st = run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, 1e-5, dtype, 0,
+                         shape=(0, 0, 0, vb), flags=flags)
+            if G * (4 if dtype == F32 else 2) % vb and vb != 16:
+                assert st == g.ERROR_NOT_SUPPORTED, (vb, st)
+                continue
+            assert st == g.SUCCESS, (vb, g.ggrms_status_string(st))
+            torch.cuda.synchronize()
+            say(f"case forced vector {vb} B rows={rows} G={G} dtype={DT_IDS[dtype]} flags={flags}")
+            ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                              gate_row_stride=width, out_row_stride=width, eps=1e-5, dtype=dtype,
+                              round_intermediate=flags & FLAG_RI,
+                              norm_before_gate=bool(flags & FLAG_NBG))
+            assert_parity(host_bits(od, dtype), ref, dtype, f"vector {vb} B flags {flags}")
 
 
 # ------------------------------------------------------------ packed groups
@@ -225,7 +262,7 @@ PACKED_CASES = [(100, F16), (100, BF16), (99, BF16), (97, F16), (50, BF16), (9, 
 
 
 def _plan_of(g, yd, gd, wd, od, rows, width, G, sy, sg, so, dtype, flags):
-    st, p = g.ggrms_plan_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od.data_ptr(), rows,
+    st, p = g.ggrms_plan_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od.data_ptr(), rows,
                             width, G, sy, sg, so, 1e-5, dtype, flags)
     assert st == g.SUCCESS
     return p
@@ -316,7 +353,7 @@ def test_rows_split_over_launches(g, orc, shape):
     y, gt, w = random_case(rows, G, BF16, seed=2021)
     yd, gd, wd = dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(w).cuda()
     od = torch.empty_like(yd)
-    st, p = g.ggrms_plan_ex(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od.data_ptr(), rows, G,
+    st, p = g.ggrms_plan_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(), od.data_ptr(), rows, G,
                             G, G, G, G, 1e-5, BF16, FLAG_RI, shape)
     assert st == g.SUCCESS and p["launches"] == 2, p
     say(f"case rows split over launches shape={shape}")
@@ -577,16 +614,22 @@ def test_side_stream(g, orc):
     assert_parity(host_bits(od, BF16), ref, BF16, "side stream")
 
 
-def test_graph_capture_replays(g):
-    """21 decode launches captured once and replayed several times, with
-    eager work and synchronisations between replays; every replay matches the
-    eager result bit for bit."""
+def test_graph_capture_replays(g, orc):
+    """21 decode launches (the 21 layers' own inputs) captured once and
+    replayed several times, with eager work and synchronisations between
+    replays: every layer of the eager burst meets the bar against the oracle,
+    and every replay matches the eager result bit for bit (so every layer of
+    every replay meets it too)."""
     w = S.WORKLOADS["mamba2_decode_1x7680_bf16_g960"]
-    layers = []
+    layers, refs_ = [], []
     for layer in range(S.DECODE_LAYERS):
         y, gt, wt, _ = S.make_inputs(w, layer)
         layers.append((dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(wt).cuda(),
                        torch.empty(w.width, dtype=torch.bfloat16, device="cuda")))
+        refs_.append(orc.forward(y, gt, wt, rows=1, width=w.width, group_size=w.group_size,
+                                 y_row_stride=w.width, gate_row_stride=w.width,
+                                 out_row_stride=w.width, eps=w.eps, dtype=BF16,
+                                 round_intermediate=w.round_intermediate))
     torch.cuda.synchronize()
 
     def burst(stream):
@@ -597,6 +640,8 @@ def test_graph_capture_replays(g):
     burst(torch.cuda.current_stream())
     torch.cuda.synchronize()
     eager = [o.clone() for *_, o in layers]
+    for layer, (e, ref) in enumerate(zip(eager, refs_)):
+        assert_parity(host_bits(e, BF16), ref, BF16, f"decode layer {layer}")
     graph = torch.cuda.CUDAGraph()
     cs = torch.cuda.Stream()
     with torch.cuda.graph(graph, stream=cs):
@@ -615,8 +660,9 @@ def test_graph_capture_replays(g):
 # ------------------------------------------------------------ torch wrapper
 
 def test_torch_wrapper(g, orc):
-    """forward() folds leading axes, reads strided slices, allocates out and
-    builds the per-column weight from a per-head scale."""
+    """forward() folds leading axes, reads strided slices, allocates out,
+    builds the per-column weight from a per-head scale, and takes the scale
+    as the GatedRMSNorm page's Inputs table spells it."""
     B, T, H, C = 2, 5, 8, 128
     width = H * C
     fused = torch.randn(B, T, 3 * width, generator=torch.Generator().manual_seed(1)).to(torch.float16)
@@ -635,8 +681,26 @@ def test_torch_wrapper(g, orc):
     assert_parity(out.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1), ref, F16, "wrapper")
     with pytest.raises(ValueError):
         g.forward(fd[..., :width:2], gate[..., :width // 2], wt[:width // 2], C)
+    # the page's scale spellings: (C), (1, C), (C, 1), in the input's dtype or f32, shared
+    # by every head; and the per-column weight in fp16 -- all give the tiled f32 weight's bits
+    sc = scale.cuda()
+    for spelled in (sc, sc.reshape(1, C), sc.reshape(C, 1), sc.float().reshape(1, C),
+                    wt.half(), wt.half().reshape(1, width)):
+        o2 = g.forward(y, gate, spelled, C, eps=1e-6, round_intermediate=False)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), tuple(spelled.shape)
+    # a bf16 scale is widened exactly: the same bits as its f32 widening passed as is
+    sb = (torch.rand(C, generator=torch.Generator().manual_seed(3)) + 0.5).to(torch.bfloat16).cuda()
+    o3 = g.forward(y, gate, sb.reshape(C, 1), C, eps=1e-6, round_intermediate=False)
+    o4 = g.forward(y, gate, sb.float(), C, eps=1e-6, round_intermediate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o3.view(torch.int16), o4.view(torch.int16))
+    with pytest.raises(ValueError):
+        g.forward(y, gate, sc.reshape(2, C // 2), C)  # neither axis of length 1
+    with pytest.raises(ValueError):
+        g.forward(y, gate, sc[:C - 1], C)  # neither width nor group_size values
     with pytest.raises(TypeError):
-        g.forward(y, gate, wt.half(), C)
+        g.forward(y, gate, sc.double(), C)
     # cache policy: this 61 KB job keeps its lines cached by default; forcing
     # either policy gives the same bits, and a wrong name is refused
     assert g.plan(y, gate, wt, C, eps=1e-6, round_intermediate=False)["streaming"] == 0

@@ -123,7 +123,7 @@ def test_random_configuration(g, orc, i):
     g_ptr = gd[og:].data_ptr()
     o_ptr = od[base + oo:].data_ptr()
     w_ptr = wbuf[c["w_off"]:].data_ptr()
-    st = g.ggrms_forward_ex(y_ptr, g_ptr, w_ptr, o_ptr, rows, width, G, sy, sg, so, c["eps"],
+    st = g.ggrms_forward_tuned(y_ptr, g_ptr, w_ptr, o_ptr, rows, width, G, sy, sg, so, c["eps"],
                             dtype, c["flags"], torch.cuda.current_stream().cuda_stream)
     assert st == g.SUCCESS, g.ggrms_status_string(st)
     torch.cuda.synchronize()
