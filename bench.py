@@ -17,7 +17,8 @@ four-op chain in PyTorch eager, and the CPU oracle timed on a bounded
 sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--only prefill|decode|copy|workloads|unfused|shapes]
+                  [--only prefill|decode|copy|workloads|unfused|shapes|evidence]
+                  [--part prefill|gdn|decode] [--variant NAME]
 """
 from __future__ import annotations
 
@@ -69,8 +70,14 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for this long after the warmup steps")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads", "unfused",
-                                       "shapes"], default=None)
+                                       "shapes", "evidence"], default=None)
+    ap.add_argument("--part", choices=list(UNFUSED_PARTS), default=None,
+                    help="with --only unfused: time one chain only")
+    ap.add_argument("--variant", choices=sorted(EVIDENCE), default="prefill_staged",
+                    help="with --only evidence: the launch-choice job to time")
     ap.add_argument("--decode-bursts", type=int, default=200)
+    ap.add_argument("--decode-eager-only", action="store_true",
+                    help="with --only decode: eager bursts only, no graph capture")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shape", default=None,
@@ -225,7 +232,7 @@ def bench_prefill(torch, g, S, args, shape):
     return res
 
 
-def bench_decode(torch, g, S, bursts):
+def bench_decode(torch, g, S, bursts, eager_only=False):
     """21 back-to-back launches (distinct layer inputs) per burst, issued from
     C through libggrms.so (libggrms_bench.so's loop: no interpreter between
     launches), timed with events around each burst; eager and as one replayed
@@ -262,8 +269,14 @@ def bench_decode(torch, g, S, bursts):
 
     flags = layers[0].flags
     eager, host = native(0, flags)
-    graph, _ = native(1, flags)
     floor_eager, floor_host = native(2, flags)
+    if eager_only:  # no graph capture (counter collection runs)
+        res = {"workload": w.name, "us_per_launch_eager": eager, "host_us_per_call": host,
+               "floor_us_per_launch_eager": floor_eager, "floor_host_us_per_call": floor_host,
+               "grid": [plan["workgroups"], plan["block_threads"]]}
+        log(f"decode (eager only): {json.dumps(res)}")
+        return res
+    graph, _ = native(1, flags)
     floor_graph, _ = native(3, flags)
     eager_nt, _ = native(0, flags | g.FLAG_CACHE_STREAM)
     graph_nt, _ = native(1, flags | g.FLAG_CACHE_STREAM)
@@ -500,6 +513,74 @@ def bench_shapes(torch, g, steps):
     return out
 
 
+# Launch-choice A/B jobs whose counters back the design (each ~377 MB, three
+# rotating sets of random inputs): (dtype, rows, width, group size, flags of
+# ggrms_forward_tuned, forced shape or None).  The prefill with its weights
+# staged in LDS (4 rows of a group per workgroup, the default) and with one
+# row per workgroup (each unit reads its own weights); 9 groups of 960 per
+# row, where the row-major order makes every XCD read every group's weights,
+# in the XCD-banded order (the default) and in row-major order; the
+# single-group rows of Mamba-2 mixers with one group (G = 5120, 8192); and
+# packed groups.
+EVIDENCE = {
+    "prefill_staged": (2, 8192, 7680, 960, 1, None),
+    "prefill_unstaged": (2, 8192, 7680, 960, 1, (128, 1, 1)),
+    "g9_banded": (2, 7281, 8640, 960, 1 | 64, None),
+    "g9_rows": (2, 7281, 8640, 960, 1 | 32, None),
+    "g5120": (2, 12288, 5120, 5120, 1, None),
+    "g8192": (2, 7680, 8192, 8192, 1, None),
+    # 100-wide fp16 groups (200 bytes: packed 16-byte vectors), one vector per
+    # lane on 16 lanes (the default for a job this size) and two vectors per
+    # lane on 8 lanes (the default for jobs resident at once)
+    "packed_g100": (1, 13107, 4800, 100, 1, None),
+    "packed_g100_8x2": (1, 13107, 4800, 100, 1, (8, 2)),
+}
+
+
+def bench_evidence(torch, g, variant, steps, warmup, settle_s):
+    """Event-timed average launch of one EVIDENCE job (for counter runs:
+    `rocprofv3 --pmc ... -- python3 bench.py --only evidence --variant X`)."""
+    dt, rows, width, G, flags, shape = EVIDENCE[variant]
+    esz = 4 if dt == 0 else 2
+    tdt = {0: torch.float32, 1: torch.float16, 2: torch.bfloat16}[dt]
+    sets = [[torch.randn(rows * width, device="cuda").to(tdt) for _ in range(2)] +
+            [torch.empty(rows * width, dtype=tdt, device="cuda")] for _ in range(3)]
+    weight = torch.rand(width, device="cuda") + 0.5
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def launch(i):
+        y, gt, o = sets[i % 3]
+        st = g.ggrms_forward_tuned(y.data_ptr(), gt.data_ptr(), weight.data_ptr(), o.data_ptr(),
+                                   rows, width, G, width, width, width, 1e-5, dt, flags, sp, shape)
+        if st != 0:
+            raise RuntimeError(f"{variant}: {g.ggrms_status_string(st)}")
+
+    for i in range(warmup):
+        launch(i)
+    if settle_s > 0:
+        settle(torch, launch, settle_s)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(steps):
+        launch(i)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    _, p = g.ggrms_plan_tuned(sets[0][0].data_ptr(), sets[0][1].data_ptr(), weight.data_ptr(),
+                              sets[0][2].data_ptr(), rows, width, G, width, width, width, 1e-5,
+                              dt, flags, shape)
+    nbytes = 3 * rows * width * esz + 4 * width
+    rec = {"variant": variant, "rows": rows, "width": width, "group_size": G, "flags": flags,
+           "us": round(us, 2), "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "plan": {k: p[k] for k in ("kernel_name", "lanes_per_group", "vectors_per_lane",
+                                      "rows_per_workgroup", "block_threads", "workgroups",
+                                      "tile_order", "vector_bytes")}}
+    print(json.dumps(rec), flush=True)
+    return rec
+
+
 def unfused_chain(torch, y, gate, w, group_size, eps, ri):
     """The four-op chain the fused kernel replaces, in PyTorch eager: widen,
     silu(gate) * y, group RMSNorm (torch's rms_norm over groups), weight
@@ -523,11 +604,29 @@ def unfused_chain_norm_first(torch, y, gate, w, group_size, eps):
     return t.to(y.dtype)
 
 
-def bench_unfused(torch, S, steps):
+UNFUSED_PARTS = ("prefill", "gdn", "decode")
+
+
+def bench_unfused(torch, S, steps, parts=UNFUSED_PARTS, settle_s=0.2):
     """Per-launch time of the unfused chain beside the fused kernel: the
     prefill batch (eager, back to back), the norm-first chain on the
     16384x8192 fp16 GDN-shaped batch, and the 21-layer decode burst (eager
-    and as one replayed graph)."""
+    and as one replayed graph); `parts` picks which (a kernel trace of one
+    part counts that chain's dispatches per pass)."""
+    import numpy as np
+
+    res = {}
+    if "prefill" in parts:
+        res.update(_unfused_prefill(torch, S, steps, settle_s))
+    if "gdn" in parts:
+        res.update(_unfused_gdn(torch, S, steps, settle_s))
+    if "decode" in parts:
+        res.update(_unfused_decode(torch, S, settle_s))
+    log(f"unfused chain: {json.dumps(res)}")
+    return res
+
+
+def _unfused_prefill(torch, S, steps, settle_s):
     import numpy as np
 
     res = {}
@@ -537,7 +636,7 @@ def bench_unfused(torch, S, steps):
     gt = torch.from_numpy(gb.view(np.int16)).view(torch.bfloat16).reshape(w.rows, w.width).cuda()
     wd = torch.from_numpy(wt).cuda()
     run = lambda i: unfused_chain(torch, y, gt, wd, w.group_size, w.eps, w.round_intermediate)
-    settle(torch, run, 0.2)
+    settle(torch, run, settle_s)
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
@@ -548,14 +647,22 @@ def bench_unfused(torch, S, steps):
     res["prefill_us"] = a.elapsed_time(b) * 1e3 / steps
     del y, gt
     torch.cuda.empty_cache()
+    return res
 
+
+def _unfused_gdn(torch, S, steps, settle_s):
+    import numpy as np
+
+    res = {}
     n = S.WORKLOADS["gdn_head_16384x8192_f16_g128"]
     yb, gb, wt, _ = S.make_inputs(n)
     y = torch.from_numpy(yb.view(np.int16)).view(torch.float16).reshape(n.rows, n.width).cuda()
     gt = torch.from_numpy(gb.view(np.int16)).view(torch.float16).reshape(n.rows, n.width).cuda()
     wd = torch.from_numpy(np.ascontiguousarray(wt[:n.group_size])).cuda()
     run = lambda i: unfused_chain_norm_first(torch, y, gt, wd, n.group_size, n.eps)
-    settle(torch, run, 0.2)
+    settle(torch, run, settle_s)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(steps):
         run(i)
@@ -564,7 +671,13 @@ def bench_unfused(torch, S, steps):
     res["gdn_norm_first_us"] = a.elapsed_time(b) * 1e3 / steps
     del y, gt
     torch.cuda.empty_cache()
+    return res
 
+
+def _unfused_decode(torch, S, settle_s):
+    import numpy as np
+
+    res = {}
     d = S.WORKLOADS[DECODE]
     layers = []
     for layer in range(S.DECODE_LAYERS):
@@ -577,7 +690,7 @@ def bench_unfused(torch, S, steps):
         for ly, lg, lw in layers:
             unfused_chain(torch, ly, lg, lw, d.group_size, d.eps, d.round_intermediate)
 
-    settle(torch, burst, 0.1)
+    settle(torch, burst, settle_s / 2)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(100)]
     for x, z in evs:
@@ -590,14 +703,13 @@ def bench_unfused(torch, S, steps):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=cs):
         burst()
-    settle(torch, lambda i: graph.replay(), 0.1)
+    settle(torch, lambda i: graph.replay(), settle_s / 2)
     for x, z in evs:
         x.record()
         graph.replay()
         z.record()
     torch.cuda.synchronize()
     res["decode_us_per_layer_graph"] = statistics.median(x.elapsed_time(z) for x, z in evs) * 1e3 / len(layers)
-    log(f"unfused chain: {json.dumps(res)}")
     return res
 
 
@@ -743,13 +855,18 @@ def main():
         bench_copy(torch, args.steps)
         return
     if args.only == "decode":
-        bench_decode(torch, g, S, args.decode_bursts)
+        bench_decode(torch, g, S, args.decode_bursts, args.decode_eager_only)
         return
     if args.only == "workloads":
         bench_workloads(torch, g, S, args.steps)
         return
     if args.only == "unfused":
-        bench_unfused(torch, S, 100)
+        bench_unfused(torch, S, min(args.steps, 100),
+                      (args.part,) if args.part else UNFUSED_PARTS, args.settle_ms / 1e3)
+        return
+    if args.only == "evidence":
+        bench_evidence(torch, g, args.variant, min(args.steps, 200), args.warmup,
+                       args.settle_ms / 1e3)
         return
     if args.only == "shapes":
         print(json.dumps(bench_shapes(torch, g, min(args.steps, 300))), flush=True)

@@ -33,7 +33,8 @@ __all__ = [
     "F32", "F16", "BF16", "FLAG_ROUND_INTERMEDIATE", "FLAG_NORM_BEFORE_GATE",
     "FLAG_WEIGHT_PER_GROUP", "FLAG_CACHE_STREAM", "FLAG_CACHE_KEEP", "FLAG_ORDER_ROWS",
     "FLAG_ORDER_BANDED", "FLAG_WAVE_ONE", "FLAG_WAVE_FOUR", "STREAM_MIN_BYTES", "SUCCESS",
-    "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED", "ERROR_LAUNCH", "KERNEL_NAMES", "GgrmsError",
+    "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED", "ERROR_LAUNCH", "KERNEL_NAMES", "KERNEL_RUN",
+    "GgrmsError",
     "ggrms_forward", "ggrms_forward_ex", "ggrms_forward_tuned", "ggrms_plan", "ggrms_plan_ex",
     "ggrms_plan_tuned", "ggrms_status_string", "ggrms_abi_version", "forward", "plan",
     "expand_head_scale", "library_path",
@@ -48,7 +49,8 @@ FLAG_CACHE_STREAM, FLAG_CACHE_KEEP = 8, 16
 FLAG_ORDER_ROWS, FLAG_ORDER_BANDED, FLAG_WAVE_ONE, FLAG_WAVE_FOUR = 32, 64, 128, 256
 STREAM_MIN_BYTES = 4 << 20  # default policy: jobs of at least this many y+gate+out bytes stream
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
-KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide"}
+KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide", 4: "run"}
+KERNEL_RUN = 4
 ABI_VERSION = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,7 +69,8 @@ class GgrmsError(RuntimeError):
 
 class _Shape(ctypes.Structure):
     _fields_ = [("lanes_per_group", ctypes.c_int32), ("vectors_per_lane", ctypes.c_int32),
-                ("rows_per_workgroup", ctypes.c_int32), ("vector_bytes", ctypes.c_int32)]
+                ("rows_per_workgroup", ctypes.c_int32), ("vector_bytes", ctypes.c_int32),
+                ("kernel", ctypes.c_int32)]
 
 
 class _Plan(ctypes.Structure):
@@ -76,7 +79,8 @@ class _Plan(ctypes.Structure):
                 ("block_threads", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("rows_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("streaming", ctypes.c_int32),
-                ("piece_bytes", ctypes.c_int32), ("tile_order", ctypes.c_int32)]
+                ("piece_bytes", ctypes.c_int32), ("tile_order", ctypes.c_int32),
+                ("groups_per_run", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -127,11 +131,12 @@ def ggrms_forward(y: int, gate: int, norm_weight: int, out: int, rows: int, widt
 
 
 def _shape_arg(shape):
-    """None, or (lanes, vectors[, rows per workgroup[, vector bytes]]) as a ggrms_shape_t."""
+    """None, or (lanes, vectors[, rows per workgroup[, vector bytes[, kernel]]]) as a
+    ggrms_shape_t (kernel: 0, or KERNEL_RUN for runs of packed groups)."""
     if shape is None:
         return None
-    f = list(shape) + [0] * (4 - len(shape))
-    return ctypes.byref(_Shape(*f[:4]))
+    f = list(shape) + [0] * (5 - len(shape))
+    return ctypes.byref(_Shape(*f[:5]))
 
 
 def _plan_dict(p) -> dict:
@@ -156,7 +161,8 @@ def ggrms_forward_tuned(y: int, gate: int, norm_weight: int, out: int, rows: int
                         shape=None) -> int:
     """ggrms_forward_ex with launch controls: flags may also hold the FLAG_CACHE_*,
     FLAG_ORDER_* and FLAG_WAVE_* bits, and shape = (lanes, vectors[, rows per
-    workgroup[, vector bytes]]) forces the kernel shape; returns the status."""
+    workgroup[, vector bytes[, kernel]]]) forces the kernel shape; returns the
+    status."""
     return _lib.ggrms_forward_tuned(y, gate, norm_weight, out, rows, width, group_size,
                                     y_row_stride, gate_row_stride, out_row_stride, eps, dtype,
                                     flags, _shape_arg(shape), stream)

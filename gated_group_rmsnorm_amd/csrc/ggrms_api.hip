@@ -73,7 +73,8 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     a.so = out_row_stride;
     a.groups = (uint32_t)lp.groups;
     uint32_t div_s = 0, xc_s = 0;
-    div_magic(a.groups, &a.div_m, &div_s);
+    // the row of a row-major tile: x / groups, or (RUN) x / runs per row
+    div_magic(p.kernel == GGRMS_KERNEL_RUN ? (uint32_t)lp.runs_per_row : a.groups, &a.div_m, &div_s);
     a.G = (uint32_t)group_size;
     a.nvec = (uint32_t)lp.nvec;
     a.Ginv = (float)(1.0 / (double)group_size);

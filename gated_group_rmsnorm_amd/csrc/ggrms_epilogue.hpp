@@ -28,6 +28,9 @@
 //      optional intermediate cast, the weight and the narrowing cast, giving
 //      each slot's output vector in storage format, ready for the caller's
 //      own stores.
+// A lane whose vector straddles the boundary of two units uses
+// gate_and_square2 and finish_by_piece, which keep the two units' pieces
+// apart.
 // Steps 1 and 3 are per lane; a caller is free to lay slots over lanes as its
 // own tile dictates, as long as step 2 combines exactly the unit's lanes.
 // Results are deterministic and, for a given grouping of lanes, identical to
@@ -416,15 +419,108 @@ __device__ __forceinline__ float gate_and_square(
     return acc;
 }
 
+// Step 1 for a lane whose slots hold elements of two consecutive units: each
+// PB-byte piece goes to the first unit's share, s_first, or -- where
+// second(k, q) holds -- to the second unit's, s_second (each a chain over its
+// pieces in element order, slots added in slot order, as gate_and_square
+// does for one unit).  Slots that are not live add to neither.
+template <class T, int VB, int PB, int K, bool NBG, class Live, class Second>
+__device__ __forceinline__ void gate_and_square2(
+    const typename VecWord<VB>::type (&yr)[K], const typename VecWord<VB>::type (&gr)[K],
+    LaneUnit<T, VB, K, NBG>& L, Live live, Second second, float& s_first, float& s_second) {
+    static_assert(VB >= 4, "whole 32-bit words per slot");
+    using P = Packet<T, VB>;
+    constexpr int N = P::N;
+    constexpr int PE = PB / T::kSize;
+    constexpr int NPIECE = VB / PB;
+    constexpr bool kMix = kMixMul<T, VB, NBG>;
+    const float nz = kMix ? opaque_neg_zero() : 0.0f;
+
+    auto slot_sums = [&](int k, auto value, float& p0, float& p1) {
+        p0 = 0.0f;
+        p1 = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NPIECE; ++q) {
+            const bool to1 = second(k, q);
+            float p = to1 ? p1 : p0;
+#pragma unroll
+            for (int i = 0; i < PE; ++i) {
+                const int e = q * PE + i;
+                const float x = value(e);
+                L.a[k][e] = x;
+                p = __builtin_fmaf(x, x, p);
+            }
+            p0 = to1 ? p0 : p;
+            p1 = to1 ? p : p1;
+        }
+    };
+
+    float acc0 = 0.0f, acc1 = 0.0f;
+    u32 gmax = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float yf[N], gf[N];
+        if constexpr (!kMix) {
+            P::unpack(yr[k], yf);
+            P::unpack(gr[k], gf);
+        }
+#pragma unroll
+        for (int i = 0; i < VB / 4; ++i) gmax = gate_max_word<T>(gmax, word_of<VB>(gr[k], i));
+        if constexpr (NBG) {
+#pragma unroll
+            for (int e = 0; e < N; ++e) L.s[k][e] = silu_fast(gf[e]);
+        }
+        float p0, p1;
+        slot_sums(k, [&](int e) {
+            if constexpr (kMix)
+                return gated_f16(word_of<VB>(yr[k], e / 2), word_of<VB>(gr[k], e / 2), e & 1, nz);
+            else if constexpr (NBG)
+                return yf[e];
+            else
+                return yf[e] * silu_fast(gf[e]);
+        }, p0, p1);
+        acc0 += live(k) ? p0 : 0.0f;
+        acc1 += live(k) ? p1 : 0.0f;
+    }
+    const bool exact_silu = __builtin_expect(__any(gate_below_fast_min<T>(gmax)), 0);
+    if (NBG && exact_silu) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float gf[N];
+            P::unpack(gr[k], gf);
+#pragma unroll
+            for (int e = 0; e < N; ++e) L.s[k][e] = silu_exact(gf[e]);
+        }
+    }
+    if (!NBG && exact_silu) {
+        acc0 = 0.0f;
+        acc1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float yf[N], gf[N];
+            P::unpack(yr[k], yf);
+            P::unpack(gr[k], gf);
+            float p0, p1;
+            slot_sums(k, [&](int e) { return yf[e] * silu_exact(gf[e]); }, p0, p1);
+            acc0 += live(k) ? p0 : 0.0f;
+            acc1 += live(k) ? p1 : 0.0f;
+        }
+    }
+    s_first = acc0;
+    s_second = acc1;
+}
+
 // Step 3 (A5 scale and optional intermediate cast, A6 weight and narrowing
 // cast): the output vector of every slot, in storage format, from the unit's
 // normaliser nf = norm_factor(m2, 1/G, eps) (A4; the same bits on every lane
 // of the unit, as m2 is) and the slots' f32 weights.  RI: cast a*nf to T and
-// back before the weight multiply (gate first only).
-template <bool RI, class T, int VB, int K, bool NBG>
-__device__ __forceinline__ void finish(const LaneUnit<T, VB, K, NBG>& L, float nf,
-                                       const float (&w)[K][Packet<T, VB>::N],
-                                       typename VecWord<VB>::type (&res)[K]) {
+// back before the weight multiply (gate first only).  finish_by_piece takes
+// the normaliser per PE-element piece, nf(k, q), for slots that hold the
+// elements of two units.
+template <bool RI, int PE, class T, int VB, int K, bool NBG, class NF>
+__device__ __forceinline__ void finish_by_piece(const LaneUnit<T, VB, K, NBG>& L, NF nf,
+                                                const float (&w)[K][Packet<T, VB>::N],
+                                                typename VecWord<VB>::type (&res)[K]) {
     using P = Packet<T, VB>;
     using W = typename P::W;
     constexpr int N = P::N;
@@ -434,7 +530,7 @@ __device__ __forceinline__ void finish(const LaneUnit<T, VB, K, NBG>& L, float n
     for (int k = 0; k < K; ++k) {
         float t[N];
 #pragma unroll
-        for (int e = 0; e < N; ++e) t[e] = L.a[k][e] * nf;
+        for (int e = 0; e < N; ++e) t[e] = L.a[k][e] * nf(k, e / PE);
         if constexpr (NBG) {
             // ((y * nf) * w) * silu(gate), every intermediate f32
 #pragma unroll
@@ -451,6 +547,13 @@ __device__ __forceinline__ void finish(const LaneUnit<T, VB, K, NBG>& L, float n
         }
         res[k] = P::pack(t);
     }
+}
+
+template <bool RI, class T, int VB, int K, bool NBG>
+__device__ __forceinline__ void finish(const LaneUnit<T, VB, K, NBG>& L, float nf,
+                                       const float (&w)[K][Packet<T, VB>::N],
+                                       typename VecWord<VB>::type (&res)[K]) {
+    finish_by_piece<RI, Packet<T, VB>::N>(L, [nf](int, int) { return nf; }, w, res);
 }
 
 }  // namespace epi

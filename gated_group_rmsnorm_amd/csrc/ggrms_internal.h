@@ -39,9 +39,9 @@ struct KArgs {
     uint32_t rows;    // rows in this launch
     uint32_t groups;  // groups per row
     uint32_t G;       // group size in elements
-    uint32_t nvec;    // vectors per group
-    uint32_t div_m;   // magic multiplier for x / groups (shift in bits)
-    uint32_t xc;      // banded order: tile columns C
+    uint32_t nvec;    // vectors per group; RUN: groups per run
+    uint32_t div_m;   // magic multiplier for x / groups (RUN: x / runs per row; shift in bits)
+    uint32_t xc;      // banded order: tile columns C (RUN: runs per row, either order)
     uint32_t xc_m;    // magic multiplier for x / C (shift in bits)
     float Ginv;       // 1/G rounded to f32 (the normaliser multiplies by it)
     float eps;
@@ -60,12 +60,16 @@ constexpr uint32_t kBitBand = 1u << 12;   // XCD-banded tile order
 constexpr uint32_t kXcds = 8;
 
 // Supported shapes.  WAVE: lanes in {1..64} (powers of two); vectors per lane
-// 1 for lanes < 64, 1..4 for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
+// 1 for lanes < 64 (also 2 with 8, 16 or 32 lanes for packed groups), 1..4
+// for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
 // vectors per lane 1..4, and 6 with 256 lanes.  WIDE: 1024 lanes, vectors per
-// lane 0 (it loops over the group).  A WAVE workgroup is a single wave or 4
+// lane 0 (it loops over the group).  RUN: 64 lanes, one vector each, over a
+// run of packed groups.  A WAVE workgroup is a single wave or 4
 // waves (the kernel takes its size from the launch; the planner's rule says
 // which).
 constexpr int kWaveBlock = 256;
+// Most groups one RUN wave takes (its loop over the groups' sums is unrolled).
+constexpr int kRunMaxGroups = 8;
 constexpr int kWaveBlockOneWave = 64;
 constexpr int kWideBlock = 1024;
 
@@ -80,8 +84,9 @@ inline bool rows_per_workgroup_supported(int kernel, int lanes, int upb) {
 
 inline bool shape_supported(int kernel, int lanes, int vpt) {
     switch (kernel) {
-    case GGRMS_KERNEL_WAVE:
+    case GGRMS_KERNEL_WAVE:  // (8, 16 or 32) x 2: packed groups only
         if (lanes == 64) return vpt >= 1 && vpt <= 4;
+        if ((lanes == 8 || lanes == 16 || lanes == 32) && vpt == 2) return true;
         return (lanes == 1 || lanes == 2 || lanes == 4 || lanes == 8 || lanes == 16 ||
                 lanes == 32) &&
                vpt == 1;
@@ -90,6 +95,8 @@ inline bool shape_supported(int kernel, int lanes, int vpt) {
                ((vpt >= 1 && vpt <= 4) || (lanes == 256 && vpt == 6));
     case GGRMS_KERNEL_WIDE:
         return lanes == kWideBlock;
+    case GGRMS_KERNEL_RUN:
+        return lanes == 64 && vpt == 1;
     default:
         return false;
     }
@@ -104,6 +111,7 @@ struct LaunchPlan {
     int64_t nvec;
     int64_t rows_per_launch;  // rows handled by each launch (the last one may have fewer)
     bool xband;               // XCD-banded tile order (kBitBand)
+    int64_t runs_per_row;     // RUN: tiles of one row
 };
 
 // WAVE: groups one workgroup covers (lanes <= 64).
@@ -119,6 +127,9 @@ inline void launch_tiles(const LaunchPlan& lp, int64_t r, int64_t* R, int64_t* C
     } else if (p.kernel == GGRMS_KERNEL_WIDE) {  // one unit per workgroup, row-major only
         *R = r;
         *C = lp.groups;
+    } else if (p.kernel == GGRMS_KERNEL_RUN) {  // one run per one-wave workgroup
+        *R = r;
+        *C = lp.runs_per_row;
     } else {
         const int64_t gpw = wave_groups_per_workgroup(p.lanes_per_group, p.block_threads);
         *R = r;
@@ -142,6 +153,7 @@ inline int64_t launch_workgroups(const LaunchPlan& lp, int64_t r) {
         return (threads + p.block_threads - 1) / p.block_threads;
     }
     case GGRMS_KERNEL_WIDE: return r * lp.groups;
+    case GGRMS_KERNEL_RUN: return r * lp.runs_per_row;
     default: return 0;
     }
 }

@@ -377,6 +377,103 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     });
 }
 
+// RUN: one wave takes a run of up to gpw = a.nvec consecutive packed groups of
+// one row (tile (row, run) of the job's rows x runs_per_row = a.xc tiles),
+// one 16-byte vector per lane, the vectors counted from the row start, so the
+// lanes load one contiguous stretch: 100-wide fp16 groups (12.5 vectors) fill
+// 63 of 64 lanes five groups at a time, where 16-lane segments per group fill
+// 13 of 16 and load every boundary vector twice.  A vector on a group
+// boundary holds pieces of two groups, whose sums are kept apart
+// (gate_and_square2); each group's sum over the wave is a 64-lane sum of the
+// lanes' shares for that group (every lane adds its share or 0, in a fixed
+// order); the pieces are then normalised with their own group's nf and
+// stored, a vector whose pieces belong to groups of two runs in pieces.
+template <class T, int PB, bool NBG, bool NT>
+__global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
+    constexpr int VB = 16;
+    using P = Packet<T, VB>;
+    using W = typename P::W;
+    constexpr int N = P::N;
+    constexpr int PE = PB / T::kSize;  // elements per piece
+    constexpr int NP = VB / PB;        // pieces per vector
+    static_assert(PB < VB, "runs are built for packed groups");
+    using S = typename VecWord<T::kSize>::type;
+
+    uint32_t n, c;  // row, run
+    if (banded(a)) {
+        xcd_band_tile(a, a.rows, n, c);
+    } else {
+        n = row_div(a, blockIdx.x);  // runs per row (div_m holds its magic number)
+        c = blockIdx.x - n * a.xc;
+    }
+    const uint32_t gpw = a.nvec;
+    const uint32_t g0 = c * gpw;
+    const int32_t cnt = (int32_t)(a.groups - g0 < gpw ? a.groups - g0 : gpw);
+    const int64_t e0 = (int64_t)g0 * a.G;                // the run's first element in the row
+    const int64_t e1 = e0 + (int64_t)cnt * a.G;          // one past its last
+    const uint32_t v0 = (uint32_t)(e0 / N);
+    const uint32_t nv = (uint32_t)((e1 + N - 1) / N) - v0;  // <= 64 (the planner's gpw)
+    const uint32_t l = threadIdx.x;
+    const bool live_l = l < nv;
+    const uint32_t v = v0 + (live_l ? l : nv - 1);
+    // k: the group (relative to g0) of the vector's first element, -1 for a
+    // vector that starts in the previous run; 1/G in f32 corrected to exact
+    const int32_t off = (int32_t)((int64_t)v * N - e0);  // >= -(N - 1)
+    const int32_t G = (int32_t)a.G;
+    int32_t k = -1;
+    if (off >= 0) {
+        k = (int32_t)((float)off * a.Ginv);
+        k -= k * G > off ? 1 : 0;
+        k += (k + 1) * G <= off ? 1 : 0;
+    }
+    const int32_t bnd = (k + 1) * G - off;  // elements of group k in the vector (>= N: all)
+
+    const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy);
+    const W* gv = reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg);
+    W yr[1], gr[1];
+    float wr[1][N];
+    yr[0] = load_stream<NT>(yv + v);
+    gr[0] = load_stream<NT>(gv + v);
+    load_weights<N>(a.w + (int64_t)v * N, wr[0]);
+
+    auto live = [&](int) { return live_l; };
+    auto second = [&](int, int q) { return q * PE >= bnd; };
+    epi::LaneUnit<T, VB, 1, NBG> L;
+    float s_k, s_k1;
+    epi::gate_and_square2<T, VB, PB, 1, NBG>(yr, gr, L, live, second, s_k, s_k1);
+
+    // each group's sum over the wave; the lane keeps those of groups k, k + 1
+    float m_k = 0.0f, m_k1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRunMaxGroups; ++j) {
+        if (j >= cnt) break;
+        const float share = k == j ? s_k : (k + 1 == j ? s_k1 : 0.0f);
+        const float m = segment_sum<64>(share);
+        m_k = k == j ? m : m_k;
+        m_k1 = k + 1 == j ? m : m_k1;
+    }
+    const float nf_k = norm_factor(m_k, a.Ginv, a.eps);
+    const float nf_k1 = norm_factor(m_k1, a.Ginv, a.eps);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    W res[1];
+    auto nf = [&](int, int q) { return q * PE >= bnd ? nf_k1 : nf_k; };
+    if (!NBG && round_intermediate(a))
+        epi::finish_by_piece<true, PE>(L, nf, wr, res);
+    else
+        epi::finish_by_piece<false, PE>(L, nf, wr, res);
+    if (!live_l) return;
+    W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so) + v;
+    const bool own_k = k >= 0 && k < cnt, own_k1 = k + 1 < cnt;
+    if (bnd >= N ? own_k : (own_k && own_k1)) {
+        store_stream<NT>(ov, res[0]);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+            if (q * PE >= bnd ? own_k1 : own_k)
+                store_piece_stream<NT, PB>(reinterpret_cast<char*>(ov) + q * PB, res[0], q);
+    }
+}
+
 // WIDE: one 1024-thread workgroup per unit, for groups with more vectors than
 // the BLOCK shapes hold in registers.  Pass 1 reads the group and reduces;
 // pass 2 reads it again and writes (the only path that reads inputs twice).
@@ -454,6 +551,11 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
         if (upb != 1) return nullptr;
         GG_W(1, 1); GG_W(2, 1); GG_W(4, 1); GG_W(8, 1); GG_W(16, 1); GG_W(32, 1);
         GG_W(64, 1); GG_W(64, 2); GG_W(64, 3); GG_W(64, 4);
+        // packed groups: two vectors per lane on half the lanes (the same
+        // slots), so each wave's fixed work covers twice the elements
+        if constexpr (kPacked) {
+            GG_W(8, 2); GG_W(16, 2); GG_W(32, 2);
+        }
     } else if (kernel == GGRMS_KERNEL_BLOCK) {
         GG_B4(128, 1); GG_B4(256, 1); GG_B4(512, 1); GG_B4(1024, 1);
         GG_B(256, 6, 1);
@@ -465,6 +567,12 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
         if constexpr (kPacked) return nullptr;
         if (upb != 1) return nullptr;
         return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB, NBG, NT>);
+    } else if (kernel == GGRMS_KERNEL_RUN) {
+        if constexpr (kPacked) {
+            if (lanes == 64 && vpt == 1 && upb == 1)
+                return reinterpret_cast<const void*>(&ggrms_run_kernel<T, PB, NBG, NT>);
+        }
+        return nullptr;
     }
 #undef GG_W
 #undef GG_B

@@ -75,6 +75,10 @@ int64_t round_up_pow2(int64_t x) {
 // groups keep the narrower vectors.
 constexpr int64_t kMaxPackedVectors = 2048;
 
+// Waves of a job that the part holds at once with room to spare (256 CUs x 4
+// SIMDs x 4 waves): such a job is a single round of loads and arithmetic.
+constexpr int64_t kSmallJobWaves = 4096;
+
 int kernel_for_shape(int lanes, int vpt) {
     if (vpt == 0) return GGRMS_KERNEL_WIDE;
     return lanes <= 64 ? GGRMS_KERNEL_WAVE : GGRMS_KERNEL_BLOCK;
@@ -172,7 +176,8 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
                   shape->rows_per_workgroup < 0 ||
                   (shape->vector_bytes != 0 && shape->vector_bytes != 2 &&
                    shape->vector_bytes != 4 && shape->vector_bytes != 8 &&
-                   shape->vector_bytes != 16)))
+                   shape->vector_bytes != 16) ||
+                  (shape->kernel != 0 && shape->kernel != GGRMS_KERNEL_RUN)))
         return GGRMS_ERROR_INVALID_VALUE;
     if (((flags & GGRMS_FLAG_ORDER_ROWS) && (flags & GGRMS_FLAG_ORDER_BANDED)) ||
         ((flags & GGRMS_FLAG_WAVE_ONE) && (flags & GGRMS_FLAG_WAVE_FOUR)))
@@ -264,7 +269,19 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     const bool packed = pb < vb;
     int kernel = 0, lanes = 0, vpt = 0, rule_upb = 1;
     const int force_upb = shape ? shape->rows_per_workgroup : 0;
-    if (shape && (shape->lanes_per_group != 0 || shape->vectors_per_lane != 0)) {
+    // RUN: a wave takes gpw consecutive packed groups whose vectors, however the
+    // run is aligned, fit 64 lanes (ceil((16 - pb + gpw * group bytes) / 16) <= 64)
+    const int64_t gpw_fit = packed ? (64 * 16 - 16 + pb) / gbytes : 0;
+    const int64_t gpw = gpw_fit < kRunMaxGroups ? gpw_fit : kRunMaxGroups;
+    const bool run_fits = packed && gpw >= 2 && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP);
+    if (shape && shape->kernel == GGRMS_KERNEL_RUN) {
+        if (!run_fits || !(shape->lanes_per_group == 0 || shape->lanes_per_group == 64) ||
+            !(shape->vectors_per_lane == 0 || shape->vectors_per_lane == 1) || force_upb > 1)
+            return GGRMS_ERROR_NOT_SUPPORTED;
+        kernel = GGRMS_KERNEL_RUN;
+        lanes = 64;
+        vpt = 1;
+    } else if (shape && (shape->lanes_per_group != 0 || shape->vectors_per_lane != 0)) {
         kernel = kernel_for_shape(shape->lanes_per_group, shape->vectors_per_lane);
         lanes = shape->lanes_per_group;
         vpt = shape->vectors_per_lane;
@@ -277,8 +294,46 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         if (vpt > 2) rule_upb = 1;
     } else {
         choose_shape(nvec, &kernel, &lanes, &vpt, &rule_upb);
+        // Packed groups of 9-64 vectors in a job small enough to be resident at
+        // once (at most kSmallJobWaves waves): the same slots as half the lanes
+        // with two vectors each, which spreads each wave's fixed work
+        // (indexing, the sum across lanes, the normaliser, the boundary pieces)
+        // over twice the elements -- such a job is one round of loads followed
+        // by its arithmetic, which no other wave's loads hide (the strided 256 x
+        // 4800 fp16 job: 4.19 against 4.66 us).  In larger jobs each load
+        // instruction would then touch twice the cache lines, half of each
+        // (377 MB of 100-wide fp16 groups: 104.9 against 70.4 us), so they keep
+        // one vector per lane.
+        const bool small_job = rows * plan->groups * lanes <= kSmallJobWaves * 64;
+        if (packed && kernel == GGRMS_KERNEL_WAVE && small_job && lanes >= 16 && lanes <= 64 &&
+            vpt == 1) {
+            lanes /= 2;
+            vpt = 2;
+        } else if (packed && kernel == GGRMS_KERNEL_WAVE && !small_job && run_fits && pb <= 4 &&
+                   2 * gpw * gbytes >= 64 * 16 && vpt == 1) {
+            // Larger jobs of packed groups whose boundary vectors would be
+            // stored in 2- or 4-byte pieces: runs of groups per wave, one
+            // vector per lane over a contiguous stretch of the row, so that
+            // only the run's two end vectors are stored in pieces (377 MB of
+            // 99-wide bf16 groups: 73.6 against 112.4 us; 50-wide bf16 80.6
+            // against 95.2; 127-wide bf16 84.6 against 109.7), as long as the
+            // run fills at least half of the wave (13-wide bf16 groups, 8 to a
+            // run, fill a fifth: 270.6 against 160.7 us).  With 8-byte pieces the
+            // lane segments stay ahead (100-wide fp16: 67.0 against 70.5 us):
+            // the per-group sums over the wave cost more than the pieces.
+            kernel = GGRMS_KERNEL_RUN;
+            lanes = 64;
+        }
+    }
+    if (kernel == GGRMS_KERNEL_RUN) {
+        plan->runs_per_row = (plan->groups + gpw - 1) / gpw;
+        plan->pub.groups_per_run = (int32_t)gpw;
+        nvec = gpw;  // the kernel takes the run length in the vector-count field
     }
     if (packed && kernel == GGRMS_KERNEL_WIDE) return GGRMS_ERROR_NOT_SUPPORTED;  // not built
+    // two vectors per lane below 64 lanes: built for packed groups only
+    if (!packed && kernel == GGRMS_KERNEL_WAVE && lanes < 64 && vpt > 1)
+        return GGRMS_ERROR_NOT_SUPPORTED;
 
     const int64_t groups = plan->groups;
     // Rows of one group per BLOCK workgroup: the group's weights are staged
@@ -299,14 +354,14 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->pub.kernel = kernel;
     plan->pub.lanes_per_group = lanes;
     plan->pub.rows_per_workgroup = upb;
-    // WAVE workgroups: one wave for 16-byte vectors, whose slot is freed the
-    // moment it retires (128-wide groups: 0.83 against 0.79 of HBM peak with
-    // four); four waves for narrower vectors, which need 2-4x the workgroups
-    // for the same bytes (4-byte vectors: 96 against 107 us with one), and for
-    // packed groups, whose extra VALU work after the loads ends sooner when
-    // each CU's four SIMDs hold one wave of every workgroup (the 256 x 4800
-    // fp16 strided job: 3.8 against 4.2 us).
-    bool four = kernel == GGRMS_KERNEL_WAVE && (packed || vb < 16);
+    // WAVE workgroups: one wave for 16-byte vectors, packed groups included,
+    // whose slot is freed the moment it retires (128-wide groups: 0.83
+    // against 0.79 of HBM peak with four; 377 MB of 100-wide packed fp16
+    // groups: 66.9 against 70.4 us; the strided 256 x 4800 fp16 job: equal
+    // with 16 x 1, 4.19 against 4.61 us with 8 x 2); four waves for narrower
+    // vectors, which need 2-4x the workgroups for the same bytes (4-byte
+    // vectors: 96 against 107 us with one).
+    bool four = kernel == GGRMS_KERNEL_WAVE && vb < 16;
     if (flags & GGRMS_FLAG_WAVE_ONE) four = false;
     if (kernel == GGRMS_KERNEL_WAVE && (flags & GGRMS_FLAG_WAVE_FOUR)) four = true;
     int block = four ? kWaveBlock : kWaveBlockOneWave;
@@ -318,18 +373,21 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     // if the groups per workgroup divide the row).
     int64_t R1, C1;
     launch_tiles(*plan, rows, &R1, &C1);
-    const int64_t gpw = kernel == GGRMS_KERNEL_WAVE ? wave_groups_per_workgroup(lanes, block) : 1;
+    const int64_t gpwg = kernel == GGRMS_KERNEL_WAVE ? wave_groups_per_workgroup(lanes, block) : 1;
+    const int64_t tiles_per_row = kernel == GGRMS_KERNEL_RUN ? plan->runs_per_row : groups;
     plan->xband = kernel != GGRMS_KERNEL_WIDE && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) &&
-                  groups % (kXcds * gpw) != 0;
+                  tiles_per_row % (kXcds * gpwg) != 0;
     if (flags & GGRMS_FLAG_ORDER_ROWS) plan->xband = false;
     if ((flags & GGRMS_FLAG_ORDER_BANDED) && kernel != GGRMS_KERNEL_WIDE) plan->xband = true;
     if (kernel == GGRMS_KERNEL_BLOCK) block = lanes * upb;
     if (kernel == GGRMS_KERNEL_WIDE) block = kWideBlock;
+    if (kernel == GGRMS_KERNEL_RUN) block = 64;
     plan->pub.block_threads = block;
     // Threads per row of the grid.  Each launch stays within 2^31 threads
     // (so within 2^31 units and tiles too) and the kernels index with 32-bit
     // integers; larger jobs are split by rows.
     int64_t row_threads = groups * (kernel == GGRMS_KERNEL_WIDE ? kWideBlock : lanes);
+    if (kernel == GGRMS_KERNEL_RUN) row_threads = plan->runs_per_row * 64;
     if (kernel == GGRMS_KERNEL_WAVE && plan->xband) row_threads = C1 * block;
     int64_t rows_per_launch = ((int64_t)1 << 31) / row_threads;
     if (rows_per_launch < 1) return GGRMS_ERROR_INVALID_VALUE;  // one row alone too large

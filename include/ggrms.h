@@ -133,7 +133,9 @@ typedef enum {
     GGRMS_KERNEL_NONE = 0,   /* rows == 0: nothing to launch */
     GGRMS_KERNEL_WAVE = 1,   /* one span of <= 64 lanes per (row, group); no LDS, no barrier */
     GGRMS_KERNEL_BLOCK = 2,  /* one (row, group) across 2..16 waves; LDS combine, one barrier */
-    GGRMS_KERNEL_WIDE = 3    /* groups too wide for registers: two passes over the group */
+    GGRMS_KERNEL_WIDE = 3,   /* groups too wide for registers: two passes over the group */
+    GGRMS_KERNEL_RUN = 4     /* packed groups: one wave over a run of consecutive groups of a
+                                row, one vector per lane; 64-lane sums per group */
 } ggrms_kernel_t;
 
 typedef struct {
@@ -152,6 +154,8 @@ typedef struct {
                                  boundary; 2, 4 or 8 for packed groups (see below) */
     int32_t tile_order;       /* order in which workgroups take the job's tiles:
                                  0 row-major, 1 XCD-banded (see below) */
+    int32_t groups_per_run;   /* RUN: groups one wave takes (the last run of a row may
+                                 hold fewer); 0 for the other kernels */
 } ggrms_plan_t;
 
 /*
@@ -165,7 +169,10 @@ typedef struct {
  * the start of the row, a vector on a group boundary is read by both groups
  * (each uses its own elements) and written in pieces of
  * piece_bytes = gcd(group bytes, 16), so no element is written twice and no
- * read leaves the row.
+ * read leaves the row.  In a large job, packed groups stored in 2- or 4-byte
+ * pieces (RUN) are taken a run of consecutive groups per wave, the lanes
+ * holding the run's vectors one each, so only the run's end vectors are
+ * stored in pieces.
  */
 
 /*

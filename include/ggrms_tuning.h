@@ -55,6 +55,9 @@ typedef enum {
  *                     access is a vector of that size, which the pointers,
  *                     row strides and the group's byte length must allow
  *                     (16 also allows packed groups, see ggrms.h)
+ *   kernel            0: the kernel family follows from lanes and vectors;
+ *                     GGRMS_KERNEL_RUN: runs of packed groups (lanes and
+ *                     vectors 0, or 64 and 1; groups of at most 32 vectors)
  *
  * For packed groups the shape must cover the vectors of the worst-aligned
  * group, WIDE is not built and rows_per_workgroup must be 0 or 1.
@@ -64,14 +67,15 @@ typedef struct {
     int32_t vectors_per_lane;
     int32_t rows_per_workgroup;
     int32_t vector_bytes;
+    int32_t kernel;
 } ggrms_shape_t;
 
 /*
  * ggrms_forward_tuned -- ggrms_forward_ex with launch controls: `flags` may
  * also hold ggrms_tuning_flag_t bits, and `shape` (NULL: the library
  * chooses) forces the kernel shape.  GGRMS_ERROR_INVALID_VALUE for a shape
- * field out of range (negative, or a vector_bytes that is not 0, 2, 4, 8 or
- * 16); GGRMS_ERROR_NOT_SUPPORTED for a shape that is not built, whose
+ * field out of range (negative, a vector_bytes that is not 0, 2, 4, 8 or 16,
+ * or a kernel that is not 0 or GGRMS_KERNEL_RUN); GGRMS_ERROR_NOT_SUPPORTED for a shape that is not built, whose
  * lanes_per_group * vectors_per_lane vectors do not cover one group, whose
  * rows_per_workgroup cannot be used, or whose vector_bytes the alignment
  * does not allow.  Otherwise as ggrms_forward_ex.

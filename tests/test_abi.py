@@ -162,6 +162,7 @@ def test_interleaved_views_do_not_overlap(g):
 
 
 RI, NBG, PER_GROUP, STREAM, KEEP = 1, 2, 4, 8, 16
+KERNEL_RUN = 4
 ROWS, BANDED, WAVE1, WAVE4 = 32, 64, 128, 256
 
 
@@ -303,16 +304,32 @@ def test_tile_order_and_wave_workgroups(g):
     assert (p["tile_order"], p["workgroups"]) == (1, 8192 // 4 * 8)
     # WIDE is always row-major
     assert plan(RI | BANDED, 4, 3 * 40960, 40960)["tile_order"] == 0
-    # packed groups (200-byte groups of the strided layout): 4-wave workgroups of 16
-    # groups, 3 per row -> banded; one wave if forced
+    # packed groups (200-byte groups of the strided layout, a job of 3072 waves at 16
+    # lanes per group, resident at once): 8 lanes x 2 vectors per group in one-wave
+    # workgroups of 8 groups, 6 per row, banded; four waves if forced (2 tiles per
+    # row, the second half full); row-major if forced
     fused = dict(y=A, gate=A + 9600)
     p = plan(RI, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["piece_bytes"], p["block_threads"], p["tile_order"], p["workgroups"]) == \
-        (8, 256, 1, 256 * 3)
-    p = plan(RI | WAVE1, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 1, 256 * 12)
+    assert (p["lanes_per_group"], p["vectors_per_lane"], p["piece_bytes"], p["block_threads"],
+            p["tile_order"], p["workgroups"]) == (8, 2, 8, 64, 1, 256 * 6)
+    p = plan(RI | WAVE4, 256, 4800, 100, F16, stride=9856, **fused)
+    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (256, 1, 256 * 2)
     p = plan(RI | ROWS, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (256, 0, 256 * 48 * 16 // 256)
+    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 0, 256 * 48 * 8 // 64)
+    # a larger packed job (12288 waves): 16 lanes x 1 vector per group (8-byte pieces)
+    p = plan(RI, 1024, 4800, 100, F16, stride=9856, **fused)
+    assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["block_threads"],
+            p["workgroups"]) == ("wave", 16, 1, 64, 1024 * 12)
+    # 99-wide bf16 groups (2-byte pieces) in a large job: runs of 5 groups per wave
+    # (12.4 vectors each, 63 of 64 lanes), 10 runs per row (the last of 3 groups), banded
+    p = plan(RI, 1024, 48 * 99, 99, BF16)
+    assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["groups_per_run"],
+            p["block_threads"], p["workgroups"], p["tile_order"]) == \
+        ("run", 64, 1, 5, 64, 1024 * 10, 1)
+    # 80 such groups per row: 16 runs, a multiple of the 8 XCDs -> row-major
+    p = plan(RI, 1024, 80 * 99, 99, BF16)
+    assert (p["kernel_name"], p["workgroups"], p["tile_order"]) == ("run", 1024 * 16, 0)
+
     # one row: banded over the row's tiles (XCD x takes a run of columns)
     p = plan(RI, 1, 7680, 128)
     assert (p["tile_order"], p["workgroups"]) == (1, 15)
@@ -432,12 +449,14 @@ def test_plans_for_the_workloads(g):
     assert st == OK and (p["block_threads"], p["workgroups"], p["tile_order"]) == (64, 16384 * 16, 0)
     # 256x4800 fp16 slices of a [256, 9856] buffer, G = 100: 200-byte groups in 9600-byte
     # rows -> packed: 16-byte vectors from the row start, boundary vectors in 8-byte pieces;
-    # a group touches at most ceil((8 + 200) / 16) = 13 vectors -> 16-lane segments
+    # a group touches at most ceil((8 + 200) / 16) = 13 vectors -> 16 slots, as
+    # 8 lanes with 2 vectors each
     p = _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)
-    assert (p["kernel_name"], p["vector_bytes"], p["piece_bytes"], p["lanes_per_group"]) == \
-        ("wave", 16, 8, 16)
-    # packed groups: 4-wave workgroups of 16 groups, 3 per row -> banded
-    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (256, 256 * 3, 1)
+    assert (p["kernel_name"], p["vector_bytes"], p["piece_bytes"], p["lanes_per_group"],
+            p["vectors_per_lane"]) == ("wave", 16, 8, 8, 2)
+    # packed groups in a job resident at once: 8 lanes x 2 vectors per group, one-wave
+    # workgroups of 8 groups, 6 per row -> banded
+    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (64, 256 * 6, 1)
     # tiny f32, G = 64: 16 vectors
     p = _plan(g, 4, 256, 64, F32)
     assert (p["vector_bytes"], p["lanes_per_group"]) == (16, 16)
@@ -516,6 +535,50 @@ def test_packed_groups_need_aligned_rows(g):
                      y_row_stride=16 * G, gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
                      gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
     assert st == NOTSUP
+
+
+def test_runs_of_packed_groups_plan(g):
+    """Runs: packed groups in 2- or 4-byte pieces in a job of more than 4096
+    waves, as many groups per wave as fit 64 vectors at any alignment (at
+    most 8) when they fill at least half of the wave, one-wave workgroups;
+    forced through the tuning shape's kernel field for any packed group that
+    fits twice; refused for groups that are not packed, a shared weight, or
+    groups too wide for two per wave."""
+    kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
+    def plan(rows, G, dtype, groups=16, flags=RI, shape=None):
+        width = G * groups
+        return _plan_ex(g, flags, shape, rows=rows, width=width, group_size=G, y_row_stride=width,
+                        gate_row_stride=width, out_row_stride=width, dtype=dtype, **kw)
+    # (G, dtype, groups per run, taken by default): 64 * 16 - 16 + piece bytes over the
+    # group's bytes, at most 8; by default with 2- or 4-byte pieces filling >= 1/2 of a wave
+    for G, dtype, gpw, default in ((100, F16, 5, False), (99, BF16, 5, True),
+                                   (50, BF16, 8, True), (127, BF16, 3, True), (250, F16, 2, True),
+                                   (25, F32, 8, True), (99, F32, 2, True), (13, F16, 8, False)):
+        st, p = plan(8000, G, dtype, shape=(0, 0, 0, 0, KERNEL_RUN))
+        assert st == OK and (p["kernel_name"], p["groups_per_run"], p["block_threads"],
+                             p["workgroups"]) == ("run", gpw, 64, 8000 * (-(-16 // gpw))), (G, dtype, p)
+        assert p["vectors_per_lane"] == 1 and p["lanes_per_group"] == 64
+        assert plan(8000, G, dtype, shape=(64, 1, 0, 16, KERNEL_RUN))[1] == p
+        assert (plan(8000, G, dtype)[1] == p) == default, (G, dtype)
+        # a small job stays on lane segments (two vectors per lane from 16 lanes); a run
+        # can be forced
+        st, q = plan(20, G, dtype)
+        assert q["kernel_name"] == "wave", (G, q)
+        st, q = plan(20, G, dtype, shape=(0, 0, 0, 0, KERNEL_RUN))
+        assert st == OK and q["kernel_name"] == "run" and q["groups_per_run"] == gpw
+    # groups of 33+ vectors (two would not fit a wave), and groups of <= 2 vectors stay WAVE
+    assert plan(8000, 300, F16)[1]["kernel_name"] == "wave"
+    assert plan(8000, 9, BF16)[1]["kernel_name"] == "wave"
+    # refusals: aligned groups, a shared weight, a wide group, other lane shapes
+    assert plan(2000, 128, F16, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 100, F16, flags=RI | PER_GROUP, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 300, F16, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 100, F16, shape=(32, 1, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 100, F16, shape=(64, 1, 2, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 100, F16, shape=(0, 0, 0, 0, 7))[0] == INVALID
+    # 8 groups per row: a run of 5 and one of 3
+    st, p = plan(50000, 99, BF16, groups=8)
+    assert (p["kernel_name"], p["groups_per_run"], p["workgroups"]) == ("run", 5, 50000 * 2)
 
 
 def test_rows_split_over_launches(g):

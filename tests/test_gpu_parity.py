@@ -5,6 +5,7 @@ within 2 units in the last place (NaN matches NaN, +0 matches -0).  Inputs
 are seeded synthetic data (synthetic/), generated on the host; the oracle
 sees the same host arrays the GPU copies.
 """
+import math
 import os
 
 import numpy as np
@@ -305,6 +306,100 @@ def test_packed_groups(g, orc, G, dtype):
         assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
             "packed stores touched elements outside the view"
         assert_parity(got[view], ref[view], dtype, f"packed G={G} flags={flags}")
+        if p["kernel_name"] == "wave" and p["vectors_per_lane"] == 2:
+            # the same slots as twice the lanes with one vector each
+            shape = (2 * p["lanes_per_group"], 1)
+            say(f"case packed G={G} dtype={DT_IDS[dtype]} flags={flags} shape={shape}")
+            od = dev_buf(ob, dtype)
+            assert run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
+                           dtype, 0, shape=shape, flags=flags) == g.SUCCESS
+            torch.cuda.synchronize()
+            got1 = host_bits(od, dtype)
+            assert np.array_equal(got1[~view].view(np.uint8), ob[~view].view(np.uint8))
+            assert_parity(got1[view], ref[view], dtype, f"packed G={G} flags={flags} {shape}")
+
+
+RUN_CASES = [(100, F16), (100, BF16), (99, BF16), (97, F16), (50, BF16), (127, BF16), (250, F16),
+             (25, F32), (99, F32), (13, F16)]
+
+
+@pytest.mark.parametrize("G,dtype", RUN_CASES, ids=[f"G{G}-{DT_IDS[d]}" for G, d in RUN_CASES])
+def test_runs_of_packed_groups(g, orc, G, dtype):
+    """Runs of packed groups per wave (forced; the library takes them for large
+    jobs): rows of 1, 2, 3 and 5 times the fewest groups that make a 16-byte
+    aligned row, and about 48 groups -- so runs of fewer groups than a full
+    run, a short last run, several full runs; both operators; out rows padded
+    and guarded, nothing outside the view written; the banded and the
+    row-major tile order give the same bits."""
+    esz = 4 if dtype == F32 else 2
+    period = 16 // math.gcd(G * esz, 16)  # groups per 16-byte aligned row length
+    for groups in sorted({period, 2 * period, 3 * period, 5 * period, 48 // period * period}):
+        width = G * groups
+        rows, pad = 7, 16 // esz
+        so = width + pad
+        guard = 64
+        y, gt, w = random_case(rows, width, dtype, seed=G * 5 + groups + dtype)
+        canary = {F32: np.float32(-1234.5), F16: np.uint16(0x7BFF), BF16: np.uint16(0x4B4B)}[dtype]
+        ob = np.full(guard + (rows - 1) * so + width + guard, canary, dtype=S.storage_dtype(dtype))
+        view = np.zeros(ob.shape, dtype=bool)
+        for r in range(rows):
+            view[guard + r * so: guard + r * so + width] = True
+        yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+        for flags in ((FLAG_RI,) if dtype != F32 else (0,)) + (FLAG_NBG,):
+            outs = []
+            for order in (0, 32, 64):  # the library's order, row-major, banded
+                od = dev_buf(ob, dtype)
+                say(f"case run G={G} dtype={DT_IDS[dtype]} groups={groups} flags={flags} order={order}")
+                st = run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
+                             dtype, 0, shape=(0, 0, 0, 0, g.KERNEL_RUN), flags=flags | order)
+                assert st == g.SUCCESS, g.ggrms_status_string(st)
+                torch.cuda.synchronize()
+                outs.append(host_bits(od, dtype))
+            got = outs[0]
+            assert all(np.array_equal(o.view(np.uint8), got.view(np.uint8)) for o in outs[1:])
+            assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
+                "run stores touched elements outside the view"
+            ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                              gate_row_stride=width, out_row_stride=so, eps=1e-5, dtype=dtype,
+                              round_intermediate=flags & FLAG_RI,
+                              norm_before_gate=bool(flags & FLAG_NBG), out=ob.copy(),
+                              out_offset=guard)
+            assert_parity(got[view], ref[view], dtype, f"run G={G} groups={groups} flags={flags}")
+
+
+def test_runs_in_place_and_by_default(g, orc):
+    """The strided fused layout normalised in place over the gate with runs
+    (a boundary vector of two runs is read by both waves while each writes
+    its own pieces), and a job of 2-byte-piece groups large enough that the
+    library takes runs itself, against the oracle."""
+    rows, width, G, fused = 64, 4800, 100, 9856
+    buf = S.tensor(93, S.TID_Y, rows * fused, F16, ("normal", 1.0))
+    w = S.tensor(93, S.TID_W, width, F32, ("uniform", 0.5, 1.5))
+    ref = orc.forward(buf, buf, w, rows=rows, width=width, group_size=G, y_row_stride=fused,
+                      gate_row_stride=fused, out_row_stride=fused, eps=1e-5, dtype=F16,
+                      round_intermediate=1, gate_offset=width, out_offset=width, out=buf.copy())
+    fd = dev_buf(buf, F16)
+    wd = torch.from_numpy(w).cuda()
+    say("case run in place over the gate")
+    assert run_gpu(g, fd, fd[width:], wd, fd[width:], rows, width, G, fused, fused, fused, 1e-5,
+                   F16, 1, shape=(0, 0, 0, 0, g.KERNEL_RUN)) == g.SUCCESS
+    torch.cuda.synchronize()
+    assert_parity(host_bits(fd, F16), ref, F16, "run in place")
+    # 1500 rows x 48 groups of 99 bf16 (2-byte pieces) x 16 lanes = 18000 waves: runs by default
+    rows, G = 1500, 99
+    width = 48 * G
+    y, gt, w = random_case(rows, width, BF16, seed=94)
+    yd, gd, wd = dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(w).cuda()
+    od = torch.empty_like(yd)
+    p = _plan_of(g, yd, gd, wd, od, rows, width, G, width, width, width, BF16, FLAG_RI)
+    assert (p["kernel_name"], p["groups_per_run"]) == ("run", 5), p
+    say("case run by default, 1500 x 4752 bf16")
+    assert run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, 1e-5, BF16, 1) == g.SUCCESS
+    torch.cuda.synchronize()
+    ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                      gate_row_stride=width, out_row_stride=width, eps=1e-5, dtype=BF16,
+                      round_intermediate=1)
+    assert_parity(host_bits(od, BF16), ref, BF16, "run by default")
 
 
 def test_packed_in_place_over_the_gate(g, orc):
