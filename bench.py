@@ -534,6 +534,13 @@ EVIDENCE = {
     # lane on 8 lanes (the default for jobs resident at once)
     "packed_g100": (1, 13107, 4800, 100, 1, None),
     "packed_g100_8x2": (1, 13107, 4800, 100, 1, (8, 2)),
+    # the same groups in runs of 5 per wave (one vector per lane)
+    "packed_g100_run": (1, 13107, 4800, 100, 1, (64, 1, 0, 0, 4)),
+    # 16 x 1 in four-wave workgroups (16 groups = 3200 bytes, whole 128-byte
+    # lines, per workgroup), and both workgroup sizes in row-major order
+    "packed_g100_four": (1, 13107, 4800, 100, 1 | 256, None),
+    "packed_g100_rows": (1, 13107, 4800, 100, 1 | 32, None),
+    "packed_g100_rows_four": (1, 13107, 4800, 100, 1 | 32 | 256, None),
 }
 
 

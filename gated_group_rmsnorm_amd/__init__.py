@@ -80,7 +80,7 @@ class _Plan(ctypes.Structure):
                 ("rows_per_workgroup", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("streaming", ctypes.c_int32),
                 ("piece_bytes", ctypes.c_int32), ("tile_order", ctypes.c_int32),
-                ("groups_per_run", ctypes.c_int32)]
+                ("groups_per_run", ctypes.c_int32), ("super_tile", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:

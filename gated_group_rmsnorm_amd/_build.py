@@ -32,6 +32,9 @@ LIB_HIP = ["ggrms_api.hip", "table_f32.hip", "table_f16.hip", "table_bf16.hip",
            "table_f32_nbg.hip", "table_f16_nbg.hip", "table_bf16_nbg.hip"]
 LIB_CXX = ["plan.cpp"]
 BENCH_HIP = ["bench_aux.hip"]
+# the epilogue called from a producer kernel (an example, not part of the ABI)
+EXAMPLE_HIP = ["example_producer.hip"]
+EXAMPLE_LIB = os.path.join(PKG, "libggrms_example.so")
 
 
 def _run(cmd):
@@ -64,7 +67,7 @@ def build(verbose: bool = False) -> str:
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
-    srcs = LIB_HIP + LIB_CXX + BENCH_HIP
+    srcs = LIB_HIP + LIB_CXX + BENCH_HIP + EXAMPLE_HIP
     with cf.ThreadPoolExecutor(min(8, len(srcs))) as ex:
         objs = dict(zip(srcs, ex.map(_compile, srcs)))
     _link([objs[s] for s in LIB_HIP + LIB_CXX], LIB,
@@ -72,8 +75,9 @@ def build(verbose: bool = False) -> str:
     # the benchmark helpers call the product library itself (found next to them)
     _link([objs[s] for s in BENCH_HIP], BENCH_LIB,
           ["-L", PKG, "-l:libggrms.so", "-Wl,-rpath,$ORIGIN"])
+    _link([objs[s] for s in EXAMPLE_HIP], EXAMPLE_LIB)
     if verbose:
-        print(f"built {LIB} and {BENCH_LIB}")
+        print(f"built {LIB}, {BENCH_LIB} and {EXAMPLE_LIB}")
     return LIB
 
 

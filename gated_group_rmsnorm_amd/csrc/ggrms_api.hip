@@ -87,7 +87,8 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     div_magic(a.xc, &a.xc_m, &xc_s);
     a.bits = (div_s << kBitDivShift) | (xc_s << kBitXcShift) |
              ((dtype != GGRMS_F32 && (flags & GGRMS_FLAG_ROUND_INTERMEDIATE)) ? kBitRound : 0u) |
-             ((flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? kBitShared : 0u) | (lp.xband ? kBitBand : 0u);
+             ((flags & GGRMS_FLAG_WEIGHT_PER_GROUP) ? kBitShared : 0u) | (lp.xband ? kBitBand : 0u) |
+             ((uint32_t)lp.super_shift << kBitSuperShift);
     const int es = lp.esize;
 
     for (int64_t r0 = 0; r0 < rows; r0 += lp.rows_per_launch) {

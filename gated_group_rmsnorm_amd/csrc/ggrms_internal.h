@@ -30,6 +30,13 @@ namespace ggrms {
 // while each XCD reads the weights of only its band, which then stay in its
 // L2 and its CUs' L1.  The last R % 8 rows form a short block, shared out the
 // same way.
+// With super-tiles of S = 2^kBitSuperShift tiles (WAVE tiles of packed
+// groups, whose byte length is not a multiple of the 128-byte cache line), a
+// full block is numbered by S consecutive tiles of one row at a time (super-
+// tile (s, r) holds columns s*S .. s*S + S-1 of row r; super-tiles taken
+// column-major), so the S tiles that share lines at their edges run on one
+// XCD, one after the other, and each line is fetched into one L2 only.  The
+// launch has C % S == 0; S = 1 is the plain banded order.
 struct KArgs {
     const void* y;
     const void* gate;
@@ -55,6 +62,7 @@ constexpr uint32_t kBitXcShift = 5;       // 5 bits: shift for x / C
 constexpr uint32_t kBitRound = 1u << 10;  // round the intermediate (16-bit types only)
 constexpr uint32_t kBitShared = 1u << 11; // one weight vector shared by every group
 constexpr uint32_t kBitBand = 1u << 12;   // XCD-banded tile order
+constexpr uint32_t kBitSuperShift = 13;   // 3 bits: log2 of the banded order's super-tile
 
 // Workgroups are dealt to XCDs in turn on the 8-XCD part.
 constexpr uint32_t kXcds = 8;
@@ -111,6 +119,7 @@ struct LaunchPlan {
     int64_t nvec;
     int64_t rows_per_launch;  // rows handled by each launch (the last one may have fewer)
     bool xband;               // XCD-banded tile order (kBitBand)
+    int super_shift;          // log2 of the banded order's super-tile (kBitSuperShift)
     int64_t runs_per_row;     // RUN: tiles of one row
 };
 

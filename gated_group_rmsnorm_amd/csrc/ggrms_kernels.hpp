@@ -96,6 +96,7 @@ __device__ inline uint32_t div_shift(const KArgs& a) { return (a.bits >> kBitDiv
 __device__ inline uint32_t xc_shift(const KArgs& a) { return (a.bits >> kBitXcShift) & 31u; }
 __device__ inline bool round_intermediate(const KArgs& a) { return (a.bits & kBitRound) != 0; }
 __device__ inline bool banded(const KArgs& a) { return (a.bits & kBitBand) != 0; }
+__device__ inline uint32_t super_shift(const KArgs& a) { return (a.bits >> kBitSuperShift) & 7u; }
 // the weight's offset between groups: G (one weight per column) or 0 (shared)
 __device__ inline int64_t weight_group_stride(const KArgs& a) {
     return (a.bits & kBitShared) ? 0 : (int64_t)a.G;
@@ -152,6 +153,24 @@ __device__ inline void store_piece_stream(char* p, const W& v, int piece) {
     }
 }
 
+// The 16-byte vector whose PB-byte pieces are those of `own` where
+// mine(q) holds and those of `other` elsewhere.
+template <int PB, class Mine>
+__device__ inline u32x4 merge_pieces(const u32x4& own, const u32x4& other, Mine mine) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (PB >= 4) {
+            r[i] = mine(i * 4 / PB) ? own[i] : other[i];
+        } else {
+            const u32 lo = mine(2 * i) ? own[i] : other[i];
+            const u32 hi = mine(2 * i + 1) ? own[i] : other[i];
+            r[i] = (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
+        }
+    }
+    return r;
+}
+
 // Lane `sl` of the SEG lanes that own the unit (row n, group g) loads VPT
 // vectors (indices sl, sl+SEG, ...), runs the epilogue's per-unit steps on
 // them, sums its share with `reduce`, and stores if `store_ok`.  With
@@ -163,10 +182,11 @@ __device__ inline void store_piece_stream(char* p, const W& v, int piece) {
 // the 16-byte vector but the rows are, so vectors are counted from the row's
 // start and the unit takes the vectors that hold any of its elements; a
 // vector on a group boundary also holds a neighbour's elements, which are
-// left out of the sum and not written: such a vector is stored in PB-byte
-// pieces (PB = gcd(group bytes, 16), so a group boundary never splits a
-// piece).  Reads stay inside the row; every element is written by exactly
-// one unit.
+// left out of the sum and not written by this unit: such a vector is stored
+// whole by the left unit's lane when both units sit on segments of one wave,
+// and in PB-byte pieces otherwise (PB = gcd(group bytes, 16), so a group
+// boundary never splits a piece).  Reads stay inside the row; every element
+// is written by exactly one unit.
 template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT, WSource WS, class Reduce>
 __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g, uint32_t sl,
                                           bool store_ok, const float* wl, Reduce reduce) {
@@ -237,13 +257,43 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     // completion between the wave's stores.  The builtin form lets the
     // compiler's wait insertion see the wait.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // Packed groups on lane segments of one wave (one vector per lane): a
+    // vector on the boundary between two groups of the wave is the last
+    // vector of the left group's segment and the first of the next segment.
+    // The left lane takes the right unit's pieces of it from lane 0 of the
+    // next segment (ds_bpermute) and stores the whole vector; the right lane
+    // stores nothing there.  Boundary vectors shared with a group outside
+    // the wave (or with the next row's first group) keep the piece stores.
+    // Same bytes, one 16-byte store in place of two partial ones (377 MB of
+    // 100-wide fp16 groups: 63.1 against 67.1 us).  In either tile order a
+    // wave's segments hold consecutive units, so segment s + 1 holds group
+    // g + 1 of the same row whenever g + 1 < groups.
+    constexpr bool kMerge = kPacked && VPT == 1 && SEG < 64 && WS == WSource::Global;
+    const uint32_t seg = (threadIdx.x & 63u) / SEG;
+    const bool has_right = seg + 1 < 64u / SEG && g + 1 < a.groups;  // next segment: group g+1
+    const bool has_left = seg > 0 && g > 0;                            // previous one: group g-1
     auto store = [&](auto ri_tag) {
         W res[VPT];
         epi::finish<decltype(ri_tag)::value>(L, nf, wr, res);
+        W nb{};
+        if constexpr (kMerge) {
+            const int src = (int)((((seg + 1) * SEG) & 63u) << 2);
+#pragma unroll
+            for (int i = 0; i < VB / 4; ++i)
+                nb[i] = (u32)__builtin_amdgcn_ds_bpermute(src, (int)res[0][i]);
+        }
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
             const uint32_t idx = sl + k * SEG;
             if (!store_ok || idx >= nv) continue;
+            if constexpr (kMerge) {
+                if (rel[k] < 0 && has_left) continue;  // stored whole by the left lane
+                if (rel[k] + N > (int32_t)a.G && has_right) {
+                    store_stream<NT>(ov + v0 + idx,
+                                     merge_pieces<PB>(res[k], nb, [&](int q) { return owned(k, q); }));
+                    continue;
+                }
+            }
             if constexpr (kPacked) {
                 if (rel[k] < 0 || rel[k] + N > (int32_t)a.G) {
                     // a vector on a group boundary: only this unit's pieces
@@ -267,9 +317,11 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
 
 // Tile (row or row tile rt, tile column c) of workgroup blockIdx.x in the
 // XCD-banded order over R x C tiles (C = KArgs::xc): XCD x = b % 8 takes, in
-// each block of 8 rows numbered column-major, the tiles x*C .. x*C + C-1,
-// block after block; then its share of the short block of the last R % 8
-// rows.  A bijection of the launch's R * C workgroups onto its tiles.
+// each block of 8 rows numbered column-major by super-tiles of S tiles of one
+// row (S = 1: by tiles), the tiles x*C .. x*C + C-1, block after block; then
+// its share of the short block of the last R % 8 rows (numbered by tiles).
+// With C % S == 0 a bijection of the launch's R * C workgroups onto its
+// tiles.
 __device__ inline void xcd_band_tile(const KArgs& a, uint32_t R, uint32_t& rt, uint32_t& c) {
     const uint32_t b = blockIdx.x;
     const uint32_t x = b % kXcds, k = b / kXcds;
@@ -277,9 +329,11 @@ __device__ inline void xcd_band_tile(const KArgs& a, uint32_t R, uint32_t& rt, u
     const uint32_t fullk = (R / kXcds) * C;  // each XCD's workgroups in the full blocks
     if (k < fullk) {
         const uint32_t blk = fast_div(k, a.xc_m, xc_shift(a));
-        const uint32_t idx = x * C + (k - blk * C);
-        c = idx / kXcds;
-        rt = blk * kXcds + idx % kXcds;
+        const uint32_t idx = x * C + (k - blk * C);  // = (s * 8 + r) * S + t
+        const uint32_t ss = super_shift(a);
+        const uint32_t q = idx >> ss;
+        c = ((q / kXcds) << ss) | (idx & ((1u << ss) - 1u));
+        rt = blk * kXcds + q % kXcds;
     } else {
         const uint32_t rr = R % kXcds;  // >= 1 here
         const uint32_t t2 = rr * C;     // tiles of the short block

@@ -309,18 +309,19 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
             vpt == 1) {
             lanes /= 2;
             vpt = 2;
-        } else if (packed && kernel == GGRMS_KERNEL_WAVE && !small_job && run_fits && pb <= 4 &&
-                   2 * gpw * gbytes >= 64 * 16 && vpt == 1) {
-            // Larger jobs of packed groups whose boundary vectors would be
-            // stored in 2- or 4-byte pieces: runs of groups per wave, one
-            // vector per lane over a contiguous stretch of the row, so that
-            // only the run's two end vectors are stored in pieces (377 MB of
-            // 99-wide bf16 groups: 73.6 against 112.4 us; 50-wide bf16 80.6
-            // against 95.2; 127-wide bf16 84.6 against 109.7), as long as the
-            // run fills at least half of the wave (13-wide bf16 groups, 8 to a
-            // run, fill a fifth: 270.6 against 160.7 us).  With 8-byte pieces the
-            // lane segments stay ahead (100-wide fp16: 67.0 against 70.5 us):
-            // the per-group sums over the wave cost more than the pieces.
+        } else if (packed && kernel == GGRMS_KERNEL_WAVE && !small_job && run_fits &&
+                   2 * gpw * gbytes >= 64 * 16 && 10 * gbytes < 6 * 16 * lanes && vpt == 1) {
+            // Larger jobs of packed groups that fill less than 60% of their
+            // lane segment (groups just over a power of two of vectors): runs
+            // of groups per wave, one vector per lane over a contiguous
+            // stretch of the row, as long as the run fills at least half of
+            // the wave.  377 MB of 127-wide bf16 groups (15.9 vectors on 32
+            // lanes): 86.6 against 93.4 us.  Fuller segments stay ahead, the
+            // per-group sums over the wave costing more than the idle lanes
+            // save (99-wide bf16, 12.4 vectors on 16 lanes: 71.4 against
+            // 73.8 us; 50-wide bf16: 68.1 against 78.8; 25-wide f32: 64.9
+            // against 66.8), and so do runs that would fill a fifth of the
+            // wave (13-wide bf16 groups, 8 to a run: 111 against 271 us).
             kernel = GGRMS_KERNEL_RUN;
             lanes = 64;
         }
@@ -377,8 +378,29 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     const int64_t tiles_per_row = kernel == GGRMS_KERNEL_RUN ? plan->runs_per_row : groups;
     plan->xband = kernel != GGRMS_KERNEL_WIDE && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) &&
                   tiles_per_row % (kXcds * gpwg) != 0;
+    // Packed groups in one-wave WAVE workgroups: a tile's bytes (its groups'
+    // bytes) are not a multiple of the 128-byte cache line, so neighbouring
+    // tiles of a row share a line at their edge.  Run by different XCDs, both
+    // L2s fetch that line and each writes back its part (377 MB of 100-wide
+    // fp16 groups in 800-byte tiles: 8% more bytes fetched than the inputs
+    // hold, 116K partial-line writes).  The banded order then deals S
+    // consecutive tiles of a row to one XCD together -- S the smallest power
+    // of two with S tiles a whole number of lines, or the largest power of
+    // two below it that divides the row's tiles -- and is taken for such jobs
+    // whatever the row's tile count.
+    int64_t super = 1;
+    if (kernel == GGRMS_KERNEL_WAVE && packed && block == kWaveBlockOneWave &&
+        !(flags & GGRMS_FLAG_ORDER_ROWS)) {
+        const int64_t tile_bytes = gpwg * gbytes;
+        while ((super * tile_bytes) % 128 != 0) super <<= 1;
+        while (super > 1 && C1 % super != 0) super >>= 1;
+        if (super > 1) plan->xband = true;
+    }
     if (flags & GGRMS_FLAG_ORDER_ROWS) plan->xband = false;
     if ((flags & GGRMS_FLAG_ORDER_BANDED) && kernel != GGRMS_KERNEL_WIDE) plan->xband = true;
+    plan->super_shift = 0;
+    if (plan->xband)
+        while ((int64_t)1 << plan->super_shift < super) ++plan->super_shift;
     if (kernel == GGRMS_KERNEL_BLOCK) block = lanes * upb;
     if (kernel == GGRMS_KERNEL_WIDE) block = kWideBlock;
     if (kernel == GGRMS_KERNEL_RUN) block = 64;
@@ -411,6 +433,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->pub.lds_bytes = upb > 1 ? (int32_t)(group_size * 4) : 0;
     plan->pub.workgroups = workgroups;
     plan->pub.tile_order = plan->xband ? 1 : 0;
+    plan->pub.super_tile = 1 << plan->super_shift;
     // Cache policy: stream large jobs, keep small ones cached.  The job is
     // 3 * rows * row_bytes bytes; rows * row_bytes is at most y's extent, so
     // it does not overflow, and comparing it with ceil(min / 3) is exact.

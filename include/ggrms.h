@@ -156,6 +156,10 @@ typedef struct {
                                  0 row-major, 1 XCD-banded (see below) */
     int32_t groups_per_run;   /* RUN: groups one wave takes (the last run of a row may
                                  hold fewer); 0 for the other kernels */
+    int32_t super_tile;       /* XCD-banded order: consecutive tiles of a row dealt to one
+                                 XCD together, so that tiles sharing cache lines meet in
+                                 one L2 (> 1 only for packed groups in one-wave WAVE
+                                 workgroups); 1 otherwise */
 } ggrms_plan_t;
 
 /*

@@ -30,8 +30,8 @@ typedef enum {
     GGRMS_FLAG_ORDER_ROWS = 32,
     GGRMS_FLAG_ORDER_BANDED = 64,
     /* WAVE workgroups of one or four waves (by default one for 16-byte
-     * vectors, four for narrower vectors and packed groups; no effect on
-     * BLOCK and WIDE). */
+     * vectors, packed groups included, and four for narrower vectors; no
+     * effect on BLOCK, WIDE and RUN). */
     GGRMS_FLAG_WAVE_ONE = 128,
     GGRMS_FLAG_WAVE_FOUR = 256
 } ggrms_tuning_flag_t;

@@ -309,26 +309,45 @@ def test_tile_order_and_wave_workgroups(g):
     # workgroups of 8 groups, 6 per row, banded; four waves if forced (2 tiles per
     # row, the second half full); row-major if forced
     fused = dict(y=A, gate=A + 9600)
+    # (1600-byte tiles: super-tiles of 2, 25 cache lines); four waves if forced
+    # (2 tiles of 6400 bytes per row, the second half full); row-major if forced
     p = plan(RI, 256, 4800, 100, F16, stride=9856, **fused)
     assert (p["lanes_per_group"], p["vectors_per_lane"], p["piece_bytes"], p["block_threads"],
-            p["tile_order"], p["workgroups"]) == (8, 2, 8, 64, 1, 256 * 6)
+            p["tile_order"], p["super_tile"], p["workgroups"]) == (8, 2, 8, 64, 1, 2, 256 * 6)
     p = plan(RI | WAVE4, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (256, 1, 256 * 2)
+    assert (p["block_threads"], p["tile_order"], p["super_tile"], p["workgroups"]) == \
+        (256, 1, 1, 256 * 2)
     p = plan(RI | ROWS, 256, 4800, 100, F16, stride=9856, **fused)
-    assert (p["block_threads"], p["tile_order"], p["workgroups"]) == (64, 0, 256 * 48 * 8 // 64)
-    # a larger packed job (12288 waves): 16 lanes x 1 vector per group (8-byte pieces)
+    assert (p["block_threads"], p["tile_order"], p["super_tile"], p["workgroups"]) == \
+        (64, 0, 1, 256 * 48 * 8 // 64)
+    # a larger packed job (12288 waves): 16 lanes x 1 vector per group (8-byte
+    # pieces), 800-byte tiles in super-tiles of 4 (3200 bytes, 25 lines)
     p = plan(RI, 1024, 4800, 100, F16, stride=9856, **fused)
     assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["block_threads"],
-            p["workgroups"]) == ("wave", 16, 1, 64, 1024 * 12)
-    # 99-wide bf16 groups (2-byte pieces) in a large job: runs of 5 groups per wave
-    # (12.4 vectors each, 63 of 64 lanes), 10 runs per row (the last of 3 groups), banded
+            p["workgroups"], p["tile_order"], p["super_tile"]) == ("wave", 16, 1, 64, 1024 * 12, 1, 4)
+    # 64 such groups per row: 16 tiles, a multiple of the 8 XCDs, banded all the same
+    p = plan(RI, 1024, 6400, 100, F16)
+    assert (p["tile_order"], p["super_tile"], p["workgroups"]) == (1, 4, 1024 * 16)
+    # 36 per row: 9 tiles, no power of two above 1 divides them -> plain banded
+    p = plan(RI, 1024, 3600, 100, F16)
+    assert (p["tile_order"], p["super_tile"], p["workgroups"]) == (1, 1, 1024 * 9)
+    # 40 per row: 10 tiles -> super-tiles of 2 (1600 bytes, half a line over)
+    p = plan(RI, 1024, 4000, 100, F16)
+    assert (p["tile_order"], p["super_tile"]) == (1, 2)
+    # 99-wide bf16 groups (2-byte pieces, 12.4 vectors on 16 lanes) in a large job: 16 x 1,
+    # 792-byte tiles in super-tiles of 4 (16 would be whole lines, but 12 tiles per row)
     p = plan(RI, 1024, 48 * 99, 99, BF16)
     assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["groups_per_run"],
-            p["block_threads"], p["workgroups"], p["tile_order"]) == \
-        ("run", 64, 1, 5, 64, 1024 * 10, 1)
-    # 80 such groups per row: 16 runs, a multiple of the 8 XCDs -> row-major
-    p = plan(RI, 1024, 80 * 99, 99, BF16)
-    assert (p["kernel_name"], p["workgroups"], p["tile_order"]) == ("run", 1024 * 16, 0)
+            p["workgroups"], p["tile_order"], p["super_tile"]) == ("wave", 16, 1, 0, 1024 * 12, 1, 4)
+    # 127-wide bf16 groups (15.9 vectors on 32 lanes, half-full segments): runs of 3 groups per
+    # wave, 16 runs per row, a multiple of the 8 XCDs -> row-major
+    p = plan(RI, 1024, 48 * 127, 127, BF16)
+    assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["groups_per_run"],
+            p["block_threads"], p["workgroups"], p["tile_order"], p["super_tile"]) == \
+        ("run", 64, 1, 3, 64, 1024 * 16, 0, 1)
+    # 40 such groups per row: 14 runs (the last of one group) -> banded
+    p = plan(RI, 1024, 40 * 127, 127, BF16)
+    assert (p["kernel_name"], p["workgroups"], p["tile_order"]) == ("run", 1024 * 14, 1)
 
     # one row: banded over the row's tiles (XCD x takes a run of columns)
     p = plan(RI, 1, 7680, 128)
@@ -538,22 +557,25 @@ def test_packed_groups_need_aligned_rows(g):
 
 
 def test_runs_of_packed_groups_plan(g):
-    """Runs: packed groups in 2- or 4-byte pieces in a job of more than 4096
-    waves, as many groups per wave as fit 64 vectors at any alignment (at
-    most 8) when they fill at least half of the wave, one-wave workgroups;
-    forced through the tuning shape's kernel field for any packed group that
-    fits twice; refused for groups that are not packed, a shared weight, or
-    groups too wide for two per wave."""
+    """Runs: packed groups that fill less than 60% of their lane segment, in a
+    job of more than 4096 waves, as many groups per wave as fit 64 vectors at
+    any alignment (at most 8) when they fill at least half of the wave,
+    one-wave workgroups; forced through the tuning shape's kernel field for
+    any packed group that fits twice; refused for groups that are not packed,
+    a shared weight, or groups too wide for two per wave."""
     kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
     def plan(rows, G, dtype, groups=16, flags=RI, shape=None):
         width = G * groups
         return _plan_ex(g, flags, shape, rows=rows, width=width, group_size=G, y_row_stride=width,
                         gate_row_stride=width, out_row_stride=width, dtype=dtype, **kw)
     # (G, dtype, groups per run, taken by default): 64 * 16 - 16 + piece bytes over the
-    # group's bytes, at most 8; by default with 2- or 4-byte pieces filling >= 1/2 of a wave
-    for G, dtype, gpw, default in ((100, F16, 5, False), (99, BF16, 5, True),
-                                   (50, BF16, 8, True), (127, BF16, 3, True), (250, F16, 2, True),
-                                   (25, F32, 8, True), (99, F32, 2, True), (13, F16, 8, False)):
+    # group's bytes, at most 8; by default for segments under 60% full (the group's
+    # bytes / 16 over the segment's lanes) and runs filling >= 1/2 of a wave
+    for G, dtype, gpw, default in ((100, F16, 5, False), (99, BF16, 5, False),
+                                   (50, BF16, 8, False), (127, BF16, 3, True), (250, F16, 2, False),
+                                   (25, F32, 8, False), (99, F32, 2, False), (13, F16, 8, False),
+                                   (68, F16, 7, True), (76, F16, 6, True), (84, F16, 6, False),
+                                   (140, BF16, 3, True), (150, BF16, 3, True), (180, BF16, 2, False)):
         st, p = plan(8000, G, dtype, shape=(0, 0, 0, 0, KERNEL_RUN))
         assert st == OK and (p["kernel_name"], p["groups_per_run"], p["block_threads"],
                              p["workgroups"]) == ("run", gpw, 64, 8000 * (-(-16 // gpw))), (G, dtype, p)
@@ -576,9 +598,9 @@ def test_runs_of_packed_groups_plan(g):
     assert plan(2000, 100, F16, shape=(32, 1, 0, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 100, F16, shape=(64, 1, 2, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 100, F16, shape=(0, 0, 0, 0, 7))[0] == INVALID
-    # 8 groups per row: a run of 5 and one of 3
-    st, p = plan(50000, 99, BF16, groups=8)
-    assert (p["kernel_name"], p["groups_per_run"], p["workgroups"]) == ("run", 5, 50000 * 2)
+    # 8 groups per row: a run of 3, 3 and 2
+    st, p = plan(50000, 127, BF16, groups=8)
+    assert (p["kernel_name"], p["groups_per_run"], p["workgroups"]) == ("run", 3, 50000 * 3)
 
 
 def test_rows_split_over_launches(g):

@@ -367,6 +367,63 @@ def test_runs_of_packed_groups(g, orc, G, dtype):
             assert_parity(got[view], ref[view], dtype, f"run G={G} groups={groups} flags={flags}")
 
 
+MERGE_CASES = [(100, F16), (99, BF16), (50, BF16), (25, F32), (13, F16), (180, BF16), (250, F16)]
+
+
+@pytest.mark.parametrize("G,dtype", MERGE_CASES, ids=[f"G{G}-{DT_IDS[d]}" for G, d in MERGE_CASES])
+def test_packed_boundaries_merged_in_waves(g, orc, G, dtype):
+    """Packed groups on lane segments with one vector per lane, where a vector
+    shared by two groups of one wave is stored whole by the left group's lane
+    (with the right group's pieces taken from the next segment) and pieces
+    are stored only at a wave's edges or a row's end: rows of 1, 2, 3 and 5
+    times the fewest groups that make a 16-byte aligned row and about 48
+    groups, so that in row-major order a wave's segments straddle row ends;
+    both operators; every tile order and WAVE workgroup size gives the same
+    bits; out rows padded and guarded."""
+    esz = 4 if dtype == F32 else 2
+    gb = G * esz
+    pb = 16
+    while gb % pb:
+        pb //= 2
+    lanes = 1
+    while lanes < (16 - pb + gb + 15) // 16:
+        lanes *= 2
+    period = 16 // math.gcd(gb, 16)
+    for groups in sorted({period, 2 * period, 3 * period, 5 * period, 48 // period * period}):
+        width = G * groups
+        rows, pad = 9, 16 // esz
+        so = width + pad
+        guard = 64
+        y, gt, w = random_case(rows, width, dtype, seed=G * 7 + groups + dtype)
+        canary = {F32: np.float32(-1234.5), F16: np.uint16(0x7BFF), BF16: np.uint16(0x4B4B)}[dtype]
+        ob = np.full(guard + (rows - 1) * so + width + guard, canary, dtype=S.storage_dtype(dtype))
+        view = np.zeros(ob.shape, dtype=bool)
+        for r in range(rows):
+            view[guard + r * so: guard + r * so + width] = True
+        yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+        for flags in ((FLAG_RI,) if dtype != F32 else (0,)) + (FLAG_NBG,):
+            outs = []
+            for order in (0, 32, 64, 32 | 256, 64 | 256):
+                od = dev_buf(ob, dtype)
+                say(f"case merged G={G} dtype={DT_IDS[dtype]} groups={groups} flags={flags} "
+                    f"order={order}")
+                st = run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
+                             dtype, 0, shape=(lanes, 1), flags=flags | order)
+                assert st == g.SUCCESS, g.ggrms_status_string(st)
+                torch.cuda.synchronize()
+                outs.append(host_bits(od, dtype))
+            got = outs[0]
+            assert all(np.array_equal(o.view(np.uint8), got.view(np.uint8)) for o in outs[1:])
+            assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
+                "stores touched elements outside the view"
+            ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                              gate_row_stride=width, out_row_stride=so, eps=1e-5, dtype=dtype,
+                              round_intermediate=flags & FLAG_RI,
+                              norm_before_gate=bool(flags & FLAG_NBG), out=ob.copy(),
+                              out_offset=guard)
+            assert_parity(got[view], ref[view], dtype, f"merged G={G} groups={groups} flags={flags}")
+
+
 def test_runs_in_place_and_by_default(g, orc):
     """The strided fused layout normalised in place over the gate with runs
     (a boundary vector of two runs is read by both waves while each writes
@@ -385,15 +442,16 @@ def test_runs_in_place_and_by_default(g, orc):
                    F16, 1, shape=(0, 0, 0, 0, g.KERNEL_RUN)) == g.SUCCESS
     torch.cuda.synchronize()
     assert_parity(host_bits(fd, F16), ref, F16, "run in place")
-    # 1500 rows x 48 groups of 99 bf16 (2-byte pieces) x 16 lanes = 18000 waves: runs by default
-    rows, G = 1500, 99
+    # 1500 rows x 48 groups of 127 bf16 (2-byte pieces, 15.9 vectors on 32 lanes) = 36000
+    # waves: runs of 3 by default
+    rows, G = 1500, 127
     width = 48 * G
     y, gt, w = random_case(rows, width, BF16, seed=94)
     yd, gd, wd = dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(w).cuda()
     od = torch.empty_like(yd)
     p = _plan_of(g, yd, gd, wd, od, rows, width, G, width, width, width, BF16, FLAG_RI)
-    assert (p["kernel_name"], p["groups_per_run"]) == ("run", 5), p
-    say("case run by default, 1500 x 4752 bf16")
+    assert (p["kernel_name"], p["groups_per_run"]) == ("run", 3), p
+    say("case run by default, 1500 x 6096 bf16")
     assert run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, 1e-5, BF16, 1) == g.SUCCESS
     torch.cuda.synchronize()
     ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
