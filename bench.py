@@ -442,6 +442,9 @@ SHAPES = [
     ("fp16 G256 heads, shared head weight", 1, 256, 8192, 4),
     ("f32 G128 heads, shared head weight", 0, 128, 4096, 4),
     ("fp16 G100 packed groups, per-column weight", 1, 100, 4800, 1),
+    ("bf16 G99 packed groups (2-byte pieces)", 2, 99, 4752, 1),
+    ("bf16 G127 packed groups (runs of 3)", 2, 127, 6096, 1),
+    ("fp16 G250 packed groups (4-byte pieces)", 1, 250, 12000, 1),
     # the same groups in rows padded by 4 elements: rows not 16-byte aligned,
     # so the whole group falls back to 8-byte vectors
     ("fp16 G100 in padded rows (8-byte vectors)", 1, 100, 4800, 1, 4804),
@@ -527,6 +530,13 @@ EVIDENCE = {
     "prefill_unstaged": (2, 8192, 7680, 960, 1, (128, 1, 1)),
     "g9_banded": (2, 7281, 8640, 960, 1 | 64, None),
     "g9_rows": (2, 7281, 8640, 960, 1 | 32, None),
+    # WAVE shapes whose row is not a whole number of 8 workgroups: 60 groups of
+    # 128 (15 one-wave workgroups of 4 groups per row) and 12 groups of 640
+    # (64 x 2, one wave per group), banded and row-major
+    "g128x60_banded": (2, 8192, 7680, 128, 1 | 64, None),
+    "g128x60_rows": (2, 8192, 7680, 128, 1 | 32, None),
+    "g640x12_banded": (2, 8192, 7680, 640, 1 | 64, None),
+    "g640x12_rows": (2, 8192, 7680, 640, 1 | 32, None),
     "g5120": (2, 12288, 5120, 5120, 1, None),
     "g8192": (2, 7680, 8192, 8192, 1, None),
     # 100-wide fp16 groups (200 bytes: packed 16-byte vectors), one vector per
@@ -541,6 +551,10 @@ EVIDENCE = {
     "packed_g100_four": (1, 13107, 4800, 100, 1 | 256, None),
     "packed_g100_rows": (1, 13107, 4800, 100, 1 | 32, None),
     "packed_g100_rows_four": (1, 13107, 4800, 100, 1 | 32 | 256, None),
+    # 127-wide bf16 groups (15.9 vectors on 32 lanes): runs of 3 (the default)
+    # and the 32-lane segments
+    "packed_g127_run": (2, 10320, 6096, 127, 1, None),
+    "packed_g127_wave": (2, 10320, 6096, 127, 1, (32, 1)),
 }
 
 
