@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed launches for this long after the warmup steps")
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "workloads", "unfused",
-                                       "shapes", "evidence"], default=None)
+                                       "shapes", "evidence", "producer"], default=None)
     ap.add_argument("--part", choices=list(UNFUSED_PARTS), default=None,
                     help="with --only unfused: time one chain only")
     ap.add_argument("--variant", choices=sorted(EVIDENCE), default="prefill_staged",
@@ -734,6 +734,75 @@ def _unfused_decode(torch, S, settle_s):
     return res
 
 
+def bench_producer(torch, steps, settle_s=0.2):
+    """The epilogue called from a producer kernel (libggrms_example.so: y =
+    bf16(x @ wt^T) on the matrix cores, normalised in the same kernel) against
+    the same producer storing y followed by the library's launch on it, on the
+    8192 x 7680 bf16 prefill shape with groups of 960 and K = 64; three rotating
+    sets of gate, y and out.  Random bf16 x and wt: timing only (the example's
+    results are checked by tests/test_gpu_example_producer.py)."""
+    import ctypes
+
+    import gated_group_rmsnorm_amd as g
+
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(g.__file__)),
+                                   "libggrms_example.so"))
+    ex = lib.ggrms_example_gemm_norm
+    ex.restype = ctypes.c_int
+    ex.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                                   ctypes.c_int, ctypes.c_void_p]
+    rows, width, G, K = 8192, 7680, 960, 64
+    bf = torch.bfloat16
+    x = (torch.randn(rows * K, device="cuda") * 0.1).to(bf)
+    wt = (torch.randn(width * K, device="cuda") * 0.1).to(bf)
+    w = torch.rand(width, device="cuda") + 0.5
+    sets = [[torch.randn(rows * width, device="cuda").to(bf), torch.empty(rows * width, dtype=bf, device="cuda"),
+             torch.empty(rows * width, dtype=bf, device="cuda")] for _ in range(3)]
+    sp = torch.cuda.current_stream().cuda_stream
+
+    def fused(i):
+        gt, _, o = sets[i % 3]
+        if ex(x.data_ptr(), wt.data_ptr(), gt.data_ptr(), w.data_ptr(), o.data_ptr(), rows, width,
+              K, G, 1e-5, 1, 0, sp) != 0:
+            raise RuntimeError("example producer refused its arguments")
+
+    def produce(i):
+        gt, y, _ = sets[i % 3]
+        if ex(x.data_ptr(), wt.data_ptr(), gt.data_ptr(), w.data_ptr(), y.data_ptr(), rows, width,
+              K, G, 1e-5, 1, 1, sp) != 0:
+            raise RuntimeError("example producer refused its arguments")
+
+    def norm(i):
+        gt, y, o = sets[i % 3]
+        st = g.ggrms_forward_ex(y.data_ptr(), gt.data_ptr(), w.data_ptr(), o.data_ptr(), rows,
+                                width, G, width, width, width, 1e-5, 2, 1, sp)
+        if st != 0:
+            raise RuntimeError(g.ggrms_status_string(st))
+
+    def unfused(i):
+        produce(i)
+        norm(i)
+
+    res = {}
+    for name, fn in (("fused_us", fused), ("producer_alone_us", produce), ("norm_alone_us", norm),
+                     ("producer_then_norm_us", unfused)):
+        settle(torch, fn, settle_s)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / steps
+    e = rows * width
+    res["fused_bytes"] = 2 * (rows * K + width * K) + 2 * e * 2 + 4 * width
+    res["unfused_bytes"] = 2 * (rows * K + width * K) + 2 * e + 3 * 2 * e + 4 * width
+    res["launches_fused"], res["launches_unfused"] = 1, 2
+    return res
+
+
 def cpu_baseline(S, seconds):
     """The oracle, single-threaded, on leading rows of the prefill workload,
     repeated for about `seconds` of CPU time."""
@@ -888,6 +957,12 @@ def main():
     if args.only == "evidence":
         bench_evidence(torch, g, args.variant, min(args.steps, 200), args.warmup,
                        args.settle_ms / 1e3)
+        return
+    if args.only == "producer":
+        res = bench_producer(torch, args.steps, args.settle_ms / 1e3)
+        log("producer example: " + json.dumps({k: (round(v, 2) if isinstance(v, float) else v)
+                                               for k, v in res.items()}))
+        print(json.dumps({"producer_fusion_example": res}), flush=True)
         return
     if args.only == "shapes":
         print(json.dumps(bench_shapes(torch, g, min(args.steps, 300))), flush=True)

@@ -9,8 +9,8 @@
 // product on the matrix cores (v_mfma_f32_16x16x16_bf16), whose output tile
 // arrives in the accumulator layout of the MFMA instruction, like any
 // contraction's.  What carries over to a real producer is the hand-off:
-//   * a workgroup owns whole (row, group) units -- here 16 rows x one group
-//     of G columns, the four waves each computing G/4 of the columns;
+//   * a workgroup owns whole (row, group) units -- here row tiles of 16 rows
+//     x one group of G columns, G/64 waves each computing 64 of the columns;
 //   * the accumulators are rounded to the storage type (the values the
 //     standalone op would have read back) and re-laid through LDS from the
 //     MFMA layout (lane = column, 4 consecutive rows per lane) to the
@@ -39,8 +39,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerTile = 16;   // one MFMA tile of rows
-constexpr int kWaves = 4;
+constexpr int kTilesPerGroup = 8;  // row tiles one workgroup takes in turn
 constexpr int kMaxGroup = 1024;    // 128 vectors of bf16: two per lane
+constexpr int kMaxK = 64;          // the B fragments of every k step stay in registers
 constexpr int kLdsPad = 8;         // bf16 elements of padding per LDS row
 
 struct ExArgs {
@@ -54,99 +55,109 @@ struct ExArgs {
     uint32_t produce_only;  // 1: store y itself (the unfused producer)
 };
 
-// One workgroup: rows r0 .. r0+15, group g.  Wave w computes columns
-// g*G + w*G/4 .. + G/4 - 1 as NT = G/64 MFMA tiles of 16 columns.
-template <int NT, bool RI>
-__global__ __launch_bounds__(kWaves * 64) void example_gemm_norm_kernel(ExArgs a) {
+// One workgroup: group g, row tiles blockIdx.x * 8 .. + 7 (16 rows each, the
+// last workgroup's may be fewer), G / 64 waves.  Wave w computes columns
+// g*G + 64w .. 64w + 63 as four MFMA tiles of 16 columns; its B fragments (wt
+// for those columns, every k step) are loaded once and reused for every row
+// tile, and so are the lanes' weights of the epilogue.
+template <bool RI>
+__global__ __launch_bounds__(kMaxGroup) void example_gemm_norm_kernel(ExArgs a) {
+    constexpr int NT = 4;  // column tiles per wave
     // rows of 2064 bytes: every 16-byte vector of a row stays 16-byte aligned
     __shared__ __attribute__((aligned(16))) u16 ys[kRowsPerTile][kMaxGroup + kLdsPad];
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t r0 = blockIdx.x * kRowsPerTile;
+    const uint32_t waves = blockDim.x >> 6;  // G / 64
     const uint32_t g = blockIdx.y;
     const uint32_t G = a.G;
-    const uint32_t ccol0 = wave * (G / kWaves);  // first column of this wave in the group
+    const uint32_t ccol0 = wave * 64;  // first column of this wave in the group
+    const uint32_t ntiles = a.rows / kRowsPerTile;
+    const uint32_t t0 = blockIdx.x * kTilesPerGroup;
+    const uint32_t t1 = t0 + kTilesPerGroup < ntiles ? t0 + kTilesPerGroup : ntiles;
+    const uint32_t nks = a.K / 16;  // k steps, <= kMaxK / 16
 
-    // --- producer: y tile in MFMA accumulators.  v_mfma_f32_16x16x16_bf16:
-    // lane l supplies A[l % 16][4*(l/16) + i] and B[4*(l/16) + i][l % 16]
-    // (i = 0..3) and holds D[4*(l/16) + i][l % 16].
-    f32x4v acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    // v_mfma_f32_16x16x16_bf16: lane l supplies A[l % 16][4*(l/16) + i] and
+    // B[4*(l/16) + i][l % 16] (i = 0..3) and holds D[4*(l/16) + i][l % 16].
     const uint32_t m = lane & 15, kq = (lane >> 4) * 4;
-    for (uint32_t k0 = 0; k0 < a.K; k0 += 16) {
-        const s16x4 av = *reinterpret_cast<const s16x4*>(a.x + (size_t)(r0 + m) * a.K + k0 + kq);
+    s16x4 bv[NT][kMaxK / 16];
+#pragma unroll
+    for (int ks = 0; ks < kMaxK / 16; ++ks) {
+        if ((uint32_t)ks >= nks) break;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint32_t col = g * G + ccol0 + t * 16 + m;
-            const s16x4 bv = *reinterpret_cast<const s16x4*>(a.wt + (size_t)col * a.K + k0 + kq);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc[t], 0, 0, 0);
+            bv[t][ks] = *reinterpret_cast<const s16x4*>(a.wt + (size_t)col * a.K + ks * 16 + kq);
         }
     }
-    // round to bf16 and re-lay: D[4*(l/16) + i][l % 16] -> ys[row][column in group]
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ys[kq + i][ccol0 + t * 16 + m] = Cvt<TBF16>::pack_half(acc[t][i]);
-    }
-    __syncthreads();
-
-    // --- epilogue: wave w takes rows w, w+4, w+8, w+12 of the tile; a row's
-    // group is nvec = G/8 vectors, lane l holds vectors l and l + 64.
+    // the epilogue's slots: a row's group is nvec = G/8 vectors, lane l holds
+    // vectors l and l + 64 (the same columns for every row)
     const uint32_t nvec = G / 8;
     constexpr int K = 2;
-    for (uint32_t rr = wave; rr < kRowsPerTile; rr += kWaves) {
-        const uint32_t n = r0 + rr;
-        u32x4 yr[K], gr[K];
-        float wr[K][8];
-        uint32_t ci[K];
+    uint32_t ci[K];
+    float wr[K][8];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const uint32_t idx = lane + k * 64;
-            ci[k] = idx < nvec ? idx : nvec - 1;  // past the end: a copy of the last vector
-            yr[k] = *reinterpret_cast<const u32x4*>(&ys[rr][ci[k] * 8]);
-            const size_t v = ((size_t)n * a.width + (size_t)g * G) / 8 + ci[k];
-            gr[k] = a.gate[v];
-            const f32x4* wp = reinterpret_cast<const f32x4*>(a.w + (size_t)g * G + ci[k] * 8);
-            const f32x4 w0 = wp[0], w1 = wp[1];
-            wr[k][0] = w0.x; wr[k][1] = w0.y; wr[k][2] = w0.z; wr[k][3] = w0.w;
-            wr[k][4] = w1.x; wr[k][5] = w1.y; wr[k][6] = w1.z; wr[k][7] = w1.w;
+    for (int k = 0; k < K; ++k) {
+        const uint32_t idx = lane + k * 64;
+        ci[k] = idx < nvec ? idx : nvec - 1;  // past the end: a copy of the last vector
+        const f32x4* wp = reinterpret_cast<const f32x4*>(a.w + (size_t)g * G + ci[k] * 8);
+        const f32x4 w0 = wp[0], w1 = wp[1];
+        wr[k][0] = w0.x; wr[k][1] = w0.y; wr[k][2] = w0.z; wr[k][3] = w0.w;
+        wr[k][4] = w1.x; wr[k][5] = w1.y; wr[k][6] = w1.z; wr[k][7] = w1.w;
+    }
+    auto live = [&](int k) { return lane + k * 64 < nvec; };
+    auto owned = [](int, int) { return true; };
+
+    for (uint32_t tile = t0; tile < t1; ++tile) {
+        const uint32_t r0 = tile * kRowsPerTile;
+        // --- producer: the tile of y in MFMA accumulators
+        f32x4v acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < kMaxK / 16; ++ks) {
+            if ((uint32_t)ks >= nks) break;
+            const s16x4 av = *reinterpret_cast<const s16x4*>(a.x + (size_t)(r0 + m) * a.K + ks * 16 + kq);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv[t][ks], acc[t], 0, 0, 0);
         }
-        u32x4* ov = reinterpret_cast<u32x4*>(a.out) + ((size_t)n * a.width + (size_t)g * G) / 8;
-        if (a.produce_only) {  // the unfused producer: y goes to memory
+        __syncthreads();  // the previous tile's epilogue has read ys
+        // round to bf16 and re-lay: D[4*(l/16) + i][l % 16] -> ys[row][column in group]
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ys[kq + i][ccol0 + t * 16 + m] = Cvt<TBF16>::pack_half(acc[t][i]);
+        }
+        __syncthreads();
+
+        // --- epilogue: wave w takes rows w, w + waves, ... of the tile
+        for (uint32_t rr = wave; rr < kRowsPerTile; rr += waves) {
+            const uint32_t n = r0 + rr;
+            u32x4 yr[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) yr[k] = *reinterpret_cast<const u32x4*>(&ys[rr][ci[k] * 8]);
+            u32x4* ov = reinterpret_cast<u32x4*>(a.out) + ((size_t)n * a.width + (size_t)g * G) / 8;
+            if (a.produce_only) {  // the unfused producer: y goes to memory
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    if (live(k)) __builtin_nontemporal_store(yr[k], ov + ci[k]);
+                continue;
+            }
+            u32x4 gr[K];
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                if (lane + k * 64 < nvec) ov[ci[k]] = yr[k];
-            continue;
-        }
-        auto live = [&](int k) { return lane + k * 64 < nvec; };
-        auto owned = [](int, int) { return true; };
-        epi::LaneUnit<TBF16, 16, K, false> L;
-        const float part = epi::gate_and_square<TBF16, 16, 16, K, false>(yr, gr, L, live, owned);
-        const float m2 = segment_sum<64>(part);
-        const float nf = norm_factor(m2, a.Ginv, a.eps);
-        u32x4 res[K];
-        epi::finish<RI>(L, nf, wr, res);
+                gr[k] = __builtin_nontemporal_load(
+                    a.gate + ((size_t)n * a.width + (size_t)g * G) / 8 + ci[k]);
+            epi::LaneUnit<TBF16, 16, K, false> L;
+            const float part = epi::gate_and_square<TBF16, 16, 16, K, false>(yr, gr, L, live, owned);
+            const float m2 = segment_sum<64>(part);
+            const float nf = norm_factor(m2, a.Ginv, a.eps);
+            u32x4 res[K];
+            epi::finish<RI>(L, nf, wr, res);
 #pragma unroll
-        for (int k = 0; k < K; ++k)
-            if (live(k)) ov[ci[k]] = res[k];
-    }
-}
-
-template <int NT> const void* pick_nt(bool ri) {
-    return ri ? reinterpret_cast<const void*>(&example_gemm_norm_kernel<NT, true>)
-              : reinterpret_cast<const void*>(&example_gemm_norm_kernel<NT, false>);
-}
-
-const void* pick(uint32_t G, bool ri) {
-    switch (G / 64) {
-    case 1: return pick_nt<1>(ri);
-    case 2: return pick_nt<2>(ri);
-    case 4: return pick_nt<4>(ri);
-    case 8: return pick_nt<8>(ri);
-    case 15: return pick_nt<15>(ri);
-    case 16: return pick_nt<16>(ri);
-    default: return nullptr;
+            for (int k = 0; k < K; ++k)
+                if (live(k)) __builtin_nontemporal_store(res[k], ov + ci[k]);
+        }
     }
 }
 
@@ -157,7 +168,7 @@ const void* pick(uint32_t G, bool ri) {
 // G, into out [rows, width]; all bf16 except the weight, contiguous rows,
 // 16-byte aligned pointers.  produce_only = 1 stores y itself into out (the
 // producer of an unfused pipeline).  rows % 16 == 0, K % 16 == 0, width % G
-// == 0, G in {64, 128, 256, 512, 960, 1024}.  Returns 0 on success, 1 for
+// == 0, K <= 64, G a multiple of 64 up to 1024.  Returns 0 on success, 1 for
 // arguments outside these limits, 2 if the launch fails.  Enqueued on
 // `stream` (a hipStream_t; NULL is the default stream).
 extern "C" __attribute__((visibility("default"))) int ggrms_example_gemm_norm(
@@ -166,13 +177,15 @@ extern "C" __attribute__((visibility("default"))) int ggrms_example_gemm_norm(
     int round_intermediate, int produce_only, void* stream) {
     if (!x || !wt || !gate || !norm_weight || !out) return 1;
     if (rows <= 0 || width <= 0 || K <= 0 || group_size <= 0) return 1;
-    if (rows % kRowsPerTile || K % 16 || width % group_size || group_size > kMaxGroup) return 1;
-    if (rows > (int64_t)65535 * kRowsPerTile || width / group_size > 65535 || K > 4096) return 1;
+    if (rows % kRowsPerTile || K % 16 || K > kMaxK || width % group_size || group_size > kMaxGroup)
+        return 1;
+    if (rows > ((int64_t)1 << 30) || width / group_size > 65535) return 1;
     if (((uintptr_t)x | (uintptr_t)wt | (uintptr_t)gate | (uintptr_t)norm_weight |
          (uintptr_t)out) % 16)
         return 1;
-    const void* fn = pick((uint32_t)group_size, round_intermediate != 0);
-    if (!fn || group_size % 64) return 1;
+    if (group_size % 64) return 1;
+    const void* fn = round_intermediate ? reinterpret_cast<const void*>(&example_gemm_norm_kernel<true>)
+                                        : reinterpret_cast<const void*>(&example_gemm_norm_kernel<false>);
     ExArgs a;
     a.x = static_cast<const u16*>(x);
     a.wt = static_cast<const u16*>(wt);
@@ -187,8 +200,11 @@ extern "C" __attribute__((visibility("default"))) int ggrms_example_gemm_norm(
     a.eps = eps;
     a.produce_only = produce_only != 0;
     void* args[] = {&a};
-    const dim3 grid((uint32_t)(rows / kRowsPerTile), (uint32_t)(width / group_size));
-    if (hipLaunchKernel(fn, grid, dim3(kWaves * 64), args, 0, static_cast<hipStream_t>(stream)) !=
+    const int64_t tiles = rows / kRowsPerTile;
+    const dim3 grid((uint32_t)((tiles + kTilesPerGroup - 1) / kTilesPerGroup),
+                    (uint32_t)(width / group_size));
+    if (hipLaunchKernel(fn, grid, dim3((uint32_t)group_size), args, 0,
+                        static_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return 2;
     return 0;

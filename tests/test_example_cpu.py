@@ -34,9 +34,9 @@ def test_producer_rejects_what_it_does_not_handle(ex):
     assert call(rows=24) == 1             # rows not a multiple of 16
     assert call(rows=0) == 1
     assert call(K=40) == 1                # K not a multiple of 16
+    assert call(K=80) == 1                # K above 64
     assert call(G=96, width=960) == 1     # group not a multiple of 64
     assert call(G=2048, width=2048) == 1  # wider than 1024
-    assert call(G=192, width=1920) == 1   # no kernel for 3 column tiles per wave
     assert call(width=1000) == 1          # width not a multiple of the group
     assert ex(None, p, p, p, p, 32, 1024, 32, 512, 1e-5, 1, 0, None) == 1
     q = ctypes.c_void_p((1 << 20) + 8)    # 8-byte aligned only

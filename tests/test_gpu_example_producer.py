@@ -64,7 +64,8 @@ CASES = [  # rows, width, K, group size, round_intermediate
     (48, 2048, 64, 1024, 1),
     (128, 7680, 64, 960, 1),
     (32, 1920, 48, 960, 0),
-    (16, 512, 256, 128, 1),
+    (16, 512, 64, 128, 1),
+    (272, 1024, 64, 256, 1),  # 17 row tiles: a workgroup of 8, 8 and 1
 ]
 
 
