@@ -395,20 +395,50 @@ OTHER_WORKLOADS = [
 ]
 
 
+def native_job_us(setup, kind, launches, bursts=20):
+    """Per-launch time of `launches` back-to-back launches issued from C
+    (libggrms_bench.so's ggrms_bench_job_native) over the setup's rotating
+    buffer sets, median of `bursts` runs: kind 0 the fused kernel (the
+    library's own launch choice), kind 1 the plain two-read-one-write kernel
+    over the same bytes (y and gate read, out written).  Issued from C, a small
+    job's figure is the GPU's: from Python each launch costs about 4 us of
+    interpreter and ctypes time, as long as the strided workload's kernel."""
+    aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
+    f = aux.ggrms_bench_job_native
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    n = len(setup.sets)
+    arr = lambda vals: (ctypes.c_void_p * n)(*vals)
+    ys = arr([y.data_ptr() for y, _, _ in setup.sets])
+    gs = arr([gt.data_ptr() for _, gt, _ in setup.sets])
+    os_ = arr([o.data_ptr() for _, _, o in setup.sets])
+    w, lay = setup.w, setup.lay
+    us = ctypes.c_double()
+    rc = f(ys, gs, setup.weight.data_ptr(), os_, n, w.rows, w.width, w.group_size,
+           lay["y_row_stride"], lay["gate_row_stride"], w.width, w.eps, w.dtype, setup.flags, None,
+           kind, launches, bursts, ctypes.byref(us))
+    if rc != 0:
+        raise RuntimeError(f"ggrms_bench_job_native kind {kind}: status {rc}")
+    return us.value
+
+
 def bench_workloads(torch, g, S, steps):
     """Kernel time of the other configured workloads and of the norm-first
-    operator (reported beside the headline)."""
+    operator (reported beside the headline): back-to-back launches issued
+    from C, next to the plain stream kernel over the same buffers."""
     out = {}
     for label, name, flags in OTHER_WORKLOADS:
         w = S.WORKLOADS[name]
         sets = max(2, math.ceil(3 * 256e6 / w.algorithmic_bytes()))
         setup = Setup(torch, S, w, min(sets, 64), flags=flags)
-        _, ev_ms = time_kernel(torch, g, setup, steps, 5, settle_s=0.1)
-        avg = ev_ms / steps
+        avg = native_job_us(setup, 0, steps) * 1e-3  # ms
+        ceil_us = native_job_us(setup, 1, steps)
         nbytes = w.algorithmic_bytes(per_group_weight=bool(setup.flags & 4))
         del setup
         torch.cuda.empty_cache()
-        ceil_us = stream_ceiling(torch, w.rows * w.width * w.esize, steps)
         out[label] = {"kernel_us_avg": avg * 1e3,
                       "gbs": nbytes / (avg * 1e-3) / 1e9,
                       "frac_of_peak": nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS,

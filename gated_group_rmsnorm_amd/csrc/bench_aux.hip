@@ -9,6 +9,9 @@
 //     empty kernel, so the per-launch figure carries no interpreter overhead;
 //   * a plain 16-byte vector copy of known size: the calibration that turns
 //     the FETCH_SIZE / WRITE_SIZE counters into HBM bytes;
+//   * whole jobs (the fused kernel or the plain stream kernel) launched back
+//     to back from C, for jobs small enough that a launch from the
+//     interpreter takes longer than the kernel;
 //   * the simplest kernel that moves a workload's bytes: two streams read and
 //     one written, 16-byte non-temporal accesses, one vector per lane,
 //     one-wave workgroups (the fastest plain form in a sweep of vectors per
@@ -202,5 +205,59 @@ extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const
     }
     *dev_us = median_of(dev);
     *host_us = median_of(host);
+    return 0;
+}
+
+// Back-to-back launches of one job issued from C, so that a small job's
+// per-launch figure is the GPU's and not the interpreter's: `launches`
+// launches in a row, cycling over `sets` buffer sets (set i: y[i], gate[i],
+// out[i]; one weight), timed between two events on a stream of its own, after
+// about 100 ms of the same untimed; `bursts` such runs, median per launch.
+// kind 0: ggrms_forward_tuned with `flags` / `shape` over [rows, width] views
+// with the given row strides; kind 1: the plain two-read-one-write kernel
+// (ggrms_bench_stream3) over nbytes = rows * width * element bytes per stream,
+// y[i] and gate[i] read, out[i] written.  Returns 0, a ggrms status, or -1 for
+// a HIP error.
+extern "C" int ggrms_bench_job_native(const void* const* y, const void* const* gate,
+                                      const float* w, void* const* out, int sets, int64_t rows,
+                                      int64_t width, int64_t group_size, int64_t y_row_stride,
+                                      int64_t gate_row_stride, int64_t out_row_stride, float eps,
+                                      int dtype, uint32_t flags, const ggrms_shape_t* shape,
+                                      int kind, int launches, int bursts, double* dev_us) {
+    if (sets <= 0 || launches <= 0 || bursts <= 0 || (kind != 0 && kind != 1))
+        return GGRMS_ERROR_INVALID_VALUE;
+    const int64_t esize = dtype == GGRMS_F32 ? 4 : 2;
+    const int64_t nbytes = rows * width * esize;
+    BurstRes r;
+    if (hipStreamCreate(&r.s) != hipSuccess || hipEventCreate(&r.e0) != hipSuccess ||
+        hipEventCreate(&r.e1) != hipSuccess)
+        return -1;
+    auto one = [&](int i) -> int {
+        const int k = i % sets;
+        if (kind == 1) return ggrms_bench_stream3(y[k], gate[k], out[k], nbytes, r.s) ? -1 : 0;
+        return ggrms_forward_tuned(y[k], gate[k], w, out[k], rows, width, group_size, y_row_stride,
+                                   gate_row_stride, out_row_stride, eps, (ggrms_dtype_t)dtype,
+                                   flags, shape, r.s);
+    };
+    const auto t0 = std::chrono::steady_clock::now();
+    int i = 0;
+    while (std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() < 0.1) {
+        for (int j = 0; j < 64; ++j)
+            if (const int rc = one(i++)) return rc;
+        if (hipStreamSynchronize(r.s) != hipSuccess) return -1;
+    }
+    std::vector<double> dev;
+    for (int b = 0; b < bursts; ++b) {
+        if (hipStreamSynchronize(r.s) != hipSuccess || hipEventRecord(r.e0, r.s) != hipSuccess)
+            return -1;
+        for (int j = 0; j < launches; ++j)
+            if (const int rc = one(i++)) return rc;
+        float ms = 0.0f;
+        if (hipEventRecord(r.e1, r.s) != hipSuccess || hipEventSynchronize(r.e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess)
+            return -1;
+        dev.push_back(ms * 1e3 / launches);
+    }
+    *dev_us = median_of(dev);
     return 0;
 }
