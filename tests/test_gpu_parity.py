@@ -460,10 +460,13 @@ def test_runs_in_place_and_by_default(g, orc):
     assert_parity(host_bits(od, BF16), ref, BF16, "run by default")
 
 
-def test_packed_in_place_over_the_gate(g, orc):
+@pytest.mark.parametrize("shape", [None, (16, 1)], ids=["default", "16x1-merged"])
+def test_packed_in_place_over_the_gate(g, orc, shape):
     """The strided layout (y and gate column slices of one fused fp16 buffer,
     200-byte groups) normalised in place over the gate: a vector on a group
-    boundary is read by two units while each writes its own pieces."""
+    boundary is read by two units while each writes its own pieces (the
+    library's 8 x 2 shape for this small job), or while the left unit's lane
+    writes it whole for both (16 x 1, boundaries merged inside a wave)."""
     rows, width, G, fused = 64, 4800, 100, 9856
     buf = S.tensor(91, S.TID_Y, rows * fused, F16, ("normal", 1.0))
     w = S.tensor(91, S.TID_W, width, F32, ("uniform", 0.5, 1.5))
@@ -475,9 +478,9 @@ def test_packed_in_place_over_the_gate(g, orc):
     p = _plan_of(g, fd, fd[width:], wd, fd[width:], rows, width, G, fused, fused, fused, F16,
                  FLAG_RI)
     assert (p["vector_bytes"], p["piece_bytes"]) == (16, 8)
-    say("case packed in place over the gate")
+    say(f"case packed in place over the gate, shape {shape}")
     assert run_gpu(g, fd, fd[width:], wd, fd[width:], rows, width, G, fused, fused, fused, 1e-5,
-                   F16, 1) == g.SUCCESS
+                   F16, 1, shape=shape) == g.SUCCESS
     torch.cuda.synchronize()
     assert_parity(host_bits(fd, F16), ref, F16, "packed in place")
 
