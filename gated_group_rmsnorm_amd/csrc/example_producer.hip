@@ -59,12 +59,17 @@ struct ExArgs {
 // last workgroup's may be fewer), G / 64 waves.  Wave w computes columns
 // g*G + 64w .. 64w + 63 as four MFMA tiles of 16 columns; its B fragments (wt
 // for those columns, every k step) are loaded once and reused for every row
-// tile, and so are the lanes' weights of the epilogue.
+// tile, and so are the lanes' weights of the epilogue.  The workgroup's rows
+// of x are staged in LDS up front: a global load issued after a store is
+// counted behind it (memory counters retire in order), so loading x tile by
+// tile would make every tile wait for the previous tile's stores.
 template <bool RI>
 __global__ __launch_bounds__(kMaxGroup) void example_gemm_norm_kernel(ExArgs a) {
     constexpr int NT = 4;  // column tiles per wave
-    // rows of 2064 bytes: every 16-byte vector of a row stays 16-byte aligned
-    __shared__ __attribute__((aligned(16))) u16 ys[kRowsPerTile][kMaxGroup + kLdsPad];
+    // two re-lay buffers, used by alternate tiles: one barrier per tile; rows
+    // of 2064 bytes keep every 16-byte vector of a row 16-byte aligned
+    __shared__ __attribute__((aligned(16))) u16 ys[2][kRowsPerTile][kMaxGroup + kLdsPad];
+    __shared__ __attribute__((aligned(16))) u16 xs[kTilesPerGroup * kRowsPerTile][kMaxK];
     const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t waves = blockDim.x >> 6;  // G / 64
     const uint32_t g = blockIdx.y;
@@ -74,6 +79,17 @@ __global__ __launch_bounds__(kMaxGroup) void example_gemm_norm_kernel(ExArgs a) 
     const uint32_t t0 = blockIdx.x * kTilesPerGroup;
     const uint32_t t1 = t0 + kTilesPerGroup < ntiles ? t0 + kTilesPerGroup : ntiles;
     const uint32_t nks = a.K / 16;  // k steps, <= kMaxK / 16
+
+    // x rows of the workgroup's tiles into LDS, 16 bytes at a time
+    {
+        const uint32_t r0 = t0 * kRowsPerTile, nr = (t1 - t0) * kRowsPerTile;
+        const uint32_t per_row = a.K / 8;  // 16-byte pieces per row
+        for (uint32_t i = threadIdx.x; i < nr * per_row; i += blockDim.x) {
+            const uint32_t r = i / per_row, c = i - r * per_row;
+            *reinterpret_cast<u32x4*>(&xs[r][c * 8]) =
+                *reinterpret_cast<const u32x4*>(a.x + (size_t)(r0 + r) * a.K + c * 8);
+        }
+    }
 
     // v_mfma_f32_16x16x16_bf16: lane l supplies A[l % 16][4*(l/16) + i] and
     // B[4*(l/16) + i][l % 16] (i = 0..3) and holds D[4*(l/16) + i][l % 16].
@@ -105,9 +121,20 @@ __global__ __launch_bounds__(kMaxGroup) void example_gemm_norm_kernel(ExArgs a) 
     }
     auto live = [&](int k) { return lane + k * 64 < nvec; };
     auto owned = [](int, int) { return true; };
+    auto gate_at = [&](uint32_t n, int k) {
+        return a.gate + ((size_t)n * a.width + (size_t)g * G) / 8 + ci[k];
+    };
+    __syncthreads();  // xs is complete
 
     for (uint32_t tile = t0; tile < t1; ++tile) {
         const uint32_t r0 = tile * kRowsPerTile;
+        // the gate of this wave's first row of the tile, requested before the
+        // multiply and the re-lay so that its latency overlaps them
+        u32x4 gp[K] = {};
+        if (!a.produce_only) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) gp[k] = __builtin_nontemporal_load(gate_at(r0 + wave, k));
+        }
         // --- producer: the tile of y in MFMA accumulators
         f32x4v acc[NT];
 #pragma unroll
@@ -115,27 +142,30 @@ __global__ __launch_bounds__(kMaxGroup) void example_gemm_norm_kernel(ExArgs a) 
 #pragma unroll
         for (int ks = 0; ks < kMaxK / 16; ++ks) {
             if ((uint32_t)ks >= nks) break;
-            const s16x4 av = *reinterpret_cast<const s16x4*>(a.x + (size_t)(r0 + m) * a.K + ks * 16 + kq);
+            const s16x4 av = *reinterpret_cast<const s16x4*>(&xs[(tile - t0) * kRowsPerTile + m][ks * 16 + kq]);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv[t][ks], acc[t], 0, 0, 0);
         }
-        __syncthreads();  // the previous tile's epilogue has read ys
-        // round to bf16 and re-lay: D[4*(l/16) + i][l % 16] -> ys[row][column in group]
+        // round to bf16 and re-lay: D[4*(l/16) + i][l % 16] -> yb[row][column in
+        // group].  The buffer was last read two tiles ago, before every wave
+        // passed the previous tile's barrier.
+        u16 (*yb)[kMaxGroup + kLdsPad] = ys[(tile - t0) & 1];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                ys[kq + i][ccol0 + t * 16 + m] = Cvt<TBF16>::pack_half(acc[t][i]);
+                yb[kq + i][ccol0 + t * 16 + m] = Cvt<TBF16>::pack_half(acc[t][i]);
         }
         __syncthreads();
 
         // --- epilogue: wave w takes rows w, w + waves, ... of the tile
         for (uint32_t rr = wave; rr < kRowsPerTile; rr += waves) {
+            const bool first = rr == wave;
             const uint32_t n = r0 + rr;
             u32x4 yr[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) yr[k] = *reinterpret_cast<const u32x4*>(&ys[rr][ci[k] * 8]);
+            for (int k = 0; k < K; ++k) yr[k] = *reinterpret_cast<const u32x4*>(&yb[rr][ci[k] * 8]);
             u32x4* ov = reinterpret_cast<u32x4*>(a.out) + ((size_t)n * a.width + (size_t)g * G) / 8;
             if (a.produce_only) {  // the unfused producer: y goes to memory
 #pragma unroll
@@ -146,8 +176,7 @@ __global__ __launch_bounds__(kMaxGroup) void example_gemm_norm_kernel(ExArgs a) 
             u32x4 gr[K];
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                gr[k] = __builtin_nontemporal_load(
-                    a.gate + ((size_t)n * a.width + (size_t)g * G) / 8 + ci[k]);
+                gr[k] = first ? gp[k] : __builtin_nontemporal_load(gate_at(n, k));
             epi::LaneUnit<TBF16, 16, K, false> L;
             const float part = epi::gate_and_square<TBF16, 16, 16, K, false>(yr, gr, L, live, owned);
             const float m2 = segment_sum<64>(part);
