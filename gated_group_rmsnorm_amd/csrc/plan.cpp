@@ -300,9 +300,10 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         // (indexing, the sum across lanes, the normaliser, the boundary pieces)
         // over twice the elements -- such a job is one round of loads followed
         // by its arithmetic, which no other wave's loads hide (the strided 256 x
-        // 4800 fp16 job: 4.19 against 4.66 us).  In larger jobs each load
+        // 4800 fp16 job: 4.02 against 4.65 us).  In larger jobs each load
         // instruction would then touch twice the cache lines, half of each
-        // (377 MB of 100-wide fp16 groups: 104.9 against 70.4 us), so they keep
+        // (377 MB of 100-wide fp16 groups: 104.6 against 63.1 us for one
+        // vector per lane with boundaries merged inside the wave), so they keep
         // one vector per lane.
         const bool small_job = rows * plan->groups * lanes <= kSmallJobWaves * 64;
         if (packed && kernel == GGRMS_KERNEL_WAVE && small_job && lanes >= 16 && lanes <= 64 &&
@@ -358,8 +359,9 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     // WAVE workgroups: one wave for 16-byte vectors, packed groups included,
     // whose slot is freed the moment it retires (128-wide groups: 0.83
     // against 0.79 of HBM peak with four; 377 MB of 100-wide packed fp16
-    // groups: 66.9 against 70.4 us; the strided 256 x 4800 fp16 job: equal
-    // with 16 x 1, 4.19 against 4.61 us with 8 x 2); four waves for narrower
+    // groups: 62.7 against 67.7 us; the strided 256 x 4800 fp16 job: equal
+    // with 16 x 1, 4.19 against 4.61 us with 8 x 2 before the boundary
+    // merge); four waves for narrower
     // vectors, which need 2-4x the workgroups for the same bytes (4-byte
     // vectors: 96 against 107 us with one).
     bool four = kernel == GGRMS_KERNEL_WAVE && vb < 16;
