@@ -10,13 +10,13 @@
 // arrives in the accumulator layout of the MFMA instruction, like any
 // contraction's.  What carries over to a real producer is the hand-off:
 //   * a workgroup owns whole (row, group) units -- here row tiles of 16 rows
-//     x one group of G columns, G/64 waves each computing 64 of the columns;
+//     x one group of G columns, its 16 waves sharing the group's columns;
 //   * the accumulators are rounded to the storage type (the values the
 //     standalone op would have read back) and re-laid through LDS from the
 //     MFMA layout (lane = column, 4 consecutive rows per lane) to the
 //     epilogue's (lane = 16 bytes of one row);
-//   * each wave then takes rows of the tile and runs the epilogue's steps on
-//     them: gate_and_square on y from LDS and the gate from global memory,
+//   * each wave then takes one row of the tile and runs the epilogue's steps
+//     on it: gate_and_square on y from LDS and the gate from global memory,
 //     segment_sum over the unit's 64 lanes, norm_factor, finish, one
 //     16-byte store per slot.  gate, the weight and out are the only HBM
 //     traffic of the norm; a separate norm kernel would also write and then
@@ -39,10 +39,18 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerTile = 16;   // one MFMA tile of rows
-constexpr int kTilesPerGroup = 8;  // row tiles one workgroup takes in turn
+constexpr int kWaves = 16;         // one wave per row of a tile in the epilogue
+constexpr int kMaxTilesPerWg = 16;  // row tiles one workgroup takes in turn, at most
+constexpr int kCus = 256;           // compute units of the part
 constexpr int kMaxGroup = 1024;    // 128 vectors of bf16: two per lane
 constexpr int kMaxK = 64;          // the B fragments of every k step stay in registers
-constexpr int kLdsPad = 8;         // bf16 elements of padding per LDS row
+constexpr int kLdsPad = 8;         // bf16 elements of padding per re-lay row
+constexpr int kXPad = 8;           // and per staged row of x: 144-byte rows, so that
+                                   // 16 lanes reading 16 rows hit 64 distinct banks
+constexpr int NT = kMaxGroup / 16 / kWaves;  // column tiles per wave, at most
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt at their maxima
+constexpr int kBufferFormat = 0x00020000;  // word 3 of a raw gfx9 buffer resource (32-bit data)
+constexpr int kNonTemporal = 2;            // cache policy operand of a buffer access: nt
 
 struct ExArgs {
     const u16* x;      // [rows, K] bf16
@@ -51,143 +59,231 @@ struct ExArgs {
     const float* w;    // [width] f32
     void* out;         // [rows, width] bf16
     uint32_t rows, width, K, G;
+    uint32_t tiles_per_wg;  // 1 .. kMaxTilesPerWg
     float Ginv, eps;
-    uint32_t produce_only;  // 1: store y itself (the unfused producer)
 };
 
-// One workgroup: group g, row tiles blockIdx.x * 8 .. + 7 (16 rows each, the
-// last workgroup's may be fewer), G / 64 waves.  Wave w computes columns
-// g*G + 64w .. 64w + 63 as four MFMA tiles of 16 columns; its B fragments (wt
-// for those columns, every k step) are loaded once and reused for every row
-// tile, and so are the lanes' weights of the epilogue.  The workgroup's rows
-// of x are staged in LDS up front: a global load issued after a store is
-// counted behind it (memory counters retire in order), so loading x tile by
-// tile would make every tile wait for the previous tile's stores.
-template <bool RI>
-__global__ __launch_bounds__(kMaxGroup) void example_gemm_norm_kernel(ExArgs a) {
-    constexpr int NT = 4;  // column tiles per wave
-    // two re-lay buffers, used by alternate tiles: one barrier per tile; rows
-    // of 2064 bytes keep every 16-byte vector of a row 16-byte aligned
+constexpr int kDppSwapPairs = 0xB1;  // DPP quad_perm [1, 0, 3, 2]: swap lanes 2i and 2i+1
+
+// The 4 bf16 (8 bytes) of half h of a 16-byte vector, as an MFMA operand.
+__device__ inline s16x4 frag(const u32x4& v, int h) {
+    typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+    const u32x2v p = h ? u32x2v{v[2], v[3]} : u32x2v{v[0], v[1]};
+    return __builtin_bit_cast(s16x4, p);
+}
+
+// One workgroup of 16 waves: group g, row tiles blockIdx.x * tiles_per_wg
+// onwards (16 rows each; the last workgroup's may be fewer).  The multiply:
+// the group's G / 16 column tiles of 16 go round the waves (wave w: tiles w,
+// w + 16, ...), each an MFMA tile whose B fragments (wt for those columns)
+// are loaded once and reused for every row tile.  The epilogue: wave w takes
+// row w of each tile, so every wave has one unit per tile.  What keeps the
+// memory latency off the loop:
+//   * the workgroup's rows of x and the group's weights are staged in LDS
+//     up front;
+//   * the gate of a wave's row two tiles ahead is requested before its
+//     stores of this tile: a global load issued after a store waits for
+//     that store's completion as well (memory counters retire in order), so
+//     a load issued after the stores would expose the store and the load
+//     latency once per tile, and two tiles of gate in flight per wave keep
+//     the bytes in flight up while every tile passes a barrier;
+//   * the re-lay buffer alternates between two halves, so each tile needs
+//     one barrier.
+// PRODUCE: store y itself (the producer of an unfused pipeline).
+template <bool RI, bool PRODUCE>
+__global__ __launch_bounds__(kWaves * 64) void example_gemm_norm_kernel(ExArgs a) {
+    // rows of 2064 bytes keep every 16-byte vector of a row 16-byte aligned
     __shared__ __attribute__((aligned(16))) u16 ys[2][kRowsPerTile][kMaxGroup + kLdsPad];
-    __shared__ __attribute__((aligned(16))) u16 xs[kTilesPerGroup * kRowsPerTile][kMaxK];
-    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t waves = blockDim.x >> 6;  // G / 64
+    __shared__ __attribute__((aligned(16))) u16 xs[kMaxTilesPerWg * kRowsPerTile][kMaxK + kXPad];
+    __shared__ __attribute__((aligned(16))) float ws[kMaxGroup];
+    const uint32_t lane = threadIdx.x & 63;
+    // the wave's index, in a scalar register (the same on every lane)
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t g = blockIdx.y;
     const uint32_t G = a.G;
-    const uint32_t ccol0 = wave * 64;  // first column of this wave in the group
+    const uint32_t nct = G / 16;  // column tiles of the group
     const uint32_t ntiles = a.rows / kRowsPerTile;
-    const uint32_t t0 = blockIdx.x * kTilesPerGroup;
-    const uint32_t t1 = t0 + kTilesPerGroup < ntiles ? t0 + kTilesPerGroup : ntiles;
-    const uint32_t nks = a.K / 16;  // k steps, <= kMaxK / 16
+    const uint32_t t0 = blockIdx.x * a.tiles_per_wg;
+    const uint32_t t1 = t0 + a.tiles_per_wg < ntiles ? t0 + a.tiles_per_wg : ntiles;
 
-    // x rows of the workgroup's tiles into LDS, 16 bytes at a time
-    {
-        const uint32_t r0 = t0 * kRowsPerTile, nr = (t1 - t0) * kRowsPerTile;
-        const uint32_t per_row = a.K / 8;  // 16-byte pieces per row
-        for (uint32_t i = threadIdx.x; i < nr * per_row; i += blockDim.x) {
-            const uint32_t r = i / per_row, c = i - r * per_row;
-            *reinterpret_cast<u32x4*>(&xs[r][c * 8]) =
-                *reinterpret_cast<const u32x4*>(a.x + (size_t)(r0 + r) * a.K + c * 8);
-        }
-    }
-
-    // v_mfma_f32_16x16x16_bf16: lane l supplies A[l % 16][4*(l/16) + i] and
-    // B[4*(l/16) + i][l % 16] (i = 0..3) and holds D[4*(l/16) + i][l % 16].
-    const uint32_t m = lane & 15, kq = (lane >> 4) * 4;
-    s16x4 bv[NT][kMaxK / 16];
-#pragma unroll
-    for (int ks = 0; ks < kMaxK / 16; ++ks) {
-        if ((uint32_t)ks >= nks) break;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const uint32_t col = g * G + ccol0 + t * 16 + m;
-            bv[t][ks] = *reinterpret_cast<const s16x4*>(a.wt + (size_t)col * a.K + ks * 16 + kq);
-        }
-    }
     // the epilogue's slots: a row's group is nvec = G/8 vectors, lane l holds
     // vectors l and l + 64 (the same columns for every row)
     const uint32_t nvec = G / 8;
     constexpr int K = 2;
     uint32_t ci[K];
-    float wr[K][8];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const uint32_t idx = lane + k * 64;
         ci[k] = idx < nvec ? idx : nvec - 1;  // past the end: a copy of the last vector
-        const f32x4* wp = reinterpret_cast<const f32x4*>(a.w + (size_t)g * G + ci[k] * 8);
-        const f32x4 w0 = wp[0], w1 = wp[1];
-        wr[k][0] = w0.x; wr[k][1] = w0.y; wr[k][2] = w0.z; wr[k][3] = w0.w;
-        wr[k][4] = w1.x; wr[k][5] = w1.y; wr[k][6] = w1.z; wr[k][7] = w1.w;
     }
     auto live = [&](int k) { return lane + k * 64 < nvec; };
     auto owned = [](int, int) { return true; };
     auto gate_at = [&](uint32_t n, int k) {
         return a.gate + ((size_t)n * a.width + (size_t)g * G) / 8 + ci[k];
     };
-    __syncthreads();  // xs is complete
-
-    for (uint32_t tile = t0; tile < t1; ++tile) {
-        const uint32_t r0 = tile * kRowsPerTile;
-        // the gate of this wave's first row of the tile, requested before the
-        // multiply and the re-lay so that its latency overlaps them
-        u32x4 gp[K] = {};
-        if (!a.produce_only) {
+    // the gate of this wave's row of the first two tiles
+    u32x4 gA[K] = {}, gB[K] = {};
+    if constexpr (!PRODUCE) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) gp[k] = __builtin_nontemporal_load(gate_at(r0 + wave, k));
+        for (int k = 0; k < K; ++k)
+            gA[k] = __builtin_nontemporal_load(gate_at(t0 * kRowsPerTile + wave, k));
+        const uint32_t second = t0 + 1 < t1 ? t0 + 1 : t0;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            gB[k] = __builtin_nontemporal_load(gate_at(second * kRowsPerTile + wave, k));
+    }
+
+    // x rows of the workgroup's tiles into LDS, 16 bytes at a time, zero
+    // past column K: every tile then takes all kMaxK / 16 k steps, the
+    // missing ones adding products of zeros (exactly +0, which leaves every
+    // sum as it is)
+    {
+        const uint32_t r0 = t0 * kRowsPerTile, nr = (t1 - t0) * kRowsPerTile;
+        const uint32_t per_row = a.K / 8;  // 16-byte pieces of x per row
+        for (uint32_t i = threadIdx.x; i < nr * (kMaxK / 8); i += blockDim.x) {
+            const uint32_t r = i / (kMaxK / 8), c = i % (kMaxK / 8);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (c < per_row) v = *reinterpret_cast<const u32x4*>(a.x + (size_t)(r0 + r) * a.K + c * 8);
+            *reinterpret_cast<u32x4*>(&xs[r][c * 8]) = v;
         }
-        // --- producer: the tile of y in MFMA accumulators
+    }
+    // the group's weights into LDS
+    if constexpr (!PRODUCE) {
+        for (uint32_t i = threadIdx.x; i < G / 4; i += blockDim.x)
+            *reinterpret_cast<f32x4*>(&ws[4 * i]) =
+                *reinterpret_cast<const f32x4*>(a.w + (size_t)g * G + 4 * i);
+    }
+
+    // v_mfma_f32_16x16x16_bf16: lane l supplies A[l % 16][4*(l/16) + i] and
+    // B[4*(l/16) + i][l % 16] (i = 0..3) and holds D[4*(l/16) + i][l % 16].
+    // The k index is free to permute (the same way for A and B): at k step s,
+    // lane l's A[.][4*(l/16) + i] is x[.][16*(l/16) + 4s + i], so over the
+    // kMaxK / 16 steps a lane reads 32 contiguous bytes of one row of x, and
+    // of one row of wt for B -- two 16-byte accesses instead of four 8-byte
+    // ones.
+    const uint32_t m = lane & 15, q = lane >> 4;
+    // B for the wave's column tiles (zero past K and past the group's end)
+    u32x4 bw[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const bool ok = wave + t * kWaves < nct && 16 * q < a.K;
+        const uint32_t col = g * G + (wave + t * kWaves) * 16 + m;
+        const u32x4* p = reinterpret_cast<const u32x4*>(a.wt + (size_t)col * a.K + 16 * q);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            bw[t][h] = u32x4{0u, 0u, 0u, 0u};
+            if (ok) bw[t][h] = p[h];
+        }
+    }
+    // Every load so far has landed before the loop starts (s_waitcnt vmcnt(0);
+    // the other counters untouched), so that inside the loop the compiler's
+    // waits track only the loop's own gate loads and stores and never hold a
+    // tile's gate behind that tile's stores.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();  // xs and ws are complete
+
+    // One row tile, re-laid through buffer yb, with the gate of this wave's
+    // row in gcur; gcur then receives the gate of the tile two ahead.
+    auto tile_pass = [&](uint32_t tile, u16 (*yb)[kMaxGroup + kLdsPad], u32x4 (&gcur)[K])
+        __attribute__((always_inline)) {
+        // --- producer: the tile of y in MFMA accumulators, rounded to bf16
+        // and re-laid: D[4*(l/16) + i][l % 16] -> yb[row][column in group].
+        // The buffer was last read two tiles ago, before every wave passed
+        // the previous tile's barrier.  Each k step's A fragment feeds the
+        // NT independent accumulator chains.
         f32x4v acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+        u32x4 xa[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            xa[h] = *reinterpret_cast<const u32x4*>(&xs[(tile - t0) * kRowsPerTile + m][16 * q + 8 * h]);
 #pragma unroll
         for (int ks = 0; ks < kMaxK / 16; ++ks) {
-            if ((uint32_t)ks >= nks) break;
-            const s16x4 av = *reinterpret_cast<const s16x4*>(&xs[(tile - t0) * kRowsPerTile + m][ks * 16 + kq]);
+            const s16x4 av = frag(xa[ks / 2], ks % 2);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv[t][ks], acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, frag(bw[t][ks / 2], ks % 2),
+                                                                  acc[t], 0, 0, 0);
         }
-        // round to bf16 and re-lay: D[4*(l/16) + i][l % 16] -> yb[row][column in
-        // group].  The buffer was last read two tiles ago, before every wave
-        // passed the previous tile's barrier.
-        u16 (*yb)[kMaxGroup + kLdsPad] = ys[(tile - t0) & 1];
+        // Lanes m and m + 1 (m even) hold columns c and c + 1 of rows 4q..4q+3;
+        // after one swap of a bf16 pair between them, the even lane writes
+        // rows 4q and 4q+1 and the odd lane rows 4q+2 and 4q+3, each as
+        // 32-bit words of both columns (64 distinct banks per write).
+        const bool odd = m & 1;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                yb[kq + i][ccol0 + t * 16 + m] = Cvt<TBF16>::pack_half(acc[t][i]);
+            if (wave + t * kWaves >= nct) break;
+            const uint32_t c = (wave + t * kWaves) * 16 + (m & ~1u);
+            const float r01[2] = {acc[t][0], acc[t][1]}, r23[2] = {acc[t][2], acc[t][3]};
+            const u32 p0 = Cvt<TBF16>::pack_word(r01);  // rows 4q, 4q+1 (low half: 4q)
+            const u32 p1 = Cvt<TBF16>::pack_word(r23);  // rows 4q+2, 4q+3
+            const u32 recv = (u32)__builtin_amdgcn_update_dpp(0, (int)(odd ? p0 : p1), kDppSwapPairs,
+                                                              0xF, 0xF, false);
+            const u32 mine = odd ? p1 : p0;
+            // even lane: (own, partner's) element of each row; odd: (partner's, own)
+            const u32 lo = odd ? recv : mine, hi = odd ? mine : recv;
+            const uint32_t row = 4 * q + (odd ? 2 : 0);
+            *reinterpret_cast<u32*>(&yb[row][c]) = (lo & 0xFFFFu) | (hi << 16);
+            *reinterpret_cast<u32*>(&yb[row + 1][c]) = (lo >> 16) | (hi & 0xFFFF0000u);
         }
         __syncthreads();
 
-        // --- epilogue: wave w takes rows w, w + waves, ... of the tile
-        for (uint32_t rr = wave; rr < kRowsPerTile; rr += waves) {
-            const bool first = rr == wave;
-            const uint32_t n = r0 + rr;
-            u32x4 yr[K];
+        // --- epilogue: wave w takes row w of the tile
+        const uint32_t n = tile * kRowsPerTile + wave;
+        u32x4 yr[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) yr[k] = *reinterpret_cast<const u32x4*>(&yb[rr][ci[k] * 8]);
-            u32x4* ov = reinterpret_cast<u32x4*>(a.out) + ((size_t)n * a.width + (size_t)g * G) / 8;
-            if (a.produce_only) {  // the unfused producer: y goes to memory
+        for (int k = 0; k < K; ++k) yr[k] = *reinterpret_cast<const u32x4*>(&yb[wave][ci[k] * 8]);
+        // out's unit (row n, group g) as a buffer of nvec vectors: a lane
+        // past the group's end gets an offset outside it, and the buffer
+        // store drops it -- no predicated store, so no path through the loop
+        // skips one and the compiler's count of the memory operations after
+        // the gate loads stays exact
+        const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<u16*>(a.out) + (size_t)n * a.width + (size_t)g * G, 0, (int)(nvec * 16),
+            kBufferFormat);
+        int off[K];
 #pragma unroll
-                for (int k = 0; k < K; ++k)
-                    if (live(k)) __builtin_nontemporal_store(yr[k], ov + ci[k]);
-                continue;
-            }
-            u32x4 gr[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k)
-                gr[k] = first ? gp[k] : __builtin_nontemporal_load(gate_at(n, k));
-            epi::LaneUnit<TBF16, 16, K, false> L;
-            const float part = epi::gate_and_square<TBF16, 16, 16, K, false>(yr, gr, L, live, owned);
-            const float m2 = segment_sum<64>(part);
-            const float nf = norm_factor(m2, a.Ginv, a.eps);
-            u32x4 res[K];
-            epi::finish<RI>(L, nf, wr, res);
+        for (int k = 0; k < K; ++k) off[k] = live(k) ? (int)(ci[k] * 16) : (int)(nvec * 16);
+        if constexpr (PRODUCE) {  // the unfused producer: y goes to memory
 #pragma unroll
             for (int k = 0; k < K; ++k)
-                if (live(k)) __builtin_nontemporal_store(res[k], ov + ci[k]);
+                __builtin_amdgcn_raw_buffer_store_b128(yr[k], ob, off[k], 0, kNonTemporal);
+            return;
         }
+        epi::LaneUnit<TBF16, 16, K, false> L;
+        const float part = epi::gate_and_square<TBF16, 16, 16, K, false>(yr, gcur, L, live, owned);
+        const float m2 = segment_sum<64>(part);
+        const float nf = norm_factor(m2, a.Ginv, a.eps);
+        float wr[K][8];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(&ws[ci[k] * 8]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(&ws[ci[k] * 8 + 4]);
+            wr[k][0] = w0.x; wr[k][1] = w0.y; wr[k][2] = w0.z; wr[k][3] = w0.w;
+            wr[k][4] = w1.x; wr[k][5] = w1.y; wr[k][6] = w1.z; wr[k][7] = w1.w;
+        }
+        u32x4 res[K];
+        epi::finish<RI>(L, nf, wr, res);
+        // the gate two tiles ahead, before this tile's stores (past the last
+        // tile: the last tile's row again, so that no path skips the loads)
+        const uint32_t ahead = tile + 2 < t1 ? tile + 2 : t1 - 1;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            gcur[k] = __builtin_nontemporal_load(gate_at(ahead * kRowsPerTile + wave, k));
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(res[k], ob, off[k], 0, kNonTemporal);
+    };
+
+    // tiles in pairs, so that the two gate buffers and the two re-lay
+    // buffers keep fixed registers and addresses
+    uint32_t tile = t0;
+    for (; tile + 1 < t1; tile += 2) {
+        tile_pass(tile, ys[0], gA);
+        tile_pass(tile + 1, ys[1], gB);
     }
+    if (tile < t1) tile_pass(tile, ys[0], gA);
 }
 
 }  // namespace
@@ -213,8 +309,13 @@ extern "C" __attribute__((visibility("default"))) int ggrms_example_gemm_norm(
          (uintptr_t)out) % 16)
         return 1;
     if (group_size % 64) return 1;
-    const void* fn = round_intermediate ? reinterpret_cast<const void*>(&example_gemm_norm_kernel<true>)
-                                        : reinterpret_cast<const void*>(&example_gemm_norm_kernel<false>);
+    const void* fn =
+        produce_only ? (round_intermediate
+                            ? reinterpret_cast<const void*>(&example_gemm_norm_kernel<true, true>)
+                            : reinterpret_cast<const void*>(&example_gemm_norm_kernel<false, true>))
+                     : (round_intermediate
+                            ? reinterpret_cast<const void*>(&example_gemm_norm_kernel<true, false>)
+                            : reinterpret_cast<const void*>(&example_gemm_norm_kernel<false, false>));
     ExArgs a;
     a.x = static_cast<const u16*>(x);
     a.wt = static_cast<const u16*>(wt);
@@ -227,12 +328,17 @@ extern "C" __attribute__((visibility("default"))) int ggrms_example_gemm_norm(
     a.G = (uint32_t)group_size;
     a.Ginv = (float)(1.0 / (double)group_size);
     a.eps = eps;
-    a.produce_only = produce_only != 0;
     void* args[] = {&a};
-    const int64_t tiles = rows / kRowsPerTile;
-    const dim3 grid((uint32_t)((tiles + kTilesPerGroup - 1) / kTilesPerGroup),
-                    (uint32_t)(width / group_size));
-    if (hipLaunchKernel(fn, grid, dim3((uint32_t)group_size), args, 0,
+    // Row tiles per workgroup: enough that the grid is about one workgroup
+    // per compute unit (each workgroup is a whole CU's worth of waves and
+    // loads its B fragments and x once), at most kMaxTilesPerWg.
+    const int64_t tiles = rows / kRowsPerTile, groups = width / group_size;
+    int64_t tpw = (tiles * groups + kCus - 1) / kCus;
+    if (tpw < 1) tpw = 1;
+    if (tpw > kMaxTilesPerWg) tpw = kMaxTilesPerWg;
+    a.tiles_per_wg = (uint32_t)tpw;
+    const dim3 grid((uint32_t)((tiles + tpw - 1) / tpw), (uint32_t)groups);
+    if (hipLaunchKernel(fn, grid, dim3(kWaves * 64), args, 0,
                         static_cast<hipStream_t>(stream)) !=
         hipSuccess)
         return 2;

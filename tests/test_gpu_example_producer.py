@@ -65,7 +65,15 @@ CASES = [  # rows, width, K, group size, round_intermediate
     (128, 7680, 64, 960, 1),
     (32, 1920, 48, 960, 0),
     (16, 512, 64, 128, 1),
-    (272, 1024, 64, 256, 1),  # 17 row tiles: a workgroup of 8, 8 and 1
+    (272, 1024, 64, 256, 1),
+    # enough tiles that each workgroup takes several in turn (tiles x groups
+    # / 256 compute units, at most 16): pairs, an odd count with a single last
+    # tile, K below the MFMA's 64, and 16 tiles of 64-wide groups (4 column
+    # tiles for 16 waves, 8 live lanes per row)
+    (2048, 4096, 64, 512, 1),     # 4 tiles per workgroup
+    (4112, 2048, 64, 1024, 0),    # 3 per workgroup, the last one 2
+    (8192, 1920, 32, 960, 1),     # 4, K = 32
+    (4096, 1024, 16, 64, 1),      # 16, K = 16
 ]
 
 
