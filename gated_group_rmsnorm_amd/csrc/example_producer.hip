@@ -6,7 +6,7 @@
 // (the norm_before_gate=False branch of its combined scan), and the standalone
 // op is a port of it.  The pages do not define the scan, so the producer here
 // is a stand-in with a plain definition: y = bf16(x @ wt^T), a bf16 matrix
-// product on the matrix cores (v_mfma_f32_16x16x16_bf16), whose output tile
+// product on the matrix cores (v_mfma_f32_16x16x32_bf16), whose output tile
 // arrives in the accumulator layout of the MFMA instruction, like any
 // contraction's.  What carries over to a real producer is the hand-off:
 //   * a workgroup owns whole (row, group) units -- here row tiles of 16 rows
@@ -35,7 +35,7 @@ namespace {
 
 using namespace ggrms;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerTile = 16;   // one MFMA tile of rows
@@ -43,7 +43,7 @@ constexpr int kWaves = 16;         // one wave per row of a tile in the epilogue
 constexpr int kMaxTilesPerWg = 16;  // row tiles one workgroup takes in turn, at most
 constexpr int kCus = 256;           // compute units of the part
 constexpr int kMaxGroup = 1024;    // 128 vectors of bf16: two per lane
-constexpr int kMaxK = 64;          // the B fragments of every k step stay in registers
+constexpr int kMaxK = 64;          // two MFMA k steps of 32; their B fragments stay in registers
 constexpr int kLdsPad = 8;         // bf16 elements of padding per re-lay row
 constexpr int kXPad = 8;           // and per staged row of x: 144-byte rows, so that
                                    // 16 lanes reading 16 rows hit 64 distinct banks
@@ -64,13 +64,6 @@ struct ExArgs {
 };
 
 constexpr int kDppSwapPairs = 0xB1;  // DPP quad_perm [1, 0, 3, 2]: swap lanes 2i and 2i+1
-
-// The 4 bf16 (8 bytes) of half h of a 16-byte vector, as an MFMA operand.
-__device__ inline s16x4 frag(const u32x4& v, int h) {
-    typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
-    const u32x2v p = h ? u32x2v{v[2], v[3]} : u32x2v{v[0], v[1]};
-    return __builtin_bit_cast(s16x4, p);
-}
 
 // One workgroup of 16 waves: group g, row tiles blockIdx.x * tiles_per_wg
 // onwards (16 rows each; the last workgroup's may be fewer).  The multiply:
@@ -118,23 +111,29 @@ __global__ __launch_bounds__(kWaves * 64) void example_gemm_norm_kernel(ExArgs a
     }
     auto live = [&](int k) { return lane + k * 64 < nvec; };
     auto owned = [](int, int) { return true; };
-    auto gate_at = [&](uint32_t n, int k) {
-        return a.gate + ((size_t)n * a.width + (size_t)g * G) / 8 + ci[k];
+    // The gate of the unit (row n, group g) into g_out, by buffer loads: with
+    // want false, or for a lane past the group's end, the offset lies outside
+    // the unit and the load returns zeros without touching memory -- every
+    // path issues the same loads (the compiler's counts stay exact) and no
+    // byte is fetched twice.
+    auto load_gate = [&](uint32_t n, bool want, u32x4 (&g_out)[K]) {
+        const __amdgpu_buffer_rsrc_t gb = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<u32x4*>(a.gate) + ((size_t)n * a.width + (size_t)g * G) / 8, 0,
+            (int)(nvec * 16), kBufferFormat);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            g_out[k] = __builtin_amdgcn_raw_buffer_load_b128(
+                gb, want && live(k) ? (int)(ci[k] * 16) : (int)(nvec * 16), 0, kNonTemporal);
     };
     // the gate of this wave's row of the first two tiles
     u32x4 gA[K] = {}, gB[K] = {};
     if constexpr (!PRODUCE) {
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            gA[k] = __builtin_nontemporal_load(gate_at(t0 * kRowsPerTile + wave, k));
-        const uint32_t second = t0 + 1 < t1 ? t0 + 1 : t0;
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            gB[k] = __builtin_nontemporal_load(gate_at(second * kRowsPerTile + wave, k));
+        load_gate(t0 * kRowsPerTile + wave, true, gA);
+        load_gate((t0 + 1 < t1 ? t0 + 1 : t0) * kRowsPerTile + wave, t0 + 1 < t1, gB);
     }
 
     // x rows of the workgroup's tiles into LDS, 16 bytes at a time, zero
-    // past column K: every tile then takes all kMaxK / 16 k steps, the
+    // past column K: every tile then takes both k steps of 32, the
     // missing ones adding products of zeros (exactly +0, which leaves every
     // sum as it is)
     {
@@ -154,13 +153,13 @@ __global__ __launch_bounds__(kWaves * 64) void example_gemm_norm_kernel(ExArgs a
                 *reinterpret_cast<const f32x4*>(a.w + (size_t)g * G + 4 * i);
     }
 
-    // v_mfma_f32_16x16x16_bf16: lane l supplies A[l % 16][4*(l/16) + i] and
-    // B[4*(l/16) + i][l % 16] (i = 0..3) and holds D[4*(l/16) + i][l % 16].
-    // The k index is free to permute (the same way for A and B): at k step s,
-    // lane l's A[.][4*(l/16) + i] is x[.][16*(l/16) + 4s + i], so over the
-    // kMaxK / 16 steps a lane reads 32 contiguous bytes of one row of x, and
-    // of one row of wt for B -- two 16-byte accesses instead of four 8-byte
-    // ones.
+    // v_mfma_f32_16x16x32_bf16: lane l supplies 8 consecutive k of row
+    // l % 16 of A and of column l % 16 of B, the k chunk chosen by l / 16, and
+    // holds D[4*(l/16) + i][l % 16] (i = 0..3).  The k index is free to
+    // permute (the same way for A and B): at k step h (0, 1), lane l's chunk
+    // is x[.][16*(l/16) + 8h .. + 7], so over the two steps a lane reads 32
+    // contiguous bytes of one row of x, and of one row of wt for B, as two
+    // 16-byte accesses.
     const uint32_t m = lane & 15, q = lane >> 4;
     // B for the wave's column tiles (zero past K and past the group's end)
     u32x4 bw[NT][2];
@@ -199,12 +198,12 @@ __global__ __launch_bounds__(kWaves * 64) void example_gemm_norm_kernel(ExArgs a
         for (int h = 0; h < 2; ++h)
             xa[h] = *reinterpret_cast<const u32x4*>(&xs[(tile - t0) * kRowsPerTile + m][16 * q + 8 * h]);
 #pragma unroll
-        for (int ks = 0; ks < kMaxK / 16; ++ks) {
-            const s16x4 av = frag(xa[ks / 2], ks % 2);
+        for (int h = 0; h < 2; ++h) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, xa[h]);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, frag(bw[t][ks / 2], ks % 2),
-                                                                  acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    av, __builtin_bit_cast(bf16x8, bw[t][h]), acc[t], 0, 0, 0);
         }
         // Lanes m and m + 1 (m even) hold columns c and c + 1 of rows 4q..4q+3;
         // after one swap of a bf16 pair between them, the even lane writes
@@ -266,11 +265,9 @@ __global__ __launch_bounds__(kWaves * 64) void example_gemm_norm_kernel(ExArgs a
         u32x4 res[K];
         epi::finish<RI>(L, nf, wr, res);
         // the gate two tiles ahead, before this tile's stores (past the last
-        // tile: the last tile's row again, so that no path skips the loads)
-        const uint32_t ahead = tile + 2 < t1 ? tile + 2 : t1 - 1;
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-            gcur[k] = __builtin_nontemporal_load(gate_at(ahead * kRowsPerTile + wave, k));
+        // tile: loads that fetch nothing, so that no path skips them)
+        const bool more = tile + 2 < t1;
+        load_gate(more ? n + 2 * kRowsPerTile : n, more, gcur);
 #pragma unroll
         for (int k = 0; k < K; ++k)
             __builtin_amdgcn_raw_buffer_store_b128(res[k], ob, off[k], 0, kNonTemporal);
