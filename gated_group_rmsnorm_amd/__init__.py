@@ -34,6 +34,7 @@ __all__ = [
     "FLAG_WEIGHT_PER_GROUP", "FLAG_CACHE_STREAM", "FLAG_CACHE_KEEP", "FLAG_ORDER_ROWS",
     "FLAG_ORDER_BANDED", "FLAG_WAVE_ONE", "FLAG_WAVE_FOUR", "STREAM_MIN_BYTES", "SUCCESS",
     "ERROR_INVALID_VALUE", "ERROR_NOT_SUPPORTED", "ERROR_LAUNCH", "KERNEL_NAMES", "KERNEL_RUN",
+    "KERNEL_ROWS",
     "GgrmsError",
     "ggrms_forward", "ggrms_forward_ex", "ggrms_forward_tuned", "ggrms_plan", "ggrms_plan_ex",
     "ggrms_plan_tuned", "ggrms_status_string", "ggrms_abi_version", "forward", "plan",
@@ -49,8 +50,8 @@ FLAG_CACHE_STREAM, FLAG_CACHE_KEEP = 8, 16
 FLAG_ORDER_ROWS, FLAG_ORDER_BANDED, FLAG_WAVE_ONE, FLAG_WAVE_FOUR = 32, 64, 128, 256
 STREAM_MIN_BYTES = 4 << 20  # default policy: jobs of at least this many y+gate+out bytes stream
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
-KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide", 4: "run"}
-KERNEL_RUN = 4
+KERNEL_NAMES = {0: "none", 1: "wave", 2: "block", 3: "wide", 4: "run", 5: "rows"}
+KERNEL_RUN, KERNEL_ROWS = 4, 5
 ABI_VERSION = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -132,7 +133,8 @@ def ggrms_forward(y: int, gate: int, norm_weight: int, out: int, rows: int, widt
 
 def _shape_arg(shape):
     """None, or (lanes, vectors[, rows per workgroup[, vector bytes[, kernel]]]) as a
-    ggrms_shape_t (kernel: 0, or KERNEL_RUN for runs of packed groups)."""
+    ggrms_shape_t (kernel: 0, KERNEL_RUN for runs of packed groups, or KERNEL_ROWS for
+    workgroups that take rows in turn)."""
     if shape is None:
         return None
     f = list(shape) + [0] * (5 - len(shape))

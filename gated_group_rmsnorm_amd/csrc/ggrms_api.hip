@@ -60,9 +60,11 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     const ggrms_plan_t& p = lp.pub;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool nbg = (flags & GGRMS_FLAG_NORM_BEFORE_GATE) != 0;
+    // (ROWS reports the rows each workgroup takes in turn; its kernels are
+    // built for one unit at a time)
     const void* fn = pick((int)dtype, nbg, p.streaming != 0, p.kernel, p.vector_bytes,
                           p.piece_bytes, p.lanes_per_group, p.vectors_per_lane,
-                          p.rows_per_workgroup);
+                          p.kernel == GGRMS_KERNEL_ROWS ? 1 : p.rows_per_workgroup);
     if (!fn) return GGRMS_ERROR_NOT_SUPPORTED;
 
     if (rows == 1) y_row_stride = gate_row_stride = out_row_stride = width;
@@ -83,7 +85,8 @@ ggrms_status_t forward_impl(const void* y, const void* gate, const float* norm_w
     int64_t R, C;
     launch_tiles(lp, lp.rows_per_launch, &R, &C);
     (void)R;
-    a.xc = (uint32_t)C;
+    // (ROWS: the step between a workgroup's rows)
+    a.xc = p.kernel == GGRMS_KERNEL_ROWS ? (uint32_t)lp.rows_stride : (uint32_t)C;
     div_magic(a.xc, &a.xc_m, &xc_s);
     a.bits = (div_s << kBitDivShift) | (xc_s << kBitXcShift) |
              ((dtype != GGRMS_F32 && (flags & GGRMS_FLAG_ROUND_INTERMEDIATE)) ? kBitRound : 0u) |

@@ -72,7 +72,8 @@ constexpr uint32_t kXcds = 8;
 // for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
 // vectors per lane 1..4, and 6 with 256 lanes.  WIDE: 1024 lanes, vectors per
 // lane 0 (it loops over the group).  RUN: 64 lanes, one vector each, over a
-// run of packed groups.  A WAVE workgroup is a single wave or 4
+// run of packed groups.  ROWS: 256 lanes x 3 vectors, or 320, 384, 448 or
+// 512 lanes x 2 (16-byte vectors, not packed).  A WAVE workgroup is a single wave or 4
 // waves (the kernel takes its size from the launch; the planner's rule says
 // which).
 constexpr int kWaveBlock = 256;
@@ -80,6 +81,11 @@ constexpr int kWaveBlock = 256;
 constexpr int kRunMaxGroups = 8;
 constexpr int kWaveBlockOneWave = 64;
 constexpr int kWideBlock = 1024;
+// ROWS: one workgroup per compute unit of the part (gfx950: 256), taken for
+// jobs of at least kRowsMinUnits (row, group) units -- eight rows or more per
+// workgroup, enough to amortise loading its weights and to keep rows in flight.
+constexpr int64_t kRowsWorkgroups = 256;
+constexpr int64_t kRowsMinUnits = 2048;
 
 // Rows of one group per BLOCK workgroup (the workgroup stays <= 512 threads).
 inline bool rows_per_workgroup_supported(int kernel, int lanes, int upb) {
@@ -105,6 +111,9 @@ inline bool shape_supported(int kernel, int lanes, int vpt) {
         return lanes == kWideBlock;
     case GGRMS_KERNEL_RUN:
         return lanes == 64 && vpt == 1;
+    case GGRMS_KERNEL_ROWS:
+        return (lanes == 256 && vpt == 3) ||
+               ((lanes == 320 || lanes == 384 || lanes == 448 || lanes == 512) && vpt == 2);
     default:
         return false;
     }
@@ -121,6 +130,7 @@ struct LaunchPlan {
     bool xband;               // XCD-banded tile order (kBitBand)
     int super_shift;          // log2 of the banded order's super-tile (kBitSuperShift)
     int64_t runs_per_row;     // RUN: tiles of one row
+    int64_t rows_stride;      // ROWS: workgroups per group, the step between a workgroup's rows
 };
 
 // WAVE: groups one workgroup covers (lanes <= 64).
@@ -139,6 +149,9 @@ inline void launch_tiles(const LaunchPlan& lp, int64_t r, int64_t* R, int64_t* C
     } else if (p.kernel == GGRMS_KERNEL_RUN) {  // one run per one-wave workgroup
         *R = r;
         *C = lp.runs_per_row;
+    } else if (p.kernel == GGRMS_KERNEL_ROWS) {  // its own order (no banding)
+        *R = r;
+        *C = lp.groups;
     } else {
         const int64_t gpw = wave_groups_per_workgroup(p.lanes_per_group, p.block_threads);
         *R = r;
@@ -163,6 +176,7 @@ inline int64_t launch_workgroups(const LaunchPlan& lp, int64_t r) {
     }
     case GGRMS_KERNEL_WIDE: return r * lp.groups;
     case GGRMS_KERNEL_RUN: return r * lp.runs_per_row;
+    case GGRMS_KERNEL_ROWS: return lp.rows_stride * lp.groups;
     default: return 0;
     }
 }

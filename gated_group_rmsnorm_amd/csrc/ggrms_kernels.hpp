@@ -528,6 +528,125 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
     }
 }
 
+// ROWS: wide groups (513-1024 16-byte vectors) in large jobs.  The grid is
+// one workgroup per compute unit (a.xc = S rows per group): workgroup b takes
+// group b % groups and rows b / groups, + S, + 2S, ...  Its SEG lanes hold VPT
+// vectors of a row each (the slots and the order of the sums are those of
+// the BLOCK kernel with the same lanes and vectors, so both give the same
+// bits), its weights stay in registers for every row, and it keeps the rows
+// two ahead in flight: the inputs of row i + 2S are requested as soon as row
+// i's inputs have been turned into gated values, before row i's barrier and
+// stores.  All y/gate/out accesses are buffer accesses over the unit's
+// vectors: a lane past the group's end, or a prefetch past the last row,
+// gets an offset outside the unit, which the hardware drops (stores) or
+// answers with zeros without touching memory (loads).  No path through the
+// loop then skips a memory operation, so the compiler's counts of
+// outstanding operations stay exact and a row's loads never wait for the
+// previous row's stores (memory counters retire in order).
+template <class T, int SEG, int VPT, bool NBG, bool NT>
+__global__ __launch_bounds__(SEG) void ggrms_rows_kernel(KArgs a) {
+    constexpr int VB = 16;
+    using P = Packet<T, VB>;
+    using W = typename P::W;
+    constexpr int N = P::N;
+    constexpr int WPG = SEG / 64;
+    constexpr int D = 2;             // rows in flight per workgroup
+    constexpr int kFmt = 0x00020000;  // word 3 of a raw buffer resource: 32-bit data
+    constexpr int kPol = NT ? 2 : 0;  // cache policy operand: nt
+    using S = typename VecWord<T::kSize>::type;
+    __shared__ float part[D][WPG];
+
+    const uint32_t n0 = row_div(a, blockIdx.x);
+    const uint32_t g = blockIdx.x - n0 * a.groups;
+    const uint32_t stride = a.xc, rows = a.rows, nvec = a.nvec;
+    const uint32_t sl = threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int beyond = (int)(nvec * VB);  // an offset outside the unit
+    uint32_t ci[VPT];
+    bool lv[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const uint32_t idx = sl + k * SEG;
+        lv[k] = idx < nvec;
+        ci[k] = lv[k] ? idx : nvec - 1;
+    }
+    float wr[VPT][N];
+    const float* wp = a.w + (int64_t)g * weight_group_stride(a);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
+
+    // the unit (row n, group g) of a [rows, width] view with row stride ld
+    auto unit_rsrc = [&](const void* base, int64_t ld, uint32_t n) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<S*>(static_cast<const S*>(base)) + (int64_t)n * ld + (int64_t)g * a.G, 0,
+            beyond, kFmt);
+    };
+    auto load_unit = [&](uint32_t n, bool want, W (&yr)[VPT], W (&gr)[VPT]) {
+        const auto ry = unit_rsrc(a.y, a.sy, n), rg = unit_rsrc(a.gate, a.sg, n);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            const int off = want && lv[k] ? (int)(ci[k] * VB) : beyond;
+            yr[k] = __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, kPol);
+            gr[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, kPol);
+        }
+    };
+
+    W yb[D][VPT], gb[D][VPT];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const uint32_t nd = n0 + d * stride;
+        load_unit(nd < rows ? nd : n0, nd < rows, yb[d], gb[d]);
+    }
+    // The weights and the first rows have landed before the loop: inside it
+    // the compiler's waits then follow only the loop's own loads and stores.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    auto live = [&](int k) { return lv[k]; };
+    auto owned = [](int, int) { return true; };
+    // the loop, one copy per rounding mode (no branch inside it)
+    auto run = [&](auto ri_tag) __attribute__((always_inline)) {
+        constexpr bool RI = decltype(ri_tag)::value;
+        auto pass = [&](uint32_t n, W (&yr)[VPT], W (&gr)[VPT], float* pt)
+            __attribute__((always_inline)) {
+            epi::LaneUnit<T, VB, VPT, NBG> L;
+            const float acc = epi::gate_and_square<T, VB, VB, VPT, NBG>(yr, gr, L, live, owned);
+            // the raw inputs are now in L: their registers take the row D ahead
+            const uint32_t nn = n + D * stride;
+            load_unit(nn < rows ? nn : n, nn < rows, yr, gr);
+            const float s = segment_sum<64>(acc);
+            if ((threadIdx.x & 63) == 0) pt[wave] = s;
+            __syncthreads();
+            float m2 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < WPG; ++i) m2 += pt[i];
+            const float nf = norm_factor(m2, a.Ginv, a.eps);
+            W res[VPT];
+            epi::finish<RI>(L, nf, wr, res);
+            const auto ro = unit_rsrc(a.out, a.so, n);
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int off = lv[k] ? (int)(ci[k] * VB) : beyond;
+                __builtin_amdgcn_raw_buffer_store_b128(res[k], ro, off, 0, kPol);
+            }
+        };
+        // D rows per trip, so that each row's registers and partial-sum slot are
+        // fixed (consecutive rows use different slots: a wave still reading one
+        // row's partial sums never meets the next row's writes)
+        uint32_t n = n0;
+        for (; n + (D - 1) * stride < rows; n += D * stride) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) pass(n + d * stride, yb[d], gb[d], part[d]);
+        }
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (n + d * stride < rows) pass(n + d * stride, yb[d], gb[d], part[d]);
+    };
+    if (!NBG && round_intermediate(a))
+        run(std::true_type{});
+    else
+        run(std::false_type{});
+}
+
 // WIDE: one 1024-thread workgroup per unit, for groups with more vectors than
 // the BLOCK shapes hold in registers.  Pass 1 reads the group and reduces;
 // pass 2 reads it again and writes (the only path that reads inputs twice).
@@ -621,6 +740,16 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
         if constexpr (kPacked) return nullptr;
         if (upb != 1) return nullptr;
         return reinterpret_cast<const void*>(&ggrms_wide_kernel<T, VB, NBG, NT>);
+    } else if (kernel == GGRMS_KERNEL_ROWS) {
+        if constexpr (VB == 16 && !kPacked) {
+            if (upb != 1) return nullptr;
+#define GG_R(L, V)              \
+    if (lanes == L && vpt == V) \
+    return reinterpret_cast<const void*>(&ggrms_rows_kernel<T, L, V, NBG, NT>)
+            GG_R(256, 3); GG_R(320, 2); GG_R(384, 2); GG_R(448, 2); GG_R(512, 2);
+#undef GG_R
+        }
+        return nullptr;
     } else if (kernel == GGRMS_KERNEL_RUN) {
         if constexpr (kPacked) {
             if (lanes == 64 && vpt == 1 && upb == 1)

@@ -79,6 +79,22 @@ constexpr int64_t kMaxPackedVectors = 2048;
 // SIMDs x 4 waves): such a job is a single round of loads and arithmetic.
 constexpr int64_t kSmallJobWaves = 4096;
 
+// ROWS shape for a group of nvec 16-byte vectors (nvec <= 1024): 256 lanes x
+// 3 up to 608 vectors, above that two vectors on the next multiple of 64
+// lanes -- the fastest of the built shapes in a sweep of 377 MB single-group
+// bf16 jobs over groups of 528-1024 vectors (0.77-0.81 of HBM peak against
+// 0.74-0.77 for the BLOCK kernel's one row per workgroup; 320 x 2 on the
+// 5120-wide group: 58.6 against 63.0 us).
+void rows_shape(int64_t nvec, int* lanes, int* vpt) {
+    if (nvec <= 608) {
+        *lanes = 256;
+        *vpt = 3;
+    } else {
+        *lanes = (int)((nvec + 127) / 128 * 64);
+        *vpt = 2;
+    }
+}
+
 int kernel_for_shape(int lanes, int vpt) {
     if (vpt == 0) return GGRMS_KERNEL_WIDE;
     return lanes <= 64 ? GGRMS_KERNEL_WAVE : GGRMS_KERNEL_BLOCK;
@@ -177,7 +193,8 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
                   (shape->vector_bytes != 0 && shape->vector_bytes != 2 &&
                    shape->vector_bytes != 4 && shape->vector_bytes != 8 &&
                    shape->vector_bytes != 16) ||
-                  (shape->kernel != 0 && shape->kernel != GGRMS_KERNEL_RUN)))
+                  (shape->kernel != 0 && shape->kernel != GGRMS_KERNEL_RUN &&
+                   shape->kernel != GGRMS_KERNEL_ROWS)))
         return GGRMS_ERROR_INVALID_VALUE;
     if (((flags & GGRMS_FLAG_ORDER_ROWS) && (flags & GGRMS_FLAG_ORDER_BANDED)) ||
         ((flags & GGRMS_FLAG_WAVE_ONE) && (flags & GGRMS_FLAG_WAVE_FOUR)))
@@ -274,7 +291,21 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     const int64_t gpw_fit = packed ? (64 * 16 - 16 + pb) / gbytes : 0;
     const int64_t gpw = gpw_fit < kRunMaxGroups ? gpw_fit : kRunMaxGroups;
     const bool run_fits = packed && gpw >= 2 && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP);
-    if (shape && shape->kernel == GGRMS_KERNEL_RUN) {
+    // ROWS needs 16-byte vectors that are not packed and a launch of
+    // 32-bit row indices
+    const bool rows_fit = !packed && vb == 16 && rows < ((int64_t)1 << 31) && nvec <= 1024;
+    if (shape && shape->kernel == GGRMS_KERNEL_ROWS) {
+        if (!rows_fit || force_upb > 1) return GGRMS_ERROR_NOT_SUPPORTED;
+        if (shape->lanes_per_group == 0 && shape->vectors_per_lane == 0) {
+            rows_shape(nvec, &lanes, &vpt);
+        } else {
+            lanes = shape->lanes_per_group;
+            vpt = shape->vectors_per_lane;
+        }
+        if (!shape_supported(GGRMS_KERNEL_ROWS, lanes, vpt) || (int64_t)lanes * vpt < nvec)
+            return GGRMS_ERROR_NOT_SUPPORTED;
+        kernel = GGRMS_KERNEL_ROWS;
+    } else if (shape && shape->kernel == GGRMS_KERNEL_RUN) {
         if (!run_fits || !(shape->lanes_per_group == 0 || shape->lanes_per_group == 64) ||
             !(shape->vectors_per_lane == 0 || shape->vectors_per_lane == 1) || force_upb > 1)
             return GGRMS_ERROR_NOT_SUPPORTED;
@@ -325,6 +356,14 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
             // wave (13-wide bf16 groups, 8 to a run: 111 against 271 us).
             kernel = GGRMS_KERNEL_RUN;
             lanes = 64;
+        } else if (kernel == GGRMS_KERNEL_BLOCK && rows_fit && nvec > 512 &&
+                   plan->groups <= kRowsWorkgroups && rows * plan->groups >= kRowsMinUnits) {
+            // Wide groups in large jobs: one workgroup per compute unit
+            // taking rows in turn, with the next rows' inputs in flight
+            // while it stores, instead of one workgroup per row (whose
+            // loads start only when a slot frees).
+            kernel = GGRMS_KERNEL_ROWS;
+            rows_shape(nvec, &lanes, &vpt);
         }
     }
     if (kernel == GGRMS_KERNEL_RUN) {
@@ -378,7 +417,8 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     launch_tiles(*plan, rows, &R1, &C1);
     const int64_t gpwg = kernel == GGRMS_KERNEL_WAVE ? wave_groups_per_workgroup(lanes, block) : 1;
     const int64_t tiles_per_row = kernel == GGRMS_KERNEL_RUN ? plan->runs_per_row : groups;
-    plan->xband = kernel != GGRMS_KERNEL_WIDE && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) &&
+    const bool orderable = kernel != GGRMS_KERNEL_WIDE && kernel != GGRMS_KERNEL_ROWS;
+    plan->xband = orderable && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) &&
                   tiles_per_row % (kXcds * gpwg) != 0;
     // Packed groups in one-wave WAVE workgroups: a tile's bytes (its groups'
     // bytes) are not a multiple of the 128-byte cache line, so neighbouring
@@ -399,14 +439,23 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         if (super > 1) plan->xband = true;
     }
     if (flags & GGRMS_FLAG_ORDER_ROWS) plan->xband = false;
-    if ((flags & GGRMS_FLAG_ORDER_BANDED) && kernel != GGRMS_KERNEL_WIDE) plan->xband = true;
+    if ((flags & GGRMS_FLAG_ORDER_BANDED) && orderable) plan->xband = true;
     plan->super_shift = 0;
     if (plan->xband)
         while ((int64_t)1 << plan->super_shift < super) ++plan->super_shift;
     if (kernel == GGRMS_KERNEL_BLOCK) block = lanes * upb;
     if (kernel == GGRMS_KERNEL_WIDE) block = kWideBlock;
     if (kernel == GGRMS_KERNEL_RUN) block = 64;
+    if (kernel == GGRMS_KERNEL_ROWS) block = lanes;
     plan->pub.block_threads = block;
+    // ROWS: S workgroups per group, S <= rows; workgroup b takes rows
+    // b / groups + k * S of group b % groups.
+    if (kernel == GGRMS_KERNEL_ROWS) {
+        int64_t S = kRowsWorkgroups / groups;
+        if (S < 1) S = 1;
+        if (S > rows) S = rows;
+        plan->rows_stride = S;
+    }
     // Threads per row of the grid.  Each launch stays within 2^31 threads
     // (so within 2^31 units and tiles too) and the kernels index with 32-bit
     // integers; larger jobs are split by rows.
@@ -415,7 +464,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     if (kernel == GGRMS_KERNEL_WAVE && plan->xband) row_threads = C1 * block;
     int64_t rows_per_launch = ((int64_t)1 << 31) / row_threads;
     if (rows_per_launch < 1) return GGRMS_ERROR_INVALID_VALUE;  // one row alone too large
-    if (rows_per_launch > rows) rows_per_launch = rows;
+    if (rows_per_launch > rows || kernel == GGRMS_KERNEL_ROWS) rows_per_launch = rows;
     const int64_t launches = (rows + rows_per_launch - 1) / rows_per_launch;
     int64_t workgroups = 0;
     for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
@@ -432,6 +481,8 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     plan->pub.block_threads = block;
     plan->pub.launches = (int32_t)launches;
     plan->pub.rows_per_workgroup = upb;
+    if (kernel == GGRMS_KERNEL_ROWS)
+        plan->pub.rows_per_workgroup = (int32_t)((rows + plan->rows_stride - 1) / plan->rows_stride);
     plan->pub.lds_bytes = upb > 1 ? (int32_t)(group_size * 4) : 0;
     plan->pub.workgroups = workgroups;
     plan->pub.tile_order = plan->xband ? 1 : 0;

@@ -134,8 +134,11 @@ typedef enum {
     GGRMS_KERNEL_WAVE = 1,   /* one span of <= 64 lanes per (row, group); no LDS, no barrier */
     GGRMS_KERNEL_BLOCK = 2,  /* one (row, group) across 2..16 waves; LDS combine, one barrier */
     GGRMS_KERNEL_WIDE = 3,   /* groups too wide for registers: two passes over the group */
-    GGRMS_KERNEL_RUN = 4     /* packed groups: one wave over a run of consecutive groups of a
+    GGRMS_KERNEL_RUN = 4,    /* packed groups: one wave over a run of consecutive groups of a
                                 row, one vector per lane; 64-lane sums per group */
+    GGRMS_KERNEL_ROWS = 5    /* wide groups in large jobs: one workgroup per compute unit
+                                takes rows of one group in turn, the next rows' inputs in
+                                flight while it stores; LDS combine, one barrier per row */
 } ggrms_kernel_t;
 
 typedef struct {
@@ -145,7 +148,8 @@ typedef struct {
     int32_t vectors_per_lane; /* vectors each lane holds per group (0 for WIDE: it loops) */
     int32_t block_threads;    /* threads per workgroup */
     int32_t launches;         /* kernel launches (rows are split if a grid would be too large) */
-    int32_t rows_per_workgroup; /* BLOCK: rows of one group per workgroup (weights shared in LDS) */
+    int32_t rows_per_workgroup; /* BLOCK: rows of one group per workgroup (weights shared in
+                                   LDS); ROWS: the most rows one workgroup takes in turn */
     int32_t lds_bytes;        /* dynamic LDS per workgroup (the staged weights) */
     int64_t workgroups;       /* workgroups over all launches */
     int32_t streaming;        /* 1: y/gate/out loads and stores carry the non-temporal hint

@@ -26,12 +26,13 @@ typedef enum {
     GGRMS_FLAG_CACHE_STREAM = 8,
     GGRMS_FLAG_CACHE_KEEP = 16,
     /* Tile order (plan field tile_order): ORDER_ROWS / ORDER_BANDED force
-     * the row-major or the XCD-banded order (BANDED has no effect on WIDE). */
+     * the row-major or the XCD-banded order (no effect on WIDE and ROWS,
+     * whose workgroups take their own rows). */
     GGRMS_FLAG_ORDER_ROWS = 32,
     GGRMS_FLAG_ORDER_BANDED = 64,
     /* WAVE workgroups of one or four waves (by default one for 16-byte
      * vectors, packed groups included, and four for narrower vectors; no
-     * effect on BLOCK, WIDE and RUN). */
+     * effect on BLOCK, WIDE, RUN and ROWS). */
     GGRMS_FLAG_WAVE_ONE = 128,
     GGRMS_FLAG_WAVE_FOUR = 256
 } ggrms_tuning_flag_t;
@@ -57,7 +58,11 @@ typedef enum {
  *                     (16 also allows packed groups, see ggrms.h)
  *   kernel            0: the kernel family follows from lanes and vectors;
  *                     GGRMS_KERNEL_RUN: runs of packed groups (lanes and
- *                     vectors 0, or 64 and 1; groups of at most 32 vectors)
+ *                     vectors 0, or 64 and 1; groups of at most 32 vectors);
+ *                     GGRMS_KERNEL_ROWS: rows in turn per workgroup, for
+ *                     16-byte vectors that are not packed (lanes and vectors
+ *                     0 for the library's choice, or 256 x 3, 320 x 2,
+ *                     384 x 2, 448 x 2, 512 x 2; rows_per_workgroup 0 or 1)
  *
  * For packed groups the shape must cover the vectors of the worst-aligned
  * group, WIDE is not built and rows_per_workgroup must be 0 or 1.
@@ -75,7 +80,8 @@ typedef struct {
  * also hold ggrms_tuning_flag_t bits, and `shape` (NULL: the library
  * chooses) forces the kernel shape.  GGRMS_ERROR_INVALID_VALUE for a shape
  * field out of range (negative, a vector_bytes that is not 0, 2, 4, 8 or 16,
- * or a kernel that is not 0 or GGRMS_KERNEL_RUN); GGRMS_ERROR_NOT_SUPPORTED for a shape that is not built, whose
+ * or a kernel that is not 0, GGRMS_KERNEL_RUN or GGRMS_KERNEL_ROWS);
+ * GGRMS_ERROR_NOT_SUPPORTED for a shape that is not built, whose
  * lanes_per_group * vectors_per_lane vectors do not cover one group, whose
  * rows_per_workgroup cannot be used, or whose vector_bytes the alignment
  * does not allow.  Otherwise as ggrms_forward_ex.

@@ -162,7 +162,7 @@ def test_interleaved_views_do_not_overlap(g):
 
 
 RI, NBG, PER_GROUP, STREAM, KEEP = 1, 2, 4, 8, 16
-KERNEL_RUN = 4
+KERNEL_RUN, KERNEL_ROWS = 4, 5
 ROWS, BANDED, WAVE1, WAVE4 = 32, 64, 128, 256
 
 
@@ -554,6 +554,74 @@ def test_packed_groups_need_aligned_rows(g):
                      y_row_stride=16 * G, gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
                      gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
     assert st == NOTSUP
+
+
+def test_rows_plan(g):
+    """ROWS: groups of 513-1024 16-byte vectors that are not packed, in jobs of
+    at least 2048 (row, group) units with at most 256 groups per row: one
+    workgroup per compute unit (256 / groups per group, at most one per row),
+    256 lanes x 3 up to 608 vectors and two vectors on the next multiple of
+    64 lanes above; one launch, no banded order.  Forced through the tuning
+    shape's kernel field for any group of at most 1024 16-byte vectors (the
+    library's lanes, or a built pair that covers the group); refused for
+    narrower vectors, packed groups, unbuilt pairs and several rows per
+    workgroup."""
+    kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
+
+    def plan(rows, G, dtype=BF16, groups=1, flags=RI, shape=None, **more):
+        width = G * groups
+        args = dict(rows=rows, width=width, group_size=G, y_row_stride=width,
+                    gate_row_stride=width, out_row_stride=width, dtype=dtype, **kw)
+        args.update(more)
+        return _plan_ex(g, flags, shape, **args)
+
+    # the rule by vectors per group (bf16: 8 elements per vector; f32: 4)
+    for G, dtype, lanes, vpt in ((4104, BF16, 256, 3), (4864, BF16, 256, 3), (4872, BF16, 320, 2),
+                                 (5120, BF16, 320, 2), (5128, BF16, 384, 2), (6144, F16, 384, 2),
+                                 (6152, BF16, 448, 2), (7168, BF16, 448, 2), (7176, BF16, 512, 2),
+                                 (8192, BF16, 512, 2), (2560, F32, 320, 2), (4096, F32, 512, 2)):
+        st, p = plan(12288, G, dtype)
+        assert st == OK and (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"],
+                             p["block_threads"], p["workgroups"], p["launches"], p["tile_order"],
+                             p["rows_per_workgroup"], p["lds_bytes"]) == \
+            ("rows", lanes, vpt, lanes, 256, 1, 0, 48, 0), (G, dtype, p)
+        assert plan(12288, G, dtype, shape=(0, 0, 0, 0, KERNEL_ROWS))[1] == p
+        assert plan(12288, G, dtype, shape=(lanes, vpt, 1, 16, KERNEL_ROWS))[1] == p
+        # norm first and a shared weight: the same choice
+        assert plan(12288, G, dtype, flags=NBG)[1]["kernel_name"] == "rows"
+        assert plan(12288, G, dtype, flags=RI | PER_GROUP, groups=2)[1]["kernel_name"] == "rows"
+    # several groups per row: 256 / groups workgroups per group; at least 2048 units
+    st, p = plan(1024, 5120, groups=2)
+    assert (p["kernel_name"], p["workgroups"], p["rows_per_workgroup"]) == ("rows", 256, 8)
+    st, p = plan(700, 5120, groups=3)
+    assert (p["kernel_name"], p["workgroups"], p["rows_per_workgroup"]) == ("rows", 255, 9)
+    assert plan(1023, 5120, groups=2)[1]["kernel_name"] == "block"
+    assert plan(2047, 5120)[1]["kernel_name"] == "block"
+    assert plan(2048, 5120)[1]["kernel_name"] == "rows"
+    # wider and narrower groups, narrower vectors, a strided view that is
+    # not 16-byte aligned: the other kernels
+    assert plan(12288, 8200)[1]["kernel_name"] == "block"
+    assert plan(12288, 4096)[1]["kernel_name"] == "block"
+    p = plan(12288, 5120, y_row_stride=5124)[1]
+    assert (p["kernel_name"], p["vector_bytes"]) == ("block", 8)
+    # a forced ROWS launch with fewer rows than compute units: one workgroup per row
+    st, p = plan(100, 5120, shape=(0, 0, 0, 0, KERNEL_ROWS))
+    assert st == OK and (p["workgroups"], p["rows_per_workgroup"]) == (100, 1)
+    st, p = plan(300, 960, shape=(0, 0, 0, 0, KERNEL_ROWS))
+    assert st == OK and (p["lanes_per_group"], p["vectors_per_lane"], p["workgroups"],
+                         p["rows_per_workgroup"]) == (256, 3, 256, 2)
+    st, p = plan(300, 960, shape=(320, 2, 0, 0, KERNEL_ROWS))
+    assert st == OK and (p["kernel_name"], p["lanes_per_group"]) == ("rows", 320)
+    # refusals: more than 1024 vectors, packed groups, narrower vectors, pairs
+    # not built or too small, rows per workgroup
+    assert plan(300, 8200, shape=(0, 0, 0, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 100, dtype=F16, groups=16, shape=(0, 0, 0, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 5120, shape=(0, 0, 0, 8, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 5120, shape=(256, 4, 0, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 5120, shape=(256, 3, 0, 0, KERNEL_ROWS))[0] == OK
+    assert plan(300, 6144, shape=(320, 2, 0, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 5120, shape=(320, 2, 2, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 5120, shape=(0, 0, 0, 0, 6))[0] == INVALID
 
 
 def test_runs_of_packed_groups_plan(g):

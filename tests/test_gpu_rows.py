@@ -1,0 +1,163 @@
+"""GPU parity of the ROWS kernel (workgroups that take rows of one group in
+turn, the next rows' inputs in flight while they store) against the CPU
+oracle, and its bits against the BLOCK kernel with the same lanes and vectors.
+
+Bar as in test_gpu_parity.py: f32 within a relative 1e-5 of the oracle,
+fp16/bf16 within 2 units in the last place.  Sizes: forced ROWS launches on
+a few hundred rows (every workgroup's loop, its trailing single row and the
+prefetch past the last row), and the library's own choice on jobs of 2048+
+(row, group) units.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from gpu_util import (BF16, DT_IDS, F16, F32, FLAG_KEEP, FLAG_NBG, FLAG_PER_GROUP, FLAG_RI,
+                      FLAG_STREAM, assert_parity, check_contiguous, dev_buf, host_bits,
+                      random_case, run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+KERNEL_ROWS = 5
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_group_rmsnorm_amd as g  # raises if libggrms.so is missing
+
+    return g
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+
+    oracle.build(force=False)
+    return oracle
+
+
+def _plan(g, rows, width, G, dtype, flags, shape=None):
+    n = rows * width * (4 if dtype == F32 else 2)
+    st, p = g.ggrms_plan_tuned(1 << 40, (1 << 40) + 2 * n, (1 << 40) + 4 * n, (1 << 40) + 6 * n,
+                               rows, width, G, width, width, width, 1e-5, dtype, flags, shape)
+    assert st == g.SUCCESS, g.ggrms_status_string(st)
+    return p
+
+
+# (rows, groups per row, G, dtype, lanes x vectors): every built pair, rows
+# below, at and above 256 / groups (one row per workgroup; two or three rows
+# for some workgroups and one for the rest, so both the paired loop and its
+# trailing single row run), several groups per row
+FORCED = [
+    (300, 1, 4104, BF16, (256, 3)),   # 513 vectors: one past the BLOCK 256 x 2 limit
+    (300, 1, 5120, BF16, (320, 2)),
+    (37, 1, 5120, BF16, (320, 2)),    # fewer rows than compute units
+    (200, 3, 5120, BF16, (320, 2)),   # 85 workgroups per group, 2-3 rows each
+    (530, 1, 6144, F16, (384, 2)),
+    (260, 2, 7168, BF16, (448, 2)),
+    (513, 1, 8192, F16, (512, 2)),
+    (300, 1, 2560, F32, (320, 2)),
+    (300, 1, 4096, F32, (512, 2)),
+    (300, 1, 960, BF16, (256, 3)),    # a narrow group on the widest lanes: most lanes idle
+]
+
+
+@pytest.mark.parametrize("rows,groups,G,dtype,shape", FORCED,
+                         ids=[f"{r}x{n}xG{G}-{DT_IDS[d]}-{s[0]}x{s[1]}" for r, n, G, d, s in FORCED])
+def test_forced_rows_against_the_oracle(g, orc, rows, groups, G, dtype, shape):
+    width = G * groups
+    sh = (shape[0], shape[1], 0, 0, KERNEL_ROWS)
+    assert _plan(g, rows, width, G, dtype, FLAG_RI, sh)["kernel_name"] == "rows"
+    variants = [FLAG_RI, 0, FLAG_NBG, FLAG_RI | FLAG_PER_GROUP] if dtype != F32 else \
+        [0, FLAG_NBG, FLAG_PER_GROUP]
+    for i, flags in enumerate(variants):
+        check_contiguous(g, orc, rows, width, G, dtype, flags & FLAG_RI, seed=9100 + i + rows,
+                         shape=sh, flags=flags, tag=f"rows {shape} flags={flags}")
+
+
+# the library's own choice on jobs large enough for ROWS
+AUTO = [(2048, 1, 5120, BF16, 320), (1024, 2, 4864, BF16, 256), (2100, 1, 8192, BF16, 512),
+        (2048, 1, 2560, F32, 320), (700, 3, 6152, F16, 448)]
+
+
+@pytest.mark.parametrize("rows,groups,G,dtype,lanes", AUTO,
+                         ids=[f"{r}x{n}xG{G}-{DT_IDS[d]}" for r, n, G, d, _ in AUTO])
+def test_rows_by_default(g, orc, rows, groups, G, dtype, lanes):
+    width = G * groups
+    ri = 1 if dtype != F32 else 0
+    p = _plan(g, rows, width, G, dtype, FLAG_RI if ri else 0)
+    assert (p["kernel_name"], p["lanes_per_group"]) == ("rows", lanes), p
+    check_contiguous(g, orc, rows, width, G, dtype, ri, seed=9200 + rows, tag="rows default")
+
+
+@pytest.mark.parametrize("lanes,vpt,G,dtype", [(256, 3, 5120, BF16), (512, 2, 8192, F16),
+                                               (256, 3, 3072, F32)],
+                         ids=["256x3-bf16", "512x2-f16", "256x3-f32"])
+def test_rows_equals_block_bitwise(g, lanes, vpt, G, dtype):
+    """Same lanes and vectors: the same slots and the same order of the sums,
+    so ROWS and BLOCK (one row per workgroup) give the same bits; so do the
+    streaming and the cached accesses."""
+    rows = 300
+    say(f"case rows vs block {lanes}x{vpt} G={G} dtype={DT_IDS[dtype]}")
+    y, gt, w = random_case(rows, G, dtype, seed=9300 + G)
+    yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+    outs = []
+    ri = FLAG_RI if dtype != F32 else 0
+    for shape, extra in (((lanes, vpt, 1, 0, 0), 0), ((lanes, vpt, 0, 0, KERNEL_ROWS), 0),
+                         ((lanes, vpt, 0, 0, KERNEL_ROWS), FLAG_STREAM),
+                         ((lanes, vpt, 0, 0, KERNEL_ROWS), FLAG_KEEP)):
+        od = torch.empty_like(yd)
+        st = run_gpu(g, yd, gd, wd, od, rows, G, G, G, G, G, 1e-5, dtype, 0, shape=shape,
+                     flags=ri | extra)
+        assert st == g.SUCCESS, g.ggrms_status_string(st)
+        outs.append(od)
+    torch.cuda.synchronize()
+    view = torch.int32 if dtype == F32 else torch.int16
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(view), o.view(view))
+
+
+def test_rows_strided_in_place_and_guarded(g, orc):
+    """y and gate as column slices of one fused buffer (16-byte aligned row
+    stride), out written in place over y; a second run into a guarded,
+    padded out whose padding and guard bands must stay untouched."""
+    rows, G, groups = 2304, 5120, 1
+    width = G * groups
+    fused = 2 * width + 64
+    say(f"case rows strided rows={rows} width={width}")
+    buf = S.tensor(9401, S.TID_Y, rows * fused, BF16, ("normal", 1.0))
+    w = S.tensor(9401, S.TID_W, width, F32, ("uniform", 0.5, 1.5))
+    y = buf.reshape(rows, fused)[:, :width]
+    gt = buf.reshape(rows, fused)[:, width:2 * width]
+    ref = orc.forward(np.ascontiguousarray(y).reshape(-1), np.ascontiguousarray(gt).reshape(-1), w,
+                      rows=rows, width=width, group_size=G, y_row_stride=width,
+                      gate_row_stride=width, out_row_stride=width, eps=1e-5, dtype=BF16,
+                      round_intermediate=1)
+    fd, wd = dev_buf(buf, BF16), torch.from_numpy(w).cuda()
+    p = g.ggrms_plan_ex(fd.data_ptr(), fd[width:].data_ptr(), wd.data_ptr(), fd.data_ptr(), rows,
+                        width, G, fused, fused, fused, 1e-5, BF16, FLAG_RI)[1]
+    assert p["kernel_name"] == "rows"
+    # into a padded, guarded out
+    so, guard = width + 24, 256
+    canary = np.uint16(0x4B4B)
+    ob = np.full(guard + (rows - 1) * so + width + guard, canary, dtype=np.uint16)
+    od = dev_buf(ob, BF16)
+    assert run_gpu(g, fd, fd[width:], wd, od[guard:], rows, width, G, fused, fused, so, 1e-5, BF16,
+                   1) == g.SUCCESS
+    # in place over y
+    assert run_gpu(g, fd, fd[width:], wd, fd, rows, width, G, fused, fused, fused, 1e-5, BF16,
+                   1) == g.SUCCESS
+    torch.cuda.synchronize()
+    got = host_bits(od, BF16)
+    view = np.zeros(got.shape, dtype=bool)
+    for r in range(rows):
+        view[guard + r * so:guard + r * so + width] = True
+    assert np.array_equal(got[~view], ob[~view])
+    assert_parity(got[view], ref, BF16, "rows strided into padded out")
+    inplace = host_bits(fd, BF16).reshape(rows, fused)
+    assert_parity(np.ascontiguousarray(inplace[:, :width]).reshape(-1), ref, BF16, "rows in place")
+    # gate and the padding columns of the fused buffer are untouched
+    assert np.array_equal(inplace[:, width:], buf.reshape(rows, fused)[:, width:])
