@@ -553,8 +553,9 @@ def bench_shapes(torch, g, steps):
 # row per workgroup (each unit reads its own weights); 9 groups of 960 per
 # row, where the row-major order makes every XCD read every group's weights,
 # in the XCD-banded order (the default) and in row-major order; the
-# single-group rows of Mamba-2 mixers with one group (G = 5120, 8192); and
-# packed groups.
+# single-group rows of Mamba-2 mixers with one group (G = 5120, 8192), with
+# workgroups taking rows in turn (ROWS, the default) and one row per
+# workgroup (BLOCK); and packed groups.
 EVIDENCE = {
     "prefill_staged": (2, 8192, 7680, 960, 1, None),
     "prefill_unstaged": (2, 8192, 7680, 960, 1, (128, 1, 1)),
@@ -568,7 +569,9 @@ EVIDENCE = {
     "g640x12_banded": (2, 8192, 7680, 640, 1 | 64, None),
     "g640x12_rows": (2, 8192, 7680, 640, 1 | 32, None),
     "g5120": (2, 12288, 5120, 5120, 1, None),
+    "g5120_block": (2, 12288, 5120, 5120, 1, (256, 3, 1)),
     "g8192": (2, 7680, 8192, 8192, 1, None),
+    "g8192_block": (2, 7680, 8192, 8192, 1, (256, 4, 1)),
     # 100-wide fp16 groups (200 bytes: packed 16-byte vectors), one vector per
     # lane on 16 lanes (the default for a job this size) and two vectors per
     # lane on 8 lanes (the default for jobs resident at once)
