@@ -91,6 +91,16 @@ __device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t s) {
     return (__umulhi(n, m) + n) >> s;
 }
 
+// Materialises the argument words that only one tile order reads in scalar
+// registers at the kernel's entry, so that every argument is fetched in one
+// round of scalar loads.  Otherwise the compiler sinks those loads into the
+// order's branch, and the row-major path waits for a second round trip to
+// the argument block before it can address its first vector -- which is on
+// the critical path of a small launch such as decode.
+__device__ __forceinline__ void fetch_args_together(const KArgs& a) {
+    asm volatile("" ::"s"(a.groups), "s"(a.div_m), "s"(a.xc), "s"(a.xc_m), "s"(a.bits));
+}
+
 // Fields of KArgs::bits, and what the kernels derive from the arguments.
 __device__ inline uint32_t div_shift(const KArgs& a) { return (a.bits >> kBitDivShift) & 31u; }
 __device__ inline uint32_t xc_shift(const KArgs& a) { return (a.bits >> kBitXcShift) & 31u; }
@@ -351,6 +361,7 @@ __device__ inline void xcd_band_tile(const KArgs& a, uint32_t R, uint32_t& rt, u
 // one row.
 template <class T, int VB, int PB, int SEG, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
+    fetch_args_together(a);
     uint32_t n, g;
     if (banded(a)) {
         uint32_t c;
@@ -379,6 +390,7 @@ __global__ __launch_bounds__(kWaveBlock) void ggrms_wave_kernel(KArgs a) {
 // miss slots it held go back to the HBM streams.
 template <class T, int VB, int PB, int SEG, int VPT, int UPB, bool NBG, bool NT>
 __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
+    fetch_args_together(a);
     constexpr int BT = SEG * UPB;
     constexpr int WPG = SEG / 64;
     constexpr int N = Packet<T, VB>::N;
