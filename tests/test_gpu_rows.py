@@ -161,3 +161,44 @@ def test_rows_strided_in_place_and_guarded(g, orc):
     assert_parity(np.ascontiguousarray(inplace[:, :width]).reshape(-1), ref, BF16, "rows in place")
     # gate and the padding columns of the fused buffer are untouched
     assert np.array_equal(inplace[:, width:], buf.reshape(rows, fused)[:, width:])
+
+
+@pytest.mark.parametrize("dtype", [BF16, F16, F32], ids=DT_IDS.get)
+def test_rows_special_values(g, orc, dtype):
+    """NaN and inf inputs, all-zero groups, gates deep in silu's underflow
+    range (the exact path, taken by a whole wave) and large positive gates,
+    through a forced ROWS launch whose workgroups take several rows each, in
+    both operators."""
+    import refs
+
+    G = 5120 if dtype != F32 else 2560
+    rows, width = 300, G
+    rng = np.random.default_rng(19)
+    yv = rng.standard_normal((rows, width))
+    gv = rng.standard_normal((rows, width))
+    yv[0, 5] = np.nan
+    yv[257, 200] = np.inf                          # the second row of a workgroup
+    gv[2, 300] = np.nan
+    yv[3, :] = 0.0                                 # an all-zero group
+    gv[4, :] = rng.uniform(-104, -86, width)       # silu underflow window
+    gv[260, :] = -95.0
+    gv[6, :] = rng.uniform(80, 100, width)         # silu(x) = x
+    gv[7, 7] = -np.inf
+    gv[7, 300] = np.inf
+    y = refs.round64(yv, dtype).reshape(-1)
+    gt = refs.round64(gv, dtype).reshape(-1)
+    w = rng.uniform(0.5, 1.5, width).astype(np.float32)
+    yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+    sh = (320, 2, 0, 0, KERNEL_ROWS)
+    for eps in (1e-5, 0.0):
+        for flags in ([0, FLAG_RI, FLAG_NBG] if dtype != F32 else [0, FLAG_NBG]):
+            say(f"case rows special dtype={DT_IDS[dtype]} eps={eps} flags={flags}")
+            od = torch.empty_like(yd)
+            assert run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, eps, dtype, 0,
+                           shape=sh, flags=flags) == g.SUCCESS
+            torch.cuda.synchronize()
+            ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                              gate_row_stride=width, out_row_stride=width, eps=eps, dtype=dtype,
+                              round_intermediate=flags & FLAG_RI,
+                              norm_before_gate=bool(flags & FLAG_NBG))
+            assert_parity(host_bits(od, dtype), ref, dtype, f"rows special eps={eps} flags={flags}")
