@@ -202,3 +202,68 @@ def test_rows_special_values(g, orc, dtype):
                               round_intermediate=flags & FLAG_RI,
                               norm_before_gate=bool(flags & FLAG_NBG))
             assert_parity(host_bits(od, dtype), ref, dtype, f"rows special eps={eps} flags={flags}")
+
+
+def _draw_rows_case(i: int) -> dict:
+    """A seeded random forced-ROWS configuration: a group of 16-byte vectors
+    that some built lanes x vectors pair covers, 1-3 groups per row, rows
+    around one and two workgroups' worth, 16-byte aligned strided views, both
+    operators and both cache policies."""
+    rng = np.random.default_rng(20261203 + 104729 * i)
+    dtype = int(rng.choice([F32, F16, BF16]))
+    per_vec = 4 if dtype == F32 else 8
+    nvec = int(rng.integers(1, 1025))
+    pairs = [(256, 3), (320, 2), (384, 2), (448, 2), (512, 2)]
+    lanes, vpt = pairs[int(rng.integers(0, len(pairs)))]
+    nvec = min(nvec, lanes * vpt)
+    groups = int(rng.integers(1, 4))
+    rows = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(200, 600))]))
+    nbg = bool(rng.random() < 0.3)
+    ri = 0 if (nbg or dtype == F32) else int(rng.random() < 0.7)
+    per_group = bool(groups > 1 and rng.random() < 0.3)
+    flags = ((FLAG_RI if ri else 0) | (FLAG_NBG if nbg else 0) |
+             (FLAG_PER_GROUP if per_group else 0) | int(rng.choice([0, FLAG_STREAM, FLAG_KEEP])))
+    pad = [int(v) * per_vec for v in rng.integers(0, 3, 3)]  # row strides stay 16-byte multiples
+    return dict(dtype=dtype, G=nvec * per_vec, groups=groups, rows=rows, flags=flags, ri=ri,
+                shape=(lanes, vpt, 0, 0, KERNEL_ROWS), pads=pad,
+                eps=float(rng.choice([1e-5, 1e-6, 0.1])))
+
+
+N_ROWS_CASES = 24
+
+
+@pytest.mark.parametrize("i", range(N_ROWS_CASES))
+def test_rows_random_forced(g, orc, i):
+    c = _draw_rows_case(i)
+    dtype, G, rows = c["dtype"], c["G"], c["rows"]
+    width = G * c["groups"]
+    sy, sg, so = (width + p for p in c["pads"])
+    say(f"case rows random {i}: dtype={DT_IDS[dtype]} G={G}x{c['groups']} rows={rows} "
+        f"flags={c['flags']} shape={c['shape']} strides={(sy, sg, so)}")
+    n_y, n_g, n_o = ((rows - 1) * s + width for s in (sy, sg, so))
+    seed = 9500 + i
+    y = S.tensor(seed, S.TID_Y, n_y, dtype, ("normal", 1.0))
+    gt = S.tensor(seed, S.TID_GATE, n_g, dtype, ("normal", 2.0))
+    w = S.tensor(seed, S.TID_W, width, F32, ("uniform", 0.5, 1.5))
+    if c["flags"] & FLAG_PER_GROUP:
+        w = np.ascontiguousarray(w[:G])
+    canary = {F32: np.float32(-1234.5), F16: np.uint16(0x7BFF), BF16: np.uint16(0x4B4B)}[dtype]
+    ob = np.full(n_o, canary, dtype=S.storage_dtype(dtype))
+    yd, gd, od = dev_buf(y, dtype), dev_buf(gt, dtype), dev_buf(ob, dtype)
+    wd = torch.from_numpy(w).cuda()
+    st = run_gpu(g, yd, gd, wd, od, rows, width, G, sy, sg, so, c["eps"], dtype, c["ri"],
+                 shape=c["shape"], flags=c["flags"])
+    assert st == g.SUCCESS, g.ggrms_status_string(st)
+    torch.cuda.synchronize()
+    got = host_bits(od, dtype)
+    ref = ob.copy()
+    orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=sy,
+                gate_row_stride=sg, out_row_stride=so, eps=c["eps"], dtype=dtype,
+                round_intermediate=c["ri"], norm_before_gate=bool(c["flags"] & FLAG_NBG),
+                weight_per_group=bool(c["flags"] & FLAG_PER_GROUP), out=ref)
+    view = np.zeros(n_o, dtype=bool)
+    for r in range(rows):
+        view[r * so:r * so + width] = True
+    bits = np.uint32 if dtype == F32 else np.uint16
+    assert np.array_equal(got[~view].view(bits), ob[~view].view(bits)), "padding written"
+    assert_parity(got[view], ref[view], dtype, f"rows random {i}")
