@@ -237,7 +237,8 @@ def bench_decode(torch, g, S, bursts, eager_only=False):
     C through libggrms.so (libggrms_bench.so's loop: no interpreter between
     launches), timed with events around each burst; eager and as one replayed
     HIP graph; next to an empty kernel launched with the same grid the same
-    ways.  Also: the same bursts with the streaming cache hint forced (the
+    ways; and the graph replayed back to back (the graph's start-up overlapping
+    the previous replay).  Also: the same bursts with the streaming cache hint forced (the
     default keeps a job this small cached), and the eager burst issued from
     Python through the ctypes binding, for context."""
     w = S.WORKLOADS[DECODE]
@@ -278,6 +279,8 @@ def bench_decode(torch, g, S, bursts, eager_only=False):
         return res
     graph, _ = native(1, flags)
     floor_graph, _ = native(3, flags)
+    graph_b2b, _ = native(4, flags)
+    floor_graph_b2b, _ = native(5, flags)
     eager_nt, _ = native(0, flags | g.FLAG_CACHE_STREAM)
     graph_nt, _ = native(1, flags | g.FLAG_CACHE_STREAM)
 
@@ -309,6 +312,11 @@ def bench_decode(torch, g, S, bursts, eager_only=False):
         "floor_host_us_per_call": floor_host,
         "us_per_launch_graph": graph,
         "floor_us_per_launch_graph": floor_graph,
+        # the graph replayed back to back (each replay's start overlapping the
+        # previous one's tail), per launch; the figure above times each replay
+        # alone, its start-up included
+        "us_per_launch_graph_back_to_back": graph_b2b,
+        "floor_us_per_launch_graph_back_to_back": floor_graph_b2b,
         "us_per_launch_eager_streamed": eager_nt,
         "us_per_launch_graph_streamed": graph_nt,
         "us_per_launch_eager_python": py_eager,

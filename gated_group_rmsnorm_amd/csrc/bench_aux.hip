@@ -140,14 +140,18 @@ struct BurstRes {
 // 1: the same burst captured once and replayed as a HIP graph; 2 and 3: the
 // empty kernel with the fused launch's grid, eager and graph.  Device time
 // comes from events around each burst (median burst / layers); host time is
-// the steady-clock time of enqueueing one burst (median / layers).
+// the steady-clock time of enqueueing one burst (median / layers).  Modes 4
+// and 5 (fused, empty): the graph replayed `bursts` times back to back between
+// two events, so that each replay's start overlaps the previous one's tail
+// as in a decode loop that does not wait for every token (median of 7 such
+// runs / (bursts * layers); host time 0).
 // Returns 0, or a ggrms status / -1 for a HIP error.
 extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const* gate,
                                          const float* const* w, void* const* out, int layers,
                                          int64_t width, int64_t group_size, float eps, int dtype,
                                          uint32_t flags, const ggrms_shape_t* shape,
                                          int bursts, int mode, double* dev_us, double* host_us) {
-    if (layers <= 0 || bursts <= 0 || mode < 0 || mode > 3) return GGRMS_ERROR_INVALID_VALUE;
+    if (layers <= 0 || bursts <= 0 || mode < 0 || mode > 5) return GGRMS_ERROR_INVALID_VALUE;
     ggrms_plan_t plan;
     const int st = ggrms_plan_tuned(y[0], gate[0], w[0], out[0], 1, width, group_size, width,
                                     width, width, eps, (ggrms_dtype_t)dtype, flags, shape, &plan);
@@ -156,7 +160,7 @@ extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const
     if (hipStreamCreate(&r.s) != hipSuccess || hipEventCreate(&r.e0) != hipSuccess ||
         hipEventCreate(&r.e1) != hipSuccess)
         return -1;
-    const bool empty = mode >= 2;
+    const bool empty = mode == 2 || mode == 3 || mode == 5;
     auto burst = [&]() -> int {
         for (int l = 0; l < layers; ++l) {
             if (empty) {
@@ -170,7 +174,7 @@ extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const
         }
         return 0;
     };
-    const bool graphed = mode == 1 || mode == 3;
+    const bool graphed = mode == 1 || mode == 3 || mode >= 4;
     if (graphed) {
         if (hipStreamBeginCapture(r.s, hipStreamCaptureModeThreadLocal) != hipSuccess) return -1;
         const int rc = burst();
@@ -190,6 +194,22 @@ extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const
         if (hipStreamSynchronize(r.s) != hipSuccess) return -1;
     }
     std::vector<double> dev, host;
+    if (mode >= 4) {
+        for (int rep = 0; rep < 7; ++rep) {
+            if (hipStreamSynchronize(r.s) != hipSuccess || hipEventRecord(r.e0, r.s) != hipSuccess)
+                return -1;
+            for (int b = 0; b < bursts; ++b)
+                if (const int rc = run()) return rc;
+            float ms = 0.0f;
+            if (hipEventRecord(r.e1, r.s) != hipSuccess || hipEventSynchronize(r.e1) != hipSuccess ||
+                hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess)
+                return -1;
+            dev.push_back(ms * 1e3 / ((double)bursts * layers));
+        }
+        *dev_us = median_of(dev);
+        *host_us = 0.0;
+        return 0;
+    }
     for (int b = 0; b < bursts; ++b) {
         if (hipStreamSynchronize(r.s) != hipSuccess || hipEventRecord(r.e0, r.s) != hipSuccess)
             return -1;
