@@ -408,7 +408,8 @@ def native_job_us(setup, kind, launches, bursts=20):
     (libggrms_bench.so's ggrms_bench_job_native) over the setup's rotating
     buffer sets, median of `bursts` runs: kind 0 the fused kernel (the
     library's own launch choice), kind 1 the plain two-read-one-write kernel
-    over the same bytes (y and gate read, out written).  Issued from C, a small
+    over the same views (y and gate read, out written; strided rows where the
+    views are strided, e.g. column slices of one fused buffer).  Issued from C, a small
     job's figure is the GPU's: from Python each launch costs about 4 us of
     interpreter and ctypes time, as long as the strided workload's kernel."""
     aux = ctypes.CDLL(os.path.join(ROOT, "gated_group_rmsnorm_amd", "libggrms_bench.so"))
@@ -581,8 +582,8 @@ EVIDENCE = {
     "g8192": (2, 7680, 8192, 8192, 1, None),
     "g8192_block": (2, 7680, 8192, 8192, 1, (256, 4, 1)),
     # 100-wide fp16 groups (200 bytes: packed 16-byte vectors), one vector per
-    # lane on 16 lanes (the default for a job this size) and two vectors per
-    # lane on 8 lanes (the default for jobs resident at once)
+    # lane on 16 lanes (the library's shape) and two vectors per lane on 8
+    # lanes (boundary vectors in pieces)
     "packed_g100": (1, 13107, 4800, 100, 1, None),
     "packed_g100_8x2": (1, 13107, 4800, 100, 1, (8, 2)),
     # the same groups in runs of 5 per wave (one vector per lane)

@@ -57,6 +57,25 @@ __global__ __launch_bounds__(64) void ggrms_bench_stream3_kernel(const u32x4* __
     }
 }
 
+// The same over rows x vpr 16-byte vectors of three strided views (row
+// strides in 16-byte units): flat vector i is row i / vpr (a round-up
+// magic-number division, m and sh from the host) and vector i % vpr of it.
+// For views that are column slices of one wider buffer this reads exactly
+// the bytes a fused launch over them reads, where the flat form would read
+// two overlapping stretches of the buffer.
+__global__ __launch_bounds__(64) void ggrms_bench_stream3_rows_kernel(
+    const u32x4* __restrict__ a, const u32x4* __restrict__ b, u32x4* __restrict__ c, uint32_t n,
+    uint32_t vpr, uint32_t m, uint32_t sh, uint64_t sa, uint64_t sb, uint64_t sc) {
+    const uint32_t i = blockIdx.x * 64u + threadIdx.x;
+    if (i < n) {
+        const uint32_t r = (__umulhi(i, m) + i) >> sh;
+        const uint32_t v = i - r * vpr;
+        const u32x4 x = __builtin_nontemporal_load(a + r * sa + v);
+        const u32x4 y = __builtin_nontemporal_load(b + r * sb + v);
+        __builtin_nontemporal_store(x ^ y, c + r * sc + v);
+    }
+}
+
 }  // namespace
 
 extern "C" int ggrms_bench_empty(int64_t blocks, int threads, void* stream) {
@@ -103,6 +122,39 @@ extern "C" int ggrms_bench_stream3(const void* a, const void* b, void* c, int64_
     void* args[] = {&pa, &pb, &pc, (void*)&n};
     return hipLaunchKernel(reinterpret_cast<const void*>(&ggrms_bench_stream3_kernel),
                            dim3((uint32_t)blocks), dim3(64), args, 0,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
+               ? 0
+               : 1;
+}
+
+// c = a ^ b over [rows, row_bytes] views with row strides sa, sb, sc in bytes
+// (row_bytes and the strides multiples of 16, row_bytes <= each stride when
+// rows > 1; 16-byte aligned pointers; rows * row_bytes / 16 < 2^31).
+extern "C" int ggrms_bench_stream3_rows(const void* a, const void* b, void* c, int64_t rows,
+                                        int64_t row_bytes, int64_t sa, int64_t sb, int64_t sc,
+                                        void* stream) {
+    if (rows <= 0 || row_bytes <= 0 || row_bytes % 16 || sa % 16 || sb % 16 || sc % 16 ||
+        (uintptr_t)a % 16 || (uintptr_t)b % 16 || (uintptr_t)c % 16)
+        return 1;
+    if (rows > 1 && (sa < row_bytes || sb < row_bytes || sc < row_bytes)) return 1;
+    const uint64_t vpr = (uint64_t)row_bytes / 16;
+    if ((uint64_t)rows * vpr >= (1ull << 31)) return 1;
+    const uint32_t n = (uint32_t)(rows * vpr);
+    // x / vpr = (umulhi(x, m) + x) >> l, l = ceil(log2 vpr),
+    // m = floor(2^32 (2^l - vpr) / vpr) + 1: exact for x < 2^31
+    uint32_t l = 0;
+    while ((1ull << l) < vpr) ++l;
+    const uint32_t m = (uint32_t)(((1ull << 32) * ((1ull << l) - vpr)) / vpr + 1);
+    const uint32_t d = (uint32_t)vpr;
+    const uint64_t va = (uint64_t)sa / 16, vb = (uint64_t)sb / 16, vc = (uint64_t)sc / 16;
+    const u32x4* pa = static_cast<const u32x4*>(a);
+    const u32x4* pb = static_cast<const u32x4*>(b);
+    u32x4* pc = static_cast<u32x4*>(c);
+    uint32_t mm = m, ll = l;
+    void* args[] = {&pa, &pb, &pc, (void*)&n, (void*)&d, &mm, &ll,
+                    (void*)&va, (void*)&vb, (void*)&vc};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&ggrms_bench_stream3_rows_kernel),
+                           dim3((n + 63) / 64), dim3(64), args, 0,
                            static_cast<hipStream_t>(stream)) == hipSuccess
                ? 0
                : 1;
@@ -234,9 +286,10 @@ extern "C" int ggrms_bench_decode_native(const void* const* y, const void* const
 // out[i]; one weight), timed between two events on a stream of its own, after
 // about 100 ms of the same untimed; `bursts` such runs, median per launch.
 // kind 0: ggrms_forward_tuned with `flags` / `shape` over [rows, width] views
-// with the given row strides; kind 1: the plain two-read-one-write kernel
-// (ggrms_bench_stream3) over nbytes = rows * width * element bytes per stream,
-// y[i] and gate[i] read, out[i] written.  Returns 0, a ggrms status, or -1 for
+// with the given row strides; kind 1: the plain two-read-one-write kernel over
+// the same views, y[i] and gate[i] read, out[i] written (ggrms_bench_stream3
+// over rows * width * element bytes per stream when all three are
+// contiguous, ggrms_bench_stream3_rows over the strided rows otherwise).  Returns 0, a ggrms status, or -1 for
 // a HIP error.
 extern "C" int ggrms_bench_job_native(const void* const* y, const void* const* gate,
                                       const float* w, void* const* out, int sets, int64_t rows,
@@ -254,7 +307,15 @@ extern "C" int ggrms_bench_job_native(const void* const* y, const void* const* g
         return -1;
     auto one = [&](int i) -> int {
         const int k = i % sets;
-        if (kind == 1) return ggrms_bench_stream3(y[k], gate[k], out[k], nbytes, r.s) ? -1 : 0;
+        if (kind == 1) {
+            if (y_row_stride == width && gate_row_stride == width && out_row_stride == width)
+                return ggrms_bench_stream3(y[k], gate[k], out[k], nbytes, r.s) ? -1 : 0;
+            return ggrms_bench_stream3_rows(y[k], gate[k], out[k], rows, width * esize,
+                                            y_row_stride * esize, gate_row_stride * esize,
+                                            out_row_stride * esize, r.s)
+                       ? -1
+                       : 0;
+        }
         return ggrms_forward_tuned(y[k], gate[k], w, out[k], rows, width, group_size, y_row_stride,
                                    gate_row_stride, out_row_stride, eps, (ggrms_dtype_t)dtype,
                                    flags, shape, r.s);

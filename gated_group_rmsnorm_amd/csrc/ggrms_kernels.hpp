@@ -737,7 +737,8 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
         GG_W(1, 1); GG_W(2, 1); GG_W(4, 1); GG_W(8, 1); GG_W(16, 1); GG_W(32, 1);
         GG_W(64, 1); GG_W(64, 2); GG_W(64, 3); GG_W(64, 4);
         // packed groups: two vectors per lane on half the lanes (the same
-        // slots), so each wave's fixed work covers twice the elements
+        // slots; each wave's fixed work over twice the elements, every
+        // boundary vector stored in pieces), for forced shapes
         if constexpr (kPacked) {
             GG_W(8, 2); GG_W(16, 2); GG_W(32, 2);
         }

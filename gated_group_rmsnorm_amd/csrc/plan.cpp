@@ -325,24 +325,17 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         if (vpt > 2) rule_upb = 1;
     } else {
         choose_shape(nvec, &kernel, &lanes, &vpt, &rule_upb);
-        // Packed groups of 9-64 vectors in a job small enough to be resident at
-        // once (at most kSmallJobWaves waves): the same slots as half the lanes
-        // with two vectors each, which spreads each wave's fixed work
-        // (indexing, the sum across lanes, the normaliser, the boundary pieces)
-        // over twice the elements -- such a job is one round of loads followed
-        // by its arithmetic, which no other wave's loads hide (the strided 256 x
-        // 4800 fp16 job: 4.02 against 4.65 us).  In larger jobs each load
-        // instruction would then touch twice the cache lines, half of each
-        // (377 MB of 100-wide fp16 groups: 104.6 against 63.1 us for one
-        // vector per lane with boundaries merged inside the wave), so they keep
-        // one vector per lane.
+        // Packed groups keep one vector per lane on their lane segment, with
+        // the boundary vectors inside a wave merged, in small jobs too: half
+        // the lanes with two vectors each (the same slots, each wave's fixed
+        // work over twice the elements) stores every boundary vector in
+        // pieces, and lost on two machines for the strided 256 x 4800 fp16 job
+        // (4.17 and 3.96 us against 3.90 and 3.67 for 16 x 1; with the
+        // two-vector boundaries merged too, 4.45 and 4.43).  Jobs resident at
+        // once (at most kSmallJobWaves waves) do not take runs either.
         const bool small_job = rows * plan->groups * lanes <= kSmallJobWaves * 64;
-        if (packed && kernel == GGRMS_KERNEL_WAVE && small_job && lanes >= 16 && lanes <= 64 &&
-            vpt == 1) {
-            lanes /= 2;
-            vpt = 2;
-        } else if (packed && kernel == GGRMS_KERNEL_WAVE && !small_job && run_fits &&
-                   2 * gpw * gbytes >= 64 * 16 && 10 * gbytes < 6 * 16 * lanes && vpt == 1) {
+        if (packed && kernel == GGRMS_KERNEL_WAVE && !small_job && run_fits &&
+            2 * gpw * gbytes >= 64 * 16 && 10 * gbytes < 6 * 16 * lanes && vpt == 1) {
             // Larger jobs of packed groups that fill less than 60% of their
             // lane segment (groups just over a power of two of vectors): runs
             // of groups per wave, one vector per lane over a contiguous
@@ -399,8 +392,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     // whose slot is freed the moment it retires (128-wide groups: 0.83
     // against 0.79 of HBM peak with four; 377 MB of 100-wide packed fp16
     // groups: 62.7 against 67.7 us; the strided 256 x 4800 fp16 job: equal
-    // with 16 x 1, 4.19 against 4.61 us with 8 x 2 before the boundary
-    // merge); four waves for narrower
+    // with 16 x 1, before the boundary merge); four waves for narrower
     // vectors, which need 2-4x the workgroups for the same bytes (4-byte
     // vectors: 96 against 107 us with one).
     bool four = kernel == GGRMS_KERNEL_WAVE && vb < 16;

@@ -305,21 +305,20 @@ def test_tile_order_and_wave_workgroups(g):
     # WIDE is always row-major
     assert plan(RI | BANDED, 4, 3 * 40960, 40960)["tile_order"] == 0
     # packed groups (200-byte groups of the strided layout, a job of 3072 waves at 16
-    # lanes per group, resident at once): 8 lanes x 2 vectors per group in one-wave
-    # workgroups of 8 groups, 6 per row, banded; four waves if forced (2 tiles per
-    # row, the second half full); row-major if forced
+    # lanes per group, resident at once): 16 lanes x 1 vector per group in one-wave
+    # workgroups of 4 groups, 12 per row, banded (800-byte tiles: super-tiles of 4,
+    # 3200 bytes, 25 cache lines); four waves if forced (3 tiles of 3200 bytes per
+    # row); row-major if forced
     fused = dict(y=A, gate=A + 9600)
-    # (1600-byte tiles: super-tiles of 2, 25 cache lines); four waves if forced
-    # (2 tiles of 6400 bytes per row, the second half full); row-major if forced
     p = plan(RI, 256, 4800, 100, F16, stride=9856, **fused)
     assert (p["lanes_per_group"], p["vectors_per_lane"], p["piece_bytes"], p["block_threads"],
-            p["tile_order"], p["super_tile"], p["workgroups"]) == (8, 2, 8, 64, 1, 2, 256 * 6)
+            p["tile_order"], p["super_tile"], p["workgroups"]) == (16, 1, 8, 64, 1, 4, 256 * 12)
     p = plan(RI | WAVE4, 256, 4800, 100, F16, stride=9856, **fused)
     assert (p["block_threads"], p["tile_order"], p["super_tile"], p["workgroups"]) == \
-        (256, 1, 1, 256 * 2)
+        (256, 1, 1, 256 * 3)
     p = plan(RI | ROWS, 256, 4800, 100, F16, stride=9856, **fused)
     assert (p["block_threads"], p["tile_order"], p["super_tile"], p["workgroups"]) == \
-        (64, 0, 1, 256 * 48 * 8 // 64)
+        (64, 0, 1, 256 * 48 * 16 // 64)
     # a larger packed job (12288 waves): 16 lanes x 1 vector per group (8-byte
     # pieces), 800-byte tiles in super-tiles of 4 (3200 bytes, 25 lines)
     p = plan(RI, 1024, 4800, 100, F16, stride=9856, **fused)
@@ -468,14 +467,13 @@ def test_plans_for_the_workloads(g):
     assert st == OK and (p["block_threads"], p["workgroups"], p["tile_order"]) == (64, 16384 * 16, 0)
     # 256x4800 fp16 slices of a [256, 9856] buffer, G = 100: 200-byte groups in 9600-byte
     # rows -> packed: 16-byte vectors from the row start, boundary vectors in 8-byte pieces;
-    # a group touches at most ceil((8 + 200) / 16) = 13 vectors -> 16 slots, as
-    # 8 lanes with 2 vectors each
+    # a group touches at most ceil((8 + 200) / 16) = 13 vectors -> 16 lanes with one
+    # vector each, boundary vectors inside a wave merged
     p = _plan(g, 256, 4800, 100, F16, sy=9856, sg=9856, y=A, gate=A + 9600)
     assert (p["kernel_name"], p["vector_bytes"], p["piece_bytes"], p["lanes_per_group"],
-            p["vectors_per_lane"]) == ("wave", 16, 8, 8, 2)
-    # packed groups in a job resident at once: 8 lanes x 2 vectors per group, one-wave
-    # workgroups of 8 groups, 6 per row -> banded
-    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (64, 256 * 6, 1)
+            p["vectors_per_lane"]) == ("wave", 16, 8, 16, 1)
+    # one-wave workgroups of 4 groups, 12 per row -> banded
+    assert (p["block_threads"], p["workgroups"], p["tile_order"]) == (64, 256 * 12, 1)
     # tiny f32, G = 64: 16 vectors
     p = _plan(g, 4, 256, 64, F32)
     assert (p["vector_bytes"], p["lanes_per_group"]) == (16, 16)

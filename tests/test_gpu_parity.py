@@ -464,9 +464,9 @@ def test_runs_in_place_and_by_default(g, orc):
 def test_packed_in_place_over_the_gate(g, orc, shape):
     """The strided layout (y and gate column slices of one fused fp16 buffer,
     200-byte groups) normalised in place over the gate: a vector on a group
-    boundary is read by two units while each writes its own pieces (the
-    library's 8 x 2 shape for this small job), or while the left unit's lane
-    writes it whole for both (16 x 1, boundaries merged inside a wave)."""
+    boundary is read by two units while each writes its own pieces, or while
+    the left unit's lane writes it whole for both (16 x 1, boundaries merged
+    inside a wave: the library's shape for this job)."""
     rows, width, G, fused = 64, 4800, 100, 9856
     buf = S.tensor(91, S.TID_Y, rows * fused, F16, ("normal", 1.0))
     w = S.tensor(91, S.TID_W, width, F32, ("uniform", 0.5, 1.5))
