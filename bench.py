@@ -482,7 +482,7 @@ SHAPES = [
     ("f32 G128 heads, shared head weight", 0, 128, 4096, 4),
     ("fp16 G100 packed groups, per-column weight", 1, 100, 4800, 1),
     ("bf16 G99 packed groups (2-byte pieces)", 2, 99, 4752, 1),
-    ("bf16 G127 packed groups (runs of 3)", 2, 127, 6096, 1),
+    ("bf16 G127 packed groups (runs of 8)", 2, 127, 6096, 1),
     ("fp16 G250 packed groups (4-byte pieces)", 1, 250, 12000, 1),
     # the same groups in rows padded by 4 elements: rows not 16-byte aligned,
     # so the whole group falls back to 8-byte vectors
@@ -586,15 +586,17 @@ EVIDENCE = {
     # lanes (boundary vectors in pieces)
     "packed_g100": (1, 13107, 4800, 100, 1, None),
     "packed_g100_8x2": (1, 13107, 4800, 100, 1, (8, 2)),
-    # the same groups in runs of 5 per wave (one vector per lane)
+    # the same groups in runs of 5 per wave (one vector per lane) and of 10
+    # (two vectors per lane, every run on a vector boundary)
     "packed_g100_run": (1, 13107, 4800, 100, 1, (64, 1, 0, 0, 4)),
+    "packed_g100_run2": (1, 13107, 4800, 100, 1, (64, 2, 0, 0, 4)),
     # 16 x 1 in four-wave workgroups (16 groups = 3200 bytes, whole 128-byte
     # lines, per workgroup), and both workgroup sizes in row-major order
     "packed_g100_four": (1, 13107, 4800, 100, 1 | 256, None),
     "packed_g100_rows": (1, 13107, 4800, 100, 1 | 32, None),
     "packed_g100_rows_four": (1, 13107, 4800, 100, 1 | 32 | 256, None),
-    # 127-wide bf16 groups (15.9 vectors on 32 lanes): runs of 3 (the default)
-    # and the 32-lane segments
+    # 127-wide bf16 groups (15.9 vectors on 32 lanes): runs of 8 on two vectors
+    # per lane (the default) and the 32-lane segments
     "packed_g127_run": (2, 10320, 6096, 127, 1, None),
     "packed_g127_wave": (2, 10320, 6096, 127, 1, (32, 1)),
 }

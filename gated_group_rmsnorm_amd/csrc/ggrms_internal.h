@@ -71,14 +71,14 @@ constexpr uint32_t kXcds = 8;
 // 1 for lanes < 64 (also 2 with 8, 16 or 32 lanes for packed groups), 1..4
 // for lanes == 64.  BLOCK: lanes in {128,256,512,1024},
 // vectors per lane 1..4, and 6 with 256 lanes.  WIDE: 1024 lanes, vectors per
-// lane 0 (it loops over the group).  RUN: 64 lanes, one vector each, over a
-// run of packed groups.  ROWS: 256 lanes x 3 vectors, or 320, 384, 448 or
+// lane 0 (it loops over the group).  RUN: 64 lanes, one or two vectors each,
+// over a run of packed groups.  ROWS: 256 lanes x 3 vectors, or 320, 384, 448 or
 // 512 lanes x 2 (16-byte vectors, not packed).  A WAVE workgroup is a single wave or 4
 // waves (the kernel takes its size from the launch; the planner's rule says
 // which).
 constexpr int kWaveBlock = 256;
-// Most groups one RUN wave takes (its loop over the groups' sums is unrolled).
-constexpr int kRunMaxGroups = 8;
+// Most groups one RUN wave takes (one lane per group forms the groups' sums).
+constexpr int kRunMaxGroups = 32;
 constexpr int kWaveBlockOneWave = 64;
 constexpr int kWideBlock = 1024;
 // ROWS: one workgroup per compute unit of the part (gfx950: 256), taken for
@@ -110,7 +110,7 @@ inline bool shape_supported(int kernel, int lanes, int vpt) {
     case GGRMS_KERNEL_WIDE:
         return lanes == kWideBlock;
     case GGRMS_KERNEL_RUN:
-        return lanes == 64 && vpt == 1;
+        return lanes == 64 && (vpt == 1 || vpt == 2);
     case GGRMS_KERNEL_ROWS:
         return (lanes == 256 && vpt == 3) ||
                ((lanes == 320 || lanes == 384 || lanes == 448 || lanes == 512) && vpt == 2);

@@ -443,18 +443,27 @@ __global__ __launch_bounds__(SEG * UPB) void ggrms_block_kernel(KArgs a) {
     });
 }
 
-// RUN: one wave takes a run of up to gpw = a.nvec consecutive packed groups of
-// one row (tile (row, run) of the job's rows x runs_per_row = a.xc tiles),
-// one 16-byte vector per lane, the vectors counted from the row start, so the
-// lanes load one contiguous stretch: 100-wide fp16 groups (12.5 vectors) fill
-// 63 of 64 lanes five groups at a time, where 16-lane segments per group fill
-// 13 of 16 and load every boundary vector twice.  A vector on a group
-// boundary holds pieces of two groups, whose sums are kept apart
-// (gate_and_square2); each group's sum over the wave is a 64-lane sum of the
-// lanes' shares for that group (every lane adds its share or 0, in a fixed
-// order); the pieces are then normalised with their own group's nf and
-// stored, a vector whose pieces belong to groups of two runs in pieces.
-template <class T, int PB, bool NBG, bool NT>
+// RUN: one wave takes a run of gpw = a.nvec consecutive packed groups of one
+// row (tile (row, run) of the job's rows x runs_per_row = a.xc tiles), VPT
+// 16-byte vectors per lane (vector i of the run on lane i % 64, slot i / 64,
+// so every load instruction covers 64 consecutive vectors), the vectors
+// counted from the row start.  100-wide fp16 groups (12.5 vectors) fill 125
+// of 128 slots ten groups at a time, where 16-lane segments per group fill 13
+// of 16 and load every boundary vector twice; when gpw groups span a whole
+// number of vectors (the planner's choice where it can), every run starts on
+// a vector boundary and the wave stores whole vectors only.  A vector on a
+// group boundary holds pieces of two groups, whose sums are kept apart
+// (gate_and_square2).  The groups' sums meet in LDS: each lane parks its
+// slots' two shares, then lane j adds group j's shares in vector order (the
+// piece of its first vector that follows the boundary, then the first share
+// of each vector that starts inside the group), forms its normaliser and
+// parks it; every lane reads back the normalisers of its pieces' groups.
+// The vectors and their order depend on the group alone, so any run length
+// gives the same bits.
+// The workgroup is one wave, so its two barriers only order the LDS
+// accesses.  A vector whose pieces belong to groups of two runs is stored in
+// pieces by both waves.
+template <class T, int PB, int VPT, bool NBG, bool NT>
 __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
     constexpr int VB = 16;
     using P = Packet<T, VB>;
@@ -464,6 +473,9 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
     constexpr int NP = VB / PB;        // pieces per vector
     static_assert(PB < VB, "runs are built for packed groups");
     using S = typename VecWord<T::kSize>::type;
+    __shared__ float share0[64 * VPT], share1[64 * VPT];
+    __shared__ float nfs[kRunMaxGroups];
+    fetch_args_together(a);
 
     uint32_t n, c;  // row, run
     if (banded(a)) {
@@ -478,66 +490,92 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
     const int64_t e0 = (int64_t)g0 * a.G;                // the run's first element in the row
     const int64_t e1 = e0 + (int64_t)cnt * a.G;          // one past its last
     const uint32_t v0 = (uint32_t)(e0 / N);
-    const uint32_t nv = (uint32_t)((e1 + N - 1) / N) - v0;  // <= 64 (the planner's gpw)
+    const uint32_t nv = (uint32_t)((e1 + N - 1) / N) - v0;  // <= 64 * VPT (the planner's gpw)
+    const int32_t lead = (int32_t)(e0 - (int64_t)v0 * N);   // vector v0's elements before the run
     const uint32_t l = threadIdx.x;
-    const bool live_l = l < nv;
-    const uint32_t v = v0 + (live_l ? l : nv - 1);
-    // k: the group (relative to g0) of the vector's first element, -1 for a
-    // vector that starts in the previous run; 1/G in f32 corrected to exact
-    const int32_t off = (int32_t)((int64_t)v * N - e0);  // >= -(N - 1)
     const int32_t G = (int32_t)a.G;
-    int32_t k = -1;
-    if (off >= 0) {
-        k = (int32_t)((float)off * a.Ginv);
-        k -= k * G > off ? 1 : 0;
-        k += (k + 1) * G <= off ? 1 : 0;
-    }
-    const int32_t bnd = (k + 1) * G - off;  // elements of group k in the vector (>= N: all)
 
     const W* yv = reinterpret_cast<const W*>(static_cast<const S*>(a.y) + (int64_t)n * a.sy);
     const W* gv = reinterpret_cast<const W*>(static_cast<const S*>(a.gate) + (int64_t)n * a.sg);
-    W yr[1], gr[1];
-    float wr[1][N];
-    yr[0] = load_stream<NT>(yv + v);
-    gr[0] = load_stream<NT>(gv + v);
-    load_weights<N>(a.w + (int64_t)v * N, wr[0]);
-
-    auto live = [&](int) { return live_l; };
-    auto second = [&](int, int q) { return q * PE >= bnd; };
-    epi::LaneUnit<T, VB, 1, NBG> L;
-    float s_k, s_k1;
-    epi::gate_and_square2<T, VB, PB, 1, NBG>(yr, gr, L, live, second, s_k, s_k1);
-
-    // each group's sum over the wave; the lane keeps those of groups k, k + 1
-    float m_k = 0.0f, m_k1 = 0.0f;
+    W yr[VPT][1], gr[VPT][1];
+    float wr[VPT][1][N];
+    uint32_t vi[VPT];
+    bool lv[VPT];
+    // kv: the group (relative to g0) of the vector's first element, -1 for a
+    // vector that starts in the previous run; bnd: elements of group kv in
+    // the vector (>= N: all of them)
+    int32_t kv[VPT], bnd[VPT];
 #pragma unroll
-    for (int j = 0; j < kRunMaxGroups; ++j) {
-        if (j >= cnt) break;
-        const float share = k == j ? s_k : (k + 1 == j ? s_k1 : 0.0f);
-        const float m = segment_sum<64>(share);
-        m_k = k == j ? m : m_k;
-        m_k1 = k + 1 == j ? m : m_k1;
+    for (int k = 0; k < VPT; ++k) {
+        const uint32_t idx = l + 64u * k;
+        lv[k] = idx < nv;
+        vi[k] = v0 + (lv[k] ? idx : nv - 1);
+        const int32_t off = (int32_t)((int64_t)vi[k] * N - e0);  // >= -(N - 1)
+        int32_t kk = -1;
+        if (off >= 0) {  // off / G, by the f32 reciprocal and exact corrections
+            kk = (int32_t)((float)off * a.Ginv);
+            kk -= kk * G > off ? 1 : 0;
+            kk += (kk + 1) * G <= off ? 1 : 0;
+        }
+        kv[k] = kk;
+        bnd[k] = (kk + 1) * G - off;
+        yr[k][0] = load_stream<NT>(yv + vi[k]);
+        gr[k][0] = load_stream<NT>(gv + vi[k]);
+        load_weights<N>(a.w + (int64_t)vi[k] * N, wr[k][0]);
     }
-    const float nf_k = norm_factor(m_k, a.Ginv, a.eps);
-    const float nf_k1 = norm_factor(m_k1, a.Ginv, a.eps);
+
+    epi::LaneUnit<T, VB, 1, NBG> L[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        float s_k, s_k1;  // 0 for a slot past the run's end
+        epi::gate_and_square2<T, VB, PB, 1, NBG>(
+            yr[k], gr[k], L[k], [&](int) { return lv[k]; },
+            [&](int, int q) { return q * PE >= bnd[k]; }, s_k, s_k1);
+        share0[l + 64u * k] = s_k;
+        share1[l + 64u * k] = s_k1;
+    }
+    __syncthreads();
+    if ((int32_t)l < cnt) {
+        // group l: its first element is element s of the run's vectors
+        const int32_t s = lead + (int32_t)l * G;
+        const int32_t f = s / N, hi = (s + G - 1) / N;
+        const bool straddle = s % N != 0;  // vector f starts in group l - 1
+        float m2 = straddle ? share1[f] : 0.0f;
+        for (int32_t i = straddle ? f + 1 : f; i <= hi; ++i) m2 += share0[i];
+        nfs[l] = norm_factor(m2, a.Ginv, a.eps);
+    }
+    __syncthreads();
+    float nf_k[VPT], nf_k1[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        nf_k[k] = kv[k] >= 0 ? nfs[kv[k]] : 0.0f;
+        nf_k1[k] = kv[k] + 1 < cnt ? nfs[kv[k] + 1] : 0.0f;
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    W res[1];
-    auto nf = [&](int, int q) { return q * PE >= bnd ? nf_k1 : nf_k; };
-    if (!NBG && round_intermediate(a))
-        epi::finish_by_piece<true, PE>(L, nf, wr, res);
-    else
-        epi::finish_by_piece<false, PE>(L, nf, wr, res);
-    if (!live_l) return;
-    W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so) + v;
-    const bool own_k = k >= 0 && k < cnt, own_k1 = k + 1 < cnt;
-    if (bnd >= N ? own_k : (own_k && own_k1)) {
-        store_stream<NT>(ov, res[0]);
-    } else {
+    W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so);
+    auto store = [&](auto ri_tag) {
 #pragma unroll
-        for (int q = 0; q < NP; ++q)
-            if (q * PE >= bnd ? own_k1 : own_k)
-                store_piece_stream<NT, PB>(reinterpret_cast<char*>(ov) + q * PB, res[0], q);
-    }
+        for (int k = 0; k < VPT; ++k) {
+            W res[1];
+            auto nf = [&](int, int q) { return q * PE >= bnd[k] ? nf_k1[k] : nf_k[k]; };
+            epi::finish_by_piece<decltype(ri_tag)::value, PE>(L[k], nf, wr[k], res);
+            if (!lv[k]) continue;
+            const bool own_k = kv[k] >= 0, own_k1 = kv[k] + 1 < cnt;
+            if (bnd[k] >= N ? own_k : (own_k && own_k1)) {
+                store_stream<NT>(ov + vi[k], res[0]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < NP; ++q)
+                    if (q * PE >= bnd[k] ? own_k1 : own_k)
+                        store_piece_stream<NT, PB>(reinterpret_cast<char*>(ov + vi[k]) + q * PB,
+                                                   res[0], q);
+            }
+        }
+    };
+    if (!NBG && round_intermediate(a))
+        store(std::true_type{});
+    else
+        store(std::false_type{});
 }
 
 // ROWS: wide groups (513-1024 16-byte vectors) in large jobs.  The grid is
@@ -766,7 +804,9 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
     } else if (kernel == GGRMS_KERNEL_RUN) {
         if constexpr (kPacked) {
             if (lanes == 64 && vpt == 1 && upb == 1)
-                return reinterpret_cast<const void*>(&ggrms_run_kernel<T, PB, NBG, NT>);
+                return reinterpret_cast<const void*>(&ggrms_run_kernel<T, PB, 1, NBG, NT>);
+            if (lanes == 64 && vpt == 2 && upb == 1)
+                return reinterpret_cast<const void*>(&ggrms_run_kernel<T, PB, 2, NBG, NT>);
         }
         return nullptr;
     }

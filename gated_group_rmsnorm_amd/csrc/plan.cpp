@@ -143,6 +143,41 @@ const ShapeRule kRules[] = {
     {4096, GGRMS_KERNEL_BLOCK, 1024, 4, 1},
 };
 
+// RUN length for packed groups of gbytes bytes (pb = gcd(gbytes, 16)): the
+// groups per wave and, unless forced (force_vpt 1 or 2), the vectors per lane.
+// A run of a multiple of 16 / pb groups spans a whole number of vectors, so
+// every run of the row starts on a vector boundary and is stored in whole
+// vectors; another run takes up to ceil((16 - pb + gpw * gbytes) / 16)
+// vectors and shares a boundary vector with each neighbour.  Taken: the run
+// that fills the most of its 64 x vpt slots, an aligned run counting 0.1
+// more, two vectors per lane on a tie.  At most kRunMaxGroups groups.
+int64_t run_length(int64_t gbytes, int pb, int force_vpt, int* vpt_out) {
+    const int64_t k0 = 16 / pb;
+    double best = -1.0;
+    int64_t best_gpw = 0;
+    int best_vpt = 0;
+    for (int vpt = 2; vpt >= 1; --vpt) {
+        if (force_vpt && vpt != force_vpt) continue;
+        const int64_t cap = 64 * 16 * (int64_t)vpt;  // bytes the slots hold
+        int64_t ga = cap / gbytes;
+        if (ga > kRunMaxGroups) ga = kRunMaxGroups;
+        ga = ga / k0 * k0;
+        int64_t gm = (cap - 16 + pb) / gbytes;
+        if (gm > kRunMaxGroups) gm = kRunMaxGroups;
+        const double fa = ga >= 2 ? (double)(ga * gbytes) / (double)cap + 0.1 : -1.0;
+        const double fm = gm >= 2 ? (double)(gm * gbytes) / (double)cap : -1.0;
+        const int64_t g = fa >= fm ? ga : gm;
+        const double f = fa >= fm ? fa : fm;
+        if (f > best + 1e-9) {
+            best = f;
+            best_gpw = g;
+            best_vpt = vpt;
+        }
+    }
+    *vpt_out = best_vpt;
+    return best > 0.0 ? best_gpw : 0;
+}
+
 void choose_shape(int64_t nvec, int* kernel, int* lanes, int* vpt, int* upb) {
     if (nvec <= 64) {
         *kernel = GGRMS_KERNEL_WAVE;
@@ -286,10 +321,12 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     const bool packed = pb < vb;
     int kernel = 0, lanes = 0, vpt = 0, rule_upb = 1;
     const int force_upb = shape ? shape->rows_per_workgroup : 0;
-    // RUN: a wave takes gpw consecutive packed groups whose vectors, however the
-    // run is aligned, fit 64 lanes (ceil((16 - pb + gpw * group bytes) / 16) <= 64)
-    const int64_t gpw_fit = packed ? (64 * 16 - 16 + pb) / gbytes : 0;
-    const int64_t gpw = gpw_fit < kRunMaxGroups ? gpw_fit : kRunMaxGroups;
+    // RUN: a wave takes gpw consecutive packed groups of a row on run_vpt
+    // vectors per lane (forced: the shape's, if it gives one).
+    const int force_run_vpt =
+        shape && shape->kernel == GGRMS_KERNEL_RUN ? shape->vectors_per_lane : 0;
+    int run_vpt = 0;
+    const int64_t gpw = packed ? run_length(gbytes, pb, force_run_vpt, &run_vpt) : 0;
     const bool run_fits = packed && gpw >= 2 && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP);
     // ROWS needs 16-byte vectors that are not packed and a launch of
     // 32-bit row indices
@@ -307,11 +344,13 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         kernel = GGRMS_KERNEL_ROWS;
     } else if (shape && shape->kernel == GGRMS_KERNEL_RUN) {
         if (!run_fits || !(shape->lanes_per_group == 0 || shape->lanes_per_group == 64) ||
-            !(shape->vectors_per_lane == 0 || shape->vectors_per_lane == 1) || force_upb > 1)
+            !(shape->vectors_per_lane == 0 || shape_supported(GGRMS_KERNEL_RUN, 64,
+                                                              shape->vectors_per_lane)) ||
+            force_upb > 1)
             return GGRMS_ERROR_NOT_SUPPORTED;
         kernel = GGRMS_KERNEL_RUN;
         lanes = 64;
-        vpt = 1;
+        vpt = run_vpt;
     } else if (shape && (shape->lanes_per_group != 0 || shape->vectors_per_lane != 0)) {
         kernel = kernel_for_shape(shape->lanes_per_group, shape->vectors_per_lane);
         lanes = shape->lanes_per_group;
@@ -334,21 +373,29 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         // two-vector boundaries merged too, 4.45 and 4.43).  Jobs resident at
         // once (at most kSmallJobWaves waves) do not take runs either.
         const bool small_job = rows * plan->groups * lanes <= kSmallJobWaves * 64;
-        if (packed && kernel == GGRMS_KERNEL_WAVE && !small_job && run_fits &&
-            2 * gpw * gbytes >= 64 * 16 && 10 * gbytes < 6 * 16 * lanes && vpt == 1) {
+        if (packed && kernel == GGRMS_KERNEL_WAVE && !small_job && run_fits && lanes < 64 &&
+            2 * gpw * gbytes >= 64 * 16 * run_vpt && 10 * gbytes < 6 * 16 * lanes && vpt == 1) {
             // Larger jobs of packed groups that fill less than 60% of their
-            // lane segment (groups just over a power of two of vectors): runs
-            // of groups per wave, one vector per lane over a contiguous
+            // lane segment (groups just over a power of two of vectors, or
+            // a few vectors): runs of groups per wave over a contiguous
             // stretch of the row, as long as the run fills at least half of
-            // the wave.  377 MB of 127-wide bf16 groups (15.9 vectors on 32
-            // lanes): 86.6 against 93.4 us.  Fuller segments stay ahead, the
-            // per-group sums over the wave costing more than the idle lanes
-            // save (99-wide bf16, 12.4 vectors on 16 lanes: 71.4 against
-            // 73.8 us; 50-wide bf16: 68.1 against 78.8; 25-wide f32: 64.9
-            // against 66.8), and so do runs that would fill a fifth of the
-            // wave (13-wide bf16 groups, 8 to a run: 111 against 271 us).
+            // its slots.  377 MB of 127-wide bf16 groups (15.9 vectors on 32
+            // lanes): 70.4 us in runs of 8 with two vectors per lane (every
+            // run on a vector boundary), against 86-88 for runs of 3 with one
+            // vector per lane and 93.4 for the segments; 13-wide fp16 groups
+            // (3.25 vectors on 4 lanes): 62 us in runs of 32.  Fuller
+            // segments stay ahead (same machine; runs with one and with two
+            // vectors per lane): 100-wide fp16 63.3 against 71.2 / 69.5 us,
+            // 99-wide bf16 72.0 against 74.7 / 78.4, 50-wide bf16 67.7
+            // against 73.6 / 78.0, 25-wide f32 65.0 against 71.6 / 73.1 --
+            // except 250-wide fp16 (31.3 vectors on 32 lanes), where runs of
+            // 4 on two vectors per lane were 4% ahead (66.4 against 69.6).
+            // Groups of 33-38 vectors (64-lane segments under 60% full) stay
+            // on their segments too: 300-wide fp16 66.7 against 76.5 us for
+            // runs of 3 on two vectors per lane, 290-wide 73.7 against 78.2.
             kernel = GGRMS_KERNEL_RUN;
             lanes = 64;
+            vpt = run_vpt;
         } else if (kernel == GGRMS_KERNEL_BLOCK && rows_fit && nvec > 512 &&
                    plan->groups <= kRowsWorkgroups && rows * plan->groups >= kRowsMinUnits) {
             // Wide groups in large jobs: one workgroup per compute unit

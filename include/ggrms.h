@@ -135,7 +135,7 @@ typedef enum {
     GGRMS_KERNEL_BLOCK = 2,  /* one (row, group) across 2..16 waves; LDS combine, one barrier */
     GGRMS_KERNEL_WIDE = 3,   /* groups too wide for registers: two passes over the group */
     GGRMS_KERNEL_RUN = 4,    /* packed groups: one wave over a run of consecutive groups of a
-                                row, one vector per lane; 64-lane sums per group */
+                                row, one or two vectors per lane; group sums in LDS */
     GGRMS_KERNEL_ROWS = 5    /* wide groups in large jobs: one workgroup per compute unit
                                 takes rows of one group in turn, the next rows' inputs in
                                 flight while it stores; LDS combine, one barrier per row */
@@ -177,10 +177,11 @@ typedef struct {
  * the start of the row, a vector on a group boundary is read by both groups
  * (each uses its own elements) and written in pieces of
  * piece_bytes = gcd(group bytes, 16), so no element is written twice and no
- * read leaves the row.  In a large job, packed groups stored in 2- or 4-byte
- * pieces (RUN) are taken a run of consecutive groups per wave, the lanes
- * holding the run's vectors one each, so only the run's end vectors are
- * stored in pieces.
+ * read leaves the row.  In a large job, packed groups that would leave most
+ * of their lane segment idle (RUN) are taken a run of consecutive groups per
+ * wave, the lanes holding the run's vectors one or two each; a run of a
+ * whole number of vectors is stored in whole vectors, another one only in
+ * pieces at its two ends.
  */
 
 /*

@@ -58,7 +58,8 @@ typedef enum {
  *                     (16 also allows packed groups, see ggrms.h)
  *   kernel            0: the kernel family follows from lanes and vectors;
  *                     GGRMS_KERNEL_RUN: runs of packed groups (lanes and
- *                     vectors 0, or 64 and 1; groups of at most 32 vectors);
+ *                     vectors 0, or 64 and 1 or 2; two groups must fit in
+ *                     64 x vectors slots);
  *                     GGRMS_KERNEL_ROWS: rows in turn per workgroup, for
  *                     16-byte vectors that are not packed (lanes and vectors
  *                     0 for the library's choice, or 256 x 3, 320 x 2,

@@ -2,6 +2,7 @@
 include/ggrms_tuning.h declare, rejects bad arguments before any HIP call, and
 plans kernels as documented.  Nothing here launches a kernel or needs a GPU."""
 import ctypes
+import math
 import os
 import re
 import subprocess
@@ -338,15 +339,16 @@ def test_tile_order_and_wave_workgroups(g):
     p = plan(RI, 1024, 48 * 99, 99, BF16)
     assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["groups_per_run"],
             p["workgroups"], p["tile_order"], p["super_tile"]) == ("wave", 16, 1, 0, 1024 * 12, 1, 4)
-    # 127-wide bf16 groups (15.9 vectors on 32 lanes, half-full segments): runs of 3 groups per
-    # wave, 16 runs per row, a multiple of the 8 XCDs -> row-major
+    # 127-wide bf16 groups (15.9 vectors on 32 lanes, half-full segments): runs of 8 groups
+    # (2032 bytes, 127 vectors: two per lane, every run on a vector boundary), 6 runs per
+    # row, not a multiple of the 8 XCDs -> banded
     p = plan(RI, 1024, 48 * 127, 127, BF16)
     assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["groups_per_run"],
             p["block_threads"], p["workgroups"], p["tile_order"], p["super_tile"]) == \
-        ("run", 64, 1, 3, 64, 1024 * 16, 0, 1)
-    # 40 such groups per row: 14 runs (the last of one group) -> banded
+        ("run", 64, 2, 8, 64, 1024 * 6, 1, 1)
+    # 40 such groups per row: 5 runs -> banded
     p = plan(RI, 1024, 40 * 127, 127, BF16)
-    assert (p["kernel_name"], p["workgroups"], p["tile_order"]) == ("run", 1024 * 14, 1)
+    assert (p["kernel_name"], p["workgroups"], p["tile_order"]) == ("run", 1024 * 5, 1)
 
     # one row: banded over the row's tiles (XCD x takes a run of columns)
     p = plan(RI, 1, 7680, 128)
@@ -623,50 +625,96 @@ def test_rows_plan(g):
 
 
 def test_runs_of_packed_groups_plan(g):
-    """Runs: packed groups that fill less than 60% of their lane segment, in a
-    job of more than 4096 waves, as many groups per wave as fit 64 vectors at
-    any alignment (at most 8) when they fill at least half of the wave,
-    one-wave workgroups; forced through the tuning shape's kernel field for
-    any packed group that fits twice; refused for groups that are not packed,
-    a shared weight, or groups too wide for two per wave."""
+    """Runs: packed groups of at most 32 vectors that fill less than 60% of
+    their lane segment, in a job of more than 4096 waves, when the run fills
+    at least half of its slots; the run is the one that fills the most of its 64 x (1 or 2) slots,
+    a run that spans a whole number of vectors (a multiple of 16 / piece
+    bytes groups) counting 0.1 more, two vectors per lane on a tie, at most
+    32 groups; one-wave workgroups; forced through the tuning shape's kernel
+    field (optionally with the vectors per lane) for any packed group that
+    fits twice; refused for groups that are not packed, a shared weight, or
+    groups too wide for two per wave."""
     kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
     def plan(rows, G, dtype, groups=16, flags=RI, shape=None):
         width = G * groups
         return _plan_ex(g, flags, shape, rows=rows, width=width, group_size=G, y_row_stride=width,
                         gate_row_stride=width, out_row_stride=width, dtype=dtype, **kw)
-    # (G, dtype, groups per run, taken by default): 64 * 16 - 16 + piece bytes over the
-    # group's bytes, at most 8; by default for segments under 60% full (the group's
-    # bytes / 16 over the segment's lanes) and runs filling >= 1/2 of a wave
-    for G, dtype, gpw, default in ((100, F16, 5, False), (99, BF16, 5, False),
-                                   (50, BF16, 8, False), (127, BF16, 3, True), (250, F16, 2, False),
-                                   (25, F32, 8, False), (99, F32, 2, False), (13, F16, 8, False),
-                                   (68, F16, 7, True), (76, F16, 6, True), (84, F16, 6, False),
-                                   (140, BF16, 3, True), (150, BF16, 3, True), (180, BF16, 2, False)):
+
+    def run_rule(gb, pb, force=0):  # -> (groups per run, vectors per lane)
+        best, pick = -1.0, (0, 0)
+        for v in (2, 1):
+            if force and v != force:
+                continue
+            cap = 64 * 16 * v
+            ga = min(cap // gb, 32) // (16 // pb) * (16 // pb)
+            gm = min((cap - 16 + pb) // gb, 32)
+            fa = ga * gb / cap + 0.1 if ga >= 2 else -1.0
+            fm = gm * gb / cap if gm >= 2 else -1.0
+            cand = (fa, ga) if fa >= fm else (fm, gm)
+            if cand[0] > best + 1e-9:
+                best, pick = cand[0], (cand[1], v)
+        return pick
+
+    cases = ((100, F16), (99, BF16), (50, BF16), (127, BF16), (250, F16), (25, F32), (99, F32),
+             (13, F16), (68, F16), (76, F16), (84, F16), (140, BF16), (150, BF16), (180, BF16))
+    chosen = {}
+    for G, dtype in cases:
+        esz = 4 if dtype == F32 else 2
+        gb = G * esz
+        pb = math.gcd(gb, 16)
+        gpw, vpt = run_rule(gb, pb)
+        lanes = 1
+        while lanes < (16 - pb + gb + 15) // 16:
+            lanes *= 2
+        default = lanes < 64 and 2 * gpw * gb >= 64 * 16 * vpt and 10 * gb < 6 * 16 * lanes
         st, p = plan(8000, G, dtype, shape=(0, 0, 0, 0, KERNEL_RUN))
-        assert st == OK and (p["kernel_name"], p["groups_per_run"], p["block_threads"],
-                             p["workgroups"]) == ("run", gpw, 64, 8000 * (-(-16 // gpw))), (G, dtype, p)
-        assert p["vectors_per_lane"] == 1 and p["lanes_per_group"] == 64
-        assert plan(8000, G, dtype, shape=(64, 1, 0, 16, KERNEL_RUN))[1] == p
+        assert st == OK and (p["kernel_name"], p["groups_per_run"], p["vectors_per_lane"],
+                             p["block_threads"], p["workgroups"]) == \
+            ("run", gpw, vpt, 64, 8000 * (-(-16 // gpw))), (G, dtype, p)
+        assert p["lanes_per_group"] == 64
+        chosen[(G, dtype)] = (gpw, vpt, default)
+        assert plan(8000, G, dtype, shape=(64, vpt, 0, 16, KERNEL_RUN))[1] == p
+        for v in (1, 2):  # a forced vector count takes the best run for it
+            st, q = plan(8000, G, dtype, shape=(64, v, 0, 0, KERNEL_RUN))
+            want = run_rule(gb, pb, v)
+            if want[0] >= 2:
+                assert st == OK and (q["groups_per_run"], q["vectors_per_lane"]) == want, (G, v, q)
+            else:
+                assert st == NOTSUP, (G, v)
         assert (plan(8000, G, dtype)[1] == p) == default, (G, dtype)
-        # a small job stays on lane segments (two vectors per lane from 16 lanes); a run
-        # can be forced
+        # a small job stays on lane segments; a run can be forced
         st, q = plan(20, G, dtype)
         assert q["kernel_name"] == "wave", (G, q)
         st, q = plan(20, G, dtype, shape=(0, 0, 0, 0, KERNEL_RUN))
         assert st == OK and q["kernel_name"] == "run" and q["groups_per_run"] == gpw
-    # groups of 33+ vectors (two would not fit a wave), and groups of <= 2 vectors stay WAVE
+    # anchors: aligned runs of 10 100-wide fp16 groups (125 vectors) and of 8 127-wide
+    # bf16 groups (127 vectors) on two vectors per lane, 32 13-wide fp16 groups (52
+    # vectors) on one; only the last two by default
+    assert chosen[(100, F16)] == (10, 2, False)
+    assert chosen[(127, BF16)] == (8, 2, True)
+    assert chosen[(13, F16)] == (32, 1, True)
+    # groups of 33-38 vectors (64-lane segments under 60% full) stay WAVE by default and
+    # run three to a wave on two vectors per lane if forced; groups of <= 2 vectors stay WAVE
     assert plan(8000, 300, F16)[1]["kernel_name"] == "wave"
+    st, p = plan(8000, 300, F16, shape=(0, 0, 0, 0, KERNEL_RUN))
+    assert (p["kernel_name"], p["groups_per_run"], p["vectors_per_lane"]) == ("run", 3, 2)
     assert plan(8000, 9, BF16)[1]["kernel_name"] == "wave"
-    # refusals: aligned groups, a shared weight, a wide group, other lane shapes
+    # refusals: aligned groups, a shared weight, a group too wide for two in 128 vectors,
+    # other lane or vector shapes
     assert plan(2000, 128, F16, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 100, F16, flags=RI | PER_GROUP, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
-    assert plan(2000, 300, F16, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 1100, F16, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 300, F16, shape=(64, 1, 0, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 100, F16, shape=(32, 1, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    assert plan(2000, 100, F16, shape=(64, 3, 0, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 100, F16, shape=(64, 1, 2, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 100, F16, shape=(0, 0, 0, 0, 7))[0] == INVALID
-    # 8 groups per row: a run of 3, 3 and 2
+    # 8 groups per row: one run of all 8 (2032 bytes, two vectors per lane)
     st, p = plan(50000, 127, BF16, groups=8)
-    assert (p["kernel_name"], p["groups_per_run"], p["workgroups"]) == ("run", 3, 50000 * 3)
+    assert (p["kernel_name"], p["groups_per_run"], p["workgroups"]) == ("run", 8, 50000)
+    # 24 groups per row: three runs of 8
+    st, p = plan(50000, 127, BF16, groups=24)
+    assert (p["kernel_name"], p["groups_per_run"], p["workgroups"]) == ("run", 8, 50000 * 3)
 
 
 def test_rows_split_over_launches(g):

@@ -57,11 +57,11 @@ CASES = [
     (BF16, 4096, 3, 8, FLAG_RI),      # BLOCK 256 x 2, one full block
     (F32, 64, 20, 10, 0),             # f32, 16 lanes
     (F16, 128, 60, 12, FLAG_NBG),     # norm first, per-column weight
-    (F16, 100, 48, 300, FLAG_RI),     # packed groups (200 bytes): 8 lanes x 2, one-wave workgroups
+    (F16, 100, 48, 300, FLAG_RI),     # packed groups (200 bytes): 16 lanes x 1, one-wave workgroups
     (F16, 100, 48, 1100, FLAG_RI),    # packed groups, a larger job (16 lanes x 1)
     (BF16, 99, 48, 1500, FLAG_RI),    # packed groups in 2-byte pieces, a large job: 16 x 1
                                       # with boundary vectors merged inside each wave
-    (BF16, 127, 48, 1500, FLAG_RI),   # half-full 32-lane segments, a large job: runs of 3
+    (BF16, 127, 48, 1500, FLAG_RI),   # half-full 32-lane segments, a large job: runs of 8
     (BF16, 128, 60, 21, FLAG_RI | FLAG_PER_GROUP),  # shared weight: row-major by default
 ]
 VARIANTS = [ROWS, ROWS | WAVE4, ROWS | WAVE1, BANDED, BANDED | WAVE1, BANDED | WAVE4, WAVE1, WAVE4]

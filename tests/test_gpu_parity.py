@@ -328,9 +328,12 @@ def test_runs_of_packed_groups(g, orc, G, dtype):
     """Runs of packed groups per wave (forced; the library takes them for large
     jobs): rows of 1, 2, 3 and 5 times the fewest groups that make a 16-byte
     aligned row, and about 48 groups -- so runs of fewer groups than a full
-    run, a short last run, several full runs; both operators; out rows padded
-    and guarded, nothing outside the view written; the banded and the
-    row-major tile order give the same bits."""
+    run, a short last run, several full runs; one and two vectors per lane
+    and the library's run length (runs that start on a vector boundary or
+    share one with each neighbour); both operators; out rows padded and
+    guarded, nothing outside the view written.  A group's sum is its
+    vectors' shares added in vector order whatever the run, so every run
+    length, vector count and tile order gives the same bits."""
     esz = 4 if dtype == F32 else 2
     period = 16 // math.gcd(G * esz, 16)  # groups per 16-byte aligned row length
     for groups in sorted({period, 2 * period, 3 * period, 5 * period, 48 // period * period}):
@@ -345,16 +348,29 @@ def test_runs_of_packed_groups(g, orc, G, dtype):
         for r in range(rows):
             view[guard + r * so: guard + r * so + width] = True
         yd, gd, wd = dev_buf(y, dtype), dev_buf(gt, dtype), torch.from_numpy(w).cuda()
+        shapes = [(0, 0, 0, 0, g.KERNEL_RUN)]
+        od = dev_buf(ob, dtype)
+        for v in (1, 2):
+            shape = (64, v, 0, 0, g.KERNEL_RUN)
+            st, _ = g.ggrms_plan_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(),
+                                       od[guard:].data_ptr(), rows, width, G, width, width, so,
+                                       1e-5, dtype, 0, shape)
+            if st == g.SUCCESS:
+                shapes.append(shape)
+            else:  # two groups do not fit one vector per lane
+                assert st == g.ERROR_NOT_SUPPORTED and v == 1, (st, G, dtype)
         for flags in ((FLAG_RI,) if dtype != F32 else (0,)) + (FLAG_NBG,):
             outs = []
-            for order in (0, 32, 64):  # the library's order, row-major, banded
-                od = dev_buf(ob, dtype)
-                say(f"case run G={G} dtype={DT_IDS[dtype]} groups={groups} flags={flags} order={order}")
-                st = run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
-                             dtype, 0, shape=(0, 0, 0, 0, g.KERNEL_RUN), flags=flags | order)
-                assert st == g.SUCCESS, g.ggrms_status_string(st)
-                torch.cuda.synchronize()
-                outs.append(host_bits(od, dtype))
+            for shape in shapes:
+                for order in (0, 32, 64):  # the library's order, row-major, banded
+                    od = dev_buf(ob, dtype)
+                    say(f"case run G={G} dtype={DT_IDS[dtype]} groups={groups} flags={flags} "
+                        f"shape={shape[:2]} order={order}")
+                    st = run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
+                                 dtype, 0, shape=shape, flags=flags | order)
+                    assert st == g.SUCCESS, g.ggrms_status_string(st)
+                    torch.cuda.synchronize()
+                    outs.append(host_bits(od, dtype))
             got = outs[0]
             assert all(np.array_equal(o.view(np.uint8), got.view(np.uint8)) for o in outs[1:])
             assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
@@ -443,14 +459,15 @@ def test_runs_in_place_and_by_default(g, orc):
     torch.cuda.synchronize()
     assert_parity(host_bits(fd, F16), ref, F16, "run in place")
     # 1500 rows x 48 groups of 127 bf16 (2-byte pieces, 15.9 vectors on 32 lanes) = 36000
-    # waves: runs of 3 by default
+    # waves: by default runs of 8 groups (2032 bytes: 127 vectors, two per lane, every
+    # run starting on a vector boundary)
     rows, G = 1500, 127
     width = 48 * G
     y, gt, w = random_case(rows, width, BF16, seed=94)
     yd, gd, wd = dev_buf(y, BF16), dev_buf(gt, BF16), torch.from_numpy(w).cuda()
     od = torch.empty_like(yd)
     p = _plan_of(g, yd, gd, wd, od, rows, width, G, width, width, width, BF16, FLAG_RI)
-    assert (p["kernel_name"], p["groups_per_run"]) == ("run", 3), p
+    assert (p["kernel_name"], p["groups_per_run"], p["vectors_per_lane"]) == ("run", 8, 2), p
     say("case run by default, 1500 x 6096 bf16")
     assert run_gpu(g, yd, gd, wd, od, rows, width, G, width, width, width, 1e-5, BF16, 1) == g.SUCCESS
     torch.cuda.synchronize()
