@@ -83,6 +83,28 @@ template <int N> __device__ inline void load_weights(const float* p, float (&w)[
     }
 }
 
+// The N weights of a packed vector when one [G] weight is shared by every
+// group, piece by piece: piece q (PE elements) of the vector is columns
+// base + q*PE .. + PE - 1 of its group, inside [0, G) for the pieces the unit
+// owns; a neighbour's piece of a boundary vector (never stored by this unit)
+// reads a clamped place.  G and the vector's start are multiples of PE, so
+// every piece's weights are PE consecutive floats aligned to 4*PE bytes: two
+// 16-byte loads per 16-byte vector of 16-bit values for 8-byte pieces (as
+// with a weight per column), 8-byte loads for 4-byte pieces, one 4-byte load
+// per element for 2-byte pieces.
+template <int N, int PE> __device__ inline void load_weights_shared(const float* w, int32_t base,
+                                                                    int32_t G, float (&r)[N]) {
+#pragma unroll
+    for (int q = 0; q < N / PE; ++q) {
+        int32_t i = base + q * PE;
+        i = i < 0 ? 0 : (i > G - PE ? G - PE : i);
+        float piece[PE];
+        load_weights<PE>(w + i, piece);
+#pragma unroll
+        for (int e = 0; e < PE; ++e) r[q * PE + e] = piece[e];
+    }
+}
+
 // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15): gfx9 encoding (vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) -- waits for vector memory only.
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -234,6 +256,15 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
     float wr[VPT][N];
     uint32_t ci[VPT];
     int32_t rel[VPT];  // packed: column of the vector's first element minus col0
+    // packed groups with one shared [G] weight: weights by element (see
+    // load_weights_shared); otherwise the vector's N consecutive weights
+    const bool wshared = kPacked && (a.bits & kBitShared) != 0;
+    auto weights_of = [&](int k, float (&r)[N]) {
+        if (kPacked && wshared)
+            load_weights_shared<N, (PE < N ? PE : N)>(a.w, rel[k], (int32_t)a.G, r);
+        else
+            load_weights<N>(wp + (int64_t)ci[k] * N, r);
+    };
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const uint32_t idx = sl + k * SEG;
@@ -241,8 +272,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
         rel[k] = kPacked ? (int32_t)((int64_t)ci[k] * N - col0) : 0;
         yr[k] = load_stream<NT>(yv + ci[k]);
         gr[k] = load_stream<NT>(gv + ci[k]);
-        if constexpr (WS == WSource::Global && !kLateWeights)
-            load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
+        if constexpr (WS == WSource::Global && !kLateWeights) weights_of(k, wr[k]);
     }
     // whether piece q of vector k belongs to the unit (packed groups only)
     auto owned = [&](int k, int q) { return (uint32_t)(rel[k] + q * PE) < a.G; };
@@ -258,7 +288,7 @@ __device__ __forceinline__ void unit_pass(const KArgs& a, uint32_t n, uint32_t g
         for (int k = 0; k < VPT; ++k) load_weights<N>(wl + ci[k] * N, wr[k]);  // v0 == 0 here
     } else if constexpr (kLateWeights) {
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) load_weights<N>(wp + (int64_t)ci[k] * N, wr[k]);
+        for (int k = 0; k < VPT; ++k) weights_of(k, wr[k]);
     }
 
     // Wait for every load (the weights included) before the first store:

@@ -301,15 +301,20 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     // the vectors holding any of its elements -- at most
     // ceil((16 - pb + group bytes) / 16), since group starts fall on
     // multiples of pb = gcd(group bytes, 16) -- and stores boundary vectors in
-    // pb-byte pieces.  Only with a per-column weight (its vectors then line up
-    // with the data's) and groups of more than one vector.
+    // pb-byte pieces.  For groups of more than one vector.  A per-column
+    // weight must be 16-byte aligned (its vectors then line up with the
+    // data's); one [G] weight shared by every group is read piece by piece
+    // (a packed vector's weights wrap around the shared vector), each piece's
+    // pb / esize weights in one load, so it must be aligned to that many
+    // floats.
     const int64_t gbytes = group_size * esize;
+    const bool shared_w = (flags & GGRMS_FLAG_WEIGHT_PER_GROUP) != 0;
+    int64_t gcd = 16;
+    while (gbytes % gcd) gcd >>= 1;
     if (vb < 16 && (!force_vb || force_vb == 16) && gbytes > 16 && row_bytes % 16 == 0 &&
         py % 16 == 0 && pg % 16 == 0 &&
-        po % 16 == 0 && by % 16 == 0 && bg % 16 == 0 && bo % 16 == 0 && pw % 16 == 0 &&
-        !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP)) {
-        int64_t gcd = 16;
-        while (gbytes % gcd) gcd >>= 1;
+        po % 16 == 0 && by % 16 == 0 && bg % 16 == 0 && bo % 16 == 0 &&
+        pw % (shared_w ? 4 * gcd / esize : 16) == 0) {
         const int64_t nvp = (16 - gcd + gbytes + 15) / 16;
         if (nvp <= kMaxPackedVectors) {
             vb = 16;

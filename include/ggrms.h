@@ -171,9 +171,10 @@ typedef struct {
  * (16, 8, 4 or 2 bytes) that the three base pointers, their row strides, the
  * group's byte length and the weight's alignment allow.  When the group's
  * byte length is not a multiple of 16 (say 100 fp16 values, 200 bytes) but
- * more than 16, and the rows are: every base pointer and row stride and the
- * weight 16-byte aligned, width * element size a multiple of 16, one weight
- * per column -- the groups are "packed": 16-byte vectors are counted from
+ * more than 16, and the rows are: every base pointer and row stride 16-byte
+ * aligned, width * element size a multiple of 16, and a per-column weight
+ * 16-byte aligned or one weight shared by every group (read by element) --
+ * the groups are "packed": 16-byte vectors are counted from
  * the start of the row, a vector on a group boundary is read by both groups
  * (each uses its own elements) and written in pieces of
  * piece_bytes = gcd(group bytes, 16), so no element is written twice and no

@@ -510,9 +510,10 @@ def test_packed_groups_plan(g, G, dtype, pb, nvec):
 
 def test_packed_groups_need_aligned_rows(g):
     """The packed path only when every row is 16-byte aligned and a multiple
-    of 16 bytes long, the weight is per column and 16-byte aligned, and a
-    group is more than one vector and at most 2048 vectors; otherwise the
-    widest vector the group allows."""
+    of 16 bytes long, the weight is per column and 16-byte aligned or one
+    weight is shared by every group (any 4-byte alignment), and a group is
+    more than one vector and at most 2048 vectors; otherwise the widest
+    vector the group allows."""
     G = 100
     ok = _plan(g, 7, 16 * G, G, F16)
     assert (ok["vector_bytes"], ok["piece_bytes"]) == (16, 8)
@@ -526,11 +527,21 @@ def test_packed_groups_need_aligned_rows(g):
     # weight only 8-byte aligned: 4-byte vectors (two fp16 values, two 4-byte weights)
     p = _plan(g, 7, 16 * G, G, F16, w=A + (2 << 30) + 8)
     assert (p["vector_bytes"], p["piece_bytes"]) == (4, 4)
-    # one weight per group position (shared by every group)
-    st, p = _plan_ex(g, PER_GROUP, rows=7, width=16 * G, group_size=G, y_row_stride=16 * G,
-                     gate_row_stride=16 * G, out_row_stride=16 * G, dtype=F16,
-                     gate=A + (1 << 26), norm_weight=A + (2 << 26), out=A + (3 << 26))
-    assert st == OK and p["vector_bytes"] == 8
+    # one weight per group position (shared by every group), read piece by piece: packed
+    # when the weight is aligned to a piece's weights (8-byte pieces: 4 floats, 16 bytes;
+    # 2-byte pieces of 127 bf16: one float)
+    for Gs, dt, woff, packed in ((G, F16, 0, True), (G, F16, 8, False), (127, BF16, 4, True)):
+        st, p = _plan_ex(g, PER_GROUP, rows=7, width=16 * Gs, group_size=Gs,
+                         y_row_stride=16 * Gs, gate_row_stride=16 * Gs, out_row_stride=16 * Gs,
+                         dtype=dt, gate=A + (1 << 26), norm_weight=A + (2 << 26) + woff,
+                         out=A + (3 << 26))
+        assert st == OK and (p["vector_bytes"] == 16 and p["piece_bytes"] < 16) == packed, \
+            (Gs, woff, p)
+    # ... but never in runs
+    st, p = _plan_ex(g, PER_GROUP | RI, rows=30000, width=16 * 127, group_size=127,
+                     y_row_stride=16 * 127, gate_row_stride=16 * 127, out_row_stride=16 * 127,
+                     dtype=BF16, gate=A + (1 << 28), norm_weight=A + (2 << 28), out=A + (3 << 28))
+    assert st == OK and (p["kernel_name"], p["piece_bytes"]) == ("wave", 2)
     # groups of at most one vector (14 bytes)
     assert _plan(g, 7, 16 * 7, 7, BF16)["vector_bytes"] == 2
     # 16381 bf16 = 32762 bytes: 2049 vectors, above the packed limit

@@ -8,6 +8,8 @@ forced).
 Same bar as the gate-first tests: f32 within a relative 1e-5 of the oracle,
 fp16/bf16 within 2 units in the last place, NaN where the oracle has NaN.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -326,3 +328,63 @@ def test_torch_wrapper_nbg(g, orc):
     with pytest.raises(g.GgrmsError):
         g.forward(y, gate, w_head, C, round_intermediate=True, norm_before_gate=True)
     assert g.plan(y, gate, w_head, C, norm_before_gate=True)["kernel_name"] == "wave"
+
+
+PACKED_SHARED_CASES = [(100, F16), (99, BF16), (127, BF16), (250, F16), (13, F16), (9, BF16),
+                       (1001, BF16), (25, F32), (99, F32)]
+
+
+@pytest.mark.parametrize("G,dtype", PACKED_SHARED_CASES,
+                         ids=[f"G{G}-{DT_IDS[d]}" for G, d in PACKED_SHARED_CASES])
+def test_packed_groups_shared_weight(g, orc, G, dtype):
+    """Packed groups (byte length not a multiple of 16, rows that are) with one
+    weight of group_size values shared by every group, read piece by piece:
+    both operators, the library's shape in row-major and banded order (same
+    bits), out rows padded and guarded, nothing outside the view written; a
+    weight 4 bytes past an alignment boundary too (packed where a piece's
+    weights are one float, narrower vectors otherwise)."""
+    groups, rows = 16, (5 if G <= 1001 else 3)
+    width = G * groups
+    esz = 4 if dtype == F32 else 2
+    so = width + 16 // esz
+    guard = 64
+    y, gt, _ = random_case(rows, width, dtype, seed=G * 11 + dtype)
+    w = S.tensor(G * 11 + dtype, S.TID_W, G, F32, ("uniform", 0.5, 1.5))
+    canary = {F32: np.float32(-1234.5), F16: np.uint16(0x7BFF), BF16: np.uint16(0x4B4B)}[dtype]
+    ob = np.full(guard + (rows - 1) * so + width + guard, canary, dtype=S.storage_dtype(dtype))
+    view = np.zeros(ob.shape, dtype=bool)
+    for r in range(rows):
+        view[guard + r * so: guard + r * so + width] = True
+    yd, gd = dev_buf(y, dtype), dev_buf(gt, dtype)
+    wbuf = torch.zeros(G + 1, dtype=torch.float32, device="cuda")
+    wbuf[1:] = torch.from_numpy(w).cuda()
+    w_off = wbuf[1:]                       # 4 bytes past an allocation boundary
+    w_al = torch.from_numpy(w).cuda()      # aligned as allocated
+    pe = math.gcd(G * esz, 16) // esz      # weights per piece
+    gate_first = FLAG_RI if dtype != F32 else 0
+    for wd, base in ((w_al, gate_first), (w_off, gate_first), (w_al, FLAG_NBG), (w_off, FLAG_NBG)):
+        flags = base | FLAG_PER_GROUP
+        ref = orc.forward(y, gt, w, rows=rows, width=width, group_size=G, y_row_stride=width,
+                          gate_row_stride=width, out_row_stride=so, eps=1e-5, dtype=dtype,
+                          round_intermediate=base & FLAG_RI, norm_before_gate=bool(base & FLAG_NBG),
+                          weight_per_group=True, out=ob.copy(), out_offset=guard)
+        outs = []
+        for order in (0, 32, 64):  # the library's order, row-major, banded
+            od = dev_buf(ob, dtype)
+            st, p = g.ggrms_plan_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(),
+                                       od[guard:].data_ptr(), rows, width, G, width, width, so,
+                                       1e-5, dtype, flags | order)
+            aligned = wd.data_ptr() % (4 * pe) == 0
+            assert st == g.SUCCESS and (p["vector_bytes"] == 16 and p["piece_bytes"] < 16) == \
+                aligned, p
+            say(f"case packed shared weight G={G} dtype={DT_IDS[dtype]} flags={flags} "
+                f"order={order} {p['kernel_name']} {p['lanes_per_group']}x{p['vectors_per_lane']}")
+            assert run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
+                           dtype, 0, flags=flags | order) == g.SUCCESS
+            torch.cuda.synchronize()
+            got = host_bits(od, dtype)
+            assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
+                "stores touched elements outside the view"
+            outs.append(got)
+        assert all(np.array_equal(o.view(np.uint8), outs[0].view(np.uint8)) for o in outs[1:])
+        assert_parity(outs[0][view], ref[view], dtype, f"packed shared G={G} flags={flags}")
