@@ -481,8 +481,11 @@ SHAPES = [
     ("fp16 G256 heads, shared head weight", 1, 256, 8192, 4),
     ("f32 G128 heads, shared head weight", 0, 128, 4096, 4),
     ("fp16 G100 packed groups, per-column weight", 1, 100, 4800, 1),
+    ("fp16 G100 packed groups, shared head weight", 1, 100, 4800, 1 | 4),
     ("bf16 G99 packed groups (2-byte pieces)", 2, 99, 4752, 1),
     ("bf16 G127 packed groups (runs of 8)", 2, 127, 6096, 1),
+    ("bf16 G127 packed groups, shared head weight", 2, 127, 6096, 1 | 4),
+    ("fp16 G13 packed groups (runs of 32)", 1, 13, 4992, 1),
     ("fp16 G250 packed groups (4-byte pieces)", 1, 250, 12000, 1),
     # the same groups in rows padded by 4 elements: rows not 16-byte aligned,
     # so the whole group falls back to 8-byte vectors

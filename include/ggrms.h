@@ -163,7 +163,7 @@ typedef struct {
     int32_t super_tile;       /* XCD-banded order: consecutive tiles of a row dealt to one
                                  XCD together, so that tiles sharing cache lines meet in
                                  one L2 (> 1 only for packed groups in one-wave WAVE
-                                 workgroups); 1 otherwise */
+                                 workgroups or in runs); 1 otherwise */
 } ggrms_plan_t;
 
 /*

@@ -341,11 +341,11 @@ def test_tile_order_and_wave_workgroups(g):
             p["workgroups"], p["tile_order"], p["super_tile"]) == ("wave", 16, 1, 0, 1024 * 12, 1, 4)
     # 127-wide bf16 groups (15.9 vectors on 32 lanes, half-full segments): runs of 8 groups
     # (2032 bytes, 127 vectors: two per lane, every run on a vector boundary), 6 runs per
-    # row, not a multiple of the 8 XCDs -> banded
+    # row, banded in super-tiles of 2 runs (8 would make whole 128-byte lines, 2 divides 6)
     p = plan(RI, 1024, 48 * 127, 127, BF16)
     assert (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"], p["groups_per_run"],
             p["block_threads"], p["workgroups"], p["tile_order"], p["super_tile"]) == \
-        ("run", 64, 2, 8, 64, 1024 * 6, 1, 1)
+        ("run", 64, 2, 8, 64, 1024 * 6, 1, 2)
     # 40 such groups per row: 5 runs -> banded
     p = plan(RI, 1024, 40 * 127, 127, BF16)
     assert (p["kernel_name"], p["workgroups"], p["tile_order"]) == ("run", 1024 * 5, 1)
