@@ -143,3 +143,119 @@ def test_random_configuration(g, orc, i):
     assert np.array_equal(got[outside].view(bits), before[outside].view(bits)), \
         f"case {i}: elements outside the view changed"
     assert_parity(got[view], ref[view], dtype, f"random case {_case_id(i)}")
+
+
+N_PACKED_CASES = 96
+KERNEL_RUN = 4
+
+
+def draw_packed(i: int) -> dict:
+    """A packed layout: 16-byte aligned rows whose groups are not a whole number
+    of 16-byte vectors (more than one vector each), in runs of groups or on
+    lane segments, with a per-column weight or one shared by every group."""
+    rng = np.random.default_rng(77003 + 104729 * i)
+    dtype = int(rng.choice([F32, F16, BF16]))
+    esz = 4 if dtype == F32 else 2
+    while True:
+        G = int(rng.integers(17 // esz + 1, 700 if dtype != F32 else 300))
+        if (G * esz) % 16:
+            break
+    pb = int(np.gcd(G * esz, 16))
+    period = 16 // pb  # groups that make a 16-byte aligned row
+    kmax = max(1, min(96 // period, 16384 // (G * period)))  # rows of at most 16384 elements
+    groups = period * int(rng.integers(1, kmax + 1))
+    rows = int(rng.choice([1, 2, 3, 7, 33, 130, 600]))
+    nbg = bool(rng.random() < 0.3)
+    ri = 0 if (nbg or dtype == F32) else int(rng.random() < 0.7)
+    per_group = bool(groups > 1 and rng.random() < 0.3)
+    shape = ["default", "run", "run1", "run2", "wave"][int(rng.integers(0, 5))]
+    if per_group and shape.startswith("run"):
+        shape = "default"
+    flags = ((FLAG_RI if ri else 0) | (FLAG_NBG if nbg else 0) |
+             (FLAG_PER_GROUP if per_group else 0) |
+             int(rng.choice([0, ORDER_ROWS, ORDER_BANDED])) | int(rng.choice([0, WAVE_FOUR])))
+    pad16 = 16 // esz  # a row stride padded by whole 16-byte vectors keeps rows aligned
+    pads = tuple(int(v) * pad16 for v in rng.integers(0, 3, 3))
+    offs = tuple(int(v) * pad16 for v in rng.integers(0, 3, 3))
+    inplace = str(rng.choice(["none", "gate"], p=[0.85, 0.15]))
+    return dict(i=i, dtype=dtype, G=G, groups=groups, rows=rows, flags=flags, ri=ri, nbg=nbg,
+                per_group=per_group, shape=shape, pads=pads, offs=offs, inplace=inplace,
+                eps=float(rng.choice([1e-5, 1e-6])))
+
+
+def _packed_id(i):
+    c = draw_packed(i)
+    return (f"{i}-{DT_IDS[c['dtype']]}-G{c['G']}x{c['groups']}-r{c['rows']}-f{c['flags']}-"
+            f"{c['shape']}-{c['inplace']}")
+
+
+@pytest.mark.parametrize("i", range(N_PACKED_CASES), ids=_packed_id)
+def test_random_packed_configuration(g, orc, i):
+    """Packed groups under seeded random launch choices (the library's, runs
+    with its or a forced vector count, lane segments with boundaries merged)
+    against the oracle, guard bands and padding untouched; the plan must be
+    packed, and the forced kernel family the one that runs."""
+    c = draw_packed(i)
+    dtype, G, rows = c["dtype"], c["G"], c["rows"]
+    esz = 4 if dtype == F32 else 2
+    width = G * c["groups"]
+    oy, og, oo = c["offs"]
+    sy, sg, so = width + c["pads"][0], width + c["pads"][1], width + c["pads"][2]
+    if c["inplace"] == "gate":
+        oo, so = og, sg
+    n_y = oy + (rows - 1) * sy + width
+    n_g = og + (rows - 1) * sg + width
+    seed = 9000 + i
+    yb = S.tensor(seed, S.TID_Y, n_y, dtype, ("normal", 1.0))
+    gb = S.tensor(seed, S.TID_GATE, n_g, dtype, ("normal", 2.0))
+    wlen = G if c["per_group"] else width
+    w = S.tensor(seed, S.TID_W, wlen, F32, ("uniform", 0.5, 1.5))
+    yd, gd = dev_buf(yb, dtype), dev_buf(gb, dtype)
+    wd = torch.from_numpy(w).cuda()
+    if c["inplace"] == "gate":
+        od, base, before, o_at = gd, 0, gb, oo
+    else:
+        n_o = oo + (rows - 1) * so + width
+        before = np.full(GUARD + n_o + GUARD, CANARY[dtype], dtype=S.storage_dtype(dtype))
+        od, base, o_at = dev_buf(before, dtype), GUARD, GUARD + oo
+    ptrs = (yd[oy:].data_ptr(), gd[og:].data_ptr(), wd.data_ptr(), od[base + oo:].data_ptr())
+    shape = {"default": None, "run": (0, 0, 0, 0, KERNEL_RUN), "run1": (64, 1, 0, 0, KERNEL_RUN),
+             "run2": (64, 2, 0, 0, KERNEL_RUN), "wave": None}[c["shape"]]
+    st, p = g.ggrms_plan_tuned(*ptrs, rows, width, G, sy, sg, so, c["eps"], dtype, c["flags"])
+    assert st == g.SUCCESS, g.ggrms_status_string(st)
+    assert p["vector_bytes"] == 16 and p["piece_bytes"] < 16, p
+    if c["shape"] == "wave" and p["lanes_per_group"] <= 64:
+        lanes = 1
+        while lanes < p["lanes_per_group"] * p["vectors_per_lane"]:
+            lanes *= 2
+        shape = (lanes, 1)
+    if shape is not None:
+        st2, p2 = g.ggrms_plan_tuned(*ptrs, rows, width, G, sy, sg, so, c["eps"], dtype,
+                                     c["flags"], shape)
+        if st2 != g.SUCCESS:  # a run that two groups do not fit, a segment past 64 lanes
+            assert st2 == g.ERROR_NOT_SUPPORTED, g.ggrms_status_string(st2)
+            shape, p2 = None, p
+        p = p2
+    say(f"case random packed {_packed_id(i)} offs={(oy, og, oo)} strides={(sy, sg, so)} "
+        f"plan={p['kernel_name']} {p['lanes_per_group']}x{p['vectors_per_lane']} "
+        f"runs of {p['groups_per_run']}")
+    if shape is not None and len(shape) == 5:
+        assert p["kernel_name"] == "run", p
+    st = g.ggrms_forward_tuned(*ptrs, rows, width, G, sy, sg, so, c["eps"], dtype, c["flags"],
+                               torch.cuda.current_stream().cuda_stream, shape)
+    assert st == g.SUCCESS, g.ggrms_status_string(st)
+    torch.cuda.synchronize()
+    got = host_bits(od, dtype)
+    ref = before.copy()
+    orc.forward(yb, gb, w, rows=rows, width=width, group_size=G, y_row_stride=sy,
+                gate_row_stride=sg, out_row_stride=so, eps=c["eps"], dtype=dtype,
+                round_intermediate=c["ri"], norm_before_gate=c["nbg"],
+                weight_per_group=c["per_group"], out=ref, y_offset=oy, gate_offset=og,
+                out_offset=o_at)
+    view = np.zeros(ref.shape, dtype=bool)
+    for r in range(rows):
+        view[o_at + r * so:o_at + r * so + width] = True
+    bits = np.uint32 if dtype == F32 else np.uint16
+    assert np.array_equal(got[~view].view(bits), before[~view].view(bits)), \
+        f"case {i}: elements outside the view changed"
+    assert_parity(got[view], ref[view], dtype, f"random packed case {_packed_id(i)}")
