@@ -473,6 +473,8 @@ SHAPES = [
     ("bf16 G3584, 2 groups of a 7168-wide row", 2, 3584, 7168, 1),
     ("bf16 G5120, one group per row", 2, 5120, 5120, 1),
     ("bf16 G8192, one group per row", 2, 8192, 8192, 1),
+    ("bf16 G12288, one group per row", 2, 12288, 12288, 1),
+    ("bf16 G16384, one group per row", 2, 16384, 16384, 1),
     ("fp16 G128 heads, per-column weight", 1, 128, 8192, 0),
     ("bf16 G128, 60 groups of a 7680-wide row, per-column weight", 2, 128, 7680, 1),
     ("bf16 G128, 64 groups of a 8192-wide row, per-column weight", 2, 128, 8192, 1),

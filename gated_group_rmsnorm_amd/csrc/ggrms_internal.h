@@ -113,7 +113,9 @@ inline bool shape_supported(int kernel, int lanes, int vpt) {
         return lanes == 64 && (vpt == 1 || vpt == 2);
     case GGRMS_KERNEL_ROWS:
         return (lanes == 256 && vpt == 3) ||
-               ((lanes == 320 || lanes == 384 || lanes == 448 || lanes == 512) && vpt == 2);
+               ((lanes == 320 || lanes == 384 || lanes == 448 || lanes == 512 || lanes == 768 ||
+                 lanes == 1024) &&
+                vpt == 2);
     default:
         return false;
     }

@@ -608,7 +608,7 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
         store(std::false_type{});
 }
 
-// ROWS: wide groups (513-1024 16-byte vectors) in large jobs.  The grid is
+// ROWS: wide groups (513-2048 16-byte vectors) in large jobs.  The grid is
 // one workgroup per compute unit (a.xc = S rows per group): workgroup b takes
 // group b % groups and rows b / groups, + S, + 2S, ...  Its SEG lanes hold VPT
 // vectors of a row each (the slots and the order of the sums are those of
@@ -828,6 +828,7 @@ inline const void* pick_vb(int kernel, int lanes, int vpt, int upb) {
     if (lanes == L && vpt == V) \
     return reinterpret_cast<const void*>(&ggrms_rows_kernel<T, L, V, NBG, NT>)
             GG_R(256, 3); GG_R(320, 2); GG_R(384, 2); GG_R(448, 2); GG_R(512, 2);
+            GG_R(768, 2); GG_R(1024, 2);
 #undef GG_R
         }
         return nullptr;

@@ -75,22 +75,30 @@ int64_t round_up_pow2(int64_t x) {
 // groups keep the narrower vectors.
 constexpr int64_t kMaxPackedVectors = 2048;
 
+// Most vectors of a group for which the library takes ROWS itself (it can
+// be forced up to 2048).
+constexpr int64_t kRowsMaxDefaultVectors = 1792;
+
 // Waves of a job that the part holds at once with room to spare (256 CUs x 4
 // SIMDs x 4 waves): such a job is a single round of loads and arithmetic.
 constexpr int64_t kSmallJobWaves = 4096;
 
-// ROWS shape for a group of nvec 16-byte vectors (nvec <= 1024): 256 lanes x
+// ROWS shape for a group of nvec 16-byte vectors (nvec <= 2048): 256 lanes x
 // 3 up to 608 vectors, above that two vectors on the next multiple of 64
-// lanes -- the fastest of the built shapes in a sweep of 377 MB single-group
-// bf16 jobs over groups of 528-1024 vectors (0.77-0.81 of HBM peak against
-// 0.74-0.77 for the BLOCK kernel's one row per workgroup; 320 x 2 on the
-// 5120-wide group: 58.6 against 63.0 us).
+// lanes up to 1024 vectors -- the fastest of the built shapes in a sweep of
+// 377 MB single-group bf16 jobs over groups of 528-1024 vectors (0.77-0.81 of
+// HBM peak against 0.74-0.77 for the BLOCK kernel's one row per workgroup;
+// 320 x 2 on the 5120-wide group: 58.6 against 63.0 us) -- and 768 or 1024
+// lanes x 2 for 1025-2048 vectors.
 void rows_shape(int64_t nvec, int* lanes, int* vpt) {
     if (nvec <= 608) {
         *lanes = 256;
         *vpt = 3;
-    } else {
+    } else if (nvec <= 1024) {
         *lanes = (int)((nvec + 127) / 128 * 64);
+        *vpt = 2;
+    } else {
+        *lanes = nvec <= 1536 ? 768 : 1024;
         *vpt = 2;
     }
 }
@@ -121,6 +129,8 @@ int kernel_for_shape(int lanes, int vpt) {
 //     0.75 against 0.67-0.71 for 512 x 3; 6 vectors take 163 VGPRs, 8 took
 //     218 and lost to 512 x 4 and 1024 x 4);
 //   * wider groups loop over the row twice (WIDE).
+// In jobs of 2048 (row, group) units or more, groups of 513-1792 vectors take
+// the ROWS kernel instead (rows_shape).
 struct ShapeRule {
     int64_t max_nvec;
     int kernel, lanes, vpt, upb;
@@ -335,7 +345,7 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     const bool run_fits = packed && gpw >= 2 && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP);
     // ROWS needs 16-byte vectors that are not packed and a launch of
     // 32-bit row indices
-    const bool rows_fit = !packed && vb == 16 && rows < ((int64_t)1 << 31) && nvec <= 1024;
+    const bool rows_fit = !packed && vb == 16 && rows < ((int64_t)1 << 31) && nvec <= 2048;
     if (shape && shape->kernel == GGRMS_KERNEL_ROWS) {
         if (!rows_fit || force_upb > 1) return GGRMS_ERROR_NOT_SUPPORTED;
         if (shape->lanes_per_group == 0 && shape->vectors_per_lane == 0) {
@@ -402,11 +412,17 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
             lanes = 64;
             vpt = run_vpt;
         } else if (kernel == GGRMS_KERNEL_BLOCK && rows_fit && nvec > 512 &&
-                   plan->groups <= kRowsWorkgroups && rows * plan->groups >= kRowsMinUnits) {
+                   nvec <= kRowsMaxDefaultVectors && plan->groups <= kRowsWorkgroups &&
+                   rows * plan->groups >= kRowsMinUnits) {
             // Wide groups in large jobs: one workgroup per compute unit
             // taking rows in turn, with the next rows' inputs in flight
             // while it stores, instead of one workgroup per row (whose
-            // loads start only when a slot frees).
+            // loads start only when a slot frees).  Groups of 1025-1792
+            // vectors on 768 or 1024 lanes x 2, 377 MB bf16 jobs against
+            // the BLOCK shapes with one row per workgroup: 9216 wide 62.8
+            // against 64.8 us, 10240 61.9 / 63.4, 12288 61.8 / 62.5, 14336
+            // 64.2 / 68.2; at 16384 (2048 vectors) BLOCK 512 x 4 stays
+            // ahead, 63.7 against 64.2.
             kernel = GGRMS_KERNEL_ROWS;
             rows_shape(nvec, &lanes, &vpt);
         }

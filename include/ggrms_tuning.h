@@ -63,7 +63,8 @@ typedef enum {
  *                     GGRMS_KERNEL_ROWS: rows in turn per workgroup, for
  *                     16-byte vectors that are not packed (lanes and vectors
  *                     0 for the library's choice, or 256 x 3, 320 x 2,
- *                     384 x 2, 448 x 2, 512 x 2; rows_per_workgroup 0 or 1)
+ *                     384 x 2, 448 x 2, 512 x 2, 768 x 2, 1024 x 2;
+ *                     rows_per_workgroup 0 or 1)
  *
  * For packed groups the shape must cover the vectors of the worst-aligned
  * group, WIDE is not built and rows_per_workgroup must be 0 or 1.

@@ -568,15 +568,15 @@ def test_packed_groups_need_aligned_rows(g):
 
 
 def test_rows_plan(g):
-    """ROWS: groups of 513-1024 16-byte vectors that are not packed, in jobs of
+    """ROWS: groups of 513-1792 16-byte vectors that are not packed, in jobs of
     at least 2048 (row, group) units with at most 256 groups per row: one
     workgroup per compute unit (256 / groups per group, at most one per row),
-    256 lanes x 3 up to 608 vectors and two vectors on the next multiple of
-    64 lanes above; one launch, no banded order.  Forced through the tuning
-    shape's kernel field for any group of at most 1024 16-byte vectors (the
-    library's lanes, or a built pair that covers the group); refused for
-    narrower vectors, packed groups, unbuilt pairs and several rows per
-    workgroup."""
+    256 lanes x 3 up to 608 vectors, two vectors on the next multiple of 64
+    lanes up to 1024, 768 x 2 up to 1536 and 1024 x 2 above; one launch, no
+    banded order.  Forced through the tuning shape's kernel field for any
+    group of at most 2048 16-byte vectors (the library's lanes, or a built
+    pair that covers the group); refused for narrower vectors, packed groups,
+    unbuilt pairs and several rows per workgroup."""
     kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
 
     def plan(rows, G, dtype=BF16, groups=1, flags=RI, shape=None, **more):
@@ -590,7 +590,10 @@ def test_rows_plan(g):
     for G, dtype, lanes, vpt in ((4104, BF16, 256, 3), (4864, BF16, 256, 3), (4872, BF16, 320, 2),
                                  (5120, BF16, 320, 2), (5128, BF16, 384, 2), (6144, F16, 384, 2),
                                  (6152, BF16, 448, 2), (7168, BF16, 448, 2), (7176, BF16, 512, 2),
-                                 (8192, BF16, 512, 2), (2560, F32, 320, 2), (4096, F32, 512, 2)):
+                                 (8192, BF16, 512, 2), (2560, F32, 320, 2), (4096, F32, 512, 2),
+                                 (8200, BF16, 768, 2), (12288, BF16, 768, 2),
+                                 (12296, BF16, 1024, 2), (14336, BF16, 1024, 2),
+                                 (7168, F32, 1024, 2)):
         st, p = plan(12288, G, dtype)
         assert st == OK and (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"],
                              p["block_threads"], p["workgroups"], p["launches"], p["tile_order"],
@@ -611,8 +614,13 @@ def test_rows_plan(g):
     assert plan(2048, 5120)[1]["kernel_name"] == "rows"
     # wider and narrower groups, narrower vectors, a strided view that is
     # not 16-byte aligned: the other kernels
-    assert plan(12288, 8200)[1]["kernel_name"] == "block"
+    assert plan(12288, 14344)[1]["kernel_name"] == "block"
+    assert plan(12288, 16384)[1]["kernel_name"] == "block"
     assert plan(12288, 4096)[1]["kernel_name"] == "block"
+    # ... but up to 2048 vectors it can be forced
+    st, p = plan(12288, 16384, shape=(0, 0, 0, 0, KERNEL_ROWS))
+    assert st == OK and (p["kernel_name"], p["lanes_per_group"], p["vectors_per_lane"]) == \
+        ("rows", 1024, 2)
     p = plan(12288, 5120, y_row_stride=5124)[1]
     assert (p["kernel_name"], p["vector_bytes"]) == ("block", 8)
     # a forced ROWS launch with fewer rows than compute units: one workgroup per row
@@ -623,9 +631,11 @@ def test_rows_plan(g):
                          p["rows_per_workgroup"]) == (256, 3, 256, 2)
     st, p = plan(300, 960, shape=(320, 2, 0, 0, KERNEL_ROWS))
     assert st == OK and (p["kernel_name"], p["lanes_per_group"]) == ("rows", 320)
-    # refusals: more than 1024 vectors, packed groups, narrower vectors, pairs
+    # refusals: more than 2048 vectors, packed groups, narrower vectors, pairs
     # not built or too small, rows per workgroup
-    assert plan(300, 8200, shape=(0, 0, 0, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 16392, shape=(0, 0, 0, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 12296, shape=(768, 2, 0, 0, KERNEL_ROWS))[0] == NOTSUP
+    assert plan(300, 12296, shape=(640, 2, 0, 0, KERNEL_ROWS))[0] == NOTSUP
     assert plan(300, 100, dtype=F16, groups=16, shape=(0, 0, 0, 0, KERNEL_ROWS))[0] == NOTSUP
     assert plan(300, 5120, shape=(0, 0, 0, 8, KERNEL_ROWS))[0] == NOTSUP
     assert plan(300, 5120, shape=(256, 4, 0, 0, KERNEL_ROWS))[0] == NOTSUP

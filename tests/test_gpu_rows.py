@@ -62,6 +62,11 @@ FORCED = [
     (300, 1, 2560, F32, (320, 2)),
     (300, 1, 4096, F32, (512, 2)),
     (300, 1, 960, BF16, (256, 3)),    # a narrow group on the widest lanes: most lanes idle
+    (300, 1, 12288, BF16, (768, 2)),  # 1536 vectors
+    (37, 1, 9216, F16, (768, 2)),     # 1152 vectors, fewer rows than compute units
+    (300, 1, 10248, BF16, (768, 2)),  # 1281 vectors: the second slot mostly idle
+    (260, 2, 16384, BF16, (1024, 2)), # 2048 vectors, 128 workgroups per group
+    (300, 1, 8192, F32, (1024, 2)),
 ]
 
 
@@ -80,7 +85,8 @@ def test_forced_rows_against_the_oracle(g, orc, rows, groups, G, dtype, shape):
 
 # the library's own choice on jobs large enough for ROWS
 AUTO = [(2048, 1, 5120, BF16, 320), (1024, 2, 4864, BF16, 256), (2100, 1, 8192, BF16, 512),
-        (2048, 1, 2560, F32, 320), (700, 3, 6152, F16, 448)]
+        (2048, 1, 2560, F32, 320), (700, 3, 6152, F16, 448), (2048, 1, 12288, BF16, 768),
+        (1100, 2, 14336, F16, 1024)]
 
 
 @pytest.mark.parametrize("rows,groups,G,dtype,lanes", AUTO,
@@ -94,8 +100,8 @@ def test_rows_by_default(g, orc, rows, groups, G, dtype, lanes):
 
 
 @pytest.mark.parametrize("lanes,vpt,G,dtype", [(256, 3, 5120, BF16), (512, 2, 8192, F16),
-                                               (256, 3, 3072, F32)],
-                         ids=["256x3-bf16", "512x2-f16", "256x3-f32"])
+                                               (256, 3, 3072, F32), (1024, 2, 16384, BF16)],
+                         ids=["256x3-bf16", "512x2-f16", "256x3-f32", "1024x2-bf16"])
 def test_rows_equals_block_bitwise(g, lanes, vpt, G, dtype):
     """Same lanes and vectors: the same slots and the same order of the sums,
     so ROWS and BLOCK (one row per workgroup) give the same bits; so do the
