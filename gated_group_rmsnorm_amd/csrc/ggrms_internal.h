@@ -79,6 +79,9 @@ constexpr uint32_t kXcds = 8;
 constexpr int kWaveBlock = 256;
 // Most groups one RUN wave takes (one lane per group forms the groups' sums).
 constexpr int kRunMaxGroups = 32;
+// A weight shared by every group is staged by the RUN wave, kRunStage floats
+// per lane: groups of at most 512 elements (two of them fill the 128 slots).
+constexpr int kRunStage = 8;
 constexpr int kWaveBlockOneWave = 64;
 constexpr int kWideBlock = 1024;
 // ROWS: one workgroup per compute unit of the part (gfx950: 256), taken for

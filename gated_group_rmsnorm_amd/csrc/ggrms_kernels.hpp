@@ -505,7 +505,12 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
     using S = typename VecWord<T::kSize>::type;
     __shared__ float share0[64 * VPT], share1[64 * VPT];
     __shared__ float nfs[kRunMaxGroups];
+    // one [G] weight shared by every group (G <= 64 * kRunStage): staged in
+    // a.G floats of dynamic LDS, fetched after the inputs and parked before
+    // the first barrier
+    extern __shared__ float wsh[];
     fetch_args_together(a);
+    const bool wshared = (a.bits & kBitShared) != 0;
 
     uint32_t n, c;  // row, run
     if (banded(a)) {
@@ -551,7 +556,15 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
         bnd[k] = (kk + 1) * G - off;
         yr[k][0] = load_stream<NT>(yv + vi[k]);
         gr[k][0] = load_stream<NT>(gv + vi[k]);
-        load_weights<N>(a.w + (int64_t)vi[k] * N, wr[k][0]);
+        if (!wshared) load_weights<N>(a.w + (int64_t)vi[k] * N, wr[k][0]);
+    }
+    float wst[kRunStage];
+    if (wshared) {
+#pragma unroll
+        for (int j = 0; j < kRunStage; ++j) {
+            const uint32_t i = l + 64u * j;
+            wst[j] = i < a.G ? a.w[i] : 0.0f;
+        }
     }
 
     epi::LaneUnit<T, VB, 1, NBG> L[VPT];
@@ -563,6 +576,11 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
             [&](int, int q) { return q * PE >= bnd[k]; }, s_k, s_k1);
         share0[l + 64u * k] = s_k;
         share1[l + 64u * k] = s_k1;
+    }
+    if (wshared) {
+#pragma unroll
+        for (int j = 0; j < kRunStage; ++j)
+            if (l + 64u * j < a.G) wsh[l + 64u * j] = wst[j];
     }
     __syncthreads();
     if ((int32_t)l < cnt) {
@@ -580,6 +598,18 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
     for (int k = 0; k < VPT; ++k) {
         nf_k[k] = kv[k] >= 0 ? nfs[kv[k]] : 0.0f;
         nf_k1[k] = kv[k] + 1 < cnt ? nfs[kv[k] + 1] : 0.0f;
+        if (wshared) {
+            // element e is column off + e of group kv, or column off + e - G
+            // of group kv + 1 (e >= bnd); a slot past the run reads a clamped
+            // place (its results are not stored)
+            const int32_t off = (int32_t)((int64_t)vi[k] * N - e0) - kv[k] * G;
+#pragma unroll
+            for (int e = 0; e < N; ++e) {
+                int32_t c = off + e - (e >= bnd[k] ? G : 0);
+                c = c < 0 ? 0 : (c >= G ? G - 1 : c);
+                wr[k][0][e] = wsh[c];
+            }
+        }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     W* ov = reinterpret_cast<W*>(static_cast<S*>(a.out) + (int64_t)n * a.so);

@@ -342,7 +342,10 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
         shape && shape->kernel == GGRMS_KERNEL_RUN ? shape->vectors_per_lane : 0;
     int run_vpt = 0;
     const int64_t gpw = packed ? run_length(gbytes, pb, force_run_vpt, &run_vpt) : 0;
-    const bool run_fits = packed && gpw >= 2 && !(flags & GGRMS_FLAG_WEIGHT_PER_GROUP);
+    // (a weight shared by every group is staged in LDS by the run's wave:
+    // groups of at most 64 x kRunStage elements)
+    const bool run_fits = packed && gpw >= 2 &&
+                          (!(flags & GGRMS_FLAG_WEIGHT_PER_GROUP) || group_size <= 64 * kRunStage);
     // ROWS needs 16-byte vectors that are not packed and a launch of
     // 32-bit row indices
     const bool rows_fit = !packed && vb == 16 && rows < ((int64_t)1 << 31) && nvec <= 2048;
@@ -547,6 +550,8 @@ ggrms_status_t make_plan(const void* y, const void* gate, const float* w, const 
     if (kernel == GGRMS_KERNEL_ROWS)
         plan->pub.rows_per_workgroup = (int32_t)((rows + plan->rows_stride - 1) / plan->rows_stride);
     plan->pub.lds_bytes = upb > 1 ? (int32_t)(group_size * 4) : 0;
+    if (kernel == GGRMS_KERNEL_RUN && (flags & GGRMS_FLAG_WEIGHT_PER_GROUP))
+        plan->pub.lds_bytes = (int32_t)(group_size * 4);  // the staged shared weight
     plan->pub.workgroups = workgroups;
     plan->pub.tile_order = plan->xband ? 1 : 0;
     plan->pub.super_tile = 1 << plan->super_shift;

@@ -537,11 +537,11 @@ def test_packed_groups_need_aligned_rows(g):
                          out=A + (3 << 26))
         assert st == OK and (p["vector_bytes"] == 16 and p["piece_bytes"] < 16) == packed, \
             (Gs, woff, p)
-    # ... but never in runs
+    # ... and in runs, which stage it in LDS (groups of at most 512 elements)
     st, p = _plan_ex(g, PER_GROUP | RI, rows=30000, width=16 * 127, group_size=127,
                      y_row_stride=16 * 127, gate_row_stride=16 * 127, out_row_stride=16 * 127,
                      dtype=BF16, gate=A + (1 << 28), norm_weight=A + (2 << 28), out=A + (3 << 28))
-    assert st == OK and (p["kernel_name"], p["piece_bytes"]) == ("wave", 2)
+    assert st == OK and (p["kernel_name"], p["piece_bytes"], p["lds_bytes"]) == ("run", 2, 127 * 4)
     # groups of at most one vector (14 bytes)
     assert _plan(g, 7, 16 * 7, 7, BF16)["vector_bytes"] == 2
     # 16381 bf16 = 32762 bytes: 2049 vectors, above the packed limit
@@ -653,8 +653,9 @@ def test_runs_of_packed_groups_plan(g):
     bytes groups) counting 0.1 more, two vectors per lane on a tie, at most
     32 groups; one-wave workgroups; forced through the tuning shape's kernel
     field (optionally with the vectors per lane) for any packed group that
-    fits twice; refused for groups that are not packed, a shared weight, or
-    groups too wide for two per wave."""
+    fits twice; refused for groups that are not packed, or
+    groups too wide for two per wave; a shared weight only for groups of at
+    most 512 elements (staged in LDS)."""
     kw = dict(gate=A + (1 << 30), norm_weight=A + (2 << 30), out=A + (3 << 30))
     def plan(rows, G, dtype, groups=16, flags=RI, shape=None):
         width = G * groups
@@ -723,7 +724,9 @@ def test_runs_of_packed_groups_plan(g):
     # refusals: aligned groups, a shared weight, a group too wide for two in 128 vectors,
     # other lane or vector shapes
     assert plan(2000, 128, F16, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
-    assert plan(2000, 100, F16, flags=RI | PER_GROUP, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
+    st, p = plan(2000, 100, F16, flags=RI | PER_GROUP, shape=(0, 0, 0, 0, KERNEL_RUN))
+    assert st == OK and (p["kernel_name"], p["lds_bytes"]) == ("run", 400)
+    assert plan(2000, 516, F16, flags=RI | PER_GROUP, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 1100, F16, shape=(0, 0, 0, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 300, F16, shape=(64, 1, 0, 0, KERNEL_RUN))[0] == NOTSUP
     assert plan(2000, 100, F16, shape=(32, 1, 0, 0, KERNEL_RUN))[0] == NOTSUP

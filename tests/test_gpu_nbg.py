@@ -338,11 +338,12 @@ PACKED_SHARED_CASES = [(100, F16), (99, BF16), (127, BF16), (250, F16), (13, F16
                          ids=[f"G{G}-{DT_IDS[d]}" for G, d in PACKED_SHARED_CASES])
 def test_packed_groups_shared_weight(g, orc, G, dtype):
     """Packed groups (byte length not a multiple of 16, rows that are) with one
-    weight of group_size values shared by every group, read piece by piece:
-    both operators, the library's shape in row-major and banded order (same
-    bits), out rows padded and guarded, nothing outside the view written; a
-    weight 4 bytes past an alignment boundary too (packed where a piece's
-    weights are one float, narrower vectors otherwise)."""
+    weight of group_size values shared by every group, read piece by piece
+    on lane segments or staged in LDS by runs of groups (the library's run,
+    one and two vectors per lane): both operators, row-major and banded order
+    (same bits), out rows padded and guarded, nothing outside the view
+    written; a weight 4 bytes past an alignment boundary too (packed where a
+    piece's weights are one float, narrower vectors otherwise)."""
     groups, rows = 16, (5 if G <= 1001 else 3)
     width = G * groups
     esz = 4 if dtype == F32 else 2
@@ -368,23 +369,33 @@ def test_packed_groups_shared_weight(g, orc, G, dtype):
                           gate_row_stride=width, out_row_stride=so, eps=1e-5, dtype=dtype,
                           round_intermediate=base & FLAG_RI, norm_before_gate=bool(base & FLAG_NBG),
                           weight_per_group=True, out=ob.copy(), out_offset=guard)
-        outs = []
-        for order in (0, 32, 64):  # the library's order, row-major, banded
-            od = dev_buf(ob, dtype)
-            st, p = g.ggrms_plan_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(),
-                                       od[guard:].data_ptr(), rows, width, G, width, width, so,
-                                       1e-5, dtype, flags | order)
-            aligned = wd.data_ptr() % (4 * pe) == 0
-            assert st == g.SUCCESS and (p["vector_bytes"] == 16 and p["piece_bytes"] < 16) == \
-                aligned, p
-            say(f"case packed shared weight G={G} dtype={DT_IDS[dtype]} flags={flags} "
-                f"order={order} {p['kernel_name']} {p['lanes_per_group']}x{p['vectors_per_lane']}")
-            assert run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
-                           dtype, 0, flags=flags | order) == g.SUCCESS
-            torch.cuda.synchronize()
-            got = host_bits(od, dtype)
-            assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
-                "stores touched elements outside the view"
-            outs.append(got)
-        assert all(np.array_equal(o.view(np.uint8), outs[0].view(np.uint8)) for o in outs[1:])
-        assert_parity(outs[0][view], ref[view], dtype, f"packed shared G={G} flags={flags}")
+        aligned = wd.data_ptr() % (4 * pe) == 0
+        # the library's shape, and runs of groups with the weight staged in LDS
+        shapes = [None] + ([(0, 0, 0, 0, g.KERNEL_RUN), (64, 1, 0, 0, g.KERNEL_RUN),
+                            (64, 2, 0, 0, g.KERNEL_RUN)] if aligned and G <= 512 else [])
+        for shape in shapes:
+            outs = []
+            for order in (0, 32, 64):  # the library's order, row-major, banded
+                od = dev_buf(ob, dtype)
+                st, p = g.ggrms_plan_tuned(yd.data_ptr(), gd.data_ptr(), wd.data_ptr(),
+                                           od[guard:].data_ptr(), rows, width, G, width, width, so,
+                                           1e-5, dtype, flags | order, shape)
+                if shape is not None and st == g.ERROR_NOT_SUPPORTED:
+                    break  # two groups do not fit one vector per lane
+                assert st == g.SUCCESS and (p["vector_bytes"] == 16 and p["piece_bytes"] < 16) == \
+                    aligned, p
+                say(f"case packed shared weight G={G} dtype={DT_IDS[dtype]} flags={flags} "
+                    f"order={order} {p['kernel_name']} {p['lanes_per_group']}x"
+                    f"{p['vectors_per_lane']} runs of {p['groups_per_run']}")
+                assert run_gpu(g, yd, gd, wd, od[guard:], rows, width, G, width, width, so, 1e-5,
+                               dtype, 0, shape=shape, flags=flags | order) == g.SUCCESS
+                torch.cuda.synchronize()
+                got = host_bits(od, dtype)
+                assert np.array_equal(got[~view].view(np.uint8), ob[~view].view(np.uint8)), \
+                    "stores touched elements outside the view"
+                outs.append(got)
+            if not outs:
+                continue
+            assert all(np.array_equal(o.view(np.uint8), outs[0].view(np.uint8)) for o in outs[1:])
+            assert_parity(outs[0][view], ref[view], dtype,
+                          f"packed shared G={G} flags={flags} shape={shape}")

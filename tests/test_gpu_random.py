@@ -169,8 +169,6 @@ def draw_packed(i: int) -> dict:
     ri = 0 if (nbg or dtype == F32) else int(rng.random() < 0.7)
     per_group = bool(groups > 1 and rng.random() < 0.3)
     shape = ["default", "run", "run1", "run2", "wave"][int(rng.integers(0, 5))]
-    if per_group and shape.startswith("run"):
-        shape = "default"
     flags = ((FLAG_RI if ri else 0) | (FLAG_NBG if nbg else 0) |
              (FLAG_PER_GROUP if per_group else 0) |
              int(rng.choice([0, ORDER_ROWS, ORDER_BANDED])) | int(rng.choice([0, WAVE_FOUR])))
