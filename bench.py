@@ -604,6 +604,15 @@ EVIDENCE = {
     # per lane (the default) and the 32-lane segments
     "packed_g127_run": (2, 10320, 6096, 127, 1, None),
     "packed_g127_wave": (2, 10320, 6096, 127, 1, (32, 1)),
+    # groups that nearly fill 32-lane segments (the library's choice) against
+    # runs of groups on two vectors per lane: 250-wide fp16 (31.3 vectors),
+    # 230-wide bf16 (28.8), 180-wide bf16 (22.5)
+    "packed_g250": (1, 5242, 12000, 250, 1, None),
+    "packed_g250_run2": (1, 5242, 12000, 250, 1, (64, 2, 0, 0, 4)),
+    "packed_g230": (2, 8548, 7360, 230, 1, None),
+    "packed_g230_run2": (2, 8548, 7360, 230, 1, (64, 2, 0, 0, 4)),
+    "packed_g180": (2, 7281, 8640, 180, 1, None),
+    "packed_g180_run2": (2, 7281, 8640, 180, 1, (64, 2, 0, 0, 4)),
 }
 
 
