@@ -859,7 +859,8 @@ int main() {
 
 def test_planner_host_sanitizers(tmp_path):
     """The planner (pure host C++) under AddressSanitizer and UBSan over a
-    sweep of shapes, strides and pointers."""
+    sweep of shapes, strides and pointers, and of packed layouts (runs,
+    shared weights, forced shapes)."""
     drv = tmp_path / "plansweep.cpp"
     drv.write_text(r'''
 #include <cstdint>
@@ -903,6 +904,26 @@ int main() {
                                (void*)(base + (2u << 28) - 2 * width * (off + 1)), rows, width,
                                G, width + off, width, 3 * width, 1e-5f, (ggrms_dtype_t)dt,
                                flags & 7, &p);
+            n_ok += st == GGRMS_SUCCESS;
+        }
+    }
+    // packed groups (16-byte aligned rows of groups that are not a whole
+    // number of vectors): runs by default and forced, shared weights, ROWS
+    const int64_t Ps[] = {9, 13, 25, 99, 100, 127, 180, 230, 250, 300, 513, 1001, 4099};
+    for (int64_t G : Ps) for (int64_t rows : {1, 5, 3000, 30000}) for (int dt = 0; dt < 3; ++dt)
+    for (uint32_t flags : {0u, 1u, 2u, 4u, 5u, 6u, 33u, 65u, 257u}) {
+        ggrms_plan_t p;
+        const int64_t width = G * 16;
+        const ggrms_shape_t shapes[] = {{0, 0, 0, 0, GGRMS_KERNEL_RUN}, {64, 1, 0, 0, GGRMS_KERNEL_RUN},
+                                        {64, 2, 0, 0, GGRMS_KERNEL_RUN}, {64, 3, 0, 0, GGRMS_KERNEL_RUN},
+                                        {0, 0, 0, 0, GGRMS_KERNEL_ROWS}, {16, 1, 0, 0, 0},
+                                        {8, 2, 0, 0, 0}, {0, 0, 0, 0, 0}};
+        for (int woff : {0, 4, 8})
+        for (const ggrms_shape_t& sh : shapes) {
+            ggrms_status_t st = ggrms_plan_tuned(
+                (void*)base, (void*)(base + (1u << 28)), (const float*)(base + (2u << 28) + woff),
+                (void*)(base + (3u << 28)), rows, width, G, width, width, width, 1e-5f,
+                (ggrms_dtype_t)dt, flags, &sh, &p);
             n_ok += st == GGRMS_SUCCESS;
         }
     }
