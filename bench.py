@@ -613,6 +613,16 @@ EVIDENCE = {
     "packed_g230_run2": (2, 8548, 7360, 230, 1, (64, 2, 0, 0, 4)),
     "packed_g180": (2, 7281, 8640, 180, 1, None),
     "packed_g180_run2": (2, 7281, 8640, 180, 1, (64, 2, 0, 0, 4)),
+    # more groups on 32-lane segments with 4-byte pieces: 222-wide bf16 (27.8
+    # vectors), 210-wide fp16 (26.3), 170-wide bf16 (21.3), 99-wide f32 (24.8)
+    "packed_g222": (2, 8856, 7104, 222, 1, None),
+    "packed_g222_run2": (2, 8856, 7104, 222, 1, (64, 2, 0, 0, 4)),
+    "packed_g210": (1, 8322, 7560, 210, 1, None),
+    "packed_g210_run2": (1, 8322, 7560, 210, 1, (64, 2, 0, 0, 4)),
+    "packed_g170": (2, 8411, 7480, 170, 1, None),
+    "packed_g170_run2": (2, 8411, 7480, 170, 1, (64, 2, 0, 0, 4)),
+    "packed_g99f32": (0, 4180, 7524, 99, 0, None),
+    "packed_g99f32_run2": (0, 4180, 7524, 99, 0, (64, 2, 0, 0, 4)),
 }
 
 
