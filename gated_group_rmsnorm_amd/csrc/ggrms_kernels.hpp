@@ -605,9 +605,9 @@ __global__ __launch_bounds__(64) void ggrms_run_kernel(KArgs a) {
             const int32_t off = (int32_t)((int64_t)vi[k] * N - e0) - kv[k] * G;
 #pragma unroll
             for (int e = 0; e < N; ++e) {
-                int32_t c = off + e - (e >= bnd[k] ? G : 0);
-                c = c < 0 ? 0 : (c >= G ? G - 1 : c);
-                wr[k][0][e] = wsh[c];
+                int32_t col = off + e - (e >= bnd[k] ? G : 0);
+                col = col < 0 ? 0 : (col >= G ? G - 1 : col);
+                wr[k][0][e] = wsh[col];
             }
         }
     }
