@@ -586,6 +586,12 @@ EVIDENCE = {
     "g5120_block": (2, 12288, 5120, 5120, 1, (256, 3, 1)),
     "g8192": (2, 7680, 8192, 8192, 1, None),
     "g8192_block": (2, 7680, 8192, 8192, 1, (256, 4, 1)),
+    # one group of 12288 per row: ROWS 768 x 2 (the default) and BLOCK 256 x 6;
+    # one group of 16384: BLOCK 512 x 4 (the default) and ROWS 1024 x 2
+    "g12288": (2, 5120, 12288, 12288, 1, None),
+    "g12288_block": (2, 5120, 12288, 12288, 1, (256, 6, 1)),
+    "g16384": (2, 3840, 16384, 16384, 1, None),
+    "g16384_rows": (2, 3840, 16384, 16384, 1, (1024, 2, 0, 0, 5)),
     # 100-wide fp16 groups (200 bytes: packed 16-byte vectors), one vector per
     # lane on 16 lanes (the library's shape) and two vectors per lane on 8
     # lanes (boundary vectors in pieces)
